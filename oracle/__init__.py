@@ -1,0 +1,13 @@
+"""CPU float64 oracle for paged attention (test infrastructure only).
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` import this package; the HIP library never does, and the two share no
+code.
+"""
+from .paged_attention import (NEG_INF, attend, bf16_to_f32, bf16_to_f64, combine, decode,
+                              dequantize_int8, empty_pool, gather, kv_write, paged_attention,
+                              quantize_int8, slot_of, split_partials, visible_mask)
+
+__all__ = ["NEG_INF", "attend", "bf16_to_f32", "bf16_to_f64", "combine", "decode",
+           "dequantize_int8", "empty_pool", "gather", "kv_write", "paged_attention",
+           "quantize_int8", "slot_of", "split_partials", "visible_mask"]

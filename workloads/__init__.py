@@ -1,0 +1,241 @@
+"""Seeded synthetic inputs for paged attention, shaped like the workloads of the
+TileInfer.jl performance page (Qwen3-4B attention at 1k/8k/32k positions) and the
+model table of the Qml-engine announcement (Llama-3.1-8B, Qwen3-30B-A3B,
+gpt-oss-20b attention shapes).
+
+This module holds no attention arithmetic: it draws random numbers, rounds them to
+bfloat16 bit patterns, draws sequence lengths and assigns pool pages to sequences.
+Writing tokens into pages, quantising, and attending are done separately by the
+CPU oracle (``oracle/``) and by the HIP library; both consume what is built here.
+
+Every array is numpy.  bfloat16 tensors are carried as ``uint16`` bit patterns.
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+from typing import Optional
+
+import numpy as np
+
+BF16_NAN = np.uint16(0x7FC0)
+
+
+def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round float32 values to the nearest bfloat16 (ties to even); return bit patterns."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    b = x.view(np.uint32)
+    r = (b + np.uint32(0x7FFF) + ((b >> np.uint32(16)) & np.uint32(1))) >> np.uint32(16)
+    return r.astype(np.uint16)
+
+
+def normal_bf16(rng: np.random.Generator, shape, outlier_frac: float = 0.0,
+                outlier_mag: float = 8.0) -> np.ndarray:
+    """N(0,1) float32 draws rounded to bfloat16 bits.  With ``outlier_frac`` > 0 each
+    element is independently replaced, with that probability, by +-outlier_mag
+    (fair sign) before rounding (outlier_mag must be exact in bfloat16)."""
+    x = rng.standard_normal(size=shape, dtype=np.float32)
+    if outlier_frac > 0.0:
+        hit = rng.random(size=shape, dtype=np.float32) < np.float32(outlier_frac)
+        sign = np.where(rng.random(size=shape, dtype=np.float32) < 0.5, -1.0, 1.0).astype(np.float32)
+        x = np.where(hit, sign * np.float32(outlier_mag), x)
+    return f32_to_bf16_bits(x)
+
+
+def uniform_int_lens(rng, n, lo, hi):
+    """Integers drawn uniformly from [lo, hi], both ends included."""
+    return rng.integers(lo, hi + 1, size=n).astype(np.int32)
+
+
+def log_uniform_lens(rng, n, lo, hi):
+    """round(exp(U(ln lo, ln hi))), clipped to [lo, hi]."""
+    v = np.rint(np.exp(rng.uniform(math.log(lo), math.log(hi), size=n)))
+    return np.clip(v, lo, hi).astype(np.int32)
+
+
+def assign_pages(rng, lens, page_size, pool_pages: Optional[int] = None, slack_pages: int = 8):
+    """Give every sequence ceil(len/P) pages of a shared pool, in a seeded random order.
+
+    Returns (block_table [B, max_pages] int32, num_pages, spare_page).  Entries past a
+    sequence's pages point at ``spare_page``, a page no sequence owns (its content is
+    poison); with no spare page available they point at page 0.
+    """
+    lens = np.asarray(lens, dtype=np.int64)
+    need = [int(-(-int(n) // page_size)) for n in lens]
+    total = int(sum(need))
+    num_pages = max(total + slack_pages, pool_pages or 0)
+    perm = rng.permutation(num_pages).astype(np.int32)
+    max_pages = max(1, max(need) if need else 1)
+    spare = int(perm[total]) if total < num_pages else 0
+    bt = np.full((len(lens), max_pages), spare, dtype=np.int32)
+    off = 0
+    for s, n in enumerate(need):
+        bt[s, :n] = perm[off:off + n]
+        off += n
+    return bt, num_pages, spare
+
+
+@dataclass
+class AttnParams:
+    num_q_heads: int
+    num_kv_heads: int
+    head_dim: int
+    page_size: int = 16
+    kv_dtype: str = "bf16"          # "bf16" or "int8"
+    window: int = 0                 # 0 = full attention
+    sm_scale: float = 0.0           # 0 -> 1/sqrt(head_dim)
+    sinks: Optional[np.ndarray] = None  # float32 [num_q_heads] or None
+
+    def __post_init__(self):
+        if self.sm_scale == 0.0:
+            self.sm_scale = 1.0 / math.sqrt(self.head_dim)
+
+
+@dataclass
+class PagedCase:
+    """A batch of sequences whose K/V live in a paged pool.
+
+    ``k_tok``/``v_tok`` hold every cached token of every sequence, sequence after
+    sequence ([sum(seq_lens), Hkv, D] bf16 bits; offsets ``cu_tok``).  The last
+    ``q_lens[s]`` tokens of sequence s are the new ones of this step; the others are
+    the restored prefix.  ``q`` holds one query vector per new token
+    ([sum(q_lens), Hq, D] bf16 bits, offsets ``cu_q``).
+    """
+    name: str
+    p: AttnParams
+    seq_lens: np.ndarray      # [B] int32, after this step's tokens are appended
+    q_lens: np.ndarray        # [B] int32
+    cu_q: np.ndarray          # [B+1] int32
+    cu_tok: np.ndarray        # [B+1] int64
+    block_table: np.ndarray   # [B, max_pages] int32
+    num_pages: int
+    spare_page: int
+    k_tok: np.ndarray
+    v_tok: np.ndarray
+    q: np.ndarray
+    split_keys: int = 256
+    meta: dict = field(default_factory=dict)
+
+    @property
+    def batch(self) -> int:
+        return int(self.seq_lens.shape[0])
+
+    def prefix_lens(self) -> np.ndarray:
+        return (self.seq_lens - self.q_lens).astype(np.int32)
+
+    def token_slice(self, s: int, lo: int, hi: int):
+        """Rows [lo, hi) of sequence s in k_tok/v_tok."""
+        a = int(self.cu_tok[s])
+        return slice(a + lo, a + hi)
+
+    def new_tokens(self):
+        """(k_new, v_new, cu_new) for the tokens this step appends."""
+        ks, vs = [], []
+        for s in range(self.batch):
+            sl = self.token_slice(s, int(self.seq_lens[s] - self.q_lens[s]), int(self.seq_lens[s]))
+            ks.append(self.k_tok[sl])
+            vs.append(self.v_tok[sl])
+        cu = np.zeros(self.batch + 1, dtype=np.int32)
+        cu[1:] = np.cumsum(self.q_lens)
+        return np.concatenate(ks), np.concatenate(vs), cu
+
+    def prefix_tokens(self):
+        """(k_old, v_old, cu_old) for the restored prefix of every sequence."""
+        pl = self.prefix_lens()
+        ks, vs = [], []
+        for s in range(self.batch):
+            sl = self.token_slice(s, 0, int(pl[s]))
+            ks.append(self.k_tok[sl])
+            vs.append(self.v_tok[sl])
+        cu = np.zeros(self.batch + 1, dtype=np.int32)
+        cu[1:] = np.cumsum(pl)
+        return np.concatenate(ks), np.concatenate(vs), cu
+
+    def max_splits(self) -> int:
+        if self.split_keys <= 0:
+            return 1
+        return max(1, int(-(-int(self.seq_lens.max()) // self.split_keys)))
+
+
+def make_case(name, seed, p: AttnParams, seq_lens, q_lens, pool_pages=None,
+              outlier_frac=0.0, split_keys=256, sink_seed_offset=1000, meta=None) -> PagedCase:
+    """Draw K/V for every token, queries for the new tokens, and a page assignment."""
+    rng = np.random.default_rng(seed)
+    seq_lens = np.asarray(seq_lens, dtype=np.int32)
+    q_lens = np.asarray(q_lens, dtype=np.int32)
+    assert seq_lens.shape == q_lens.shape and np.all(q_lens <= seq_lens) and np.all(q_lens >= 0)
+    bt, num_pages, spare = assign_pages(rng, seq_lens, p.page_size, pool_pages)
+    cu_tok = np.zeros(len(seq_lens) + 1, dtype=np.int64)
+    cu_tok[1:] = np.cumsum(seq_lens.astype(np.int64))
+    T = int(cu_tok[-1])
+    k_tok = normal_bf16(rng, (T, p.num_kv_heads, p.head_dim), outlier_frac)
+    v_tok = normal_bf16(rng, (T, p.num_kv_heads, p.head_dim), outlier_frac)
+    cu_q = np.zeros(len(seq_lens) + 1, dtype=np.int32)
+    cu_q[1:] = np.cumsum(q_lens)
+    q = normal_bf16(rng, (int(cu_q[-1]), p.num_q_heads, p.head_dim))
+    return PagedCase(name=name, p=p, seq_lens=seq_lens, q_lens=q_lens, cu_q=cu_q,
+                     cu_tok=cu_tok, block_table=bt, num_pages=num_pages, spare_page=spare,
+                     k_tok=k_tok, v_tok=v_tok, q=q, split_keys=split_keys, meta=meta or {})
+
+
+def sinks_normal(seed, n):
+    """One sink logit per query head, N(0,1) float32."""
+    return np.random.default_rng(seed).standard_normal(n).astype(np.float32)
+
+
+# ---------------------------------------------------------------------------
+# The named workloads.  Each is a model's attention shape with the length mix the
+# pages measure at; sizes are the full ones unless ``small`` asks for a scaled
+# version the CPU oracle finishes in seconds.
+# ---------------------------------------------------------------------------
+
+def decode_1seq_ctx1024(seed=1, split_keys=256):
+    """One sequence, 16 q / 8 KV heads, D 128, 1024 cached positions, its 64 pages
+    drawn from a 256-page pool."""
+    p = AttnParams(16, 8, 128)
+    return make_case("decode_1seq_ctx1024", seed, p, [1024], [1], pool_pages=256,
+                     split_keys=split_keys)
+
+
+def decode_batch32_ctx512_8192(seed=2, batch=32, lo=512, hi=8192, fixed_len=None):
+    """Qwen3-4B attention shape (32 q / 8 KV heads, D 128); batch 32, lengths
+    U[512, 8192] (or all ``fixed_len``); 256-key splits."""
+    rng = np.random.default_rng(seed + 7)
+    lens = (np.full(batch, fixed_len, np.int32) if fixed_len
+            else uniform_int_lens(rng, batch, lo, hi))
+    p = AttnParams(32, 8, 128)
+    name = f"decode_batch{batch}_ctx{fixed_len}" if fixed_len else f"decode_batch{batch}_ctx{lo}_{hi}"
+    return make_case(name, seed, p, lens, np.ones(batch, np.int32), split_keys=256)
+
+
+def prefill_llama8b(seed=3, prompt=1024, prefix=0):
+    """Llama-3.1-8B attention shape (32 q / 8 KV heads, D 128), causal; a fresh
+    prompt, or ``prompt`` new tokens on a restored ``prefix``-token paged prefix."""
+    p = AttnParams(32, 8, 128)
+    name = f"prefill_causal_{prompt}" if prefix == 0 else f"prefill_chunk{prompt}_on_{prefix}"
+    return make_case(name, seed, p, [prefix + prompt], [prompt], split_keys=0)
+
+
+def decode_int8_qwen30b(seed=4, batch=8, ctx=32768):
+    """Qwen3-30B-A3B attention shape (32 q / 4 KV heads, D 128), INT8 KV, batch 8 at
+    32768 positions; raw K/V N(0,1) with 1% outliers at +-8."""
+    p = AttnParams(32, 4, 128, kv_dtype="int8")
+    return make_case(f"decode_int8_batch{batch}_ctx{ctx}", seed, p, np.full(batch, ctx, np.int32),
+                     np.ones(batch, np.int32), outlier_frac=0.01, split_keys=256)
+
+
+def mixed_gptoss(seed=5, layer="window", part="decode", batch=64, lo=128, hi=32768,
+                 chunks=2, chunk_len=2048):
+    """gpt-oss-20b attention shape (64 q / 8 KV heads, D 64, one sink logit per q
+    head).  Window layers see the last 128 positions, full layers all of them.
+    ``part`` = "decode": 64 sequences, lengths log-uniform in [128, 32768];
+    ``part`` = "prefill": fresh prompts of ``chunk_len`` tokens."""
+    window = 128 if layer == "window" else 0
+    p = AttnParams(64, 8, 64, window=window, sinks=sinks_normal(seed + 99, 64))
+    if part == "decode":
+        rng = np.random.default_rng(seed + 11)
+        lens = log_uniform_lens(rng, batch, lo, hi)
+        return make_case(f"mixed_{layer}_decode_b{batch}", seed, p, lens, np.ones(batch, np.int32),
+                         split_keys=256)
+    lens = np.full(chunks, chunk_len, np.int32)
+    return make_case(f"mixed_{layer}_prefill_{chunks}x{chunk_len}", seed, p, lens, lens, split_keys=0)
