@@ -1,0 +1,396 @@
+"""Benchmark of the paged flash attention hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+
+The default workload is batched decode with Qwen3-4B attention: 32 q / 8 KV heads,
+D 128, batch 32, lengths U[512, 8192], 16-token pages, 256-key splits.  One step
+is the whole decode hot path for one batch:
+  1. kv_write of the batch's new token;
+  2. split-KV paged decode;
+  3. combine.
+Inputs sit in HBM before the timed region starts.  Every step reads one of several
+identical pool copies in rotation, about 2 GiB in total, so the reads come from HBM
+rather than the 256 MB MALL.
+
+Exactly one JSON line is printed on stdout.  Its fields:
+* value: the step's algorithmic bytes / step time, in GB/s.  The bytes are the
+  visible K/V, q, out, the block-table entries, and the new tokens written.
+* roofline: the decode kernel alone, with its average launch time measured by HIP
+  events on its stream, against the 8 TB/s HBM peak.
+* cpu_baseline: the CPU float64 oracle on the same workload.
+* workloads: the other headline workloads of the same hot path, each with its own
+  metric: prefill TFLOP/s, INT8 decode, and the gpt-oss mixed batch.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+ROTATE_BYTES = 2 << 30         # pool copies rotated across steps
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+# ---------------------------------------------------------------------------
+# algorithmic work
+# ---------------------------------------------------------------------------
+
+def visible_keys(lens, window):
+    lens = np.asarray(lens, np.int64)
+    return np.minimum(lens, window) if window > 0 else lens
+
+
+def decode_bytes(case) -> int:
+    """Visible K/V (+ scales for INT8) + q + out + block-table entries of the decode."""
+    p = case.p
+    vis = visible_keys(case.seq_lens, p.window)
+    elem = 1 if p.kv_dtype == "int8" else 2
+    per_key = p.num_kv_heads * (2 * p.head_dim * elem + (8 if p.kv_dtype == "int8" else 0))
+    kv = int(vis.sum()) * per_key
+    q = case.batch * p.num_q_heads * p.head_dim * 2
+    out = case.batch * p.num_q_heads * p.head_dim * 4
+    lens = np.asarray(case.seq_lens, np.int64)
+    lo = np.maximum(0, lens - p.window) if p.window > 0 else np.zeros_like(lens)
+    bt = int(((lens - 1) // p.page_size - lo // p.page_size + 1).sum()) * 4
+    return kv + q + out + bt
+
+
+def kv_write_bytes(case) -> int:
+    p = case.p
+    T = int(case.q_lens.sum())
+    elem = 1 if p.kv_dtype == "int8" else 2
+    rd = T * p.num_kv_heads * p.head_dim * 2 * 2
+    wr = T * p.num_kv_heads * (2 * p.head_dim * elem + (8 if p.kv_dtype == "int8" else 0))
+    return rd + wr
+
+
+def prefill_flops(case) -> float:
+    """4*D*Hq per visible (query, key) pair: only causal/window-visible pairs count."""
+    p = case.p
+    total = 0
+    for s in range(case.batch):
+        n, ql = int(case.seq_lens[s]), int(case.q_lens[s])
+        pos = np.arange(n - ql, n, dtype=np.int64)
+        vis = pos + 1
+        if p.window > 0:
+            vis = np.minimum(vis, p.window)
+        total += int(vis.sum())
+    return 4.0 * p.head_dim * p.num_q_heads * total
+
+
+def src_digest(*names) -> str:
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "paged_flash_attention_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel: str, digest: str):
+    """HBM bytes per launch from a committed rocprofv3 counter summary, if it was
+    taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f).get(kernel)
+    except (OSError, ValueError):
+        return None
+    if not rec or rec.get("src_digest") != digest:
+        return None
+    return rec.get("bytes_per_launch")
+
+
+# ---------------------------------------------------------------------------
+# GPU legs
+# ---------------------------------------------------------------------------
+
+class Timer:
+    def __init__(self, torch):
+        self.torch = torch
+        self.pairs = {}
+
+    def mark(self, name):
+        e0 = self.torch.cuda.Event(enable_timing=True)
+        e0.record()
+        return e0
+
+    def close(self, name, e0):
+        e1 = self.torch.cuda.Event(enable_timing=True)
+        e1.record()
+        self.pairs.setdefault(name, []).append((e0, e1))
+
+    def mean_ms(self, name):
+        ps = self.pairs.get(name, [])
+        return sum(a.elapsed_time(b) for a, b in ps) / max(1, len(ps))
+
+    def reset(self):
+        self.pairs = {}
+
+
+def setup_case(case, torch, pfa, gs, copies_for_bytes=ROTATE_BYTES):
+    g = gs.GpuCase(case)
+    pool_bytes = sum(t.numel() * t.element_size() for t in (g.pool.k, g.pool.v, g.pool.k_scale, g.pool.v_scale)
+                     if t is not None)
+    n_copies = max(1, min(16, int(math.ceil(copies_for_bytes / max(pool_bytes, 1)))))
+    pools = [g.pool] + [pfa.KVPool(*(None if t is None else t.clone() for t in
+                                     (g.pool.k, g.pool.v, g.pool.k_scale, g.pool.v_scale)))
+                        for _ in range(n_copies - 1)]
+    k, v, cu = case.new_tokens()
+    new = (gs.dev_bf16(k), gs.dev_bf16(v), gs.dev_i32(cu))
+    torch.cuda.synchronize()
+    return g, pools, new
+
+
+def run_decode(case, torch, pfa, gs, steps, warmup):
+    g, pools, (kn, vn, cun) = setup_case(case, torch, pfa, gs)
+    p = case.p
+    B, Hq, D = case.batch, p.num_q_heads, p.head_dim
+    max_len = int(case.seq_lens.max())
+    S = case.split_keys
+    ms = pfa.decode_num_splits(max_len, S)
+    op = torch.empty((B, Hq, ms, D), device="cuda")
+    lp = torch.empty((B, Hq, ms), device="cuda")
+    out = torch.empty((B, Hq, D), device="cuda")
+    tm = Timer(torch)
+
+    def step(i):
+        pool = pools[i % len(pools)]
+        pfa.kv_write(g.desc, pool, kn, vn, cun, g.seq_lens, g.bt)
+        e = tm.mark("decode")
+        pfa.paged_attn_decode(g.desc, pool, g.q, g.bt, g.seq_lens, max_len, S, ms, o_part=op, lse_part=lp)
+        tm.close("decode", e)
+        pfa.paged_attn_combine(g.desc, op, lp, g.seq_lens, S, ms, out)
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    tm.reset()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for i in range(steps):
+        step(warmup + i)
+    t1.record()
+    torch.cuda.synchronize()
+    step_ms = t0.elapsed_time(t1) / steps
+    dec_ms = tm.mean_ms("decode")
+    return dict(step_ms=step_ms, decode_ms=dec_ms, pool_copies=len(pools),
+                decode_bytes=decode_bytes(case), step_bytes=decode_bytes(case) + kv_write_bytes(case),
+                partial_bytes=int(B * Hq * ms * (D + 1) * 4))
+
+
+def run_prefill(case, torch, pfa, gs, steps, warmup):
+    g, pools, (kn, vn, cun) = setup_case(case, torch, pfa, gs, copies_for_bytes=0)
+    p = case.p
+    out = torch.empty((int(case.cu_q[-1]), p.num_q_heads, p.head_dim), device="cuda")
+    max_q = int(case.q_lens.max())
+    tm = Timer(torch)
+
+    def step(i):
+        pfa.kv_write(g.desc, g.pool, kn, vn, cun, g.seq_lens, g.bt)
+        e = tm.mark("prefill")
+        pfa.paged_attn_prefill(g.desc, g.pool, g.q, g.cu_q, g.bt, g.seq_lens, max_q, out)
+        tm.close("prefill", e)
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    tm.reset()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for i in range(steps):
+        step(i)
+    t1.record()
+    torch.cuda.synchronize()
+    return dict(step_ms=t0.elapsed_time(t1) / steps, prefill_ms=tm.mean_ms("prefill"),
+                flops=prefill_flops(case))
+
+
+# ---------------------------------------------------------------------------
+# CPU baseline: the oracle as it stands
+# ---------------------------------------------------------------------------
+
+def cpu_baseline_decode(case, budget_s=20.0):
+    import oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        cores = 1
+    p = case.p
+    pool = O.empty_pool(case.num_pages, p.num_kv_heads, p.page_size, p.head_dim, p.kv_dtype)
+    k, v, cu = case.prefix_tokens()
+    O.kv_write(pool, k, v, cu, case.prefix_lens(), case.block_table, p.page_size, p.kv_dtype)
+    kn, vn, cun = case.new_tokens()
+    # timed: the oracle's own step (kv_write of the new tokens + decode), on
+    # sequences taken in order until the budget is spent (at least one)
+    t_start = time.perf_counter()
+    done, nbytes = 0, 0
+    sub_bytes = []
+    for s in range(case.batch):
+        t0 = time.perf_counter()
+        sl = slice(int(cun[s]), int(cun[s + 1]))
+        O.kv_write(pool, kn[sl], vn[sl], np.array([0, sl.stop - sl.start]), case.seq_lens[s:s + 1],
+                   case.block_table[s:s + 1], p.page_size, p.kv_dtype)
+        O.decode(case.q[s:s + 1], pool, case.block_table[s:s + 1], case.seq_lens[s:s + 1], p)
+        done += 1
+        if time.perf_counter() - t_start > budget_s:
+            break
+    elapsed = time.perf_counter() - t_start
+    # bytes of the sequences done, counted as for the GPU
+    import copy
+    sub = copy.copy(case)
+    sub.seq_lens = case.seq_lens[:done]
+    sub.q_lens = case.q_lens[:done]
+    nbytes = decode_bytes(sub) + kv_write_bytes(sub)
+    return dict(value=round(nbytes / elapsed / 1e9, 4), unit="GB/s", cores=int(cores), kind="oracle",
+                sample=f"{done} of {case.batch} sequences of the same batch (kv_write of the new token + "
+                       f"materialised-softmax decode, float64 numpy), {elapsed:.1f} s")
+
+
+# ---------------------------------------------------------------------------
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="decode_batch32_ctx512_8192")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra", action="store_true", help="skip the other headline workloads")
+    ap.add_argument("--copy-probe", type=int, default=0,
+                    help="only run N plain 1 GiB device copies (counter calibration) and exit")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(sharding is described in the design notes, not run).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import paged_flash_attention_amd as pfa
+    import workloads as W
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    import gpu_support as gs
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    pfa.lib()
+
+    if args.copy_probe:
+        a = torch.empty(1 << 28, dtype=torch.float32, device="cuda")   # 1 GiB
+        b = torch.empty_like(a)
+        a.fill_(1.0)
+        torch.cuda.synchronize()
+        for _ in range(args.copy_probe):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        log(f"copy probe: {args.copy_probe} x 1 GiB device copies")
+        return
+
+    builders = {
+        "decode_batch32_ctx512_8192": lambda: W.decode_batch32_ctx512_8192(),
+        "decode_batch32_ctx8192": lambda: W.decode_batch32_ctx512_8192(fixed_len=8192),
+        "decode_1seq_ctx1024": lambda: W.decode_1seq_ctx1024(),
+        "decode_int8_batch8_ctx32768": lambda: W.decode_int8_qwen30b(),
+        "mixed_full_decode_b64": lambda: W.mixed_gptoss(layer="full", part="decode"),
+        "mixed_window_decode_b64": lambda: W.mixed_gptoss(layer="window", part="decode"),
+        "prefill_causal_8192": lambda: W.prefill_llama8b(prompt=8192),
+        "prefill_causal_1024": lambda: W.prefill_llama8b(prompt=1024),
+        "prefill_chunk130_on_8192": lambda: W.prefill_llama8b(prompt=130, prefix=8192),
+        "mixed_full_prefill_2x2048": lambda: W.mixed_gptoss(layer="full", part="prefill"),
+        "mixed_window_prefill_2x2048": lambda: W.mixed_gptoss(layer="window", part="prefill"),
+    }
+    if args.workload not in builders:
+        print(f"unknown workload {args.workload}; choose from {sorted(builders)}", file=sys.stderr)
+        sys.exit(2)
+
+    def measure(name, steps, warmup):
+        case = builders[name]()
+        log(f"[bench] {name}: building + timing {steps} steps")
+        if name.startswith("prefill") or name.endswith("prefill_2x2048"):
+            r = run_prefill(case, torch, pfa, gs, steps, warmup)
+            tf = r["flops"] / (r["prefill_ms"] * 1e-3) / 1e12
+            r.update(metric="prefill attn TFLOP/s", kernel_tflops=round(tf, 2),
+                     frac_of_mfma_peak=round(tf / BF16_PEAK_TFLOPS, 4))
+        else:
+            r = run_decode(case, torch, pfa, gs, steps, warmup)
+            gbs = r["decode_bytes"] / (r["decode_ms"] * 1e-3) / 1e9
+            r.update(metric="decode attn GB/s", kernel_gbs=round(gbs, 1),
+                     decode_us=round(r["decode_ms"] * 1e3, 2), frac_of_hbm_peak=round(gbs / HBM_PEAK_GBS, 4))
+        return case, r
+
+    case, r = measure(args.workload, args.steps, args.warmup)
+    is_prefill = "prefill_ms" in r
+    if is_prefill:
+        value = r["flops"] / (r["step_ms"] * 1e-3) / 1e12
+        unit, metric = "TFLOP/s", "prefill attn TFLOP/s"
+        roof = dict(bound="mfma", achieved=r["kernel_tflops"], peak=BF16_PEAK_TFLOPS, unit="TFLOP/s",
+                    frac=r["frac_of_mfma_peak"], traffic=None)
+    else:
+        value = r["step_bytes"] / (r["step_ms"] * 1e-3) / 1e9
+        unit, metric = "GB/s", "decode attn GB/s (HBM)"
+        kernel = "decode_kernel"
+        traffic = measured_traffic(f"{kernel}:{args.workload}", src_digest("decode.hip", "pfa_device.h"))
+        roof = dict(bound="hbm", achieved=r["kernel_gbs"], peak=HBM_PEAK_GBS, unit="GB/s",
+                    frac=r["frac_of_hbm_peak"], traffic=traffic)
+
+    extra = {}
+    if not args.no_extra and args.workload == "decode_batch32_ctx512_8192":
+        for name, st in (("decode_batch32_ctx8192", 30), ("decode_int8_batch8_ctx32768", 30),
+                         ("mixed_full_decode_b64", 30), ("prefill_causal_8192", 10),
+                         ("prefill_chunk130_on_8192", 20), ("mixed_full_prefill_2x2048", 20)):
+            try:
+                _, rr = measure(name, st, 3)
+                if "prefill_ms" in rr:
+                    extra[name] = dict(us=round(rr["prefill_ms"] * 1e3, 1), tflops=rr["kernel_tflops"],
+                                       frac_of_mfma_peak=rr["frac_of_mfma_peak"])
+                else:
+                    extra[name] = dict(us=rr["decode_us"], gbs=rr["kernel_gbs"],
+                                       frac_of_hbm_peak=rr["frac_of_hbm_peak"])
+            except Exception as e:   # report, never hide
+                extra[name] = dict(error=str(e)[:200])
+            torch.cuda.empty_cache()
+
+    cpu = None
+    if not args.no_cpu_baseline and not is_prefill:
+        log("[bench] cpu baseline (oracle)")
+        cpu = cpu_baseline_decode(case)
+
+    p = case.p
+    line = {
+        "metric": metric, "value": round(value, 2), "unit": unit, "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(r["step_ms"], 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16" if p.kv_dtype == "bf16" else "int8", "data": "synthetic",
+        "config": {"workload": case.name, "batch": case.batch, "q_heads": p.num_q_heads,
+                   "kv_heads": p.num_kv_heads, "head_dim": p.head_dim, "page_size": p.page_size,
+                   "split_keys": case.split_keys if not is_prefill else None,
+                   "max_seq_len": int(case.seq_lens.max()), "window": p.window,
+                   "sinks": p.sinks is not None, "parallelism": "single GPU"},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "detail": {k: v for k, v in r.items() if isinstance(v, (int, float, str))},
+        "workloads": extra,
+    }
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,187 @@
+/*
+ * pfa.h - paged flash attention for AMD MI355X (gfx950): the C ABI.
+ *
+ * What it computes
+ * ----------------
+ * Attention for LLM inference over a KV cache kept in a pool of fixed-size pages.
+ * Each sequence reaches its pages through its own row of a block table.  The
+ * TileInfer.jl performance page ("Fused kernels, FlashAttention and
+ * PagedAttention") describes the operation.  The result is the one reference ops
+ * produce when they gather the pages into dense K and V and materialise the
+ * softmax.  The kernels instead read each page once, in place, with an online
+ * softmax: split-KV for decode, then a separate combine kernel.  Prefill appends
+ * a new turn to a restored prefix.  The Qml-engine announcement explains that a
+ * session turn restores the conversation's KV from the store, so only the new turn
+ * is prefilled.  Its model table also covers gpt-oss-20b, with attention sinks and
+ * a sliding window.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - All array arguments are DEVICE pointers to memory the caller owns.  The
+ *    library never allocates, frees or keeps a pointer past the call.
+ *  - Every call only enqueues work on `stream`, a hipStream_t passed as void*.
+ *    NULL means the null stream.  The caller synchronises.
+ *  - Arrays are dense, row-major, in the layouts stated below.  bf16 means IEEE
+ *    bfloat16.  Integers are int32.
+ *  - Pool layout: k_pool/v_pool [num_pages][Hkv][P][D].  Position j of sequence s
+ *    lives in page block_table[s*bt_stride + j/P], slot j%P.  INT8 pools add
+ *    k_scale/v_scale [num_pages][Hkv][P] fp32, one scale per cached vector.
+ *  - Positions: a sequence holds seq_lens[s] tokens.  That count includes the new
+ *    ones.  Its q_len new tokens sit at positions seq_lens[s]-q_len ... seq_lens[s]-1.
+ *    The query at position `pos` sees key j when j <= pos and, if window W > 0,
+ *    when pos - j < W.  GQA uses contiguous groups: query head h reads KV head
+ *    h / (Hq/Hkv).
+ *  - Sinks: when desc->sinks != NULL, query head h has one extra logit sinks[h].
+ *    It is not multiplied by sm_scale.  It enters the softmax max and denominator
+ *    only, with no value vector.
+ *  - Errors: host-checkable problems return a status and launch nothing.  That
+ *    covers NULL pointers, inconsistent sizes and unsupported shapes.  A failed
+ *    launch returns PFA_ERR_HIP, and pfa_last_hip_error() then gives the hipError_t
+ *    code (thread-local).  Device-resident contents are the caller's contract: valid
+ *    page ids and seq_lens[s] <= bt_stride*P.  The kernels clamp page ids and
+ *    lengths so that a broken contract gives wrong numbers, never an access outside
+ *    the pool.
+ *
+ * Supported shapes: head_dim 64 or 128; page_size 16; Hq % Hkv == 0.
+ *  - Decode: group size G = Hq/Hkv in {1,2,4,8}.
+ *  - Prefill: G in {1,2,4,8,16,32}.
+ */
+#ifndef PFA_H
+#define PFA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    PFA_OK = 0,
+    PFA_ERR_NULL = 1,          /* a required pointer is NULL                          */
+    PFA_ERR_SHAPE = 2,         /* sizes inconsistent or out of range                  */
+    PFA_ERR_UNSUPPORTED = 3,   /* head_dim / page_size / dtype / group size not built */
+    PFA_ERR_WORKSPACE = 4,     /* split buffers too small for max_seq_len/split_keys  */
+    PFA_ERR_HIP = 5            /* a HIP call failed; see pfa_last_hip_error()         */
+} pfa_status;
+
+typedef enum { PFA_KV_BF16 = 0, PFA_KV_INT8 = 1 } pfa_kv_dtype;
+
+/* Attention shape and options. */
+typedef struct {
+    int32_t num_q_heads;       /* Hq                                                  */
+    int32_t num_kv_heads;      /* Hkv, divides Hq                                     */
+    int32_t head_dim;          /* D: 64 or 128                                        */
+    int32_t page_size;         /* P: 16                                               */
+    int32_t kv_dtype;          /* pfa_kv_dtype                                        */
+    int32_t window;            /* 0 = full attention; W > 0: keys pos-W < j <= pos    */
+    float sm_scale;            /* multiplies q.k (e.g. 1/sqrt(D))                     */
+    const float* sinks;        /* device [Hq] fp32 sink logits, or NULL               */
+} pfa_attn_desc;
+
+/* The page pool. */
+typedef struct {
+    void* k_pool;              /* device [num_pages][Hkv][P][D], bf16 or int8         */
+    void* v_pool;              /* same                                                */
+    float* k_scale;            /* device [num_pages][Hkv][P] fp32; INT8 only, else NULL */
+    float* v_scale;            /* same                                                */
+    int32_t num_pages;
+} pfa_kv_pool;
+
+/*
+ * pfa_kv_write: append new tokens' K and V to their sequences' pages.
+ *   The TileInfer.jl performance page names this step the KV cache write.  Its
+ *   "INT8 KV cache" section adds one scale per cached vector.
+ *
+ *   k_new, v_new   device [num_tokens][Hkv][D] bf16.  The tokens of sequence s are
+ *                  rows cu_new[s] .. cu_new[s+1]-1.
+ *   cu_new         device [batch+1] int32, nondecreasing, with cu_new[0] = 0 and
+ *                  cu_new[batch] = num_tokens.
+ *   seq_lens       device [batch] int32: sequence lengths after the append.
+ *                  Token i of s goes to position seq_lens[s] - n_s + i.
+ *   block_table    device [batch][bt_stride] int32 page ids.
+ *
+ *   BF16 pools receive the bits unchanged.  INT8 pools receive codes and scales.
+ *   For each (token, KV head) vector x, computed separately for K and V:
+ *     scale = absmax(x) / 127                         (IEEE fp32 division)
+ *     code  = clamp(rint(x / scale), -127, 127)       (ties to even)
+ *   An all-zero vector gets scale 0 and codes 0.  Tokens whose slot falls outside
+ *   the block table or the pool are skipped.
+ */
+pfa_status pfa_kv_write(const pfa_attn_desc* desc, const pfa_kv_pool* pool,
+                        const void* k_new, const void* v_new, const int32_t* cu_new,
+                        const int32_t* seq_lens, const int32_t* block_table,
+                        int32_t bt_stride, int32_t batch, int32_t num_tokens,
+                        void* stream);
+
+/*
+ * pfa_paged_attn_decode: one query per sequence, at position seq_lens[s]-1.  That
+ *   token's K/V must already be written.  Split-KV: the TileInfer.jl performance
+ *   page ("Fused kernels, ...") keeps the combine as a separate kernel.
+ *
+ *   q              device [batch][Hq][D] bf16.
+ *   max_seq_len    host upper bound on seq_lens[].
+ *   split_keys     S, a multiple of P.  Split i of a sequence covers keys
+ *                  [i*S, min((i+1)*S, len)).
+ *   max_splits     >= ceil(max_seq_len / S).
+ *
+ *   If max_splits == 1 (unsplit), the kernel writes the final result, sink
+ *   included, to out [batch][Hq][D] fp32.  o_part and lse_part may be NULL.
+ *   Otherwise, for every split i < ceil(seq_lens[s]/S), it writes:
+ *     o_part   [batch][Hq][max_splits][D] fp32, the softmax-normalised partial output;
+ *     lse_part [batch][Hq][max_splits] fp32, the natural log-sum-exp of the split's
+ *              visible scores, or -inf when the window hides the whole split.
+ *   Partials never include the sink, and out is left untouched.  Then call
+ *   pfa_paged_attn_combine.
+ */
+pfa_status pfa_paged_attn_decode(const pfa_attn_desc* desc, const pfa_kv_pool* pool,
+                                 const void* q, const int32_t* block_table, int32_t bt_stride,
+                                 const int32_t* seq_lens, int32_t batch, int32_t max_seq_len,
+                                 int32_t split_keys, int32_t max_splits,
+                                 float* o_part, float* lse_part, float* out, void* stream);
+
+/*
+ * pfa_paged_attn_combine: merge the split partials (same page and section as
+ *   decode).  For each (b, h), over the ceil(seq_lens[b]/S) splits of b:
+ *     M   = max(max_i lse_i, sink_h)
+ *     out = sum_i e^(lse_i - M) o_i / (sum_i e^(lse_i - M) + e^(sink_h - M))
+ *   The sink terms appear only when desc->sinks != NULL.  out is [batch][Hq][D] fp32.
+ */
+pfa_status pfa_paged_attn_combine(const pfa_attn_desc* desc, const float* o_part,
+                                  const float* lse_part, const int32_t* seq_lens, int32_t batch,
+                                  int32_t split_keys, int32_t max_splits, float* out,
+                                  void* stream);
+
+/*
+ * pfa_paged_attn_prefill: causal attention of every new token over its sequence.
+ *   The keys are the restored prefix plus the new tokens, and the new tokens'
+ *   K/V must already be written.  This covers a fresh prompt (prefix 0) and a
+ *   chunked turn appended to a restored paged prefix.
+ *
+ *   q              device [num_q_tokens][Hq][D] bf16.  The new tokens of sequence s
+ *                  are rows cu_q[s] .. cu_q[s+1]-1.
+ *   cu_q           device [batch+1] int32, as cu_new above.
+ *   seq_lens       device [batch] int32, prefix + new tokens.
+ *   max_q_len      host upper bound on cu_q[s+1]-cu_q[s].
+ *   out            device [num_q_tokens][Hq][D] fp32.
+ */
+pfa_status pfa_paged_attn_prefill(const pfa_attn_desc* desc, const pfa_kv_pool* pool,
+                                  const void* q, const int32_t* cu_q,
+                                  const int32_t* block_table, int32_t bt_stride,
+                                  const int32_t* seq_lens, int32_t batch, int32_t max_q_len,
+                                  float* out, void* stream);
+
+/* ceil(max_seq_len / split_keys), at least 1 (0 when split_keys <= 0). */
+int32_t pfa_decode_num_splits(int32_t max_seq_len, int32_t split_keys);
+
+/* Static description of a status code; never NULL. */
+const char* pfa_status_string(pfa_status status);
+
+/* hipError_t of the last PFA_ERR_HIP on this thread (0 if none). */
+int32_t pfa_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PFA_H */

@@ -1,0 +1,235 @@
+"""Python binding of libpfa.so, the paged flash attention C ABI in include/pfa.h.
+
+This module only marshals arguments.  It checks tensor dtypes, devices and
+contiguity, packs the descriptor structs, and passes raw device pointers and the
+current HIP stream to the C entry points, which have the same names.  Every step
+of the computation runs in the HIP kernels.  If the library is missing this
+module raises; it never falls back to another implementation.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from dataclasses import dataclass
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libpfa.so")
+
+PFA_OK = 0
+STATUS_NAMES = {0: "PFA_OK", 1: "PFA_ERR_NULL", 2: "PFA_ERR_SHAPE", 3: "PFA_ERR_UNSUPPORTED",
+                4: "PFA_ERR_WORKSPACE", 5: "PFA_ERR_HIP"}
+KV_DTYPES = {"bf16": 0, "int8": 1}
+
+# every symbol include/pfa.h declares
+EXPORTS = ("pfa_kv_write", "pfa_paged_attn_decode", "pfa_paged_attn_combine",
+           "pfa_paged_attn_prefill", "pfa_decode_num_splits", "pfa_status_string",
+           "pfa_last_hip_error")
+
+
+class PfaError(RuntimeError):
+    def __init__(self, fn: str, status: int, message: str, hip_error: int = 0):
+        extra = f" (hipError {hip_error})" if status == 5 else ""
+        super().__init__(f"{fn}: {STATUS_NAMES.get(status, status)}: {message}{extra}")
+        self.status = status
+        self.hip_error = hip_error
+
+
+class CAttnDesc(ctypes.Structure):
+    _fields_ = [("num_q_heads", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("page_size", ctypes.c_int32),
+                ("kv_dtype", ctypes.c_int32), ("window", ctypes.c_int32),
+                ("sm_scale", ctypes.c_float), ("sinks", ctypes.c_void_p)]
+
+
+class CKvPool(ctypes.Structure):
+    _fields_ = [("k_pool", ctypes.c_void_p), ("v_pool", ctypes.c_void_p),
+                ("k_scale", ctypes.c_void_p), ("v_scale", ctypes.c_void_p),
+                ("num_pages", ctypes.c_int32)]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libpfa.so (built in-tree) and declare its signatures."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m paged_flash_attention_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    P, I, F, V = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float, ctypes.c_void_p
+    D, PL = ctypes.POINTER(CAttnDesc), ctypes.POINTER(CKvPool)
+    sig = {
+        "pfa_kv_write": [D, PL, P, P, P, P, P, I, I, I, V],
+        "pfa_paged_attn_decode": [D, PL, P, P, I, P, I, I, I, I, P, P, P, V],
+        "pfa_paged_attn_combine": [D, P, P, P, I, I, I, P, V],
+        "pfa_paged_attn_prefill": [D, PL, P, P, P, I, P, I, I, P, V],
+    }
+    for name, args in sig.items():
+        fn = getattr(L, name)
+        fn.argtypes = args
+        fn.restype = ctypes.c_int
+    L.pfa_decode_num_splits.argtypes = [I, I]
+    L.pfa_decode_num_splits.restype = ctypes.c_int32
+    L.pfa_status_string.argtypes = [ctypes.c_int]
+    L.pfa_status_string.restype = ctypes.c_char_p
+    L.pfa_last_hip_error.argtypes = []
+    L.pfa_last_hip_error.restype = ctypes.c_int32
+    _lib = L
+    return L
+
+
+def _check(fn: str, status: int):
+    if status != PFA_OK:
+        L = lib()
+        raise PfaError(fn, status, L.pfa_status_string(status).decode(), L.pfa_last_hip_error())
+
+
+# ---------------------------------------------------------------------------
+# descriptors
+# ---------------------------------------------------------------------------
+
+@dataclass
+class AttnDesc:
+    num_q_heads: int
+    num_kv_heads: int
+    head_dim: int
+    page_size: int = 16
+    kv_dtype: str = "bf16"
+    window: int = 0
+    sm_scale: Optional[float] = None
+    sinks: Optional[torch.Tensor] = None      # device float32 [num_q_heads]
+
+    def c(self) -> CAttnDesc:
+        if self.sinks is not None:
+            _dev(self.sinks, torch.float32, "sinks")
+            if self.sinks.numel() != self.num_q_heads:
+                raise ValueError("sinks must have num_q_heads entries")
+        scale = self.sm_scale if self.sm_scale is not None else 1.0 / math.sqrt(self.head_dim)
+        return CAttnDesc(self.num_q_heads, self.num_kv_heads, self.head_dim, self.page_size,
+                         KV_DTYPES[self.kv_dtype], self.window, scale,
+                         self.sinks.data_ptr() if self.sinks is not None else None)
+
+
+@dataclass
+class KVPool:
+    """k/v: [num_pages, Hkv, P, D] (bf16 or int8); scales [num_pages, Hkv, P] fp32 for INT8."""
+    k: torch.Tensor
+    v: torch.Tensor
+    k_scale: Optional[torch.Tensor] = None
+    v_scale: Optional[torch.Tensor] = None
+
+    @property
+    def num_pages(self) -> int:
+        return int(self.k.shape[0])
+
+    def c(self) -> CKvPool:
+        dt = self.k.dtype
+        if dt not in (torch.bfloat16, torch.int8) or self.v.dtype != dt:
+            raise TypeError("pool tensors must both be bfloat16 or both int8")
+        _dev(self.k, dt, "k_pool")
+        _dev(self.v, dt, "v_pool")
+        ks = vs = None
+        if dt == torch.int8:
+            if self.k_scale is None or self.v_scale is None:
+                raise ValueError("an INT8 pool needs k_scale and v_scale")
+            ks = _dev(self.k_scale, torch.float32, "k_scale").data_ptr()
+            vs = _dev(self.v_scale, torch.float32, "v_scale").data_ptr()
+        return CKvPool(self.k.data_ptr(), self.v.data_ptr(), ks, vs, self.num_pages)
+
+
+def _dev(t: Optional[torch.Tensor], dtype, name: str):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream, ref: torch.Tensor):
+    if stream is None:
+        stream = torch.cuda.current_stream(ref.device)
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+# ---------------------------------------------------------------------------
+# entry points (same names as the C ABI, without the pfa_ prefix)
+# ---------------------------------------------------------------------------
+
+def kv_write(desc: AttnDesc, pool: KVPool, k_new, v_new, cu_new, seq_lens, block_table, stream=None):
+    """Append k_new/v_new [T, Hkv, D] bf16 to their sequences' pages (pfa_kv_write)."""
+    for t, n in ((k_new, "k_new"), (v_new, "v_new")):
+        _dev(t, torch.bfloat16, n)
+    for t, n in ((cu_new, "cu_new"), (seq_lens, "seq_lens"), (block_table, "block_table")):
+        _dev(t, torch.int32, n)
+    batch = int(seq_lens.numel())
+    st = lib().pfa_kv_write(ctypes.byref(desc.c()), ctypes.byref(pool.c()), _ptr(k_new), _ptr(v_new),
+                            _ptr(cu_new), _ptr(seq_lens), _ptr(block_table), int(block_table.shape[1]),
+                            batch, int(k_new.shape[0]), _stream(stream, k_new))
+    _check("pfa_kv_write", st)
+
+
+def decode_num_splits(max_seq_len: int, split_keys: int) -> int:
+    return int(lib().pfa_decode_num_splits(int(max_seq_len), int(split_keys)))
+
+
+def paged_attn_decode(desc: AttnDesc, pool: KVPool, q, block_table, seq_lens, max_seq_len: int,
+                      split_keys: int, max_splits: int, o_part=None, lse_part=None, out=None,
+                      stream=None):
+    """Split-KV decode partials, or the final output when max_splits == 1."""
+    _dev(q, torch.bfloat16, "q")
+    _dev(block_table, torch.int32, "block_table")
+    _dev(seq_lens, torch.int32, "seq_lens")
+    _dev(o_part, torch.float32, "o_part")
+    _dev(lse_part, torch.float32, "lse_part")
+    _dev(out, torch.float32, "out")
+    st = lib().pfa_paged_attn_decode(ctypes.byref(desc.c()), ctypes.byref(pool.c()), _ptr(q),
+                                     _ptr(block_table), int(block_table.shape[1]), _ptr(seq_lens),
+                                     int(q.shape[0]), int(max_seq_len), int(split_keys), int(max_splits),
+                                     _ptr(o_part), _ptr(lse_part), _ptr(out), _stream(stream, q))
+    _check("pfa_paged_attn_decode", st)
+
+
+def paged_attn_combine(desc: AttnDesc, o_part, lse_part, seq_lens, split_keys: int, max_splits: int,
+                       out, stream=None):
+    """Merge split partials into out [B, Hq, D] fp32."""
+    _dev(o_part, torch.float32, "o_part")
+    _dev(lse_part, torch.float32, "lse_part")
+    _dev(seq_lens, torch.int32, "seq_lens")
+    _dev(out, torch.float32, "out")
+    st = lib().pfa_paged_attn_combine(ctypes.byref(desc.c()), _ptr(o_part), _ptr(lse_part),
+                                      _ptr(seq_lens), int(seq_lens.numel()), int(split_keys),
+                                      int(max_splits), _ptr(out), _stream(stream, out))
+    _check("pfa_paged_attn_combine", st)
+
+
+def paged_attn_prefill(desc: AttnDesc, pool: KVPool, q, cu_q, block_table, seq_lens, max_q_len: int,
+                       out, stream=None):
+    """Causal prefill of the new tokens q [Tq, Hq, D] bf16 into out [Tq, Hq, D] fp32."""
+    _dev(q, torch.bfloat16, "q")
+    _dev(cu_q, torch.int32, "cu_q")
+    _dev(block_table, torch.int32, "block_table")
+    _dev(seq_lens, torch.int32, "seq_lens")
+    _dev(out, torch.float32, "out")
+    st = lib().pfa_paged_attn_prefill(ctypes.byref(desc.c()), ctypes.byref(pool.c()), _ptr(q),
+                                      _ptr(cu_q), _ptr(block_table), int(block_table.shape[1]),
+                                      _ptr(seq_lens), int(seq_lens.numel()), int(max_q_len),
+                                      _ptr(out), _stream(stream, q))
+    _check("pfa_paged_attn_prefill", st)
+
+
+__all__ = ["AttnDesc", "KVPool", "PfaError", "EXPORTS", "lib", "kv_write", "decode_num_splits",
+           "paged_attn_decode", "paged_attn_combine", "paged_attn_prefill"]

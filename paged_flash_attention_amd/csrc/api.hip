@@ -1,0 +1,206 @@
+// The C ABI of include/pfa.h: host-side argument checks, then one launch on the
+// caller's stream.  Nothing here allocates or keeps state beyond the thread-local
+// last HIP error.
+#include "pfa.h"
+
+#include "pfa_device.h"
+
+namespace {
+
+thread_local int32_t g_last_hip_error = 0;
+
+pfa_status hip_status(hipError_t e) {
+    if (e == hipSuccess) return PFA_OK;
+    g_last_hip_error = (int32_t)e;
+    return PFA_ERR_HIP;
+}
+
+pfa_status check_desc(const pfa_attn_desc* d) {
+    if (!d) return PFA_ERR_NULL;
+    if (d->num_q_heads <= 0 || d->num_kv_heads <= 0 || d->num_q_heads % d->num_kv_heads != 0)
+        return PFA_ERR_SHAPE;
+    if (d->window < 0) return PFA_ERR_SHAPE;
+    if (d->head_dim != 64 && d->head_dim != 128) return PFA_ERR_UNSUPPORTED;
+    if (d->page_size != 16) return PFA_ERR_UNSUPPORTED;
+    if (d->kv_dtype != PFA_KV_BF16 && d->kv_dtype != PFA_KV_INT8) return PFA_ERR_UNSUPPORTED;
+    return PFA_OK;
+}
+
+pfa_status check_pool(const pfa_attn_desc* d, const pfa_kv_pool* p) {
+    if (!p || !p->k_pool || !p->v_pool) return PFA_ERR_NULL;
+    if (d->kv_dtype == PFA_KV_INT8 && (!p->k_scale || !p->v_scale)) return PFA_ERR_NULL;
+    if (p->num_pages <= 0) return PFA_ERR_SHAPE;
+    return PFA_OK;
+}
+
+bool decode_group_ok(int g) { return g == 1 || g == 2 || g == 4 || g == 8; }
+
+bool prefill_group_ok(int g) {
+    return g == 1 || g == 2 || g == 4 || g == 8 || g == 16 || g == 32;
+}
+
+#define PFA_TRY(expr)                    \
+    do {                                 \
+        pfa_status st_ = (expr);         \
+        if (st_ != PFA_OK) return st_;   \
+    } while (0)
+
+}  // namespace
+
+extern "C" {
+
+pfa_status pfa_kv_write(const pfa_attn_desc* desc, const pfa_kv_pool* pool, const void* k_new,
+                        const void* v_new, const int32_t* cu_new, const int32_t* seq_lens,
+                        const int32_t* block_table, int32_t bt_stride, int32_t batch,
+                        int32_t num_tokens, void* stream) {
+    PFA_TRY(check_desc(desc));
+    PFA_TRY(check_pool(desc, pool));
+    if (batch < 0 || num_tokens < 0 || bt_stride <= 0) return PFA_ERR_SHAPE;
+    if (num_tokens > 0 && batch == 0) return PFA_ERR_SHAPE;
+    if (num_tokens == 0) return PFA_OK;
+    if (!k_new || !v_new || !cu_new || !seq_lens || !block_table) return PFA_ERR_NULL;
+    pfa::KvWriteArgs a;
+    a.k_new = static_cast<const uint16_t*>(k_new);
+    a.v_new = static_cast<const uint16_t*>(v_new);
+    a.cu_new = cu_new;
+    a.seq_lens = seq_lens;
+    a.block_table = block_table;
+    a.k_pool = pool->k_pool;
+    a.v_pool = pool->v_pool;
+    a.k_scale = pool->k_scale;
+    a.v_scale = pool->v_scale;
+    a.bt_stride = bt_stride;
+    a.batch = batch;
+    a.num_tokens = num_tokens;
+    a.num_pages = pool->num_pages;
+    a.num_kv_heads = desc->num_kv_heads;
+    a.head_dim = desc->head_dim;
+    return hip_status(pfa::launch_kv_write(a, desc->kv_dtype == PFA_KV_INT8, (hipStream_t)stream));
+}
+
+int32_t pfa_decode_num_splits(int32_t max_seq_len, int32_t split_keys) {
+    if (split_keys <= 0) return 0;
+    if (max_seq_len <= 0) return 1;
+    return (int32_t)(((int64_t)max_seq_len + split_keys - 1) / split_keys);
+}
+
+pfa_status pfa_paged_attn_decode(const pfa_attn_desc* desc, const pfa_kv_pool* pool, const void* q,
+                                 const int32_t* block_table, int32_t bt_stride,
+                                 const int32_t* seq_lens, int32_t batch, int32_t max_seq_len,
+                                 int32_t split_keys, int32_t max_splits, float* o_part,
+                                 float* lse_part, float* out, void* stream) {
+    PFA_TRY(check_desc(desc));
+    PFA_TRY(check_pool(desc, pool));
+    const int g = desc->num_q_heads / desc->num_kv_heads;
+    if (!decode_group_ok(g)) return PFA_ERR_UNSUPPORTED;
+    if (batch < 0 || batch > 65535 || bt_stride <= 0 || max_seq_len < 0 || max_splits < 1 ||
+        desc->num_kv_heads > 65535)
+        return PFA_ERR_SHAPE;
+    if (max_seq_len > (int64_t)bt_stride * desc->page_size) return PFA_ERR_SHAPE;
+    if (batch == 0) return PFA_OK;
+    if (!q || !block_table || !seq_lens) return PFA_ERR_NULL;
+    if (max_splits == 1) {
+        if (!out) return PFA_ERR_NULL;
+    } else {
+        if (split_keys <= 0 || split_keys % desc->page_size != 0) return PFA_ERR_SHAPE;
+        if (max_splits < pfa_decode_num_splits(max_seq_len, split_keys)) return PFA_ERR_WORKSPACE;
+        if (!o_part || !lse_part) return PFA_ERR_NULL;
+    }
+    pfa::DecodeArgs a;
+    a.q = static_cast<const uint16_t*>(q);
+    a.k_pool = pool->k_pool;
+    a.v_pool = pool->v_pool;
+    a.k_scale = pool->k_scale;
+    a.v_scale = pool->v_scale;
+    a.block_table = block_table;
+    a.seq_lens = seq_lens;
+    a.sinks = desc->sinks;
+    a.o_part = o_part;
+    a.lse_part = lse_part;
+    a.out = out;
+    a.bt_stride = bt_stride;
+    a.batch = batch;
+    a.num_pages = pool->num_pages;
+    a.num_q_heads = desc->num_q_heads;
+    a.num_kv_heads = desc->num_kv_heads;
+    a.split_keys = max_splits == 1 ? 0 : split_keys;
+    a.max_splits = max_splits;
+    a.window = desc->window;
+    a.sm_scale = desc->sm_scale;
+    return hip_status(pfa::launch_decode(a, desc->head_dim, desc->kv_dtype == PFA_KV_INT8,
+                                         (hipStream_t)stream));
+}
+
+pfa_status pfa_paged_attn_combine(const pfa_attn_desc* desc, const float* o_part,
+                                  const float* lse_part, const int32_t* seq_lens, int32_t batch,
+                                  int32_t split_keys, int32_t max_splits, float* out,
+                                  void* stream) {
+    PFA_TRY(check_desc(desc));
+    if (batch < 0 || max_splits < 1 || split_keys <= 0 || split_keys % desc->page_size != 0)
+        return PFA_ERR_SHAPE;
+    if ((int64_t)batch * desc->num_q_heads > 0x7fffffff) return PFA_ERR_SHAPE;
+    if (batch == 0) return PFA_OK;
+    if (!o_part || !lse_part || !seq_lens || !out) return PFA_ERR_NULL;
+    pfa::CombineArgs a;
+    a.o_part = o_part;
+    a.lse_part = lse_part;
+    a.seq_lens = seq_lens;
+    a.sinks = desc->sinks;
+    a.out = out;
+    a.batch = batch;
+    a.num_q_heads = desc->num_q_heads;
+    a.split_keys = split_keys;
+    a.max_splits = max_splits;
+    return hip_status(pfa::launch_combine(a, desc->head_dim, (hipStream_t)stream));
+}
+
+pfa_status pfa_paged_attn_prefill(const pfa_attn_desc* desc, const pfa_kv_pool* pool, const void* q,
+                                  const int32_t* cu_q, const int32_t* block_table,
+                                  int32_t bt_stride, const int32_t* seq_lens, int32_t batch,
+                                  int32_t max_q_len, float* out, void* stream) {
+    PFA_TRY(check_desc(desc));
+    PFA_TRY(check_pool(desc, pool));
+    if (desc->kv_dtype != PFA_KV_BF16) return PFA_ERR_UNSUPPORTED;
+    const int g = desc->num_q_heads / desc->num_kv_heads;
+    if (!prefill_group_ok(g)) return PFA_ERR_UNSUPPORTED;
+    if (batch < 0 || max_q_len < 0 || bt_stride <= 0) return PFA_ERR_SHAPE;
+    const int tpb = 128 / g;
+    const int64_t items = (int64_t)batch * desc->num_kv_heads * ((max_q_len + tpb - 1) / tpb);
+    if (items > 0x7fffffff - 8) return PFA_ERR_SHAPE;
+    if (batch == 0 || max_q_len == 0) return PFA_OK;
+    if (!q || !cu_q || !block_table || !seq_lens || !out) return PFA_ERR_NULL;
+    pfa::PrefillArgs a;
+    a.q = static_cast<const uint16_t*>(q);
+    a.k_pool = static_cast<const uint16_t*>(pool->k_pool);
+    a.v_pool = static_cast<const uint16_t*>(pool->v_pool);
+    a.cu_q = cu_q;
+    a.block_table = block_table;
+    a.seq_lens = seq_lens;
+    a.sinks = desc->sinks;
+    a.out = out;
+    a.bt_stride = bt_stride;
+    a.batch = batch;
+    a.num_pages = pool->num_pages;
+    a.num_q_heads = desc->num_q_heads;
+    a.num_kv_heads = desc->num_kv_heads;
+    a.max_q_len = max_q_len;
+    a.window = desc->window;
+    a.sm_scale = desc->sm_scale;
+    return hip_status(pfa::launch_prefill(a, desc->head_dim, (hipStream_t)stream));
+}
+
+const char* pfa_status_string(pfa_status s) {
+    switch (s) {
+        case PFA_OK: return "ok";
+        case PFA_ERR_NULL: return "a required pointer is NULL";
+        case PFA_ERR_SHAPE: return "sizes inconsistent or out of range";
+        case PFA_ERR_UNSUPPORTED: return "shape or dtype not supported by this build";
+        case PFA_ERR_WORKSPACE: return "split buffers too small (max_splits < ceil(max_seq_len/split_keys))";
+        case PFA_ERR_HIP: return "HIP launch failed";
+    }
+    return "unknown status";
+}
+
+int32_t pfa_last_hip_error(void) { return g_last_hip_error; }
+
+}  // extern "C"

@@ -1,0 +1,144 @@
+// KV write: scatter new tokens' K/V rows into their pages.
+//
+// The TileInfer.jl performance page lists the KV cache write among the engine's
+// per-op kernels ("Fused kernels, FlashAttention and PagedAttention").  Its
+// "INT8 KV cache" section stores one scale per cached vector.  For BF16 pools this
+// kernel copies the bits.  For INT8 pools it quantises each (token, KV head) vector:
+//   scale = absmax/127 in IEEE fp32;
+//   code  = clamp(rint(x/scale), +-127), ties to even;
+//   a zero vector gets scale 0.
+//
+// Each thread owns 8 consecutive elements (16 B of bf16 input) of one vector for
+// both K and V, so D/8 lanes share a vector.  The absmax is a max over those lanes
+// with DPP/swizzle moves.  Loads and stores are 16 B (codes: 8 B) per lane and are
+// contiguous across the lanes of a vector.  The kernel is HBM-bound: it reads
+// 2*D*2 B and writes 2*D*b B (+8 B scales) per (token, head).
+#include "pfa_device.h"
+
+namespace pfa {
+namespace {
+
+__device__ __forceinline__ int find_seq(const int32_t* __restrict__ cu, int batch, int tok) {
+    // largest s with cu[s] <= tok (cu nondecreasing, cu[0] = 0)
+    int lo = 0, hi = batch - 1;
+    while (lo < hi) {
+        int mid = (lo + hi + 1) >> 1;
+        if (__ldg(cu + mid) <= tok) lo = mid; else hi = mid - 1;
+    }
+    return lo;
+}
+
+template <int D>
+__device__ __forceinline__ float group_absmax(float m) {
+    constexpr int L = D / 8;  // lanes per vector
+    if constexpr (L >= 16) m = xor_max<8>(m);
+    if constexpr (L >= 8) m = xor_max<4>(m);
+    m = xor_max<2>(m);
+    m = xor_max<1>(m);
+    return m;
+}
+
+// Quantise 8 elements whose vector absmax is `amax`; returns the 8 codes packed.
+__device__ __forceinline__ uint2 quantise8(const float (&x)[8], float scale) {
+    uint32_t w[2] = {0u, 0u};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        float c = 0.0f;
+        if (scale > 0.0f) {
+            c = __builtin_rintf(x[i] / scale);
+            c = fminf(fmaxf(c, -127.0f), 127.0f);
+        }
+        uint32_t b = (uint32_t)((int32_t)c) & 0xffu;
+        w[i >> 2] |= b << (8 * (i & 3));
+    }
+    return make_uint2(w[0], w[1]);
+}
+
+template <int D, bool INT8>
+__global__ __launch_bounds__(256) void kv_write_kernel(KvWriteArgs a) {
+    constexpr int L = D / 8;
+    const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t vec = t / L;
+    const int chunk = (int)(t % L);
+    const int64_t nvec = (int64_t)a.num_tokens * a.num_kv_heads;
+    bool ok = vec < nvec;
+    int tok = 0, head = 0;
+    int64_t dst = 0;  // element index of this lane's chunk in the pool
+    int64_t sdst = 0; // scale index
+    if (ok) {
+        tok = (int)(vec / a.num_kv_heads);
+        head = (int)(vec % a.num_kv_heads);
+        const int s = find_seq(a.cu_new, a.batch, tok);
+        const int c0 = __ldg(a.cu_new + s), c1 = __ldg(a.cu_new + s + 1);
+        const int pos = __ldg(a.seq_lens + s) - (c1 - c0) + (tok - c0);
+        const int pidx = pos / kPage;
+        ok = tok < c1 && pos >= 0 && pidx < a.bt_stride;
+        if (ok) {
+            const int page = __ldg(a.block_table + (int64_t)s * a.bt_stride + pidx);
+            ok = page >= 0 && page < a.num_pages;
+            sdst = ((int64_t)page * a.num_kv_heads + head) * kPage + (pos % kPage);
+            dst = sdst * D + chunk * 8;
+        }
+    }
+    const int64_t src = vec * D + chunk * 8;
+    uint4 kin = make_uint4(0, 0, 0, 0), vin = make_uint4(0, 0, 0, 0);
+    if (vec < nvec) {
+        kin = *reinterpret_cast<const uint4*>(a.k_new + src);
+        vin = *reinterpret_cast<const uint4*>(a.v_new + src);
+    }
+    if constexpr (!INT8) {
+        if (ok) {
+            *reinterpret_cast<uint4*>(static_cast<uint16_t*>(a.k_pool) + dst) = kin;
+            *reinterpret_cast<uint4*>(static_cast<uint16_t*>(a.v_pool) + dst) = vin;
+        }
+    } else {
+        float kx[8], vx[8];
+        const uint32_t kw[4] = {kin.x, kin.y, kin.z, kin.w};
+        const uint32_t vw[4] = {vin.x, vin.y, vin.z, vin.w};
+        float km = 0.0f, vm = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            kx[2 * i] = bf16_lo(kw[i]);
+            kx[2 * i + 1] = bf16_hi(kw[i]);
+            vx[2 * i] = bf16_lo(vw[i]);
+            vx[2 * i + 1] = bf16_hi(vw[i]);
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            km = fmaxf(km, fabsf(kx[i]));
+            vm = fmaxf(vm, fabsf(vx[i]));
+        }
+        km = group_absmax<D>(km);
+        vm = group_absmax<D>(vm);
+        const float ks = km / 127.0f;
+        const float vs = vm / 127.0f;
+        const uint2 kc = quantise8(kx, ks);
+        const uint2 vc = quantise8(vx, vs);
+        if (ok) {
+            *reinterpret_cast<uint2*>(static_cast<int8_t*>(a.k_pool) + dst) = kc;
+            *reinterpret_cast<uint2*>(static_cast<int8_t*>(a.v_pool) + dst) = vc;
+            if (chunk == 0) {
+                a.k_scale[sdst] = ks;
+                a.v_scale[sdst] = vs;
+            }
+        }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_kv_write(const KvWriteArgs& a, bool int8, hipStream_t s) {
+    const int64_t threads = (int64_t)a.num_tokens * a.num_kv_heads * (a.head_dim / 8);
+    if (threads == 0) return hipSuccess;
+    const unsigned grid = (unsigned)((threads + 255) / 256);
+    if (a.head_dim == 128) {
+        if (int8) hipLaunchKernelGGL((kv_write_kernel<128, true>), dim3(grid), dim3(256), 0, s, a);
+        else hipLaunchKernelGGL((kv_write_kernel<128, false>), dim3(grid), dim3(256), 0, s, a);
+    } else {
+        if (int8) hipLaunchKernelGGL((kv_write_kernel<64, true>), dim3(grid), dim3(256), 0, s, a);
+        else hipLaunchKernelGGL((kv_write_kernel<64, false>), dim3(grid), dim3(256), 0, s, a);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace pfa

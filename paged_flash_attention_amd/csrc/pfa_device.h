@@ -1,0 +1,159 @@
+// Device-side helpers shared by the gfx950 kernels: bf16 unpacking, cross-lane
+// moves within a 64-wide wavefront, and the launch-side declarations each kernel
+// file exports to the C-ABI layer.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pfa {
+
+constexpr int kWave = 64;
+constexpr int kPage = 16;
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+// bf16 pair packed in a dword -> the two floats (exact).
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+__device__ __forceinline__ bf16x2 as_bf16x2(uint32_t w) { return __builtin_bit_cast(bf16x2, w); }
+
+// Two floats that are exact in bf16 (small integers) -> packed pair, by truncation.
+__device__ __forceinline__ uint32_t pack_hi16(float lo, float hi) {
+    return __builtin_amdgcn_perm(__float_as_uint(hi), __float_as_uint(lo), 0x07060302u);
+}
+
+// Round two floats to bf16 (nearest, ties to even) and pack.
+__device__ __forceinline__ uint32_t pack_bf16_rne(float lo, float hi) {
+    bf16x2 v = {(__bf16)lo, (__bf16)hi};
+    return __builtin_bit_cast(uint32_t, v);
+}
+
+// ---- cross-lane moves -------------------------------------------------------
+// x from lane (lane ^ M).  Chooses a DPP or swizzle form where one exists.
+template <int M>
+__device__ __forceinline__ float xor_lane(float x) {
+    int v = __float_as_int(x);
+    int r;
+    if constexpr (M == 1) {
+        r = __builtin_amdgcn_mov_dpp(v, 0xB1, 0xF, 0xF, true);        // quad_perm [1,0,3,2]
+    } else if constexpr (M == 2) {
+        r = __builtin_amdgcn_mov_dpp(v, 0x4E, 0xF, 0xF, true);        // quad_perm [2,3,0,1]
+    } else if constexpr (M == 8) {
+        r = __builtin_amdgcn_mov_dpp(v, 0x128, 0xF, 0xF, true);       // row_ror:8
+    } else if constexpr (M == 4 || M == 16) {
+        r = __builtin_amdgcn_ds_swizzle(v, (M << 10) | 0x1F);         // bitmask mode, xor M
+    } else {
+        static_assert(M == 32, "xor mask");
+        r = __builtin_amdgcn_ds_bpermute((int)((__lane_id() ^ 32) << 2), v);
+    }
+    return __int_as_float(r);
+}
+
+// x from lane ((lane & ~(W-1)) | src) for groups of W lanes, W in {4, 8, 16, 32}.
+template <int W>
+__device__ __forceinline__ float group_bcast(float x, int src) {
+    return __int_as_float(__builtin_amdgcn_ds_bpermute(
+        (int)(((__lane_id() & ~(W - 1)) | src) << 2), __float_as_int(x)));
+}
+
+template <int M>
+__device__ __forceinline__ float xor_sum(float x) { return x + xor_lane<M>(x); }
+template <int M>
+__device__ __forceinline__ float xor_max(float x) { return fmaxf(x, xor_lane<M>(x)); }
+
+// Sum / max over all lanes whose ids differ only in bits [LO, 64): lane groups
+// of stride LO.  LO is a power of two < 64.
+template <int LO>
+__device__ __forceinline__ float stride_sum(float x) {
+    if constexpr (LO <= 1) x = xor_sum<1>(x);
+    if constexpr (LO <= 2) x = xor_sum<2>(x);
+    if constexpr (LO <= 4) x = xor_sum<4>(x);
+    if constexpr (LO <= 8) x = xor_sum<8>(x);
+    if constexpr (LO <= 16) x = xor_sum<16>(x);
+    x = xor_sum<32>(x);
+    return x;
+}
+template <int LO>
+__device__ __forceinline__ float stride_max(float x) {
+    if constexpr (LO <= 1) x = xor_max<1>(x);
+    if constexpr (LO <= 2) x = xor_max<2>(x);
+    if constexpr (LO <= 4) x = xor_max<4>(x);
+    if constexpr (LO <= 8) x = xor_max<8>(x);
+    if constexpr (LO <= 16) x = xor_max<16>(x);
+    x = xor_max<32>(x);
+    return x;
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+
+}  // namespace pfa
+
+// ---- launchers exported by each kernel file to the C-ABI layer ---------------
+namespace pfa {
+
+struct KvWriteArgs {
+    const uint16_t* k_new;
+    const uint16_t* v_new;
+    const int32_t* cu_new;
+    const int32_t* seq_lens;
+    const int32_t* block_table;
+    void* k_pool;
+    void* v_pool;
+    float* k_scale;
+    float* v_scale;
+    int32_t bt_stride, batch, num_tokens, num_pages, num_kv_heads, head_dim;
+};
+
+struct DecodeArgs {
+    const uint16_t* q;
+    const void* k_pool;
+    const void* v_pool;
+    const float* k_scale;
+    const float* v_scale;
+    const int32_t* block_table;
+    const int32_t* seq_lens;
+    const float* sinks;
+    float* o_part;
+    float* lse_part;
+    float* out;
+    int32_t bt_stride, batch, num_pages, num_q_heads, num_kv_heads;
+    int32_t split_keys, max_splits, window;
+    float sm_scale;
+};
+
+struct CombineArgs {
+    const float* o_part;
+    const float* lse_part;
+    const int32_t* seq_lens;
+    const float* sinks;
+    float* out;
+    int32_t batch, num_q_heads, split_keys, max_splits;
+};
+
+struct PrefillArgs {
+    const uint16_t* q;
+    const uint16_t* k_pool;
+    const uint16_t* v_pool;
+    const int32_t* cu_q;
+    const int32_t* block_table;
+    const int32_t* seq_lens;
+    const float* sinks;
+    float* out;
+    int32_t bt_stride, batch, num_pages, num_q_heads, num_kv_heads, max_q_len, window;
+    float sm_scale;
+};
+
+hipError_t launch_kv_write(const KvWriteArgs& a, bool int8, hipStream_t s);
+hipError_t launch_decode(const DecodeArgs& a, int head_dim, bool int8, hipStream_t s);
+hipError_t launch_combine(const CombineArgs& a, int head_dim, hipStream_t s);
+hipError_t launch_prefill(const PrefillArgs& a, int head_dim, hipStream_t s);
+
+}  // namespace pfa

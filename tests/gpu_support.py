@@ -1,0 +1,133 @@
+"""Helpers for the GPU parity tests: move a seeded case to the device, fill a GPU
+pool with the library's own kv_write, run decode/combine/prefill through the
+C ABI, and fill the oracle's pool the same way on the CPU.  No test lives here."""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import oracle as O
+import paged_flash_attention_amd as pfa
+import workloads as W
+
+BF16_TOL = dict(max_abs=1e-2, rel_l2=5e-3)
+INT8_TOL = dict(max_abs=3e-2, rel_l2=None)
+
+
+def dev_bf16(bits: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
+
+
+def dev_i32(x) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(x, dtype=np.int32)).cuda()
+
+
+def bits_of(t: torch.Tensor) -> np.ndarray:
+    return t.view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def desc_of(p: W.AttnParams) -> pfa.AttnDesc:
+    sinks = None if p.sinks is None else torch.from_numpy(np.asarray(p.sinks, np.float32)).cuda()
+    return pfa.AttnDesc(p.num_q_heads, p.num_kv_heads, p.head_dim, p.page_size, p.kv_dtype,
+                        p.window, p.sm_scale, sinks)
+
+
+def poisoned_pool(case: W.PagedCase) -> pfa.KVPool:
+    p = case.p
+    shape = (case.num_pages, p.num_kv_heads, p.page_size, p.head_dim)
+    if p.kv_dtype == "bf16":
+        k = torch.full(shape, float("nan"), dtype=torch.bfloat16, device="cuda")
+        return pfa.KVPool(k, k.clone())
+    k = torch.zeros(shape, dtype=torch.int8, device="cuda")
+    s = torch.full(shape[:3], float("nan"), dtype=torch.float32, device="cuda")
+    return pfa.KVPool(k, k.clone(), s, s.clone())
+
+
+class GpuCase:
+    """Device copies of a case's inputs, and the pool filled by the GPU kv_write."""
+
+    def __init__(self, case: W.PagedCase, fill=True):
+        self.case = case
+        self.desc = desc_of(case.p)
+        self.bt = dev_i32(case.block_table)
+        self.seq_lens = dev_i32(case.seq_lens)
+        self.q = dev_bf16(case.q)
+        self.cu_q = dev_i32(case.cu_q)
+        self.pool = poisoned_pool(case)
+        if fill:
+            self.write_prefix()
+            self.write_new()
+
+    def write_prefix(self):
+        k, v, cu = self.case.prefix_tokens()
+        if k.shape[0]:
+            pfa.kv_write(self.desc, self.pool, dev_bf16(k), dev_bf16(v), dev_i32(cu),
+                         dev_i32(self.case.prefix_lens()), self.bt)
+
+    def write_new(self):
+        k, v, cu = self.case.new_tokens()
+        if k.shape[0]:
+            pfa.kv_write(self.desc, self.pool, dev_bf16(k), dev_bf16(v), dev_i32(cu), self.seq_lens, self.bt)
+
+    def decode(self, split_keys=256, max_splits=None, keep_parts=False):
+        c = self.case
+        B, Hq, D = c.batch, c.p.num_q_heads, c.p.head_dim
+        max_len = int(c.seq_lens.max())
+        if max_splits is None:
+            max_splits = 1 if split_keys == 0 else pfa.decode_num_splits(max_len, split_keys)
+        out = torch.full((B, Hq, D), float("nan"), device="cuda")
+        if max_splits == 1:
+            pfa.paged_attn_decode(self.desc, self.pool, self.q, self.bt, self.seq_lens, max_len, 0, 1, out=out)
+            parts = None
+        else:
+            op = torch.full((B, Hq, max_splits, D), float("nan"), device="cuda")
+            lp = torch.full((B, Hq, max_splits), float("nan"), device="cuda")
+            pfa.paged_attn_decode(self.desc, self.pool, self.q, self.bt, self.seq_lens, max_len,
+                                  split_keys, max_splits, o_part=op, lse_part=lp)
+            pfa.paged_attn_combine(self.desc, op, lp, self.seq_lens, split_keys, max_splits, out)
+            parts = (op, lp)
+        torch.cuda.synchronize()
+        if keep_parts:
+            return out.cpu().numpy(), parts
+        return out.cpu().numpy()
+
+    def prefill(self):
+        c = self.case
+        out = torch.full((int(c.cu_q[-1]), c.p.num_q_heads, c.p.head_dim), float("nan"), device="cuda")
+        pfa.paged_attn_prefill(self.desc, self.pool, self.q, self.cu_q, self.bt, self.seq_lens,
+                               int(c.q_lens.max()), out)
+        torch.cuda.synchronize()
+        return out.cpu().numpy()
+
+
+def oracle_pool(case: W.PagedCase) -> dict:
+    p = case.p
+    pool = O.empty_pool(case.num_pages, p.num_kv_heads, p.page_size, p.head_dim, p.kv_dtype)
+    k, v, cu = case.prefix_tokens()
+    O.kv_write(pool, k, v, cu, case.prefix_lens(), case.block_table, p.page_size, p.kv_dtype)
+    k, v, cu = case.new_tokens()
+    O.kv_write(pool, k, v, cu, case.seq_lens, case.block_table, p.page_size, p.kv_dtype)
+    return pool
+
+
+def errors(got: np.ndarray, ref: np.ndarray):
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    d = got - ref
+    max_abs = float(np.max(np.abs(d))) if d.size else 0.0
+    rel = float(np.linalg.norm(d) / max(np.linalg.norm(ref), 1e-300)) if d.size else 0.0
+    return max_abs, rel
+
+
+def assert_close(got, ref, tol, what=""):
+    assert np.all(np.isfinite(got)), f"{what}: non-finite values in GPU output"
+    max_abs, rel = errors(got, ref)
+    msg = f"{what}: max_abs={max_abs:.3e} rel_l2={rel:.3e} tol={tol}"
+    print(msg, flush=True)
+    assert max_abs <= tol["max_abs"], msg
+    if tol.get("rel_l2") is not None:
+        assert rel <= tol["rel_l2"], msg
+
+
+def tol_of(case):
+    return INT8_TOL if case.p.kv_dtype == "int8" else BF16_TOL

@@ -1,0 +1,149 @@
+"""The C-ABI library on a machine without a GPU.
+
+These tests check that libpfa.so loads and exports every symbol include/pfa.h
+declares.  They also check that host-side validation returns the documented
+status codes without launching anything.  Every call here fails before any HIP
+call is made.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import paged_flash_attention_amd as pfa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "pfa.h")
+
+OK, NULL, SHAPE, UNSUP, WORKSPACE, HIP = 0, 1, 2, 3, 4, 5
+FAKE = ctypes.c_void_p(0x1000)   # never dereferenced: validation fails first
+
+
+def header_symbols():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\*?(pfa_\w+)\s*\(", text, re.M)))
+
+
+def test_library_exports_every_declared_symbol():
+    L = pfa.lib()
+    syms = header_symbols()
+    assert set(syms) == set(pfa.EXPORTS), syms
+    for s in syms:
+        assert hasattr(L, s), s
+
+
+def test_status_strings_and_splits():
+    L = pfa.lib()
+    for st in range(6):
+        assert L.pfa_status_string(st)
+    assert L.pfa_status_string(99) == b"unknown status"
+    assert pfa.decode_num_splits(8192, 256) == 32
+    assert pfa.decode_num_splits(8193, 256) == 33
+    assert pfa.decode_num_splits(1, 256) == 1
+    assert pfa.decode_num_splits(100, 0) == 0
+    assert L.pfa_last_hip_error() == 0
+
+
+def desc(**kw):
+    d = dict(num_q_heads=32, num_kv_heads=8, head_dim=128, page_size=16, kv_dtype=0, window=0,
+             sm_scale=0.088, sinks=None)
+    d.update(kw)
+    return pfa.CAttnDesc(**d)
+
+
+def pool(**kw):
+    p = dict(k_pool=FAKE.value, v_pool=FAKE.value, k_scale=None, v_scale=None, num_pages=64)
+    p.update(kw)
+    return pfa.CKvPool(**p)
+
+
+def kvw(d, p, **kw):
+    a = dict(k=FAKE, v=FAKE, cu=FAKE, sl=FAKE, bt=FAKE, stride=8, batch=2, T=2)
+    a.update(kw)
+    return pfa.lib().pfa_kv_write(ctypes.byref(d) if d is not None else None,
+                                  ctypes.byref(p) if p is not None else None,
+                                  a["k"], a["v"], a["cu"], a["sl"], a["bt"], a["stride"], a["batch"], a["T"], None)
+
+
+def test_kv_write_validation():
+    assert kvw(None, pool()) == NULL
+    assert kvw(desc(), None) == NULL
+    assert kvw(desc(num_q_heads=30), pool()) == SHAPE          # Hq % Hkv
+    assert kvw(desc(head_dim=96), pool()) == UNSUP
+    assert kvw(desc(page_size=32), pool()) == UNSUP
+    assert kvw(desc(kv_dtype=7), pool()) == UNSUP
+    assert kvw(desc(window=-1), pool()) == SHAPE
+    assert kvw(desc(kv_dtype=1), pool()) == NULL               # INT8 without scale pools
+    assert kvw(desc(), pool(num_pages=0)) == SHAPE
+    assert kvw(desc(), pool(), k=None) == NULL
+    assert kvw(desc(), pool(), stride=0) == SHAPE
+    assert kvw(desc(), pool(), T=-1) == SHAPE
+    assert kvw(desc(), pool(), batch=0) == SHAPE                # tokens but no sequences
+    assert kvw(desc(), pool(), T=0, k=None) == OK              # nothing to do, nothing launched
+
+
+def dec(d, p, **kw):
+    a = dict(q=FAKE, bt=FAKE, stride=64, sl=FAKE, batch=4, max_len=1024, S=256, ms=4,
+             op=FAKE, lp=FAKE, out=FAKE)
+    a.update(kw)
+    return pfa.lib().pfa_paged_attn_decode(ctypes.byref(d), ctypes.byref(p), a["q"], a["bt"], a["stride"],
+                                           a["sl"], a["batch"], a["max_len"], a["S"], a["ms"],
+                                           a["op"], a["lp"], a["out"], None)
+
+
+def test_decode_validation():
+    assert dec(desc(num_q_heads=48, num_kv_heads=3), pool()) == UNSUP   # G = 16
+    assert dec(desc(), pool(), S=100) == SHAPE                           # not a multiple of P
+    assert dec(desc(), pool(), S=0) == SHAPE
+    assert dec(desc(), pool(), ms=3) == WORKSPACE                        # 1024/256 = 4 splits
+    assert dec(desc(), pool(), max_len=64 * 16 + 1) == SHAPE              # beyond the block table
+    assert dec(desc(), pool(), op=None) == NULL
+    assert dec(desc(), pool(), lp=None) == NULL
+    assert dec(desc(), pool(), ms=1, out=None) == NULL
+    assert dec(desc(), pool(), q=None) == NULL
+    assert dec(desc(), pool(), ms=0) == SHAPE
+    assert dec(desc(), pool(), batch=-1) == SHAPE
+    assert dec(desc(), pool(), batch=0, q=None) == OK
+
+
+def comb(d, **kw):
+    a = dict(op=FAKE, lp=FAKE, sl=FAKE, batch=4, S=256, ms=4, out=FAKE)
+    a.update(kw)
+    return pfa.lib().pfa_paged_attn_combine(ctypes.byref(d), a["op"], a["lp"], a["sl"], a["batch"],
+                                            a["S"], a["ms"], a["out"], None)
+
+
+def test_combine_validation():
+    assert comb(desc(), out=None) == NULL
+    assert comb(desc(), S=8) == SHAPE
+    assert comb(desc(), ms=0) == SHAPE
+    assert comb(desc(head_dim=80)) == UNSUP
+    assert comb(desc(), batch=0, out=None) == OK
+
+
+def pre(d, p, **kw):
+    a = dict(q=FAKE, cu=FAKE, bt=FAKE, stride=64, sl=FAKE, batch=1, mq=1024, out=FAKE)
+    a.update(kw)
+    return pfa.lib().pfa_paged_attn_prefill(ctypes.byref(d), ctypes.byref(p), a["q"], a["cu"], a["bt"],
+                                            a["stride"], a["sl"], a["batch"], a["mq"], a["out"], None)
+
+
+def test_prefill_validation():
+    assert pre(desc(kv_dtype=1), pool(k_scale=FAKE.value, v_scale=FAKE.value)) == UNSUP
+    assert pre(desc(num_q_heads=64 * 3, num_kv_heads=3), pool()) == UNSUP   # G = 64
+    assert pre(desc(), pool(), cu=None) == NULL
+    assert pre(desc(), pool(), out=None) == NULL
+    assert pre(desc(), pool(), mq=-1) == SHAPE
+    assert pre(desc(), pool(), mq=0, q=None) == OK
+
+
+def test_binding_refuses_host_tensors():
+    import torch
+    d = pfa.AttnDesc(4, 2, 64)
+    p = pfa.KVPool(torch.zeros(4, 2, 16, 64, dtype=torch.bfloat16), torch.zeros(4, 2, 16, 64, dtype=torch.bfloat16))
+    with pytest.raises(ValueError):
+        p.c()
+    with pytest.raises(ValueError):
+        pfa.paged_attn_combine(d, torch.zeros(1), torch.zeros(1), torch.zeros(1, dtype=torch.int32), 16, 1,
+                               torch.zeros(1))

@@ -1,0 +1,95 @@
+"""Parity at the full workload sizes, in the launch configuration the benchmark
+times.  Outputs are compared whole where the oracle is quick.  For the long
+prefills the oracle computes sampled query rows one by one: the first and last
+rows of the chunk plus seeded random ones.
+
+Workloads:
+* decode, 1 sequence at 1024 positions (16 q / 8 KV heads, D 128): split and unsplit;
+* batched decode, Qwen3-4B attention (32/8, D 128), batch 32, lengths U[512, 8192];
+* causal prefill, Llama-3.1-8B attention (32/8, D 128): 1024 and 8192 tokens,
+  and 130 new tokens on a restored 8192-token prefix;
+* INT8-KV decode, Qwen3-30B-A3B attention (32/4, D 128), batch 8 at 32768 positions;
+* gpt-oss-20b attention (64/8, D 64, sinks), window-128 and full layers: batch-64
+  decode with lengths log-uniform in [128, 32768], and two 2048-token prefills.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import workloads as W
+from gpu_support import BF16_TOL, GpuCase, assert_close, oracle_pool, tol_of
+
+pytestmark = [pytest.mark.gpu, pytest.mark.slow]
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def _decode_check(case, splits=(256,)):
+    print(f"[full] {case.name}: B={case.batch} max_len={int(case.seq_lens.max())}", flush=True)
+    g = GpuCase(case)
+    ref = O.decode(case.q, oracle_pool(case), case.block_table, case.seq_lens, case.p)
+    for S in splits:
+        assert_close(g.decode(S), ref, tol_of(case), f"{case.name} S={S}")
+
+
+def _prefill_check(case, sample=None, seed=0):
+    print(f"[full] {case.name}: q_tokens={int(case.cu_q[-1])}", flush=True)
+    g = GpuCase(case)
+    got = g.prefill()
+    Tq = int(case.cu_q[-1])
+    if sample is None or sample >= Tq:
+        rows = np.arange(Tq)
+    else:
+        rng = np.random.default_rng(seed)
+        ends = []
+        for s in range(case.batch):
+            a, b = int(case.cu_q[s]), int(case.cu_q[s + 1])
+            ends += list(range(a, min(a + 16, b))) + list(range(max(a, b - 16), b))
+        rows = np.unique(np.concatenate([np.array(ends, np.int64),
+                                         rng.choice(Tq, size=sample, replace=False)]))
+    ref = O.paged_attention(case.q, case.cu_q, oracle_pool(case), case.block_table, case.seq_lens,
+                            case.p, rows=rows, max_rows_per_chunk=64)
+    assert_close(got[rows], ref, BF16_TOL, f"{case.name} ({len(rows)} rows)")
+
+
+def test_decode_1seq_ctx1024():
+    _decode_check(W.decode_1seq_ctx1024(), splits=(0, 256))
+
+
+def test_decode_batch32_ctx512_8192():
+    _decode_check(W.decode_batch32_ctx512_8192())
+
+
+def test_decode_batch32_ctx8192():
+    _decode_check(W.decode_batch32_ctx512_8192(fixed_len=8192))
+
+
+def test_prefill_causal_1024():
+    _prefill_check(W.prefill_llama8b(prompt=1024))
+
+
+def test_prefill_causal_8192_sampled():
+    _prefill_check(W.prefill_llama8b(prompt=8192), sample=224)
+
+
+def test_prefill_chunk130_on_8192():
+    _prefill_check(W.prefill_llama8b(prompt=130, prefix=8192))
+
+
+def test_decode_int8_batch8_ctx32768():
+    _decode_check(W.decode_int8_qwen30b())
+
+
+@pytest.mark.parametrize("layer", ["window", "full"])
+def test_mixed_gptoss_decode(layer):
+    _decode_check(W.mixed_gptoss(layer=layer, part="decode"), splits=(256,))
+
+
+@pytest.mark.parametrize("layer", ["window", "full"])
+def test_mixed_gptoss_prefill(layer):
+    _prefill_check(W.mixed_gptoss(layer=layer, part="prefill"), sample=256)

@@ -1,0 +1,226 @@
+"""Parity of the HIP path (through the C ABI) with the CPU float64 oracle.
+
+Bars, from the target tolerances:
+* BF16 KV: max-abs 1e-2 and rel-L2 5e-3 over each call's whole output.
+* INT8 KV: max-abs 3e-2, graded against the oracle on the dequantised cache.
+* The INT8 quantiser and the BF16 KV write: bit-exact.
+
+Every pool starts poisoned, with NaN in BF16 slots and NaN scales in INT8 ones,
+so a read of an unwritten slot shows up as a non-finite output.
+"""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import paged_flash_attention_amd as pfa
+import workloads as W
+from gpu_support import (BF16_TOL, INT8_TOL, GpuCase, assert_close, bits_of, dev_bf16, dev_i32,
+                         oracle_pool, tol_of)
+
+pytestmark = pytest.mark.gpu
+
+HERE = os.path.dirname(__file__)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    pfa.lib()
+
+
+def P(Hq, Hkv, D, window=0, sinks=False, kv="bf16", seed=0):
+    return W.AttnParams(Hq, Hkv, D, kv_dtype=kv, window=window,
+                        sinks=W.sinks_normal(seed + 31, Hq) if sinks else None)
+
+
+# ---------------------------------------------------------------------------
+# kv_write
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_kv_write_bf16_bitwise(D):
+    case = W.make_case("kvw", 1, P(8, 4, D), [1, 17, 40, 300], [1, 5, 40, 33])
+    g = GpuCase(case)
+    ref = oracle_pool(case)
+    torch.cuda.synchronize()
+    assert np.array_equal(bits_of(g.pool.k), ref["k"])
+    assert np.array_equal(bits_of(g.pool.v), ref["v"])
+
+
+def _golden_vectors(D):
+    rows = []
+    for line in open(os.path.join(HERE, "golden", "int8_quantiser.txt")):
+        line = line.split("#", 1)[0].strip()
+        if line:
+            xs = [float(t) for t in line.split()[0].split(",")]
+            v = np.zeros(D, np.float32)
+            v[: len(xs)] = xs
+            rows.append(v)
+    return W.f32_to_bf16_bits(np.stack(rows))
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_kv_write_int8_bitwise(D):
+    case = W.make_case("kvw8", 2, P(8, 2, D, kv="int8"), [3, 30, 70], [3, 30, 9], outlier_frac=0.01)
+    gold = _golden_vectors(D)                                 # ties, exact scales, a zero vector
+    n = min(len(gold), case.k_tok.shape[0])
+    case.k_tok[:n, 0] = gold[:n]
+    case.v_tok[-n:, 1] = gold[:n]
+    g = GpuCase(case)
+    ref = oracle_pool(case)
+    torch.cuda.synchronize()
+    assert np.array_equal(g.pool.k.cpu().numpy(), ref["k"])
+    assert np.array_equal(g.pool.v.cpu().numpy(), ref["v"])
+    ks, vs = g.pool.k_scale.cpu().numpy(), g.pool.v_scale.cpu().numpy()
+    assert np.array_equal(ks.view(np.uint32), ref["k_scale"].view(np.uint32))   # NaN poison included
+    assert np.array_equal(vs.view(np.uint32), ref["v_scale"].view(np.uint32))
+
+
+# ---------------------------------------------------------------------------
+# decode + combine
+# ---------------------------------------------------------------------------
+
+DECODE_CASES = [
+    # (params, lens, split_keys list)
+    (dict(Hq=16, Hkv=8, D=128), [1, 15, 16, 17, 300, 1024], [0, 256, 16]),
+    (dict(Hq=32, Hkv=8, D=128), [5, 511, 512, 513, 2049], [256, 64]),
+    (dict(Hq=8, Hkv=8, D=64), [1, 2, 64, 333], [0, 32]),
+    (dict(Hq=64, Hkv=8, D=64, window=128, sinks=True), [1, 100, 128, 129, 700, 3000], [0, 256]),
+    (dict(Hq=32, Hkv=4, D=128, kv="int8"), [1, 33, 257, 2000], [256, 0]),
+    (dict(Hq=16, Hkv=4, D=64, kv="int8", window=50, sinks=True), [7, 64, 300], [32, 0]),
+    (dict(Hq=8, Hkv=8, D=128, kv="int8", sinks=True), [1, 90], [16]),
+    (dict(Hq=16, Hkv=8, D=64, window=1), [1, 2, 17], [16, 0]),
+]
+
+
+@pytest.mark.parametrize("ci", range(len(DECODE_CASES)))
+def test_decode_parity(ci):
+    prm, lens, splits = DECODE_CASES[ci]
+    case = W.make_case(f"dec{ci}", 100 + ci, P(seed=ci, **prm), lens, np.ones(len(lens), np.int32),
+                       outlier_frac=0.01 if prm.get("kv") == "int8" else 0.0)
+    g = GpuCase(case)
+    ref = O.decode(case.q, oracle_pool(case), case.block_table, case.seq_lens, case.p)
+    for S in splits:
+        got = g.decode(split_keys=S)
+        assert_close(got, ref, tol_of(case), f"decode case {ci} S={S}")
+
+
+def test_decode_partials_match_oracle():
+    prm = dict(Hq=32, Hkv=8, D=128, window=300, sinks=True)
+    lens = [10, 256, 257, 900]
+    case = W.make_case("parts", 7, P(**prm), lens, np.ones(4, np.int32))
+    g = GpuCase(case)
+    S = 256
+    ms = pfa.decode_num_splits(max(lens), S)
+    _, (op, lp) = g.decode(split_keys=S, keep_parts=True)
+    o_ref, l_ref = O.split_partials(case.q, oracle_pool(case), case.block_table, case.seq_lens, case.p, S, ms)
+    op, lp = op.cpu().numpy(), lp.cpu().numpy()
+    for b, n in enumerate(lens):
+        ns = -(-n // S)
+        assert np.array_equal(np.isneginf(lp[b, :, :ns]), np.isneginf(l_ref[b, :, :ns]))
+        fin = np.isfinite(l_ref[b, :, :ns])
+        assert np.max(np.abs(lp[b, :, :ns][fin] - l_ref[b, :, :ns][fin])) < 1e-3
+        assert_close(op[b, :, :ns][fin], o_ref[b, :, :ns][fin], BF16_TOL, f"o_part seq {b}")
+
+
+def test_combine_on_oracle_partials():
+    """Feed the oracle's partials (float32) to the GPU combine alone."""
+    prm = dict(Hq=16, Hkv=4, D=64, window=40, sinks=True)
+    lens = [3, 64, 65, 200]
+    case = W.make_case("comb", 8, P(**prm), lens, np.ones(4, np.int32))
+    S = 32
+    ms = pfa.decode_num_splits(max(lens), S)
+    o_ref, l_ref = O.split_partials(case.q, oracle_pool(case), case.block_table, case.seq_lens, case.p, S, ms)
+    ref = O.combine(o_ref, l_ref, case.seq_lens, S, case.p.sinks)
+    g = GpuCase(case, fill=False)
+    out = torch.empty(4, 16, 64, device="cuda")
+    pfa.paged_attn_combine(g.desc, torch.from_numpy(o_ref.astype(np.float32)).cuda(),
+                           torch.from_numpy(l_ref.astype(np.float32)).cuda(), g.seq_lens, S, ms, out)
+    torch.cuda.synchronize()
+    np.testing.assert_allclose(out.cpu().numpy(), ref, rtol=0, atol=2e-6)
+
+
+# ---------------------------------------------------------------------------
+# prefill
+# ---------------------------------------------------------------------------
+
+PREFILL_CASES = [
+    # (params, seq_lens, q_lens)
+    (dict(Hq=32, Hkv=8, D=128), [1, 37, 130, 300], [1, 37, 130, 300]),
+    (dict(Hq=32, Hkv=8, D=128), [330, 64, 1001], [130, 64, 1]),          # chunks on restored prefixes
+    (dict(Hq=64, Hkv=8, D=64, window=128, sinks=True), [300, 517], [300, 200]),
+    (dict(Hq=8, Hkv=8, D=128, sinks=True), [200], [200]),
+    (dict(Hq=4, Hkv=2, D=64, window=7), [90, 33], [90, 20]),
+    (dict(Hq=32, Hkv=2, D=64), [77], [77]),                              # G = 16
+    (dict(Hq=32, Hkv=1, D=128, window=64), [150], [150]),                # G = 32
+]
+
+
+@pytest.mark.parametrize("ci", range(len(PREFILL_CASES)))
+def test_prefill_parity(ci):
+    prm, lens, qlens = PREFILL_CASES[ci]
+    case = W.make_case(f"pre{ci}", 200 + ci, P(seed=ci, **prm), lens, qlens, split_keys=0)
+    g = GpuCase(case)
+    got = g.prefill()
+    ref = O.paged_attention(case.q, case.cu_q, oracle_pool(case), case.block_table, case.seq_lens, case.p)
+    assert_close(got, ref, BF16_TOL, f"prefill case {ci}")
+
+
+# ---------------------------------------------------------------------------
+# invariants on the GPU
+# ---------------------------------------------------------------------------
+
+def _permuted(case: W.PagedCase, seed=0):
+    perm = np.random.default_rng(seed).permutation(case.num_pages).astype(np.int32)
+    return W.PagedCase(case.name + "_perm", case.p, case.seq_lens, case.q_lens, case.cu_q, case.cu_tok,
+                       perm[case.block_table], case.num_pages, int(perm[case.spare_page]),
+                       case.k_tok, case.v_tok, case.q, case.split_keys)
+
+
+def test_page_permutation_is_bitwise_invariant():
+    dcase = W.make_case("pp", 9, P(32, 8, 128, sinks=True), [100, 700], [1, 1])
+    pcase = W.make_case("ppf", 10, P(32, 8, 128), [300, 90], [130, 90], split_keys=0)
+    for case, run in ((dcase, lambda g: g.decode(256)), (pcase, lambda g: g.prefill())):
+        a = run(GpuCase(case))
+        b = run(GpuCase(_permuted(case)))
+        assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+
+
+def test_split_count_invariance():
+    case = W.make_case("sc", 11, P(32, 8, 128, window=500, sinks=True), [17, 256, 1000, 1500],
+                       np.ones(4, np.int32))
+    g = GpuCase(case)
+    ref = O.decode(case.q, oracle_pool(case), case.block_table, case.seq_lens, case.p)
+    outs = [g.decode(S) for S in (0, 16, 64, 256, 1024)]
+    for o in outs:
+        assert_close(o, ref, BF16_TOL, "split invariance")
+    for o in outs[1:]:
+        assert np.max(np.abs(o - outs[0])) < 2e-3
+
+
+def test_repeat_runs_are_bitwise_identical():
+    case = W.make_case("det", 12, P(64, 8, 64, window=128, sinks=True), [400, 2100], [1, 1])
+    g = GpuCase(case)
+    a, b = g.decode(256), g.decode(256)
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+    pc = W.make_case("detp", 13, P(32, 8, 128), [700], [700], split_keys=0)
+    gp = GpuCase(pc)
+    a, b = gp.prefill(), gp.prefill()
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+
+
+def test_decode_equals_last_prefill_row():
+    p = P(32, 8, 128, window=100, sinks=True)
+    pc = W.make_case("lastrow", 14, p, [333], [333], split_keys=0)
+    gp = GpuCase(pc)
+    pre = gp.prefill()
+    dc = W.PagedCase("lastrow_d", p, pc.seq_lens, np.array([1], np.int32), np.array([0, 1], np.int32), pc.cu_tok,
+                     pc.block_table, pc.num_pages, pc.spare_page, pc.k_tok, pc.v_tok, pc.q[-1:], 256)
+    gd = GpuCase(dc)
+    for S in (0, 256):
+        dec = gd.decode(S)
+        assert np.max(np.abs(dec[0] - pre[-1])) < 1e-2

@@ -23,23 +23,49 @@ BF16_NAN = np.uint16(0x7FC0)
 
 def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
     """Round float32 values to the nearest bfloat16 (ties to even); return bit patterns."""
-    x = np.ascontiguousarray(x, dtype=np.float32)
-    b = x.view(np.uint32)
-    r = (b + np.uint32(0x7FFF) + ((b >> np.uint32(16)) & np.uint32(1))) >> np.uint32(16)
-    return r.astype(np.uint16)
+    b = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    t = b >> np.uint32(16)
+    t &= np.uint32(1)
+    t += np.uint32(0x7FFF)
+    t += b
+    t >>= np.uint32(16)
+    return t.astype(np.uint16)
+
+
+_CHUNK = 1 << 22   # elements per independently seeded block (fixed, so draws do not depend on threads)
 
 
 def normal_bf16(rng: np.random.Generator, shape, outlier_frac: float = 0.0,
                 outlier_mag: float = 8.0) -> np.ndarray:
     """N(0,1) float32 draws rounded to bfloat16 bits.  With ``outlier_frac`` > 0 each
     element is independently replaced, with that probability, by +-outlier_mag
-    (fair sign) before rounding (outlier_mag must be exact in bfloat16)."""
-    x = rng.standard_normal(size=shape, dtype=np.float32)
-    if outlier_frac > 0.0:
-        hit = rng.random(size=shape, dtype=np.float32) < np.float32(outlier_frac)
-        sign = np.where(rng.random(size=shape, dtype=np.float32) < 0.5, -1.0, 1.0).astype(np.float32)
-        x = np.where(hit, sign * np.float32(outlier_mag), x)
-    return f32_to_bf16_bits(x)
+    (fair sign) before rounding (outlier_mag must be exact in bfloat16).
+
+    The draw is split into fixed-size blocks, each with its own child seed taken
+    from ``rng``, and the blocks are filled on a thread pool."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    n = int(np.prod(shape))
+    out = np.empty(n, dtype=np.uint16)
+    nblk = max(1, -(-n // _CHUNK))
+    seeds = rng.integers(0, 2**63 - 1, size=nblk)
+
+    def fill(i):
+        g = np.random.default_rng(int(seeds[i]))
+        a, b = i * _CHUNK, min(n, (i + 1) * _CHUNK)
+        x = g.standard_normal(size=b - a, dtype=np.float32)
+        if outlier_frac > 0.0:
+            hit = g.random(size=b - a, dtype=np.float32) < np.float32(outlier_frac)
+            sign = np.where(g.random(size=b - a, dtype=np.float32) < 0.5, np.float32(-1), np.float32(1))
+            x = np.where(hit, sign * np.float32(outlier_mag), x)
+        out[a:b] = f32_to_bf16_bits(x)
+
+    if nblk == 1:
+        fill(0)
+    else:
+        with ThreadPoolExecutor(max_workers=min(8, nblk)) as ex:
+            list(ex.map(fill, range(nblk)))
+    return out.reshape(shape)
 
 
 def uniform_int_lens(rng, n, lo, hi):
