@@ -196,14 +196,21 @@ def run_decode(case, torch, pfa, gs, steps, warmup):
 def run_prefill(case, torch, pfa, gs, steps, warmup):
     g, pools, (kn, vn, cun) = setup_case(case, torch, pfa, gs, copies_for_bytes=0)
     p = case.p
-    out = torch.empty((int(case.cu_q[-1]), p.num_q_heads, p.head_dim), device="cuda")
-    max_q = int(case.q_lens.max())
+    Tq = int(case.cu_q[-1])
+    out = torch.empty((Tq, p.num_q_heads, p.head_dim), device="cuda")
+    max_q, max_len = int(case.q_lens.max()), int(case.seq_lens.max())
+    ms, sk = pfa.prefill_num_splits(g.desc, case.batch, max_q, max_len)
+    op = lp = None
+    if ms > 1:
+        op = torch.empty((Tq, p.num_q_heads, ms, p.head_dim), device="cuda")
+        lp = torch.empty((Tq, p.num_q_heads, ms), device="cuda")
     tm = Timer(torch)
 
     def step(i):
         pfa.kv_write(g.desc, g.pool, kn, vn, cun, g.seq_lens, g.bt)
         e = tm.mark("prefill")
-        pfa.paged_attn_prefill(g.desc, g.pool, g.q, g.cu_q, g.bt, g.seq_lens, max_q, out)
+        pfa.paged_attn_prefill(g.desc, g.pool, g.q, g.cu_q, g.bt, g.seq_lens, max_q, out, max_seq_len=max_len,
+                               split_keys=sk, max_splits=ms, o_part=op, lse_part=lp)
         tm.close("prefill", e)
 
     for i in range(warmup):
@@ -218,7 +225,7 @@ def run_prefill(case, torch, pfa, gs, steps, warmup):
     t1.record()
     torch.cuda.synchronize()
     return dict(step_ms=t0.elapsed_time(t1) / steps, prefill_ms=tm.mean_ms("prefill"),
-                flops=prefill_flops(case))
+                flops=prefill_flops(case), split_keys=sk, max_splits=ms)
 
 
 # ---------------------------------------------------------------------------

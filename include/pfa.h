@@ -163,13 +163,35 @@ pfa_status pfa_paged_attn_combine(const pfa_attn_desc* desc, const float* o_part
  *   cu_q           device [batch+1] int32, as cu_new above.
  *   seq_lens       device [batch] int32, prefix + new tokens.
  *   max_q_len      host upper bound on cu_q[s+1]-cu_q[s].
+ *   max_seq_len    host upper bound on seq_lens[].
  *   out            device [num_q_tokens][Hq][D] fp32.
+ *
+ *   Split mode, when max_splits > 1: the key range is cut into ranges of
+ *   split_keys keys, a multiple of 64, with max_splits >= ceil(max_seq_len /
+ *   split_keys).  Use it when a chunk has too few query tiles to fill the GPU,
+ *   e.g. a short turn on a long prefix.  Each range writes a softmax-normalised
+ *   partial to o_part and its natural log-sum-exp to lse_part:
+ *     o_part   [num_q_tokens][Hq][max_splits][D] fp32
+ *     lse_part [num_q_tokens][Hq][max_splits] fp32
+ *   A range with no visible key writes lse -inf.  A second kernel on the same
+ *   stream then merges the partials into out, as pfa_paged_attn_combine does.
+ *   When max_splits == 1, split_keys, o_part and lse_part are ignored.
  */
 pfa_status pfa_paged_attn_prefill(const pfa_attn_desc* desc, const pfa_kv_pool* pool,
                                   const void* q, const int32_t* cu_q,
                                   const int32_t* block_table, int32_t bt_stride,
                                   const int32_t* seq_lens, int32_t batch, int32_t max_q_len,
-                                  float* out, void* stream);
+                                  int32_t max_seq_len, int32_t split_keys, int32_t max_splits,
+                                  float* o_part, float* lse_part, float* out, void* stream);
+
+/*
+ * A prefill split choice for `num_cus` compute units (0 means 256).  It returns
+ * max_splits, 1 when the query tiles alone give at least two workgroups per CU,
+ * and writes the matching split_keys to *split_keys (0 when unsplit).  This is
+ * host-side arithmetic only.
+ */
+int32_t pfa_prefill_num_splits(const pfa_attn_desc* desc, int32_t batch, int32_t max_q_len,
+                               int32_t max_seq_len, int32_t num_cus, int32_t* split_keys);
 
 /* ceil(max_seq_len / split_keys), at least 1 (0 when split_keys <= 0). */
 int32_t pfa_decode_num_splits(int32_t max_seq_len, int32_t split_keys);

@@ -3,6 +3,8 @@
 // last HIP error.
 #include "pfa.h"
 
+#include <algorithm>
+
 #include "pfa_device.h"
 
 namespace {
@@ -145,30 +147,43 @@ pfa_status pfa_paged_attn_combine(const pfa_attn_desc* desc, const float* o_part
     a.o_part = o_part;
     a.lse_part = lse_part;
     a.seq_lens = seq_lens;
+    a.cu_rows = nullptr;
     a.sinks = desc->sinks;
     a.out = out;
     a.batch = batch;
     a.num_q_heads = desc->num_q_heads;
     a.split_keys = split_keys;
     a.max_splits = max_splits;
+    a.rows_per_seq = 0;
     return hip_status(pfa::launch_combine(a, desc->head_dim, (hipStream_t)stream));
 }
 
 pfa_status pfa_paged_attn_prefill(const pfa_attn_desc* desc, const pfa_kv_pool* pool, const void* q,
                                   const int32_t* cu_q, const int32_t* block_table,
                                   int32_t bt_stride, const int32_t* seq_lens, int32_t batch,
-                                  int32_t max_q_len, float* out, void* stream) {
+                                  int32_t max_q_len, int32_t max_seq_len, int32_t split_keys,
+                                  int32_t max_splits, float* o_part, float* lse_part, float* out,
+                                  void* stream) {
     PFA_TRY(check_desc(desc));
     PFA_TRY(check_pool(desc, pool));
     if (desc->kv_dtype != PFA_KV_BF16) return PFA_ERR_UNSUPPORTED;
     const int g = desc->num_q_heads / desc->num_kv_heads;
     if (!prefill_group_ok(g)) return PFA_ERR_UNSUPPORTED;
-    if (batch < 0 || max_q_len < 0 || bt_stride <= 0) return PFA_ERR_SHAPE;
+    if (batch < 0 || max_q_len < 0 || bt_stride <= 0 || max_seq_len < max_q_len || max_splits < 1)
+        return PFA_ERR_SHAPE;
+    if (max_seq_len > (int64_t)bt_stride * desc->page_size) return PFA_ERR_SHAPE;
     const int tpb = 128 / g;
-    const int64_t items = (int64_t)batch * desc->num_kv_heads * ((max_q_len + tpb - 1) / tpb);
+    const int64_t items =
+        (int64_t)batch * desc->num_kv_heads * ((max_q_len + tpb - 1) / tpb) * max_splits;
     if (items > 0x7fffffff - 8) return PFA_ERR_SHAPE;
+    if ((int64_t)batch * max_q_len * desc->num_q_heads > 0x7fffffff) return PFA_ERR_SHAPE;
+    if (max_splits > 1) {
+        if (split_keys <= 0 || split_keys % 64 != 0) return PFA_ERR_SHAPE;
+        if (max_splits < pfa_decode_num_splits(max_seq_len, split_keys)) return PFA_ERR_WORKSPACE;
+    }
     if (batch == 0 || max_q_len == 0) return PFA_OK;
     if (!q || !cu_q || !block_table || !seq_lens || !out) return PFA_ERR_NULL;
+    if (max_splits > 1 && (!o_part || !lse_part)) return PFA_ERR_NULL;
     pfa::PrefillArgs a;
     a.q = static_cast<const uint16_t*>(q);
     a.k_pool = static_cast<const uint16_t*>(pool->k_pool);
@@ -178,6 +193,8 @@ pfa_status pfa_paged_attn_prefill(const pfa_attn_desc* desc, const pfa_kv_pool* 
     a.seq_lens = seq_lens;
     a.sinks = desc->sinks;
     a.out = out;
+    a.o_part = o_part;
+    a.lse_part = lse_part;
     a.bt_stride = bt_stride;
     a.batch = batch;
     a.num_pages = pool->num_pages;
@@ -185,8 +202,47 @@ pfa_status pfa_paged_attn_prefill(const pfa_attn_desc* desc, const pfa_kv_pool* 
     a.num_kv_heads = desc->num_kv_heads;
     a.max_q_len = max_q_len;
     a.window = desc->window;
+    a.split_keys = max_splits > 1 ? split_keys : 0;
+    a.max_splits = max_splits;
     a.sm_scale = desc->sm_scale;
-    return hip_status(pfa::launch_prefill(a, desc->head_dim, (hipStream_t)stream));
+    PFA_TRY(hip_status(pfa::launch_prefill(a, desc->head_dim, (hipStream_t)stream)));
+    if (max_splits == 1) return PFA_OK;
+    pfa::CombineArgs c;
+    c.o_part = o_part;
+    c.lse_part = lse_part;
+    c.seq_lens = nullptr;
+    c.cu_rows = cu_q;
+    c.sinks = desc->sinks;
+    c.out = out;
+    c.batch = batch;
+    c.num_q_heads = desc->num_q_heads;
+    c.split_keys = split_keys;
+    c.max_splits = max_splits;
+    c.rows_per_seq = max_q_len;
+    return hip_status(pfa::launch_combine(c, desc->head_dim, (hipStream_t)stream));
+}
+
+int32_t pfa_prefill_num_splits(const pfa_attn_desc* desc, int32_t batch, int32_t max_q_len,
+                               int32_t max_seq_len, int32_t num_cus, int32_t* split_keys) {
+    if (split_keys) *split_keys = 0;
+    if (!desc || desc->num_kv_heads <= 0 || desc->num_q_heads % desc->num_kv_heads != 0) return 1;
+    const int g = desc->num_q_heads / desc->num_kv_heads;
+    if (!prefill_group_ok(g) || batch <= 0 || max_q_len <= 0 || max_seq_len <= 0) return 1;
+    if (num_cus <= 0) num_cus = 256;
+    const int tpb = 128 / g;
+    const int64_t items = (int64_t)batch * desc->num_kv_heads * ((max_q_len + tpb - 1) / tpb);
+    const int64_t target = 2 * (int64_t)num_cus;
+    // keys a row of the chunk sees at most: the window, else the whole sequence
+    const int64_t span = desc->window > 0 ? std::min<int64_t>(max_seq_len, desc->window + max_q_len)
+                                          : max_seq_len;
+    if (items >= target || span <= 256) return 1;
+    int64_t want = (target + items - 1) / items;
+    int64_t sk = (max_seq_len + want - 1) / want;
+    sk = std::max<int64_t>(256, (sk + 63) / 64 * 64);
+    const int64_t ns = (max_seq_len + sk - 1) / sk;
+    if (ns <= 1) return 1;
+    if (split_keys) *split_keys = (int32_t)sk;
+    return (int32_t)ns;
 }
 
 const char* pfa_status_string(pfa_status s) {

@@ -132,10 +132,12 @@ struct DecodeArgs {
 struct CombineArgs {
     const float* o_part;
     const float* lse_part;
-    const int32_t* seq_lens;
+    const int32_t* seq_lens;   // decode: splits per row = ceil(len/S); NULL: all max_splits
+    const int32_t* cu_rows;    // prefill: rows of sequence s are cu_rows[s]..cu_rows[s+1]-1
     const float* sinks;
     float* out;
     int32_t batch, num_q_heads, split_keys, max_splits;
+    int32_t rows_per_seq;      // with cu_rows: host bound on rows per sequence
 };
 
 struct PrefillArgs {
@@ -147,7 +149,10 @@ struct PrefillArgs {
     const int32_t* seq_lens;
     const float* sinks;
     float* out;
+    float* o_part;             // split mode: [Tq][Hq][max_splits][D]
+    float* lse_part;           // split mode: [Tq][Hq][max_splits]
     int32_t bt_stride, batch, num_pages, num_q_heads, num_kv_heads, max_q_len, window;
+    int32_t split_keys, max_splits;   // max_splits == 1: no split
     float sm_scale;
 };
 

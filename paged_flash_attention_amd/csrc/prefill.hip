@@ -27,6 +27,11 @@
 //    skips the MFMAs of tiles that lie entirely outside its rows' ranges.
 //  * Workgroups map to XCDs so that each XCD's L2 holds the K/V of the heads it
 //    serves.  Within an XCD the longest (latest) query tiles go first.
+//  * Split mode covers a short chunk on a long prefix, such as 130 new tokens on
+//    8192.  Such a chunk has too few query tiles to fill 256 CUs, so the key
+//    range is cut into max_splits ranges of split_keys keys, a multiple of 64.
+//    Each workgroup writes a softmax-normalised partial with its natural
+//    log-sum-exp, and the combine kernel then merges them with the sink.
 #include "pfa_device.h"
 
 namespace pfa {
@@ -56,7 +61,7 @@ __device__ __forceinline__ int vt_quad_pos(int q) {
     return (q & ~3) | ((q & 1) << 1) | ((q & 2) >> 1);
 }
 
-template <int D, int G>
+template <int D, int G, bool SPLIT>
 __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
     constexpr int TPW = kRowsPerWave / G;               // tokens per wave
     constexpr int TPB = TPW * kWaves;                   // tokens per workgroup
@@ -75,14 +80,19 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
     const int half = lane / 32;
 
     // ---- work item (XCD-aware, heaviest tiles first) ----
+    // items run (b, kvh, split, tile) with tile fastest; each XCD takes a
+    // contiguous range, so the tiles that share a (b, kvh, split) K/V range share
+    // one L2.
     const int n_tiles = (a.max_q_len + TPB - 1) / TPB;
-    const int n_items = a.batch * a.num_kv_heads * n_tiles;
+    const int nsplit = SPLIT ? a.max_splits : 1;
+    const int n_items = a.batch * a.num_kv_heads * nsplit * n_tiles;
     const int per_xcd = (n_items + kXcds - 1) / kXcds;
     const int item = (blockIdx.x % kXcds) * per_xcd + blockIdx.x / kXcds;
     if (item >= n_items) return;
     const int tile = n_tiles - 1 - item % n_tiles;
-    const int kvh = (item / n_tiles) % a.num_kv_heads;
-    const int b = item / (n_tiles * a.num_kv_heads);
+    const int split = (item / n_tiles) % nsplit;
+    const int kvh = (item / (n_tiles * nsplit)) % a.num_kv_heads;
+    const int b = item / (n_tiles * nsplit * a.num_kv_heads);
 
     const int cq0 = __ldg(a.cu_q + b);
     const int q_len = __ldg(a.cu_q + b + 1) - cq0;
@@ -99,10 +109,25 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
     const bool row_ok = tok_l < q_len;
     const int pos_l = prefix + tok_l;
 
-    // key ranges: workgroup and wave
+    // key ranges: workgroup (within this split) and wave
     const int wg_last = min(tok0 + TPB, q_len) - 1;
-    const int hi = prefix + wg_last + 1;
-    const int lo = W > 0 ? max(0, prefix + tok0 - W + 1) : 0;
+    int hi = prefix + wg_last + 1;
+    int lo = W > 0 ? max(0, prefix + tok0 - W + 1) : 0;
+    if constexpr (SPLIT) {
+        lo = max(lo, split * a.split_keys);
+        hi = min(hi, (split + 1) * a.split_keys);
+        if (lo >= hi) {
+            // no key of this split is visible to any row of the tile
+            if (row_ok) {
+                const int64_t pr = ((int64_t)(cq0 + tok_l) * Hq + h_l) * a.max_splits + split;
+                float* op = a.o_part + pr * D + half * (D / 2);
+                for (int d = 0; d < D / 2; d += 4)
+                    *reinterpret_cast<float4*>(op + d) = make_float4(0.f, 0.f, 0.f, 0.f);
+                if (half == 0) a.lse_part[pr] = -INFINITY;
+            }
+            return;
+        }
+    }
     const int w_first = tok0 + wave * TPW;
     const int w_last = min(tok0 + (wave + 1) * TPW, q_len) - 1;
     const bool wave_live = w_first < q_len;
@@ -282,14 +307,24 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
         __syncthreads();
     }
 
-    // ---- finish: combine the two lanes of each row, apply the sink ----
+    // ---- finish: combine the two lanes of each row ----
     const float l_tot = l_run + xor_lane<32>(l_run);
     if (!row_ok) return;
     const float mu = (m_run == -INFINITY) ? 0.0f : m_run;
-    float z = l_tot;
-    if (a.sinks) z += fast_exp2(__ldg(a.sinks + h_l) * kLog2e - mu);
-    const float inv = z > 0.0f ? 1.0f / z : 0.0f;
-    float* op = a.out + ((int64_t)(cq0 + tok_l) * Hq + h_l) * D;
+    float inv;
+    float* op;
+    if constexpr (SPLIT) {
+        // softmax-normalised partial and its natural log-sum-exp; no sink here
+        const int64_t pr = ((int64_t)(cq0 + tok_l) * Hq + h_l) * a.max_splits + split;
+        inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+        if (half == 0) a.lse_part[pr] = l_tot > 0.0f ? (m_run + fast_log2(l_tot)) * kLn2 : -INFINITY;
+        op = a.o_part + pr * D;
+    } else {
+        float z = l_tot;
+        if (a.sinks) z += fast_exp2(__ldg(a.sinks + h_l) * kLog2e - mu);
+        inv = z > 0.0f ? 1.0f / z : 0.0f;
+        op = a.out + ((int64_t)(cq0 + tok_l) * Hq + h_l) * D;
+    }
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -305,10 +340,14 @@ template <int D, int G>
 hipError_t launch_dg(const PrefillArgs& a, hipStream_t s) {
     constexpr int TPB = kRowsPerWave / G * kWaves;
     const int n_tiles = (a.max_q_len + TPB - 1) / TPB;
-    const int64_t items = (int64_t)a.batch * a.num_kv_heads * n_tiles;
+    const bool split = a.max_splits > 1;
+    const int64_t items = (int64_t)a.batch * a.num_kv_heads * n_tiles * (split ? a.max_splits : 1);
     const int64_t grid = (items + kXcds - 1) / kXcds * kXcds;
     if (grid == 0) return hipSuccess;
-    hipLaunchKernelGGL((prefill_kernel<D, G>), dim3((unsigned)grid), dim3(256), 0, s, a);
+    if (split)
+        hipLaunchKernelGGL((prefill_kernel<D, G, true>), dim3((unsigned)grid), dim3(256), 0, s, a);
+    else
+        hipLaunchKernelGGL((prefill_kernel<D, G, false>), dim3((unsigned)grid), dim3(256), 0, s, a);
     return hipGetLastError();
 }
 

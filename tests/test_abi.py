@@ -123,10 +123,12 @@ def test_combine_validation():
 
 
 def pre(d, p, **kw):
-    a = dict(q=FAKE, cu=FAKE, bt=FAKE, stride=64, sl=FAKE, batch=1, mq=1024, out=FAKE)
+    a = dict(q=FAKE, cu=FAKE, bt=FAKE, stride=64, sl=FAKE, batch=1, mq=1024, ml=1024, S=0, ms=1,
+             op=None, lp=None, out=FAKE)
     a.update(kw)
     return pfa.lib().pfa_paged_attn_prefill(ctypes.byref(d), ctypes.byref(p), a["q"], a["cu"], a["bt"],
-                                            a["stride"], a["sl"], a["batch"], a["mq"], a["out"], None)
+                                            a["stride"], a["sl"], a["batch"], a["mq"], a["ml"], a["S"],
+                                            a["ms"], a["op"], a["lp"], a["out"], None)
 
 
 def test_prefill_validation():
@@ -135,7 +137,21 @@ def test_prefill_validation():
     assert pre(desc(), pool(), cu=None) == NULL
     assert pre(desc(), pool(), out=None) == NULL
     assert pre(desc(), pool(), mq=-1) == SHAPE
+    assert pre(desc(), pool(), ml=512) == SHAPE                              # max_seq_len < max_q_len
+    assert pre(desc(), pool(), ml=64 * 16 + 1, mq=10) == SHAPE               # beyond the block table
+    assert pre(desc(), pool(), S=100, ms=11) == SHAPE                        # not a multiple of 64
+    assert pre(desc(), pool(), S=128, ms=7) == WORKSPACE                     # 1024/128 = 8 ranges
+    assert pre(desc(), pool(), S=128, ms=8) == NULL                          # no partial buffers
     assert pre(desc(), pool(), mq=0, q=None) == OK
+
+
+def test_prefill_split_choice_host_only():
+    L = pfa.lib()
+    sk = ctypes.c_int32(-1)
+    assert L.pfa_prefill_num_splits(ctypes.byref(desc()), 1, 8192, 8192, 256, ctypes.byref(sk)) == 1
+    assert sk.value == 0
+    ms = L.pfa_prefill_num_splits(ctypes.byref(desc()), 1, 130, 8322, 256, ctypes.byref(sk))
+    assert ms > 1 and sk.value % 64 == 0 and ms * sk.value >= 8322 and sk.value >= 256
 
 
 def test_binding_refuses_host_tensors():

@@ -165,9 +165,18 @@ def test_prefill_parity(ci):
     prm, lens, qlens = PREFILL_CASES[ci]
     case = W.make_case(f"pre{ci}", 200 + ci, P(seed=ci, **prm), lens, qlens, split_keys=0)
     g = GpuCase(case)
-    got = g.prefill()
     ref = O.paged_attention(case.q, case.cu_q, oracle_pool(case), case.block_table, case.seq_lens, case.p)
-    assert_close(got, ref, BF16_TOL, f"prefill case {ci}")
+    for split in (None, (64, -(-max(lens) // 64)), (256, -(-max(lens) // 256))):
+        got = g.prefill(split=split)
+        assert_close(got, ref, BF16_TOL, f"prefill case {ci} split={split}")
+
+
+def test_prefill_split_choice():
+    """The library splits a short chunk on a long prefix, not a long prompt."""
+    d = pfa.AttnDesc(32, 8, 128)
+    ms, sk = pfa.prefill_num_splits(d, 1, 130, 8322)
+    assert ms > 1 and sk % 64 == 0 and ms * sk >= 8322
+    assert pfa.prefill_num_splits(d, 1, 8192, 8192) == (1, 0)
 
 
 # ---------------------------------------------------------------------------
