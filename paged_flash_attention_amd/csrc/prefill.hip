@@ -48,10 +48,10 @@ __device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const
 
 template <int D>
 struct Tile {
-    static constexpr int KP = D + 8;          // K row pitch (elements)
-    static constexpr int VP = kBN + 8;        // V^T row pitch (elements)
+    static constexpr int KP = D + 8;          // K row pitch (elements): 16 lanes reading one
+                                              // column of 16 rows hit 16 distinct bank quads
     uint16_t k[2][kBN][KP];
-    uint16_t vt[2][D][VP];
+    uint16_t vt[2][D][kBN];                   // V^T rows of 64 keys, 16-byte chunks swizzled
 };
 
 // position of key-quad q (0..15) of a 64-key tile inside a V^T row: within each
@@ -59,6 +59,13 @@ struct Tile {
 // (k-slots 8*(lane/32)..+8) are contiguous.
 __device__ __forceinline__ int vt_quad_pos(int q) {
     return (q & ~3) | ((q & 1) << 1) | ((q & 2) >> 1);
+}
+
+// Element offset of (row d, 16-byte chunk c, element e in chunk) in a V^T buffer.
+// A row is 128 B, half the banks; chunk c of row d sits at c ^ ((d >> 1) & 7), so
+// the 16 rows one 16-lane read touches fall on 16 distinct bank quads.
+__device__ __forceinline__ int vt_off(int d, int c, int e) {
+    return d * kBN + ((c ^ ((d >> 1) & 7)) << 3) + e;
 }
 
 template <int D, int G, bool SPLIT>
@@ -150,44 +157,48 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
     const int64_t hblk = (int64_t)kPage * D;             // elements per page-head block
 
     // ---- tile loads: global -> registers ----
+    // A 64-key tile is 4 pages.  Its page ids are wave-uniform loads; pages past the
+    // sequence end are never read (their rows are zero-filled).
     uint4 kreg[KLOADS];
     uint4 vreg[4];
-    const int vq = tid / CPR;                             // key quad of this thread (V)
-    const int vc = tid % CPR;                             // 8-dim chunk of this thread (V)
+    const int vq = tid % 16;                              // key quad of this thread (V)
+    const int vc = tid / 16;                              // 8-dim chunk of this thread (V)
+    auto sel4 = [](int j, const uint16_t* p0, const uint16_t* p1, const uint16_t* p2,
+                   const uint16_t* p3) { return j == 0 ? p0 : j == 1 ? p1 : j == 2 ? p2 : p3; };
     auto load_tile = [&](int kb) {
         const int key0 = kb * kBN;
+        const uint16_t* kp[4];
+        const uint16_t* vp[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int pi = kb * 4 + j;
+            int pg = 0;
+            if (pi * kPage < n) pg = min(max(__ldg(bt + pi), 0), a.num_pages - 1);
+            const int64_t off = ((int64_t)pg * a.num_kv_heads + kvh) * hblk;
+            kp[j] = a.k_pool + off;
+            vp[j] = a.v_pool + off;
+        }
 #pragma unroll
         for (int e = 0; e < KLOADS; ++e) {
             const int c = tid + 256 * e;
             const int key = c / CPR, col = c % CPR;
-            const int kg = key0 + key;
             uint4 v = make_uint4(0, 0, 0, 0);
-            if (kg < n) {
-                int pg = __ldg(bt + kg / kPage);
-                pg = min(max(pg, 0), a.num_pages - 1);
-                const uint16_t* src = a.k_pool + ((int64_t)pg * a.num_kv_heads + kvh) * hblk +
-                                      (kg % kPage) * D + col * 8;
-                v = *reinterpret_cast<const uint4*>(src);
-            }
+            if (key0 + key < n)
+                v = *reinterpret_cast<const uint4*>(sel4(key / kPage, kp[0], kp[1], kp[2], kp[3]) +
+                                                    (key % kPage) * D + col * 8);
             kreg[e] = v;
         }
-        if (vq < kBN / 4) {
+        if (vc < CPR) {
+            const uint16_t* vbase = sel4(vq / 4, vp[0], vp[1], vp[2], vp[3]) + (4 * (vq % 4)) * D + vc * 8;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const int kg = key0 + 4 * vq + e;
                 uint4 v = make_uint4(0, 0, 0, 0);
-                if (kg < n) {
-                    int pg = __ldg(bt + kg / kPage);
-                    pg = min(max(pg, 0), a.num_pages - 1);
-                    const uint16_t* src = a.v_pool + ((int64_t)pg * a.num_kv_heads + kvh) * hblk +
-                                          (kg % kPage) * D + vc * 8;
-                    v = *reinterpret_cast<const uint4*>(src);
-                }
+                if (key0 + 4 * vq + e < n) v = *reinterpret_cast<const uint4*>(vbase + e * D);
                 vreg[e] = v;
             }
         }
     };
-    // ---- registers -> LDS (K row-major, V transposed) ----
+    // ---- registers -> LDS (K row-major, V transposed and swizzled) ----
     auto store_tile = [&](int buf) {
 #pragma unroll
         for (int e = 0; e < KLOADS; ++e) {
@@ -195,12 +206,13 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
             const int key = c / CPR, col = c % CPR;
             *reinterpret_cast<uint4*>(&sm.k[buf][key][col * 8]) = kreg[e];
         }
-        if (vq < kBN / 4) {
+        if (vc < CPR) {
             const uint32_t w0[4] = {vreg[0].x, vreg[0].y, vreg[0].z, vreg[0].w};
             const uint32_t w1[4] = {vreg[1].x, vreg[1].y, vreg[1].z, vreg[1].w};
             const uint32_t w2[4] = {vreg[2].x, vreg[2].y, vreg[2].z, vreg[2].w};
             const uint32_t w3[4] = {vreg[3].x, vreg[3].y, vreg[3].z, vreg[3].w};
             const int kpos = 4 * vt_quad_pos(vq);
+            uint16_t* vt = &sm.vt[buf][0][0];
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
                 const uint32_t sel = (j & 1) ? 0x07060302u : 0x05040100u;
@@ -208,7 +220,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
                 uint2 t;
                 t.x = __builtin_amdgcn_perm(w1[w], w0[w], sel);
                 t.y = __builtin_amdgcn_perm(w3[w], w2[w], sel);
-                *reinterpret_cast<uint2*>(&sm.vt[buf][vc * 8 + j][kpos]) = t;
+                *reinterpret_cast<uint2*>(vt + vt_off(vc * 8 + j, kpos >> 3, kpos & 7)) = t;
             }
         }
     };
@@ -298,7 +310,8 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
                 const bf16x8 pf = __builtin_bit_cast(bf16x8, pu);
 #pragma unroll
                 for (int db = 0; db < DB; ++db) {
-                    const uint4 vv = *reinterpret_cast<const uint4*>(&sm.vt[buf][32 * db + r32][16 * m + 8 * half]);
+                    const uint4 vv = *reinterpret_cast<const uint4*>(&sm.vt[buf][0][0] +
+                                                                     vt_off(32 * db + r32, 2 * m + half, 0));
                     acc_o[db] = mfma32(__builtin_bit_cast(bf16x8, vv), pf, acc_o[db]);
                 }
             }
