@@ -5,70 +5,123 @@
 // in place, reading each page once through the block table, and splits the keys of
 // a sequence so that many workgroups share one sequence.  A separate combine then
 // merges the splits.  Its "INT8 KV cache" section keeps one scale per cached
-// vector.  At 32k positions it also loads 32-key tiles and each half of the head
-// dimension separately, so the INT8 kernel stays spill-free.
+// vector.  It also loads 32-key tiles and each half of the head dimension
+// separately, so the INT8 kernel stays spill-free.
 //
 // MI355X design.  The kernel is HBM-bound, and each K/V element is used by exactly
-// one lane group, so nothing is staged in LDS for reuse:
-//  * One 64-lane wave per (split, KV head, sequence).  The G = Hq/Hkv query heads of
-//    the group share every page read (GQA packing).
+// one lane group, so K/V go straight from HBM to registers:
+//  * One wave per (split, KV head, sequence) streams the split's pages.  The kernel
+//    is written for kNW waves per split, taking every kNW-th page and merging
+//    through LDS; kNW = 1 measured fastest.  The G = Hq/Hkv query heads of the
+//    group share every page read (GQA packing).
 //  * Page-head block = 16 keys x D.  A lane loads 8 consecutive elements of one key
 //    per load (16 B for bf16, 8 B for int8).  LPK = D/8 lanes cover a key, and one
-//    load instruction covers 64/LPK keys in one contiguous 512*elem-byte run.  The
-//    next page's K/V is prefetched while the current one is consumed.
-//  * q.k: v_dot2_f32_bf16 on (q, k) bf16 pairs.  INT8 codes are exact in bf16.
-//    Each lane's partial dots for the G heads go through a transposed butterfly
-//    over the LPK lanes (DPP / swizzle moves).  Slot j of a lane holds head
-//    (j ^ myhead), so every stage adds a partner's upper half to its own lower half
-//    with no selects, and ends with the lane holding its own head's full score.
+//    load instruction covers a contiguous 512*elem-byte run.  The wave's next page
+//    is prefetched while the current one is consumed.
+//  * q.k: v_dot2_f32_bf16 on (q, k) bf16 pairs.  INT8 codes are offset to the
+//    unsigned byte c+128 (v_cvt_f32_ubyteN, exact in bf16), and 128*sum(q) is
+//    subtracted from the dot.  A lane's partial dots for the G heads go through a
+//    transposed butterfly over the LPK lanes (DPP / swizzle moves).  Slot j of a
+//    lane holds head (j ^ myhead), so each stage adds a partner's upper half to its
+//    own lower half with no selects, and ends with the lane holding its own head's
+//    full score.
 //  * The softmax max is taken per page and the rescale is lazy: o and l are
 //    rescaled only when some head's running max grows.  The weights p are shared
-//    through a 2-slot LDS buffer, so each lane reads the G weights of its own key.
-//  * p.v: fp32 FMAs on the lane's 8 elements for all G heads.  For INT8 the value
-//    scale is folded into p.
-//  * At the end, the partial o is reduced across the lanes that held different keys.
-//    The kernel writes o/l and lse = ln(sum e^s) (split mode), or the final output
-//    with the sink applied (unsplit mode).
+//    within the wave through LDS.
+//  * p.v: for G <= 4, fp32 FMAs on the lane's 8 elements for all G heads.  For
+//    G = 8, the VALU budget forces dot2 on key pairs from two loads:
+//      - BF16: p rounded to bf16, with the (v_a, v_b) pairs built by v_perm;
+//      - INT8: p*scale_v*2^12 in fp16, with the code pairs built by a byte
+//        permute into fp16 (1024 + u).  The 1152 offset is removed by a packed
+//        fp16 add, which is exact.
+//  * At the end each wave reduces its partial o across key groups.  The waves merge
+//    through LDS, and the workgroup writes o/l with lse = ln(sum e^s) (split mode),
+//    or the final output with the sink (unsplit mode).
 #include "pfa_device.h"
 
 namespace pfa {
 namespace {
 
+// Waves per workgroup.  Each split is one page stream; measured on MI355X, 2 or 4
+// waves per split (each taking every 2nd/4th page, merged through LDS) were 1-30%
+// slower on every workload: shorter streams expose more first-page latency than
+// they save in the ragged tail.
+constexpr int kNW = 1;
+
+typedef __fp16 h2v __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
 template <bool INT8> struct Chunk;
 template <> struct Chunk<false> { typedef uint4 T; };   // 8 bf16
 template <> struct Chunk<true> { typedef uint2 T; };    // 8 int8
 
-__device__ __forceinline__ void unpack_bf16x8(const uint4& c, float (&x)[8]) {
-    x[0] = bf16_lo(c.x); x[1] = bf16_hi(c.x);
-    x[2] = bf16_lo(c.y); x[3] = bf16_hi(c.y);
-    x[4] = bf16_lo(c.z); x[5] = bf16_hi(c.z);
-    x[6] = bf16_lo(c.w); x[7] = bf16_hi(c.w);
+__device__ __forceinline__ uint32_t dw(const uint4& c, int i) {
+    return i == 0 ? c.x : i == 1 ? c.y : i == 2 ? c.z : c.w;
 }
+__device__ __forceinline__ uint32_t dw(const uint2& c, int i) { return i == 0 ? c.x : c.y; }
 
-__device__ __forceinline__ void unpack_i8x8(const uint2& c, float (&x)[8]) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        x[i] = (float)(int)(int8_t)(c.x >> (8 * i));
-        x[4 + i] = (float)(int)(int8_t)(c.y >> (8 * i));
-    }
-}
-
-// The 8 K elements as four bf16 pairs.
+// K chunk -> four bf16 pairs.  BF16: as loaded.  INT8: u = c + 128 per element,
+// exact in bf16; the caller subtracts 128*sum(q).
 __device__ __forceinline__ void k_pairs(const uint4& c, uint32_t (&k)[4]) {
     k[0] = c.x; k[1] = c.y; k[2] = c.z; k[3] = c.w;
 }
 __device__ __forceinline__ void k_pairs(const uint2& c, uint32_t (&k)[4]) {
-    float x[8];
-    unpack_i8x8(c, x);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) k[j] = pack_hi16(x[2 * j], x[2 * j + 1]);
+    for (int h = 0; h < 2; ++h) {
+        const uint32_t u = dw(c, h) ^ 0x80808080u;
+        k[2 * h] = pack_hi16((float)(u & 0xffu), (float)((u >> 8) & 0xffu));
+        k[2 * h + 1] = pack_hi16((float)((u >> 16) & 0xffu), (float)(u >> 24));
+    }
 }
-__device__ __forceinline__ void v_floats(const uint4& c, float (&x)[8]) { unpack_bf16x8(c, x); }
-__device__ __forceinline__ void v_floats(const uint2& c, float (&x)[8]) { unpack_i8x8(c, x); }
+
+// V chunk -> 8 floats (unpaired p.v).  INT8 yields the code c itself.
+__device__ __forceinline__ void v_floats(const uint4& c, float (&x)[8]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        x[2 * i] = bf16_lo(dw(c, i));
+        x[2 * i + 1] = bf16_hi(dw(c, i));
+    }
+}
+__device__ __forceinline__ void v_floats(const uint2& c, float (&x)[8]) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const uint32_t u = dw(c, h) ^ 0x80808080u;
+        x[4 * h + 0] = (float)(u & 0xffu) - 128.0f;
+        x[4 * h + 1] = (float)((u >> 8) & 0xffu) - 128.0f;
+        x[4 * h + 2] = (float)((u >> 16) & 0xffu) - 128.0f;
+        x[4 * h + 3] = (float)(u >> 24) - 128.0f;
+    }
+}
+
+// Element pairs (a[d], b[d]) of two keys' chunks, d = 0..7 (paired p.v).
+// BF16: bf16 pairs by byte permute.  INT8: fp16 pairs of the codes, exact: the
+// byte permute forms 1024 + (c ^ 0x80) = 1152 + c, then a packed fp16 add of
+// -1152 leaves c.
+__device__ __forceinline__ void v_pairs(const uint4& a, const uint4& b, uint32_t (&v)[8]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        v[2 * i] = __builtin_amdgcn_perm(dw(b, i), dw(a, i), 0x05040100u);
+        v[2 * i + 1] = __builtin_amdgcn_perm(dw(b, i), dw(a, i), 0x07060302u);
+    }
+}
+__device__ __forceinline__ void v_pairs(const uint2& a, const uint2& b, uint32_t (&v)[8]) {
+    const f16x2 off = {(_Float16)-1152.0f, (_Float16)-1152.0f};
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            // bytes: [a_k, 0, b_k, 0]  (selector 0x0c yields zero)
+            const uint32_t sel = (uint32_t)k | (0x0cu << 8) | ((uint32_t)(4 + k) << 16) | (0x0cu << 24);
+            const uint32_t w = __builtin_amdgcn_perm(dw(b, h), dw(a, h), sel) ^ 0x64806480u;
+            f16x2 f = __builtin_bit_cast(f16x2, w) + off;
+            v[4 * h + k] = __builtin_bit_cast(uint32_t, f);
+        }
+    }
+}
 
 // Transposed butterfly over the LPK lanes of a key group.  On entry, slot j of
-// this lane holds its partial dot for head (j ^ myhead).  On return, slot 0 holds
-// this lane's head's full dot over all D dims.
+// this lane holds its partial sum for head (j ^ myhead).  On return, slot 0 holds
+// this lane's head's full sum over all D dims.
 template <int LPK, int G>
 __device__ __forceinline__ float transpose_reduce(float (&acc)[G]) {
     if constexpr (G >= 16) {
@@ -87,7 +140,6 @@ __device__ __forceinline__ float transpose_reduce(float (&acc)[G]) {
     }
     constexpr int M2 = (G >= 4) ? M4 / 2 : LPK / 2;
     if constexpr (G >= 2) acc[0] += xor_lane<M2>(acc[1]);
-    // remaining masks: full sums
     constexpr int R = (G >= 2) ? M2 / 2 : LPK / 2;
     float s = acc[0];
     if constexpr (R >= 8) s += xor_lane<8>(s);
@@ -97,19 +149,30 @@ __device__ __forceinline__ float transpose_reduce(float (&acc)[G]) {
     return s;
 }
 
+__device__ __forceinline__ float lane_read(float v, int l) {
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
+}
+
 template <int D, int G, bool INT8, bool FINAL>
-__global__ __launch_bounds__(64) void decode_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(kNW * 64)
+void decode_kernel(DecodeArgs a) {
     constexpr int EB = INT8 ? 1 : 2;           // bytes per element
     constexpr int LPK = D / 8;                 // lanes per key
     constexpr int KPL = kWave / LPK;           // keys per load instruction
     constexpr int NLOAD = kPage / KPL;         // loads per page per tensor
     constexpr int HG = LPK / G;                // lanes holding each head after the reduce
+    constexpr bool PAIRED = G >= 8;            // p.v by dot2 on key pairs
     static_assert(G <= LPK, "group size");
+    static_assert(!PAIRED || NLOAD % 2 == 0, "key pairs");
     typedef typename Chunk<INT8>::T CT;
 
-    __shared__ float p_buf[2][kPage][G];
+    __shared__ __attribute__((aligned(16))) float p_buf[kNW][2][kPage][G];
+    __shared__ float m_sh[kNW][G], l_sh[kNW][G];
+    __shared__ float o_sh[kNW][G][D];
 
-    const int lane = threadIdx.x;
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+    const int lane = tid % kWave;
     const int sub = lane % LPK;
     const int kg = lane / LPK;
     const int myhead = sub / HG;
@@ -133,12 +196,12 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs a) {
 
     if (lo >= hi) {
         if constexpr (!FINAL) {
-            // whole split hidden by the window: empty partial
-            for (int e = lane; e < G * D; e += kWave) {
+            // the window hides the whole split: empty partial
+            for (int e = tid; e < G * D; e += kNW * kWave) {
                 const int g = e / D, d = e % D;
                 a.o_part[(part_row + (int64_t)g * a.max_splits) * D + d] = 0.0f;
             }
-            if (lane < G) a.lse_part[part_row + (int64_t)lane * a.max_splits] = -INFINITY;
+            if (tid < G) a.lse_part[part_row + (int64_t)tid * a.max_splits] = -INFINITY;
         }
         return;
     }
@@ -151,7 +214,21 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs a) {
         const uint4 v = *reinterpret_cast<const uint4*>(qp);
         q[j][0] = v.x; q[j][1] = v.y; q[j][2] = v.z; q[j][3] = v.w;
     }
+    float qbias = 0.0f;   // INT8: 128 * sum_d q[myhead][d]
+    if constexpr (INT8) {
+        float part[G];
+#pragma unroll
+        for (int j = 0; j < G; ++j) {
+            float t = 0.0f;
+#pragma unroll
+            for (int w = 0; w < 4; ++w) t += bf16_lo(q[j][w]) + bf16_hi(q[j][w]);
+            part[j] = t;
+        }
+        qbias = 128.0f * transpose_reduce<LPK, G>(part);
+    }
     const float c2 = a.sm_scale * kLog2e;      // scores kept in log2 units
+    // INT8 paired p.v carries p*scale_v*2^12 in fp16; undone at the end
+    constexpr float kPScale = 4096.0f;
 
     const int p0 = lo / kPage, p1 = (hi - 1) / kPage;
     const int32_t* bt = a.block_table + (int64_t)b * a.bt_stride;
@@ -160,29 +237,24 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs a) {
     const char* vbase = static_cast<const char*>(a.v_pool);
     const int lane_off = lane * 8 * EB;
 
-    auto page_id = [&](int p) -> int {
-        int id = __ldg(bt + p);
-        id = min(max(id, 0), a.num_pages - 1);
-        return id;
-    };
-
     CT kc[NLOAD], vc[NLOAD];
     float ksc[NLOAD], vsc[NLOAD];
-    auto load_page = [&](int p, CT (&kk)[NLOAD], CT (&vv)[NLOAD], float (&ks)[NLOAD], float (&vs)[NLOAD]) {
-        const int id = page_id(p);
+    auto load_page = [&](int p) {
+        int id = __ldg(bt + p);
+        id = min(max(id, 0), a.num_pages - 1);
         const int64_t blk = (int64_t)id * a.num_kv_heads + kvh;
         const char* kp = kbase + blk * head_stride * EB + lane_off;
         const char* vp = vbase + blk * head_stride * EB + lane_off;
 #pragma unroll
         for (int i = 0; i < NLOAD; ++i) {
-            kk[i] = *reinterpret_cast<const CT*>(kp + i * 512 * EB);
-            vv[i] = *reinterpret_cast<const CT*>(vp + i * 512 * EB);
+            kc[i] = *reinterpret_cast<const CT*>(kp + i * 512 * EB);
+            vc[i] = *reinterpret_cast<const CT*>(vp + i * 512 * EB);
         }
         if constexpr (INT8) {
 #pragma unroll
             for (int i = 0; i < NLOAD; ++i) {
-                ks[i] = __ldg(a.k_scale + blk * kPage + i * KPL + kg);
-                vs[i] = __ldg(a.v_scale + blk * kPage + i * KPL + kg);
+                ksc[i] = __ldg(a.k_scale + blk * kPage + i * KPL + kg);
+                vsc[i] = __ldg(a.v_scale + blk * kPage + i * KPL + kg);
             }
         }
     };
@@ -195,8 +267,9 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs a) {
     float m_run = -INFINITY;   // running max (log2 units) of this lane's head
     float l_run = 0.0f;        // this lane's share of sum 2^(s - m_run) (its keys, its head)
 
-    load_page(p0, kc, vc, ksc, vsc);
-    for (int p = p0; p <= p1; ++p) {
+    int pb = 0;
+    if (p0 + wave <= p1) load_page(p0 + wave);
+    for (int p = p0 + wave; p <= p1; p += kNW) {
         CT kcur[NLOAD], vcur[NLOAD];
         float kscur[NLOAD], vscur[NLOAD];
 #pragma unroll
@@ -204,10 +277,10 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs a) {
             kcur[i] = kc[i]; vcur[i] = vc[i];
             kscur[i] = ksc[i]; vscur[i] = vsc[i];
         }
-        if (p < p1) load_page(p + 1, kc, vc, ksc, vsc);
+        if (p + kNW <= p1) load_page(p + kNW);
 
-        const int kbase_pos = p * kPage;
-        const bool full = kbase_pos >= lo && kbase_pos + kPage <= hi;
+        const int kpos0 = p * kPage;
+        const bool full = kpos0 >= lo && kpos0 + kPage <= hi;
 
         // ---- scores ----
         float s[NLOAD];
@@ -226,9 +299,10 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs a) {
                 acc[j] = t;
             }
             float dot = transpose_reduce<LPK, G>(acc);
-            const int key = kbase_pos + i * KPL + kg;
+            if constexpr (INT8) dot -= qbias;
+            const int key = kpos0 + i * KPL + kg;
             valid[i] = key >= lo && key < hi;
-            float sc = INT8 ? c2 * kscur[i] : c2;
+            const float sc = INT8 ? c2 * kscur[i] : c2;
             s[i] = valid[i] ? dot * sc : -INFINITY;
         }
         // ---- running max, lazy rescale ----
@@ -242,72 +316,117 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs a) {
             l_run *= alpha;
 #pragma unroll
             for (int g = 0; g < G; ++g) {
-                const float ag = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(alpha), g * HG));
+                const float ag = lane_read(alpha, g * HG);
 #pragma unroll
                 for (int j = 0; j < 8; ++j) o[g][j] *= ag;
             }
             m_run = m_new;
         }
-        // ---- weights ----
-        const int pb = p & 1;
+        // ---- weights, shared within the wave ----
 #pragma unroll
         for (int i = 0; i < NLOAD; ++i) {
             const float pw = fast_exp2(s[i] - m_run);      // 0 for masked keys
             l_run += pw;
             float pv = pw;
-            if constexpr (INT8) pv = valid[i] ? pw * vscur[i] : 0.0f;
-            if (sub % HG == 0) p_buf[pb][i * KPL + kg][myhead] = pv;
+            if constexpr (INT8) pv = valid[i] ? pw * vscur[i] * (PAIRED ? kPScale : 1.0f) : 0.0f;
+            if (sub % HG == 0) p_buf[wave][pb][i * KPL + kg][myhead] = pv;
         }
-        __syncthreads();
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
         // ---- p.v ----
+        if constexpr (!INT8) {
+            if (!full) {
 #pragma unroll
-        for (int i = 0; i < NLOAD; ++i) {
-            float pw[G];
+                for (int i = 0; i < NLOAD; ++i)
+                    if (!valid[i]) vcur[i] = CT{};          // poison past the sequence end
+            }
+        }
+        if constexpr (!PAIRED) {
 #pragma unroll
-            for (int g = 0; g < G; ++g) pw[g] = p_buf[pb][i * KPL + kg][g];
-            float x[8];
-            v_floats(vcur[i], x);
-            if constexpr (!INT8) {
-                if (!full) {
+            for (int i = 0; i < NLOAD; ++i) {
+                float pw[G];
 #pragma unroll
-                    for (int j = 0; j < 8; ++j) x[j] = valid[i] ? x[j] : 0.0f;
+                for (int g = 0; g < G; ++g) pw[g] = p_buf[wave][pb][i * KPL + kg][g];
+                float x[8];
+                v_floats(vcur[i], x);
+#pragma unroll
+                for (int g = 0; g < G; ++g)
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) o[g][j] = fmaf(pw[g], x[j], o[g][j]);
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < NLOAD; i += 2) {
+                uint32_t vv[8];
+                v_pairs(vcur[i], vcur[i + 1], vv);
+                float pa[G], pbv[G];
+#pragma unroll
+                for (int g = 0; g < G; ++g) {
+                    pa[g] = p_buf[wave][pb][i * KPL + kg][g];
+                    pbv[g] = p_buf[wave][pb][(i + 1) * KPL + kg][g];
+                }
+#pragma unroll
+                for (int g = 0; g < G; ++g) {
+                    if constexpr (INT8) {
+                        const f16x2 pp = __builtin_bit_cast(f16x2, __builtin_amdgcn_cvt_pkrtz(pa[g], pbv[g]));
+#pragma unroll
+                        for (int j = 0; j < 8; ++j)
+                            o[g][j] = __builtin_amdgcn_fdot2(pp, __builtin_bit_cast(f16x2, vv[j]), o[g][j], false);
+                    } else {
+                        const bf16x2 pp = as_bf16x2(pack_bf16_rne(pa[g], pbv[g]));
+#pragma unroll
+                        for (int j = 0; j < 8; ++j)
+                            o[g][j] = __builtin_amdgcn_fdot2_f32_bf16(pp, as_bf16x2(vv[j]), o[g][j], false);
+                    }
                 }
             }
-#pragma unroll
-            for (int g = 0; g < G; ++g)
-#pragma unroll
-                for (int j = 0; j < 8; ++j) o[g][j] = fmaf(pw[g], x[j], o[g][j]);
         }
+        pb ^= 1;
     }
 
-    // ---- reduce across key groups ----
+    // ---- per wave: reduce across key groups, publish (m, l, o) ----
 #pragma unroll
     for (int g = 0; g < G; ++g)
 #pragma unroll
         for (int j = 0; j < 8; ++j) o[g][j] = stride_sum<LPK>(o[g][j]);
     const float l_tot = stride_sum<LPK>(l_run);
-
+    constexpr float kOScale = (INT8 && PAIRED) ? 1.0f / kPScale : 1.0f;
 #pragma unroll
     for (int g = 0; g < G; ++g) {
-        if (g % KPL != kg) continue;
-        const float lg = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(l_tot), g * HG));
-        const float mg = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(m_run), g * HG));
-        float inv;
-        float* dst;
-        if constexpr (FINAL) {
-            float z = lg;
-            if (a.sinks) z += fast_exp2(__ldg(a.sinks + head0 + g) * kLog2e - mg);
-            inv = 1.0f / z;
-            dst = a.out + ((int64_t)b * Hq + head0 + g) * D + sub * 8;
-        } else {
-            inv = 1.0f / lg;
-            dst = a.o_part + (part_row + (int64_t)g * a.max_splits) * D + sub * 8;
-            if (sub == 0) a.lse_part[part_row + (int64_t)g * a.max_splits] = (mg + fast_log2(lg)) * kLn2;
+        if (g % KPL == kg) {
+            float* dst = &o_sh[wave][g][sub * 8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) dst[j] = o[g][j] * kOScale;
         }
-        float4 w0 = make_float4(o[g][0] * inv, o[g][1] * inv, o[g][2] * inv, o[g][3] * inv);
-        float4 w1 = make_float4(o[g][4] * inv, o[g][5] * inv, o[g][6] * inv, o[g][7] * inv);
-        reinterpret_cast<float4*>(dst)[0] = w0;
-        reinterpret_cast<float4*>(dst)[1] = w1;
+        if (lane == g * HG) {
+            m_sh[wave][g] = m_run;
+            l_sh[wave][g] = l_tot;
+        }
+    }
+    __syncthreads();
+
+    // ---- merge the four waves ----
+    for (int e = tid; e < G * D; e += kNW * kWave) {
+        const int g = e / D, d = e % D;
+        float M = m_sh[0][g];
+#pragma unroll
+        for (int w = 1; w < kNW; ++w) M = fmaxf(M, m_sh[w][g]);
+        const float Ms = (M == -INFINITY) ? 0.0f : M;
+        float num = 0.0f, den = 0.0f;
+#pragma unroll
+        for (int w = 0; w < kNW; ++w) {
+            const float f = fast_exp2(m_sh[w][g] - Ms);      // 0 for a wave with no pages
+            num = fmaf(f, o_sh[w][g][d], num);
+            den = fmaf(f, l_sh[w][g], den);
+        }
+        if constexpr (FINAL) {
+            if (a.sinks) den += fast_exp2(__ldg(a.sinks + head0 + g) * kLog2e - Ms);
+            a.out[((int64_t)b * Hq + head0 + g) * D + d] = den > 0.0f ? num / den : 0.0f;
+        } else {
+            a.o_part[(part_row + (int64_t)g * a.max_splits) * D + d] = num / den;
+            if (d == 0) a.lse_part[part_row + (int64_t)g * a.max_splits] = (M + fast_log2(den)) * kLn2;
+        }
     }
 }
 
@@ -315,10 +434,10 @@ template <int D, int G, bool INT8>
 hipError_t launch_dg(const DecodeArgs& a, hipStream_t s) {
     if (a.max_splits == 1) {
         hipLaunchKernelGGL((decode_kernel<D, G, INT8, true>), dim3(1, a.num_kv_heads, a.batch),
-                           dim3(kWave), 0, s, a);
+                           dim3(kNW * kWave), 0, s, a);
     } else {
         hipLaunchKernelGGL((decode_kernel<D, G, INT8, false>),
-                           dim3(a.max_splits, a.num_kv_heads, a.batch), dim3(kWave), 0, s, a);
+                           dim3(a.max_splits, a.num_kv_heads, a.batch), dim3(kNW * kWave), 0, s, a);
     }
     return hipGetLastError();
 }

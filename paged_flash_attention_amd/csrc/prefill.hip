@@ -81,7 +81,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
     __shared__ Tile<D> sm;
 
     const int tid = threadIdx.x;
-    const int wave = tid / kWave;
+    const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);   // wave-uniform
     const int lane = tid % kWave;
     const int r32 = lane % 32;
     const int half = lane / 32;
@@ -250,16 +250,26 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
         const bool needed = wave_live && key0 < w_hi && key0 + kBN > w_lo;
         if (needed) {
             // ---- S^T = K Q^T for two 32-key sub-blocks ----
+            // The two accumulator chains are interleaved, and the K fragments of step
+            // kk+1 are read from LDS while the MFMAs of step kk run.
             f32x16 s[2];
 #pragma unroll
-            for (int sb = 0; sb < 2; ++sb) {
+            for (int r = 0; r < 16; ++r) s[0][r] = s[1][r] = 0.0f;
+            const uint16_t* kr0 = &sm.k[buf][r32][8 * half];
+            const uint16_t* kr1 = &sm.k[buf][32 + r32][8 * half];
+            uint4 ka0 = *reinterpret_cast<const uint4*>(kr0);
+            uint4 ka1 = *reinterpret_cast<const uint4*>(kr1);
 #pragma unroll
-                for (int r = 0; r < 16; ++r) s[sb][r] = 0.0f;
-#pragma unroll
-                for (int kk = 0; kk < KK; ++kk) {
-                    const uint4 kv = *reinterpret_cast<const uint4*>(&sm.k[buf][32 * sb + r32][16 * kk + 8 * half]);
-                    s[sb] = mfma32(__builtin_bit_cast(bf16x8, kv), qf[kk], s[sb]);
+            for (int kk = 0; kk < KK; ++kk) {
+                uint4 kn0 = ka0, kn1 = ka1;
+                if (kk + 1 < KK) {
+                    kn0 = *reinterpret_cast<const uint4*>(kr0 + 16 * (kk + 1));
+                    kn1 = *reinterpret_cast<const uint4*>(kr1 + 16 * (kk + 1));
                 }
+                s[0] = mfma32(__builtin_bit_cast(bf16x8, ka0), qf[kk], s[0]);
+                s[1] = mfma32(__builtin_bit_cast(bf16x8, ka1), qf[kk], s[1]);
+                ka0 = kn0;
+                ka1 = kn1;
             }
             // ---- scale, mask ----
             const bool full = (key0 + kBN - 1 <= prefix + w_first) &&
