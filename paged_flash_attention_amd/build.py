@@ -59,6 +59,11 @@ def build(jobs: int = 8) -> str:
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
+    # every kernel launch stub must be defined in the library
+    nm = subprocess.run(["nm", "-D", "--undefined-only", tmp], capture_output=True, text=True)
+    missing = [l.split()[-1] for l in nm.stdout.splitlines() if "__device_stub__" in l]
+    if missing:
+        raise RuntimeError("undefined kernel launch stubs in libpfa.so:\n" + "\n".join(missing))
     os.replace(tmp, LIB)
     return LIB
 

@@ -172,7 +172,7 @@ pfa_status pfa_paged_attn_prefill(const pfa_attn_desc* desc, const pfa_kv_pool* 
     if (batch < 0 || max_q_len < 0 || bt_stride <= 0 || max_seq_len < max_q_len || max_splits < 1)
         return PFA_ERR_SHAPE;
     if (max_seq_len > (int64_t)bt_stride * desc->page_size) return PFA_ERR_SHAPE;
-    const int tpb = 128 / g;
+    const int tpb = pfa::kPrefillRows / g;
     const int64_t items =
         (int64_t)batch * desc->num_kv_heads * ((max_q_len + tpb - 1) / tpb) * max_splits;
     if (items > 0x7fffffff - 8) return PFA_ERR_SHAPE;
@@ -229,7 +229,7 @@ int32_t pfa_prefill_num_splits(const pfa_attn_desc* desc, int32_t batch, int32_t
     const int g = desc->num_q_heads / desc->num_kv_heads;
     if (!prefill_group_ok(g) || batch <= 0 || max_q_len <= 0 || max_seq_len <= 0) return 1;
     if (num_cus <= 0) num_cus = 256;
-    const int tpb = 128 / g;
+    const int tpb = pfa::kPrefillRows / g;
     const int64_t items = (int64_t)batch * desc->num_kv_heads * ((max_q_len + tpb - 1) / tpb);
     const int64_t target = 2 * (int64_t)num_cus;
     // keys a row of the chunk sees at most: the window, else the whole sequence

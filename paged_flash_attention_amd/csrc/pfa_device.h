@@ -12,6 +12,7 @@ constexpr int kWave = 64;
 constexpr int kPage = 16;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
+constexpr int kPrefillRows = 256;   // query rows (token x head-of-group) per prefill workgroup
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));

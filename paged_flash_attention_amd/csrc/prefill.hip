@@ -7,24 +7,32 @@
 // restores the conversation's KV from a store and prefills only the new turn.
 //
 // MI355X design (gfx950, v_mfma_f32_32x32x16_bf16):
-//  * A workgroup is 4 waves and owns 128 query rows of one (sequence, KV head).
+//  * A workgroup is 8 waves and owns 256 query rows of one (sequence, KV head).
 //    A row is one (token, head-of-group) pair, so the G query heads sharing a KV
 //    head share every K/V tile (GQA packing).  Each wave owns 32 rows.
-//  * Each iteration takes 64 keys (4 pages).  Their page ids come from the block
-//    table.  The K tile is staged in LDS row-major; the V tile is staged
-//    transposed (V^T, keys contiguous per dim) through register permutes.  Both
-//    are double-buffered, with the next tile's global loads in flight during
-//    the current tile's math.
-//  * Scores are computed transposed: S^T = K Q^T.  Then every lane of the MFMA
-//    output holds one query row (lane % 32) and 16 of the keys, with the other
-//    16 in lane ^ 32.  The row max and row sum take one cross-lane step, and
-//    P^T is already in the B-operand layout of O^T = V^T P^T.  The O^T
+//  * K/V go HBM -> LDS with global_load_lds_dwordx4, with no register staging, in
+//    a 3-stage ring of 64-key tiles (4 pages).  Two tiles stay in flight while one
+//    is consumed, and each wave waits on its own vmcnt, so there is one barrier per
+//    tile.  The page ids of the tile after next are read (wave-uniform) while the
+//    current tile computes.
+//  * LDS rows are the page rows (keys x D), 16-byte chunks XOR-swizzled per row.
+//    The swizzle is applied on the global side of the direct loads, and it makes
+//    both read patterns below free of bank conflicts.
+//  * Scores are computed transposed: S^T = K Q^T, with Q^T in registers.  Then every
+//    lane of the MFMA output holds one query row (lane % 32) and 16 of the keys,
+//    with the other 16 in lane ^ 32.  The row max and row sum take one cross-lane
+//    step, and P^T is already in the B-operand layout of O^T = V^T P^T.  The O^T
 //    accumulator of a lane also belongs to its one row, so the online-softmax
 //    rescale is a per-lane scalar, skipped when no row's max grew.
+//  * The V^T A-operand comes straight from the row-major V tile through
+//    ds_read_b64_tr_b16.  In each 16-lane group, lane j points at
+//    V[k0 + j/4][d0 + 4(j%4)], and lane i gets V[k0..k0+3][d0 + i].
 //  * Scores are kept in log2 units (sm_scale*log2 e folded in), and
 //    exp2 -> v_exp_f32.  P is rounded to bf16 (RNE) for the PV MFMA.
 //  * Causal/window masking costs nothing on tiles that are fully visible.  A wave
-//    skips the MFMAs of tiles that lie entirely outside its rows' ranges.
+//    skips the MFMAs of tiles that lie entirely outside its rows' ranges.  V rows
+//    past the sequence end are zeroed in LDS, so poison in unwritten page slots
+//    never meets a zero weight.
 //  * Workgroups map to XCDs so that each XCD's L2 holds the K/V of the heads it
 //    serves.  Within an XCD the longest (latest) query tiles go first.
 //  * Split mode covers a short chunk on a long prefix, such as 130 new tokens on
@@ -37,48 +45,94 @@
 namespace pfa {
 namespace {
 
-constexpr int kWaves = 4;
 constexpr int kRowsPerWave = 32;
-constexpr int kBN = 64;           // keys per iteration
+constexpr int kWaves = kPrefillRows / kRowsPerWave;
+constexpr int kThreads = kWaves * kWave;
+constexpr int kBN = 64;           // keys per tile
 constexpr int kXcds = 8;
+
+#define LDS3 __attribute__((address_space(3)))
+typedef short s16x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const f32x16& c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
-template <int D>
-struct Tile {
-    static constexpr int KP = D + 8;          // K row pitch (elements): 16 lanes reading one
-                                              // column of 16 rows hit 16 distinct bank quads
-    uint16_t k[2][kBN][KP];
-    uint16_t vt[2][D][kBN];                   // V^T rows of 64 keys, 16-byte chunks swizzled
-};
+// 16-byte-chunk swizzles (chunk c of row r sits at c ^ f(r)).  K: the 16 rows one
+// 16-lane MFMA read touches land on 16 distinct bank quads.  V: the 4 rows x 2
+// chunks of a 16-lane transposed read, and 4 rows x 4 chunks per 32 lanes, are
+// distinct.  (Rows of D = 64 are 128 B, two rows per bank line.)
+template <int D> __device__ __forceinline__ int swz_k(int r) { return D == 128 ? (r & 15) : ((r >> 1) & 7); }
+template <int D> __device__ __forceinline__ int swz_v(int r) { return D == 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1); }
 
-// position of key-quad q (0..15) of a 64-key tile inside a V^T row: within each
-// 16-key group the middle two quads swap, so that the 8 keys one MFMA lane needs
-// (k-slots 8*(lane/32)..+8) are contiguous.
-__device__ __forceinline__ int vt_quad_pos(int q) {
-    return (q & ~3) | ((q & 1) << 1) | ((q & 2) >> 1);
+// Wait until at most N vector-memory operations of this wave are outstanding.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt");
+    __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
-// Element offset of (row d, 16-byte chunk c, element e in chunk) in a V^T buffer.
-// A row is 128 B, half the banks; chunk c of row d sits at c ^ ((d >> 1) & 7), so
-// the 16 rows one 16-lane read touches fall on 16 distinct bank quads.
-__device__ __forceinline__ int vt_off(int d, int c, int e) {
-    return d * kBN + ((c ^ ((d >> 1) & 7)) << 3) + e;
+// The V^T operands of one 16-key slice: for each 32-dim block db, a transposed
+// read of keys k..k+3 at addr[db] and of keys k+8..k+11 at addr[db] + HI bytes.
+// The reads are issued as one asm block that waits for them itself.  Issued
+// through the intrinsic, the compiler treats the read as possibly aliasing any
+// in-flight direct load, and would wait for the prefetched tiles too.
+template <int DB, int HI>
+__device__ __forceinline__ void tr_reads(uint2 (&lo)[DB], uint2 (&hi)[DB], const uint32_t (&addr)[DB]) {
+    if constexpr (DB == 4) {
+        asm volatile(
+            "ds_read_b64_tr_b16 %0, %8\n\t"
+            "ds_read_b64_tr_b16 %1, %8 offset:%12\n\t"
+            "ds_read_b64_tr_b16 %2, %9\n\t"
+            "ds_read_b64_tr_b16 %3, %9 offset:%12\n\t"
+            "ds_read_b64_tr_b16 %4, %10\n\t"
+            "ds_read_b64_tr_b16 %5, %10 offset:%12\n\t"
+            "ds_read_b64_tr_b16 %6, %11\n\t"
+            "ds_read_b64_tr_b16 %7, %11 offset:%12\n\t"
+            "s_waitcnt lgkmcnt(0)"
+            : "=&v"(lo[0]), "=&v"(hi[0]), "=&v"(lo[1]), "=&v"(hi[1]),
+              "=&v"(lo[2]), "=&v"(hi[2]), "=&v"(lo[3]), "=&v"(hi[3])
+            : "v"(addr[0]), "v"(addr[1]), "v"(addr[2]), "v"(addr[3]), "i"(HI)
+            : "memory");
+    } else {
+        static_assert(DB == 2, "head dim");
+        asm volatile(
+            "ds_read_b64_tr_b16 %0, %4\n\t"
+            "ds_read_b64_tr_b16 %1, %4 offset:%6\n\t"
+            "ds_read_b64_tr_b16 %2, %5\n\t"
+            "ds_read_b64_tr_b16 %3, %5 offset:%6\n\t"
+            "s_waitcnt lgkmcnt(0)"
+            : "=&v"(lo[0]), "=&v"(hi[0]), "=&v"(lo[1]), "=&v"(hi[1])
+            : "v"(addr[0]), "v"(addr[1]), "i"(HI)
+            : "memory");
+    }
+}
+
+// 16-byte direct load HBM -> LDS: lane l's bytes land at lds + 16*l.  (A plain,
+// non-template function: used straight inside the kernel template, the builtin
+// made the host pass drop the launch stubs.)
+__device__ __forceinline__ void dma16(const uint16_t* src, uint16_t* lds) {
+    __builtin_amdgcn_global_load_lds(src, (LDS3 void*)lds, 16, 0, 0);
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    return (uint32_t)(uintptr_t)(LDS3 const void*)p;
 }
 
 template <int D, int G, bool SPLIT>
-__global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
+__global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a, const int32_t* __restrict__ block_table) {
     constexpr int TPW = kRowsPerWave / G;               // tokens per wave
     constexpr int TPB = TPW * kWaves;                   // tokens per workgroup
     constexpr int KK = D / 16;                          // MFMA k-steps over D
     constexpr int DB = D / 32;                          // 32-row blocks of O^T
-    constexpr int CPR = D / 8;                          // 16-byte chunks per K row
-    constexpr int KLOADS = kBN * CPR / 256;             // K chunks per thread
-    static_assert(KLOADS * 256 == kBN * CPR, "K tile split");
+    constexpr int CPR = D / 8;                          // 16-byte chunks per row
+    constexpr int ROWS_PER_DMA = kWave / CPR;           // rows one wave-wide direct load fills
+    constexpr int DMA_PER_WAVE = kBN / ROWS_PER_DMA / kWaves;   // per tensor per tile
+    constexpr int NL = 2 * DMA_PER_WAVE;                // vector-memory ops per tile per wave
+    static_assert(DMA_PER_WAVE >= 1, "tile split");
 
-    __shared__ Tile<D> sm;
+    __shared__ __attribute__((aligned(1024))) uint16_t k_s0[kBN * D], k_s1[kBN * D], k_s2[kBN * D];
+    __shared__ __attribute__((aligned(1024))) uint16_t v_s0[kBN * D], v_s1[kBN * D], v_s2[kBN * D];
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);   // wave-uniform
@@ -153,75 +207,32 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
         }
     }
 
-    const int32_t* bt = a.block_table + (int64_t)b * a.bt_stride;
-    const int64_t hblk = (int64_t)kPage * D;             // elements per page-head block
-
-    // ---- tile loads: global -> registers ----
-    // A 64-key tile is 4 pages.  Its page ids are wave-uniform loads; pages past the
-    // sequence end are never read (their rows are zero-filled).
-    uint4 kreg[KLOADS];
-    uint4 vreg[4];
-    const int vq = tid % 16;                              // key quad of this thread (V)
-    const int vc = tid / 16;                              // 8-dim chunk of this thread (V)
-    auto sel4 = [](int j, const uint16_t* p0, const uint16_t* p1, const uint16_t* p2,
-                   const uint16_t* p3) { return j == 0 ? p0 : j == 1 ? p1 : j == 2 ? p2 : p3; };
-    auto load_tile = [&](int kb) {
-        const int key0 = kb * kBN;
-        const uint16_t* kp[4];
-        const uint16_t* vp[4];
+    // ---- direct HBM -> LDS tile loads ----
+    // a __restrict__ kernel argument: uniform reads of it become scalar loads, which
+    // stay out of the vmcnt queue the direct loads are counted on
+    const int32_t* bt = block_table + (int64_t)b * a.bt_stride;
+    const int npg = (n + kPage - 1) / kPage;
+    const int64_t hblk = (int64_t)kPage * D;            // elements per page-head block
+    const int kb0 = lo / kBN;
+    const int kb1 = (hi - 1) / kBN;
+    auto tile_pages = [&](int kb, int (&pg)[4]) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            const int pi = kb * 4 + j;
-            int pg = 0;
-            if (pi * kPage < n) pg = min(max(__ldg(bt + pi), 0), a.num_pages - 1);
-            const int64_t off = ((int64_t)pg * a.num_kv_heads + kvh) * hblk;
-            kp[j] = a.k_pool + off;
-            vp[j] = a.v_pool + off;
-        }
-#pragma unroll
-        for (int e = 0; e < KLOADS; ++e) {
-            const int c = tid + 256 * e;
-            const int key = c / CPR, col = c % CPR;
-            uint4 v = make_uint4(0, 0, 0, 0);
-            if (key0 + key < n)
-                v = *reinterpret_cast<const uint4*>(sel4(key / kPage, kp[0], kp[1], kp[2], kp[3]) +
-                                                    (key % kPage) * D + col * 8);
-            kreg[e] = v;
-        }
-        if (vc < CPR) {
-            const uint16_t* vbase = sel4(vq / 4, vp[0], vp[1], vp[2], vp[3]) + (4 * (vq % 4)) * D + vc * 8;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                uint4 v = make_uint4(0, 0, 0, 0);
-                if (key0 + 4 * vq + e < n) v = *reinterpret_cast<const uint4*>(vbase + e * D);
-                vreg[e] = v;
-            }
+            const int pi = min(kb * 4 + j, npg - 1);
+            pg[j] = min(max(__ldg(bt + pi), 0), a.num_pages - 1);
         }
     };
-    // ---- registers -> LDS (K row-major, V transposed and swizzled) ----
-    auto store_tile = [&](int buf) {
+    const int lrow = lane / CPR;                          // row within one direct load
+    const int lchunk = lane % CPR;                        // physical chunk this lane fills
+    auto issue = [&](const int (&pg)[4], uint16_t* kdst, uint16_t* vdst) {
 #pragma unroll
-        for (int e = 0; e < KLOADS; ++e) {
-            const int c = tid + 256 * e;
-            const int key = c / CPR, col = c % CPR;
-            *reinterpret_cast<uint4*>(&sm.k[buf][key][col * 8]) = kreg[e];
-        }
-        if (vc < CPR) {
-            const uint32_t w0[4] = {vreg[0].x, vreg[0].y, vreg[0].z, vreg[0].w};
-            const uint32_t w1[4] = {vreg[1].x, vreg[1].y, vreg[1].z, vreg[1].w};
-            const uint32_t w2[4] = {vreg[2].x, vreg[2].y, vreg[2].z, vreg[2].w};
-            const uint32_t w3[4] = {vreg[3].x, vreg[3].y, vreg[3].z, vreg[3].w};
-            const int kpos = 4 * vt_quad_pos(vq);
-            uint16_t* vt = &sm.vt[buf][0][0];
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const uint32_t sel = (j & 1) ? 0x07060302u : 0x05040100u;
-                const int w = j >> 1;
-                uint2 t;
-                t.x = __builtin_amdgcn_perm(w1[w], w0[w], sel);
-                t.y = __builtin_amdgcn_perm(w3[w], w2[w], sel);
-                *reinterpret_cast<uint2*>(vt + vt_off(vc * 8 + j, kpos >> 3, kpos & 7)) = t;
-            }
+        for (int i = 0; i < DMA_PER_WAVE; ++i) {
+            const int q = wave * DMA_PER_WAVE + i;        // which 1 KB slice of the tile
+            const int row0 = q * ROWS_PER_DMA;            // rows row0.. lie in one page
+            const int row = row0 + lrow;
+            const int64_t pbase = ((int64_t)pg[row0 / kPage] * a.num_kv_heads + kvh) * hblk + (row % kPage) * D;
+            dma16(a.k_pool + pbase + (lchunk ^ swz_k<D>(row)) * 8, kdst + row0 * D);
+            dma16(a.v_pool + pbase + (lchunk ^ swz_v<D>(row)) * 8, vdst + row0 * D);
         }
     };
 
@@ -235,100 +246,128 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
     float l_run = 0.0f;        // this lane's share (its 16 keys of each 32)
     const float c2 = a.sm_scale * kLog2e;
 
-    const int kb0 = lo / kBN;
-    const int kb1 = (hi - 1) / kBN;
+    // per-lane constants of the transposed V reads
+    const int tr_g = lane / 16, tr_j = lane % 16;
+    const int tr_row = 4 * (tr_g / 2) + tr_j / 4;                 // + 16m (+ 8 for the upper half)
+    const int tr_chunk = 2 * (tr_g % 2) + (tr_j % 4) / 2;         // + 4db
+    const int tr_sub = 4 * (tr_j % 2);
 
-    load_tile(kb0);
-    store_tile(0);
-    __syncthreads();
-
-    for (int kb = kb0; kb <= kb1; ++kb) {
-        const int buf = (kb - kb0) & 1;
-        if (kb < kb1) load_tile(kb + 1);
-
+    auto compute = [&](int kb, const uint16_t* ks, const uint16_t* vs) {
         const int key0 = kb * kBN;
-        const bool needed = wave_live && key0 < w_hi && key0 + kBN > w_lo;
-        if (needed) {
-            // ---- S^T = K Q^T for two 32-key sub-blocks ----
-            // The two accumulator chains are interleaved, and the K fragments of step
-            // kk+1 are read from LDS while the MFMAs of step kk run.
-            f32x16 s[2];
+        // ---- S^T = K Q^T for two 32-key sub-blocks, chains interleaved ----
+        f32x16 s[2];
 #pragma unroll
-            for (int r = 0; r < 16; ++r) s[0][r] = s[1][r] = 0.0f;
-            const uint16_t* kr0 = &sm.k[buf][r32][8 * half];
-            const uint16_t* kr1 = &sm.k[buf][32 + r32][8 * half];
-            uint4 ka0 = *reinterpret_cast<const uint4*>(kr0);
-            uint4 ka1 = *reinterpret_cast<const uint4*>(kr1);
+        for (int r = 0; r < 16; ++r) s[0][r] = s[1][r] = 0.0f;
+        const int kr0 = r32, kr1 = 32 + r32;
 #pragma unroll
-            for (int kk = 0; kk < KK; ++kk) {
-                uint4 kn0 = ka0, kn1 = ka1;
-                if (kk + 1 < KK) {
-                    kn0 = *reinterpret_cast<const uint4*>(kr0 + 16 * (kk + 1));
-                    kn1 = *reinterpret_cast<const uint4*>(kr1 + 16 * (kk + 1));
-                }
-                s[0] = mfma32(__builtin_bit_cast(bf16x8, ka0), qf[kk], s[0]);
-                s[1] = mfma32(__builtin_bit_cast(bf16x8, ka1), qf[kk], s[1]);
-                ka0 = kn0;
-                ka1 = kn1;
-            }
-            // ---- scale, mask ----
-            const bool full = (key0 + kBN - 1 <= prefix + w_first) &&
-                              (W == 0 || (prefix + w_last) - key0 < W);
-            float mt = -INFINITY;
+        for (int kk = 0; kk < KK; ++kk) {
+            const int c = 2 * kk + half;
+            const uint4 k0 = *reinterpret_cast<const uint4*>(ks + kr0 * D + ((c ^ swz_k<D>(kr0)) << 3));
+            const uint4 k1 = *reinterpret_cast<const uint4*>(ks + kr1 * D + ((c ^ swz_k<D>(kr1)) << 3));
+            s[0] = mfma32(__builtin_bit_cast(bf16x8, k0), qf[kk], s[0]);
+            s[1] = mfma32(__builtin_bit_cast(bf16x8, k1), qf[kk], s[1]);
+        }
+        // ---- scale, mask ----
+        const bool full = (key0 + kBN - 1 <= prefix + w_first) && (W == 0 || (prefix + w_last) - key0 < W);
+        float mt = -INFINITY;
+        if (full) {
 #pragma unroll
             for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
-                    float x = s[sb][r] * c2;
-                    if (!full) {
-                        const int key = key0 + 32 * sb + 8 * (r / 4) + 4 * half + (r % 4);
-                        const bool vis = key <= pos_l && (W == 0 || pos_l - key < W);
-                        x = vis ? x : -INFINITY;
-                    }
-                    s[sb][r] = x;
-                    mt = fmaxf(mt, x);
+                    s[sb][r] *= c2;
+                    mt = fmaxf(mt, s[sb][r]);
                 }
-            mt = fmaxf(mt, xor_lane<32>(mt));
-            const float m_new = fmaxf(m_run, mt);
-            if (__any(m_new > m_run)) {
-                const float mu = (m_new == -INFINITY) ? 0.0f : m_new;
-                const float alpha = fast_exp2(m_run - mu);
-                l_run *= alpha;
-#pragma unroll
-                for (int db = 0; db < DB; ++db)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) acc_o[db][r] *= alpha;
-                m_run = m_new;
-            }
-            const float mu = (m_run == -INFINITY) ? 0.0f : m_run;
-            // ---- P = 2^(x - m), packed to bf16 in the B-operand order ----
-            uint32_t pk[2][8];
+        } else {
 #pragma unroll
             for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
-                for (int r = 0; r < 16; r += 2) {
-                    const float p0 = fast_exp2(s[sb][r] - mu);
-                    const float p1 = fast_exp2(s[sb][r + 1] - mu);
-                    l_run += p0 + p1;
-                    pk[sb][r / 2] = pack_bf16_rne(p0, p1);
+                for (int r = 0; r < 16; ++r) {
+                    const int key = key0 + 32 * sb + 8 * (r / 4) + 4 * half + (r % 4);
+                    const bool vis = key <= pos_l && (W == 0 || pos_l - key < W);
+                    s[sb][r] = vis ? s[sb][r] * c2 : -INFINITY;
+                    mt = fmaxf(mt, s[sb][r]);
                 }
-            // ---- O^T += V^T P^T ----
+        }
+        mt = fmaxf(mt, xor_lane<32>(mt));
+        const float m_new = fmaxf(m_run, mt);
+        if (__any(m_new > m_run)) {
+            const float mu = (m_new == -INFINITY) ? 0.0f : m_new;
+            const float alpha = fast_exp2(m_run - mu);
+            l_run *= alpha;
 #pragma unroll
-            for (int m = 0; m < kBN / 16; ++m) {
-                const int sb = m / 2, r0 = 4 * (m % 2);
-                const uint4 pu = make_uint4(pk[sb][r0], pk[sb][r0 + 1], pk[sb][r0 + 2], pk[sb][r0 + 3]);
-                const bf16x8 pf = __builtin_bit_cast(bf16x8, pu);
+            for (int db = 0; db < DB; ++db)
 #pragma unroll
-                for (int db = 0; db < DB; ++db) {
-                    const uint4 vv = *reinterpret_cast<const uint4*>(&sm.vt[buf][0][0] +
-                                                                     vt_off(32 * db + r32, 2 * m + half, 0));
-                    acc_o[db] = mfma32(__builtin_bit_cast(bf16x8, vv), pf, acc_o[db]);
-                }
+                for (int r = 0; r < 16; ++r) acc_o[db][r] *= alpha;
+            m_run = m_new;
+        }
+        const float mu = (m_run == -INFINITY) ? 0.0f : m_run;
+        // ---- P = 2^(x - m), packed to bf16 in the B-operand order ----
+        uint32_t pk[2][8];
+#pragma unroll
+        for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+            for (int r = 0; r < 16; r += 2) {
+                const float p0 = fast_exp2(s[sb][r] - mu);
+                const float p1 = fast_exp2(s[sb][r + 1] - mu);
+                l_run += p0 + p1;
+                pk[sb][r / 2] = pack_bf16_rne(p0, p1);
+            }
+        // ---- O^T += V^T P^T, V^T fragments by transposed LDS reads ----
+#pragma unroll
+        for (int m = 0; m < kBN / 16; ++m) {
+            const int sb = m / 2, r0 = 4 * (m % 2);
+            const uint4 pu = make_uint4(pk[sb][r0], pk[sb][r0 + 1], pk[sb][r0 + 2], pk[sb][r0 + 3]);
+            const bf16x8 pf = __builtin_bit_cast(bf16x8, pu);
+            const int vr = 16 * m + tr_row;
+            uint32_t addr[DB];
+#pragma unroll
+            for (int db = 0; db < DB; ++db)
+                addr[db] = lds_addr(vs + vr * D + (((4 * db + tr_chunk) ^ swz_v<D>(vr)) << 3) + tr_sub);
+            uint2 lo[DB], hi[DB];
+            tr_reads<DB, 8 * D * 2>(lo, hi, addr);
+#pragma unroll
+            for (int db = 0; db < DB; ++db) {
+                const bf16x8 vf = __builtin_bit_cast(bf16x8, make_uint4(lo[db].x, lo[db].y, hi[db].x, hi[db].y));
+                acc_o[db] = mfma32(vf, pf, acc_o[db]);
             }
         }
-        if (kb < kb1) store_tile(buf ^ 1);
-        __syncthreads();
+    };
+
+    // One pipeline step on tile kb, read from stage (kc, vc).  It refills stage
+    // (kn, vn) with tile kb + 2.  Steps past kb1 only keep the direct loads
+    // balanced: the refill is clamped to kb1, and there is no math.
+    int pg_next[4];
+    auto step = [&](int kb, uint16_t* kc, uint16_t* vc, uint16_t* kn, uint16_t* vn) {
+        wait_vmcnt<NL>();                                  // this wave's share of tile kb landed
+        __builtin_amdgcn_s_barrier();                      // ... everyone's; stage kn is free
+        if (kb <= kb1 && kb * kBN + kBN > n) {
+            // rows past the sequence end hold whatever the page slots hold: zero V
+            const int r0 = max(0, n - kb * kBN);
+            for (int e = tid; e < (kBN - r0) * CPR; e += kThreads)
+                *reinterpret_cast<uint4*>(vc + (r0 + e / CPR) * D + (e % CPR) * 8) = make_uint4(0, 0, 0, 0);
+            __syncthreads();
+        }
+        issue(pg_next, kn, vn);                            // tile min(kb + 2, kb1)
+        tile_pages(min(kb + 3, kb1), pg_next);
+        const int key0 = kb * kBN;
+        if (kb <= kb1 && wave_live && key0 < w_hi && key0 + kBN > w_lo) compute(kb, kc, vc);
+    };
+
+    {
+        int pg[4];
+        tile_pages(kb0, pg);
+        issue(pg, k_s0, v_s0);
+        tile_pages(min(kb0 + 1, kb1), pg);
+        issue(pg, k_s1, v_s1);
+        tile_pages(min(kb0 + 2, kb1), pg_next);
     }
+    for (int kb = kb0; kb <= kb1; kb += 3) {
+        step(kb, k_s0, v_s0, k_s2, v_s2);
+        step(kb + 1, k_s1, v_s1, k_s0, v_s0);
+        step(kb + 2, k_s2, v_s2, k_s1, v_s1);
+    }
+    wait_vmcnt<0>();          // drain the trailing refills before the workgroup retires
 
     // ---- finish: combine the two lanes of each row ----
     const float l_tot = l_run + xor_lane<32>(l_run);
@@ -368,9 +407,9 @@ hipError_t launch_dg(const PrefillArgs& a, hipStream_t s) {
     const int64_t grid = (items + kXcds - 1) / kXcds * kXcds;
     if (grid == 0) return hipSuccess;
     if (split)
-        hipLaunchKernelGGL((prefill_kernel<D, G, true>), dim3((unsigned)grid), dim3(256), 0, s, a);
+        hipLaunchKernelGGL((prefill_kernel<D, G, true>), dim3((unsigned)grid), dim3(kThreads), 0, s, a, a.block_table);
     else
-        hipLaunchKernelGGL((prefill_kernel<D, G, false>), dim3((unsigned)grid), dim3(256), 0, s, a);
+        hipLaunchKernelGGL((prefill_kernel<D, G, false>), dim3((unsigned)grid), dim3(kThreads), 0, s, a, a.block_table);
     return hipGetLastError();
 }
 
