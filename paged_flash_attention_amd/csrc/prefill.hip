@@ -27,8 +27,13 @@
 //  * The V^T A-operand comes straight from the row-major V tile through
 //    ds_read_b64_tr_b16.  In each 16-lane group, lane j points at
 //    V[k0 + j/4][d0 + 4(j%4)], and lane i gets V[k0..k0+3][d0 + i].
-//  * Scores are kept in log2 units (sm_scale*log2 e folded in), and
-//    exp2 -> v_exp_f32.  P is rounded to bf16 (RNE) for the PV MFMA.
+//  * Softmax arithmetic is trimmed for the VALU:
+//      - the row max is taken on raw scores;
+//      - p = exp2(s*c - m) is one FMA plus v_exp_f32, with c = sm_scale*log2 e;
+//      - P is rounded to bf16 (RNE) for the PV MFMA;
+//      - the row sum is a dot2 of those rounded pairs with (1, 1), so l matches the
+//        numerator exactly;
+//      - the reference max moves only when a row's max grows by more than 2^8.
 //  * Causal/window masking costs nothing on tiles that are fully visible.  A wave
 //    skips the MFMAs of tiles that lie entirely outside its rows' ranges.  V rows
 //    past the sequence end are zeroed in LDS, so poison in unwritten page slots
@@ -267,31 +272,29 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a, const 
             s[0] = mfma32(__builtin_bit_cast(bf16x8, k0), qf[kk], s[0]);
             s[1] = mfma32(__builtin_bit_cast(bf16x8, k1), qf[kk], s[1]);
         }
-        // ---- scale, mask ----
+        // ---- mask, row max on the raw scores (the scale is positive) ----
         const bool full = (key0 + kBN - 1 <= prefix + w_first) && (W == 0 || (prefix + w_last) - key0 < W);
-        float mt = -INFINITY;
-        if (full) {
-#pragma unroll
-            for (int sb = 0; sb < 2; ++sb)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    s[sb][r] *= c2;
-                    mt = fmaxf(mt, s[sb][r]);
-                }
-        } else {
+        if (!full) {
 #pragma unroll
             for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     const int key = key0 + 32 * sb + 8 * (r / 4) + 4 * half + (r % 4);
                     const bool vis = key <= pos_l && (W == 0 || pos_l - key < W);
-                    s[sb][r] = vis ? s[sb][r] * c2 : -INFINITY;
-                    mt = fmaxf(mt, s[sb][r]);
+                    s[sb][r] = vis ? s[sb][r] : -INFINITY;
                 }
         }
-        mt = fmaxf(mt, xor_lane<32>(mt));
-        const float m_new = fmaxf(m_run, mt);
-        if (__any(m_new > m_run)) {
+        float mt = -INFINITY;
+#pragma unroll
+        for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) mt = fmaxf(mt, s[sb][r]);
+        mt = fmaxf(mt, xor_lane<32>(mt)) * c2;               // log2 units
+        // Lazy rescale with headroom: the reference max moves only when a row's max
+        // exceeds it by more than 8, so p <= 2^8 (exact enough in bf16, no overflow
+        // in the fp32 sums).  O and l share the reference, so o/l is unchanged.
+        if (__any(mt > m_run + 8.0f)) {
+            const float m_new = fmaxf(m_run, mt);
             const float mu = (m_new == -INFINITY) ? 0.0f : m_new;
             const float alpha = fast_exp2(m_run - mu);
             l_run *= alpha;
@@ -301,17 +304,19 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a, const 
                 for (int r = 0; r < 16; ++r) acc_o[db][r] *= alpha;
             m_run = m_new;
         }
-        const float mu = (m_run == -INFINITY) ? 0.0f : m_run;
-        // ---- P = 2^(x - m), packed to bf16 in the B-operand order ----
+        const float nmu = (m_run == -INFINITY) ? 0.0f : -m_run;
+        // ---- P = 2^(s*c2 - m), packed to bf16 in the B-operand order; l from the
+        // rounded P that the PV MFMA uses (a dot2 with (1, 1)) ----
+        const bf16x2 ones = as_bf16x2(0x3F803F80u);
         uint32_t pk[2][8];
 #pragma unroll
         for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
             for (int r = 0; r < 16; r += 2) {
-                const float p0 = fast_exp2(s[sb][r] - mu);
-                const float p1 = fast_exp2(s[sb][r + 1] - mu);
-                l_run += p0 + p1;
+                const float p0 = fast_exp2(fmaf(s[sb][r], c2, nmu));
+                const float p1 = fast_exp2(fmaf(s[sb][r + 1], c2, nmu));
                 pk[sb][r / 2] = pack_bf16_rne(p0, p1);
+                l_run = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(pk[sb][r / 2]), ones, l_run, false);
             }
         // ---- O^T += V^T P^T, V^T fragments by transposed LDS reads ----
 #pragma unroll
