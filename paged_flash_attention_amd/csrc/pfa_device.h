@@ -57,6 +57,17 @@ __device__ __forceinline__ float xor_lane(float x) {
     return __int_as_float(r);
 }
 
+// max / sum of x over lanes i and i ^ 32, on the VALU.  v_permlane32_swap with x
+// in both operands leaves (x_i, x_{i^32}) in the two results, in either order.
+__device__ __forceinline__ float xor32_max(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xor32_sum(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // x from lane ((lane & ~(W-1)) | src) for groups of W lanes, W in {4, 8, 16, 32}.
 template <int W>
 __device__ __forceinline__ float group_bcast(float x, int src) {

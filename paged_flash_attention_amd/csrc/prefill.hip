@@ -11,10 +11,16 @@
 //    A row is one (token, head-of-group) pair, so the G query heads sharing a KV
 //    head share every K/V tile (GQA packing).  Each wave owns 32 rows.
 //  * K/V go HBM -> LDS with global_load_lds_dwordx4, with no register staging, in
-//    a 3-stage ring of 64-key tiles (4 pages).  Two tiles stay in flight while one
-//    is consumed, and each wave waits on its own vmcnt, so there is one barrier per
-//    tile.  The page ids of the tile after next are read (wave-uniform) while the
-//    current tile computes.
+//    a 4-stage ring of 64-key tiles (4 pages), three tiles ahead.  Each wave
+//    waits on its own vmcnt before the one barrier per tile.  The page ids of
+//    later tiles are read (wave-uniform, scalar loads) while the current tile
+//    computes.
+//  * The loop is software-pipelined within each wave, so that the matrix cores
+//    and the VALU work at the same time (on gfx950 each MFMA issue also takes
+//    VALU issue cycles, so the VALU work is spread evenly): the QK^T MFMAs of
+//    tile j+1 are interleaved with three quarters of the exps of tile j, and the
+//    PV MFMAs of tile j with the last quarter and the row max of tile j+1.
+//    Scheduling fences bound how far the compiler hoists LDS reads (registers).
 //  * LDS rows are the page rows (keys x D), 16-byte chunks XOR-swizzled per row.
 //    The swizzle is applied on the global side of the direct loads, and it makes
 //    both read patterns below free of bank conflicts.
@@ -33,7 +39,8 @@
 //      - P is rounded to bf16 (RNE) for the PV MFMA;
 //      - the row sum is a dot2 of those rounded pairs with (1, 1), so l matches the
 //        numerator exactly;
-//      - the reference max moves only when a row's max grows by more than 2^8.
+//      - the reference max moves only when a row's max exceeds it by more than 8
+//        (log2 units), so p <= 2^8.
 //  * Causal/window masking costs nothing on tiles that are fully visible.  A wave
 //    skips the MFMAs of tiles that lie entirely outside its rows' ranges.  V rows
 //    past the sequence end are zeroed in LDS, so poison in unwritten page slots
@@ -54,10 +61,14 @@ constexpr int kRowsPerWave = 32;
 constexpr int kWaves = kPrefillRows / kRowsPerWave;
 constexpr int kThreads = kWaves * kWave;
 constexpr int kBN = 64;           // keys per tile
+constexpr int kStages = 4;        // LDS ring depth (tiles in flight: kStages - 1)
+constexpr int kPairs1 = 12;       // of a tile's 16 score pairs per lane, those whose exps
+                                  // run beside the QK^T MFMAs (the rest beside PV)
 constexpr int kXcds = 8;
 
 #define LDS3 __attribute__((address_space(3)))
 typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const f32x16& c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
@@ -77,47 +88,43 @@ __device__ __forceinline__ void wait_vmcnt() {
     __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
-// The V^T operands of one 16-key slice: for each 32-dim block db, a transposed
-// read of keys k..k+3 at addr[db] and of keys k+8..k+11 at addr[db] + HI bytes.
-// The reads are issued as one asm block that waits for them itself.  Issued
-// through the intrinsic, the compiler treats the read as possibly aliasing any
-// in-flight direct load, and would wait for the prefetched tiles too.
-template <int DB, int HI>
-__device__ __forceinline__ void tr_reads(uint2 (&lo)[DB], uint2 (&hi)[DB], const uint32_t (&addr)[DB]) {
-    if constexpr (DB == 4) {
-        asm volatile(
-            "ds_read_b64_tr_b16 %0, %8\n\t"
-            "ds_read_b64_tr_b16 %1, %8 offset:%12\n\t"
-            "ds_read_b64_tr_b16 %2, %9\n\t"
-            "ds_read_b64_tr_b16 %3, %9 offset:%12\n\t"
-            "ds_read_b64_tr_b16 %4, %10\n\t"
-            "ds_read_b64_tr_b16 %5, %10 offset:%12\n\t"
-            "ds_read_b64_tr_b16 %6, %11\n\t"
-            "ds_read_b64_tr_b16 %7, %11 offset:%12\n\t"
-            "s_waitcnt lgkmcnt(0)"
-            : "=&v"(lo[0]), "=&v"(hi[0]), "=&v"(lo[1]), "=&v"(hi[1]),
-              "=&v"(lo[2]), "=&v"(hi[2]), "=&v"(lo[3]), "=&v"(hi[3])
-            : "v"(addr[0]), "v"(addr[1]), "v"(addr[2]), "v"(addr[3]), "i"(HI)
-            : "memory");
-    } else {
-        static_assert(DB == 2, "head dim");
-        asm volatile(
-            "ds_read_b64_tr_b16 %0, %4\n\t"
-            "ds_read_b64_tr_b16 %1, %4 offset:%6\n\t"
-            "ds_read_b64_tr_b16 %2, %5\n\t"
-            "ds_read_b64_tr_b16 %3, %5 offset:%6\n\t"
-            "s_waitcnt lgkmcnt(0)"
-            : "=&v"(lo[0]), "=&v"(hi[0]), "=&v"(lo[1]), "=&v"(hi[1])
-            : "v"(addr[0]), "v"(addr[1]), "i"(HI)
-            : "memory");
-    }
+// 16-byte direct load HBM -> LDS: lane l's 16 bytes come from base + voff (bytes)
+// and land at LDS byte address lds + 16*l.  base and lds are wave-uniform.  Issued
+// as asm, so the compiler keeps no LDS-DMA bookkeeping of its own: it would
+// otherwise make every transposed LDS read wait for all direct loads in flight.
+// The caller orders LDS accesses against these loads (vmcnt waits and barriers).
+// (M0 is the LDS base; a write of M0 needs one wait state before the load.)
+__device__ __forceinline__ void dma16(const void* base, uint32_t voff, uint32_t lds) {
+    // (readfirstlane returns int: both halves go through uint32_t, so that the
+    // low word is zero-extended)
+    const uint64_t p = (uint64_t)(uintptr_t)base;
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(p >> 32));
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)p);
+    const uint64_t sb = ((uint64_t)hi << 32) | lo;
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+                 :: "v"(voff), "s"(sb), "s"(__builtin_amdgcn_readfirstlane(lds)) : "memory");
 }
 
-// 16-byte direct load HBM -> LDS: lane l's bytes land at lds + 16*l.  (A plain,
-// non-template function: used straight inside the kernel template, the builtin
-// made the host pass drop the launch stubs.)
-__device__ __forceinline__ void dma16(const uint16_t* src, uint16_t* lds) {
-    __builtin_amdgcn_global_load_lds(src, (LDS3 void*)lds, 16, 0, 0);
+// A wave-uniform pointer, held in scalar registers.
+template <typename T>
+__device__ __forceinline__ T* uniform_ptr(T* p) {
+    const uint64_t v = (uint64_t)(uintptr_t)p;
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)v);
+    return (T*)(uintptr_t)(((uint64_t)hi << 32) | lo);
+}
+
+// Barrier that the compiler may not move memory accesses across, after this
+// wave's LDS accesses (and scalar loads) have completed.
+__device__ __forceinline__ void lds_sync() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// x, hidden from the optimiser (so that values derived from it are recomputed
+// where they are used rather than hoisted)
+__device__ __forceinline__ int opaque(int x) {
+    asm volatile("" : "+v"(x));
+    return x;
 }
 
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
@@ -136,8 +143,8 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a, const 
     constexpr int NL = 2 * DMA_PER_WAVE;                // vector-memory ops per tile per wave
     static_assert(DMA_PER_WAVE >= 1, "tile split");
 
-    __shared__ __attribute__((aligned(1024))) uint16_t k_s0[kBN * D], k_s1[kBN * D], k_s2[kBN * D];
-    __shared__ __attribute__((aligned(1024))) uint16_t v_s0[kBN * D], v_s1[kBN * D], v_s2[kBN * D];
+    // ring of kStages stages, each a K tile then a V tile (keys x D, swizzled)
+    __shared__ __attribute__((aligned(1024))) uint16_t ring_lds[kStages * 2 * kBN * D];
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);   // wave-uniform
@@ -210,6 +217,10 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a, const 
             if (row_ok) v = *reinterpret_cast<const uint4*>(qp + 16 * kk);
             qf[kk] = __builtin_bit_cast(bf16x8, v);
         }
+        // The direct loads below are invisible to the compiler's vmcnt tracking.
+        // Retire the Q loads here, or the compiler would wait for them (vmcnt 0,
+        // hence for every tile in flight) at each use of Q inside the tile loop.
+        wait_vmcnt<0>();
     }
 
     // ---- direct HBM -> LDS tile loads ----
@@ -220,24 +231,39 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a, const 
     const int64_t hblk = (int64_t)kPage * D;            // elements per page-head block
     const int kb0 = lo / kBN;
     const int kb1 = (hi - 1) / kBN;
-    auto tile_pages = [&](int kb, int (&pg)[4]) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int pi = min(kb * 4 + j, npg - 1);
-            pg[j] = min(max(__ldg(bt + pi), 0), a.num_pages - 1);
-        }
+    // A wave's direct loads cover 8 consecutive rows of the tile, all in one page.
+    static_assert(DMA_PER_WAVE * ROWS_PER_DMA * kWaves == kBN && kPage % (DMA_PER_WAVE * ROWS_PER_DMA) == 0,
+                  "a wave's rows lie in one page");
+    const int wpage = wave * DMA_PER_WAVE * ROWS_PER_DMA / kPage;    // which page of the tile
+    // raw block-table entry of a tile's page for this wave (a scalar load), and
+    // its clamp to the pool; the load is issued one tile before its value is used
+    auto raw_page = [&](int kb) __attribute__((always_inline)) {
+        return __ldg(bt + min(kb * (kBN / kPage) + wpage, npg - 1));
     };
+    auto clamp_page = [&](int v) __attribute__((always_inline)) { return min(max(v, 0), a.num_pages - 1); };
     const int lrow = lane / CPR;                          // row within one direct load
     const int lchunk = lane % CPR;                        // physical chunk this lane fills
-    auto issue = [&](const int (&pg)[4], uint16_t* kdst, uint16_t* vdst) {
+    // per-lane byte offsets within a page-head block (the same for every tile)
+    uint32_t koff[DMA_PER_WAVE], voff[DMA_PER_WAVE];
+#pragma unroll
+    for (int i = 0; i < DMA_PER_WAVE; ++i) {
+        const int row = (wave * DMA_PER_WAVE + i) * ROWS_PER_DMA + lrow;
+        koff[i] = 2u * ((row % kPage) * D + (lchunk ^ swz_k<D>(row)) * 8);
+        voff[i] = 2u * ((row % kPage) * D + (lchunk ^ swz_v<D>(row)) * 8);
+    }
+    const uint16_t* kpool_h = uniform_ptr(a.k_pool + (int64_t)kvh * hblk);
+    const uint16_t* vpool_h = uniform_ptr(a.v_pool + (int64_t)kvh * hblk);
+    const int64_t page_stride = (int64_t)a.num_kv_heads * hblk;
+    // LDS byte addresses: the ring's stages, each a K tile then a V tile
+    const uint32_t ring0 = lds_addr(ring_lds);
+    constexpr uint32_t kTileBytes = kBN * D * 2;
+    auto issue = [&](int pg, uint32_t kdst, uint32_t vdst) __attribute__((always_inline)) {
+        const int64_t pbase = (int64_t)pg * page_stride;
 #pragma unroll
         for (int i = 0; i < DMA_PER_WAVE; ++i) {
-            const int q = wave * DMA_PER_WAVE + i;        // which 1 KB slice of the tile
-            const int row0 = q * ROWS_PER_DMA;            // rows row0.. lie in one page
-            const int row = row0 + lrow;
-            const int64_t pbase = ((int64_t)pg[row0 / kPage] * a.num_kv_heads + kvh) * hblk + (row % kPage) * D;
-            dma16(a.k_pool + pbase + (lchunk ^ swz_k<D>(row)) * 8, kdst + row0 * D);
-            dma16(a.v_pool + pbase + (lchunk ^ swz_v<D>(row)) * 8, vdst + row0 * D);
+            const uint32_t row0 = (wave * DMA_PER_WAVE + i) * ROWS_PER_DMA;
+            dma16(kpool_h + pbase, koff[i], kdst + row0 * D * 2);
+            dma16(vpool_h + pbase, voff[i], vdst + row0 * D * 2);
         }
     };
 
@@ -257,42 +283,46 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a, const 
     const int tr_chunk = 2 * (tr_g % 2) + (tr_j % 4) / 2;         // + 4db
     const int tr_sub = 4 * (tr_j % 2);
 
-    auto compute = [&](int kb, const uint16_t* ks, const uint16_t* vs) {
+    auto needed = [&](int kb) __attribute__((always_inline)) {
         const int key0 = kb * kBN;
-        // ---- S^T = K Q^T for two 32-key sub-blocks, chains interleaved ----
-        f32x16 s[2];
-#pragma unroll
-        for (int r = 0; r < 16; ++r) s[0][r] = s[1][r] = 0.0f;
-        const int kr0 = r32, kr1 = 32 + r32;
-#pragma unroll
-        for (int kk = 0; kk < KK; ++kk) {
-            const int c = 2 * kk + half;
-            const uint4 k0 = *reinterpret_cast<const uint4*>(ks + kr0 * D + ((c ^ swz_k<D>(kr0)) << 3));
-            const uint4 k1 = *reinterpret_cast<const uint4*>(ks + kr1 * D + ((c ^ swz_k<D>(kr1)) << 3));
-            s[0] = mfma32(__builtin_bit_cast(bf16x8, k0), qf[kk], s[0]);
-            s[1] = mfma32(__builtin_bit_cast(bf16x8, k1), qf[kk], s[1]);
-        }
-        // ---- mask, row max on the raw scores (the scale is positive) ----
-        const bool full = (key0 + kBN - 1 <= prefix + w_first) && (W == 0 || (prefix + w_last) - key0 < W);
-        if (!full) {
-#pragma unroll
-            for (int sb = 0; sb < 2; ++sb)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int key = key0 + 32 * sb + 8 * (r / 4) + 4 * half + (r % 4);
-                    const bool vis = key <= pos_l && (W == 0 || pos_l - key < W);
-                    s[sb][r] = vis ? s[sb][r] : -INFINITY;
-                }
-        }
-        float mt = -INFINITY;
+        return kb <= kb1 && wave_live && key0 < w_hi && key0 + kBN > w_lo;
+    };
+    // scheduling-group masks: VALU (not transcendental), transcendental, matrix
+    // ops, LDS reads
+    constexpr int VALU = 0x002, TRANS = 0x400, MFMA = 0x008, DSR = 0x100;
+
+    // S^T = K Q^T for the two 32-key halves of a tile, chains interleaved.  The
+    // per-lane LDS offsets are rebuilt from an opaque copy of the lane index at
+    // each call: hoisted out of the tile loop, the offsets of every stage and
+    // slice would stay live in registers.
+    auto k_frag = [&](const LDS3 char* kbase, int kr, int kk, bf16x8& k0, bf16x8& k1) __attribute__((always_inline)) {
+        const int off = (((2 * kk + half) ^ swz_k<D>(kr)) << 4);
+        k0 = *(const LDS3 bf16x8*)(kbase + off);
+        k1 = *(const LDS3 bf16x8*)(kbase + off + 2 * 32 * D);
+    };
+    // mask tile kb's scores in place (only tiles that cross a row's causal or
+    // window edge need it)
+    auto tile_full = [&](int kb) __attribute__((always_inline)) {
+        const int key0 = kb * kBN;
+        return (key0 + kBN - 1 <= prefix + w_first) && (W == 0 || (prefix + w_last) - key0 < W);
+    };
+    auto mask = [&](int kb, f32x16 (&s)[2]) __attribute__((always_inline)) {
+        // distance of this lane's first key in the tile from its row position
+        const int d0 = opaque(pos_l - kb * kBN - 4 * half);
 #pragma unroll
         for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) mt = fmaxf(mt, s[sb][r]);
-        mt = fmaxf(mt, xor_lane<32>(mt)) * c2;               // log2 units
-        // Lazy rescale with headroom: the reference max moves only when a row's max
-        // exceeds it by more than 8, so p <= 2^8 (exact enough in bf16, no overflow
-        // in the fp32 sums).  O and l share the reference, so o/l is unchanged.
+            for (int r = 0; r < 16; ++r) {
+                const int dist = d0 - (32 * sb + 8 * (r / 4) + (r % 4));      // pos - key
+                const bool vis = dist >= 0 && (W == 0 || dist < W);
+                s[sb][r] = vis ? s[sb][r] : -INFINITY;
+            }
+    };
+    // Lazy rescale with headroom: the reference max moves only when a row's max
+    // exceeds it by more than 8, so p <= 2^8 (exact enough in bf16, no overflow in
+    // the fp32 sums).  O and l share the reference, so o/l is unchanged.
+    auto rescale = [&](float mt) __attribute__((always_inline)) {
+        mt = xor32_max(mt) * c2;
         if (__any(mt > m_run + 8.0f)) {
             const float m_new = fmaxf(m_run, mt);
             const float mu = (m_new == -INFINITY) ? 0.0f : m_new;
@@ -304,78 +334,217 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a, const 
                 for (int r = 0; r < 16; ++r) acc_o[db][r] *= alpha;
             m_run = m_new;
         }
-        const float nmu = (m_run == -INFINITY) ? 0.0f : -m_run;
-        // ---- P = 2^(s*c2 - m), packed to bf16 in the B-operand order; l from the
-        // rounded P that the PV MFMA uses (a dot2 with (1, 1)) ----
-        const bf16x2 ones = as_bf16x2(0x3F803F80u);
-        uint32_t pk[2][8];
+    };
+    // the row max of the raw scores (the scale is positive), then the rescale
+    auto mask_max = [&](int kb, f32x16 (&s)[2]) __attribute__((always_inline)) {
+        if (!tile_full(kb)) mask(kb, s);
+        float mt = -INFINITY;
 #pragma unroll
         for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
-            for (int r = 0; r < 16; r += 2) {
-                const float p0 = fast_exp2(fmaf(s[sb][r], c2, nmu));
-                const float p1 = fast_exp2(fmaf(s[sb][r + 1], c2, nmu));
-                pk[sb][r / 2] = pack_bf16_rne(p0, p1);
-                l_run = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(pk[sb][r / 2]), ones, l_run, false);
+            for (int r = 0; r < 16; ++r) mt = fmaxf(mt, s[sb][r]);
+        rescale(mt);
+    };
+    // P = 2^(s*c2 - m), packed to bf16 in the B-operand order; l from the rounded P
+    // that the PV MFMA uses (a dot2 with (1, 1))
+    auto exp_pair = [&](const f32x16 (&s)[2], uint32_t (&pk)[2][8], int e, float nmu) __attribute__((always_inline)) {
+        const int sb = e / 16, r = e % 16;
+        const float p0 = fast_exp2(fmaf(s[sb][r], c2, nmu));
+        const float p1 = fast_exp2(fmaf(s[sb][r + 1], c2, nmu));
+        pk[sb][r / 2] = pack_bf16_rne(p0, p1);
+        l_run = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(pk[sb][r / 2]), as_bf16x2(0x3F803F80u), l_run, false);
+    };
+    // exp_pair pinned in place: the empty asm makes its results exist here, so the
+    // optimiser cannot sink the exps out of the bundle they are meant to fill
+    auto exp_pair_here = [&](const f32x16 (&s)[2], uint32_t (&pk)[2][8], int e, float nmu) __attribute__((always_inline)) {
+        exp_pair(s, pk, e, nmu);
+        asm volatile("" : "+v"(pk[e / 16][(e % 16) / 2]), "+v"(l_run));
+    };
+    auto softmax = [&](const f32x16 (&s)[2], uint32_t (&pk)[2][8]) __attribute__((always_inline)) {
+        const float nmu = (m_run == -INFINITY) ? 0.0f : -m_run;
+#pragma unroll
+        for (int e = 0; e < 32; e += 2) exp_pair(s, pk, e, nmu);
+    };
+    // Block 1: S' = K' Q^T (two 32-key chains), optionally with the exps of the
+    // current tile's S interleaved (EXP).  Bundles of one D-slice each: the K reads
+    // of slice kk+1, the two MFMAs of slice kk, 32/KK exps.  A scheduling fence
+    // after each bundle keeps the compiler from hoisting every read of the block
+    // (which costs registers the scores need).
+    auto qk_block = [&](bool EXP, uint32_t ks, f32x16 (&sn)[2], const f32x16 (&s)[2], uint32_t (&pk)[2][8]) __attribute__((always_inline)) {
+        const float nmu = (m_run == -INFINITY) ? 0.0f : -m_run;
+        const int kr = opaque(r32);                   // key rows kr and kr + 32 (same swizzle)
+        const LDS3 char* kbase = (const LDS3 char*)(uintptr_t)(ks + 2 * kr * D);
+        bf16x8 k0, k1;
+        k_frag(kbase, kr, 0, k0, k1);
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) {
+            bf16x8 n0, n1;
+            if (kk + 1 < KK) k_frag(kbase, kr, kk + 1, n0, n1);
+            if (kk == 0) {
+                const f32x16 z = {};
+                sn[0] = mfma32(k0, qf[0], z);
+            } else {
+                sn[0] = mfma32(k0, qf[kk], sn[0]);
             }
-        // ---- O^T += V^T P^T, V^T fragments by transposed LDS reads ----
+            // score pairs [kk*P1/KK, (kk+1)*P1/KK) of the block's P1, split over the two MFMAs
+            const int pa = kk * kPairs1 / KK, pb = (kk + 1) * kPairs1 / KK, pm = (pa + pb) / 2;
+            if (EXP) {
+#pragma unroll
+                for (int q = pa; q < pm; ++q) exp_pair_here(s, pk, 2 * q, nmu);
+            }
+            if (kk == 0) {
+                const f32x16 z = {};
+                sn[1] = mfma32(k1, qf[0], z);
+            } else {
+                sn[1] = mfma32(k1, qf[kk], sn[1]);
+            }
+            if (EXP) {
+#pragma unroll
+                for (int q = pm; q < pb; ++q) exp_pair_here(s, pk, 2 * q, nmu);
+            }
+            if (kk + 1 < KK) { k0 = n0; k1 = n1; }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+    // Block 2: O^T += V^T P^T over the four 16-key slices, optionally with the row
+    // max of the next tile's (masked) scores interleaved (MAX).  Bundles: the
+    // transposed V reads of slice m+1, the DB MFMAs of slice m, 8 max.
+    auto v_offsets = [&](int (&voffs)[DB]) __attribute__((always_inline)) {
+        // the swizzle of row 16m + tr_row is that of tr_row: slice m only adds a constant
+        const int tr = opaque(tr_row);
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+            voffs[db] = 2 * (tr * D + (((4 * db + tr_chunk) ^ swz_v<D>(tr)) << 3) + tr_sub);
+    };
+    auto v_frag = [&](const LDS3 char* vbase, const int (&voffs)[DB], int m, int db) __attribute__((always_inline)) {
+        const LDS3 char* p = vbase + voffs[db] + 2 * 16 * m * D;
+        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS3 s16x4*)p);
+        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS3 s16x4*)(p + 2 * 8 * D));
+        return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    };
+    // FUSED: also the exps of score pairs kPairs1..15 of the current tile (slice 3's
+    // P, computed during slices 0-2) and the row max of the next tile's scores sn
+    // (during slices 1-3, once block 1's MFMAs have long finished), then the rescale.
+    auto pv_block = [&](bool FUSED, uint32_t vs, uint32_t (&pk)[2][8], const f32x16 (&s)[2], const f32x16 (&sn)[2]) __attribute__((always_inline)) {
+        int voffs[DB];
+        v_offsets(voffs);
+        const LDS3 char* vbase = (const LDS3 char*)(uintptr_t)vs;
+        const float nmu = (m_run == -INFINITY) ? 0.0f : -m_run;
+        float mt = -INFINITY;
+        bf16x8 vf[DB];
+#pragma unroll
+        for (int db = 0; db < DB; ++db) vf[db] = v_frag(vbase, voffs, 0, db);
 #pragma unroll
         for (int m = 0; m < kBN / 16; ++m) {
             const int sb = m / 2, r0 = 4 * (m % 2);
-            const uint4 pu = make_uint4(pk[sb][r0], pk[sb][r0 + 1], pk[sb][r0 + 2], pk[sb][r0 + 3]);
-            const bf16x8 pf = __builtin_bit_cast(bf16x8, pu);
-            const int vr = 16 * m + tr_row;
-            uint32_t addr[DB];
-#pragma unroll
-            for (int db = 0; db < DB; ++db)
-                addr[db] = lds_addr(vs + vr * D + (((4 * db + tr_chunk) ^ swz_v<D>(vr)) << 3) + tr_sub);
-            uint2 lo[DB], hi[DB];
-            tr_reads<DB, 8 * D * 2>(lo, hi, addr);
+            const bf16x8 pf = __builtin_bit_cast(bf16x8, make_uint4(pk[sb][r0], pk[sb][r0 + 1], pk[sb][r0 + 2], pk[sb][r0 + 3]));
+            // one register set per 32-dim block: slice m+1 is read into it as soon as
+            // the MFMA of slice m that reads it has issued
 #pragma unroll
             for (int db = 0; db < DB; ++db) {
-                const bf16x8 vf = __builtin_bit_cast(bf16x8, make_uint4(lo[db].x, lo[db].y, hi[db].x, hi[db].y));
-                acc_o[db] = mfma32(vf, pf, acc_o[db]);
+                acc_o[db] = mfma32(vf[db], pf, acc_o[db]);
+                if (m + 1 < kBN / 16) vf[db] = v_frag(vbase, voffs, m + 1, db);
             }
+            if (FUSED) {
+                if (m < 3) {
+                    const int pa = kPairs1 + m * (16 - kPairs1) / 3, pb = kPairs1 + (m + 1) * (16 - kPairs1) / 3;
+#pragma unroll
+                    for (int q = pa; q < pb; ++q) exp_pair_here(s, pk, 2 * q, nmu);
+                }
+                if (m > 0) {
+#pragma unroll
+                    for (int e = 32 * (m - 1) / 3; e < 32 * m / 3; ++e) mt = fmaxf(mt, sn[e / 16][e % 16]);
+                }
+            }
+            __builtin_amdgcn_sched_barrier(0);
         }
+        if (FUSED) rescale(mt);
     };
-
-    // One pipeline step on tile kb, read from stage (kc, vc).  It refills stage
-    // (kn, vn) with tile kb + 2.  Steps past kb1 only keep the direct loads
-    // balanced: the refill is clamped to kb1, and there is no math.
-    int pg_next[4];
-    auto step = [&](int kb, uint16_t* kc, uint16_t* vc, uint16_t* kn, uint16_t* vn) {
-        wait_vmcnt<NL>();                                  // this wave's share of tile kb landed
-        __builtin_amdgcn_s_barrier();                      // ... everyone's; stage kn is free
+    // rows of a tile past the sequence end hold whatever the page slots hold: zero V
+    auto zero_tail = [&](int kb, uint32_t vs) __attribute__((always_inline)) {
         if (kb <= kb1 && kb * kBN + kBN > n) {
-            // rows past the sequence end hold whatever the page slots hold: zero V
             const int r0 = max(0, n - kb * kBN);
             for (int e = tid; e < (kBN - r0) * CPR; e += kThreads)
-                *reinterpret_cast<uint4*>(vc + (r0 + e / CPR) * D + (e % CPR) * 8) = make_uint4(0, 0, 0, 0);
-            __syncthreads();
+                *(LDS3 u32x4*)(uintptr_t)(vs + 2 * ((r0 + e / CPR) * D + (e % CPR) * 8)) = u32x4{0u, 0u, 0u, 0u};
         }
-        issue(pg_next, kn, vn);                            // tile min(kb + 2, kb1)
-        tile_pages(min(kb + 3, kb1), pg_next);
-        const int key0 = kb * kBN;
-        if (kb <= kb1 && wave_live && key0 < w_hi && key0 + kBN > w_lo) compute(kb, kc, vc);
     };
 
-    {
-        int pg[4];
-        tile_pages(kb0, pg);
-        issue(pg, k_s0, v_s0);
-        tile_pages(min(kb0 + 1, kb1), pg);
-        issue(pg, k_s1, v_s1);
-        tile_pages(min(kb0 + 2, kb1), pg_next);
+    // Software pipeline over the ring, tiles three ahead.  Tile kb sits in stage
+    // (kb - kb0) % kStages.  Every wave runs ring(kb) once for each tile kb0..kb1:
+    // it waits for tile kb+1 (each wave its own direct loads, then the barrier),
+    // refills the stage of tile kb-1 with tile kb+3 (clamped to kb1, so the load
+    // count stays balanced) and zeroes tile kb+1's V rows past the sequence end
+    // (read from the next iteration on).  A wave computes only on the tiles
+    // kw0..kw1 that its rows see; iteration kb of that range holds the masked
+    // scores S of tile kb (row max already folded into m) and runs
+    //   block 1: S' = K_{kb+1} Q^T (MFMA) interleaved with P = exp2(S - m) (VALU);
+    //   block 2: O += P V_kb (MFMA) interleaved with the row max of S' (VALU),
+    //     then the rescale for tile kb+1.
+    // The range's first tile gets its S in the iteration before, its last one
+    // only block 2's PV.
+    auto kst = [&](int kb) { return ring0 + (uint32_t)((kb - kb0) & (kStages - 1)) * (2 * kTileBytes); };
+    auto vst = [&](int kb) { return kst(kb) + kTileBytes; };
+    int pg_raw;                                // raw page entry of tile min(kb + 3, kb1)
+    auto ring = [&](int kb) __attribute__((always_inline)) {
+        const int pg = clamp_page(pg_raw);     // its load went out one tile ago
+        const uint32_t kd = kst(kb + 3), vd = vst(kb + 3);
+        // in flight: tiles kb+1 and kb+2 (kb+3 is issued below)
+        wait_vmcnt<NL>();                      // this wave's share of tile kb+1 landed
+        lds_sync();                            // everyone's; tile kb-1's stage is free
+        issue(pg, kd, vd);                     // tile min(kb + 3, kb1)
+        pg_raw = raw_page(min(kb + 4, kb1));
+        zero_tail(kb + 1, vst(kb + 1));
+    };
+    // this wave's tiles
+    int kw0 = kb0, kw1 = kb0 - 1;
+    if (wave_live) {
+        kw0 = max(kb0, w_lo / kBN);
+        kw1 = min(kb1, (w_hi - 1) / kBN);
     }
-    for (int kb = kb0; kb <= kb1; kb += 3) {
-        step(kb, k_s0, v_s0, k_s2, v_s2);
-        step(kb + 1, k_s1, v_s1, k_s0, v_s0);
-        step(kb + 2, k_s2, v_s2, k_s1, v_s1);
+    const bool any = kw0 <= kw1;
+
+    issue(clamp_page(raw_page(kb0)), kst(kb0), vst(kb0));
+    issue(clamp_page(raw_page(min(kb0 + 1, kb1))), kst(kb0 + 1), vst(kb0 + 1));
+    issue(clamp_page(raw_page(min(kb0 + 2, kb1))), kst(kb0 + 2), vst(kb0 + 2));
+    pg_raw = raw_page(min(kb0 + 3, kb1));
+    wait_vmcnt<2 * NL>();                      // tile kb0 landed (kb0+1, kb0+2 in flight)
+    lds_sync();
+    zero_tail(kb0, vst(kb0));                  // visible after the next barrier
+
+    f32x16 s_a[2], s_b[2];                     // scores of the current / next tile
+    uint32_t pk[2][8];
+    int kb = kb0;
+    if (any) {
+        for (; kb < kw0 - 1; ++kb) ring(kb);
+        if (kw0 > kb0) ring(kb++);
+        qk_block(false, kst(kw0), s_a, s_b, pk);
+        mask_max(kw0, s_a);
+        // fused iterations kw0 .. kw1-1, two per round (the score buffers swap)
+        auto fused = [&](int t, f32x16 (&sc)[2], f32x16 (&sn)[2]) __attribute__((always_inline)) {
+            ring(t);
+            qk_block(true, kst(t + 1), sn, sc, pk);
+            if (!tile_full(t + 1)) mask(t + 1, sn);
+            pv_block(true, vst(t), pk, sc, sn);
+        };
+        for (; kb + 1 < kw1; kb += 2) {
+            fused(kb, s_a, s_b);
+            fused(kb + 1, s_b, s_a);
+        }
+        if (kb < kw1) {
+            fused(kb, s_a, s_b);
+#pragma unroll
+            for (int r = 0; r < 16; ++r) { s_a[0][r] = s_b[0][r]; s_a[1][r] = s_b[1][r]; }
+            ++kb;
+        }
+        ring(kb++);                            // tile kw1: P and PV only
+        softmax(s_a, pk);
+        pv_block(false, vst(kw1), pk, s_a, s_a);
     }
+    for (; kb <= kb1; ++kb) ring(kb);
     wait_vmcnt<0>();          // drain the trailing refills before the workgroup retires
 
     // ---- finish: combine the two lanes of each row ----
-    const float l_tot = l_run + xor_lane<32>(l_run);
+    const float l_tot = xor32_sum(l_run);
     if (!row_ok) return;
     const float mu = (m_run == -INFINITY) ? 0.0f : m_run;
     float inv;
