@@ -172,7 +172,7 @@ pfa_status pfa_paged_attn_prefill(const pfa_attn_desc* desc, const pfa_kv_pool* 
     if (batch < 0 || max_q_len < 0 || bt_stride <= 0 || max_seq_len < max_q_len || max_splits < 1)
         return PFA_ERR_SHAPE;
     if (max_seq_len > (int64_t)bt_stride * desc->page_size) return PFA_ERR_SHAPE;
-    const int tpb = pfa::kPrefillRows / g;
+    const int tpb = (max_splits > 1 ? pfa::kPrefillRowsSplit : pfa::kPrefillRows) / g;
     const int64_t items =
         (int64_t)batch * desc->num_kv_heads * ((max_q_len + tpb - 1) / tpb) * max_splits;
     if (items > 0x7fffffff - 8) return PFA_ERR_SHAPE;
@@ -205,8 +205,8 @@ pfa_status pfa_paged_attn_prefill(const pfa_attn_desc* desc, const pfa_kv_pool* 
     a.split_keys = max_splits > 1 ? split_keys : 0;
     a.max_splits = max_splits;
     a.sm_scale = desc->sm_scale;
-    PFA_TRY(hip_status(pfa::launch_prefill(a, desc->head_dim, (hipStream_t)stream)));
-    if (max_splits == 1) return PFA_OK;
+    if (max_splits == 1) return hip_status(pfa::launch_prefill(a, desc->head_dim, (hipStream_t)stream));
+    PFA_TRY(hip_status(pfa::launch_prefill_split(a, desc->head_dim, (hipStream_t)stream)));
     pfa::CombineArgs c;
     c.o_part = o_part;
     c.lse_part = lse_part;
@@ -236,7 +236,11 @@ int32_t pfa_prefill_num_splits(const pfa_attn_desc* desc, int32_t batch, int32_t
     const int64_t span = desc->window > 0 ? std::min<int64_t>(max_seq_len, desc->window + max_q_len)
                                           : max_seq_len;
     if (items >= target || span <= 256) return 1;
-    int64_t want = (target + items - 1) / items;
+    // the split kernel's workgroups hold kPrefillRowsSplit rows, two per CU
+    const int tps = pfa::kPrefillRowsSplit / g;
+    const int64_t items_s = (int64_t)batch * desc->num_kv_heads * ((max_q_len + tps - 1) / tps);
+    const int64_t target_s = target;
+    int64_t want = (target_s + items_s - 1) / items_s;
     int64_t sk = (max_seq_len + want - 1) / want;
     sk = std::max<int64_t>(256, (sk + 63) / 64 * 64);
     const int64_t ns = (max_seq_len + sk - 1) / sk;

@@ -12,7 +12,8 @@ constexpr int kWave = 64;
 constexpr int kPage = 16;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
-constexpr int kPrefillRows = 256;   // query rows (token x head-of-group) per prefill workgroup
+constexpr int kPrefillRows = 256;       // query rows (token x head-of-group) per prefill workgroup
+constexpr int kPrefillRowsSplit = 128;  // the same, for the KV-split kernel (short chunks on long prefixes)
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -172,5 +173,6 @@ hipError_t launch_kv_write(const KvWriteArgs& a, bool int8, hipStream_t s);
 hipError_t launch_decode(const DecodeArgs& a, int head_dim, bool int8, hipStream_t s);
 hipError_t launch_combine(const CombineArgs& a, int head_dim, hipStream_t s);
 hipError_t launch_prefill(const PrefillArgs& a, int head_dim, hipStream_t s);
+hipError_t launch_prefill_split(const PrefillArgs& a, int head_dim, hipStream_t s);
 
 }  // namespace pfa

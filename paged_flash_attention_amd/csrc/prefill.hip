@@ -11,16 +11,19 @@
 //    A row is one (token, head-of-group) pair, so the G query heads sharing a KV
 //    head share every K/V tile (GQA packing).  Each wave owns 32 rows.
 //  * K/V go HBM -> LDS with global_load_lds_dwordx4, with no register staging, in
-//    a 4-stage ring of 64-key tiles (4 pages), three tiles ahead.  Each wave
-//    waits on its own vmcnt before the one barrier per tile.  The page ids of
-//    later tiles are read (wave-uniform, scalar loads) while the current tile
-//    computes.
+//    a 5-stage ring of 64-key tiles (4 pages).  A tile is made visible (each wave
+//    waits on its own vmcnt, then the one barrier per tile) two iterations before
+//    its PV, so the barrier sits in the middle of an iteration while the matrix
+//    core still has queued work.  The page ids of later tiles are read
+//    (wave-uniform, scalar loads) a tile before they are needed.
 //  * The loop is software-pipelined within each wave, so that the matrix cores
 //    and the VALU work at the same time (on gfx950 each MFMA issue also takes
 //    VALU issue cycles, so the VALU work is spread evenly): the QK^T MFMAs of
 //    tile j+1 are interleaved with three quarters of the exps of tile j, and the
 //    PV MFMAs of tile j with the last quarter and the row max of tile j+1.
-//    Scheduling fences bound how far the compiler hoists LDS reads (registers).
+//    Scheduling fences bound how far the compiler hoists LDS reads (registers);
+//    K fragments are read two D-slices ahead, and the per-lane LDS offsets are
+//    computed once, so a read costs one add of the stage base.
 //  * LDS rows are the page rows (keys x D), 16-byte chunks XOR-swizzled per row.
 //    The swizzle is applied on the global side of the direct loads, and it makes
 //    both read patterns below free of bank conflicts.
@@ -54,16 +57,26 @@
 //    log-sum-exp, and the combine kernel then merges them with the sink.
 #include "pfa_device.h"
 
+// Two builds of this file: the default one (256-row workgroups, 64-key tiles, one
+// workgroup per CU) and, from prefill_split.hip, the KV-split one (128-row
+// workgroups, 32-key tiles, 64 KB of LDS, two workgroups per CU), which fills the
+// chip better when a short chunk is spread over key splits.
+#ifndef PFA_PREFILL_BN
+#define PFA_PREFILL_BN 64
+#define PFA_PREFILL_ROWS_WG kPrefillRows
+#define PFA_PREFILL_LAUNCH launch_prefill
+#endif
+
 namespace pfa {
 namespace {
 
 constexpr int kRowsPerWave = 32;
-constexpr int kWaves = kPrefillRows / kRowsPerWave;
+constexpr int kWaves = PFA_PREFILL_ROWS_WG / kRowsPerWave;
 constexpr int kThreads = kWaves * kWave;
-constexpr int kBN = 64;           // keys per tile
-constexpr int kStages = 4;        // LDS ring depth (tiles in flight: kStages - 1)
-constexpr int kPairs1 = 12;       // of a tile's 16 score pairs per lane, those whose exps
-                                  // run beside the QK^T MFMAs (the rest beside PV)
+constexpr int kBN = PFA_PREFILL_BN;   // keys per tile
+constexpr int kStages = 5;        // LDS ring depth: tiles kb-1 .. kb+3 around tile kb
+constexpr int kPairs1 = kBN == 64 ? 12 : 6;   // of a tile's 8*kBN/32 score pairs per lane,
+                                  // those whose exps run beside the QK^T MFMAs (the rest beside PV)
 constexpr int kXcds = 8;
 
 #define LDS3 __attribute__((address_space(3)))
@@ -283,22 +296,27 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a, const 
     const int tr_chunk = 2 * (tr_g % 2) + (tr_j % 4) / 2;         // + 4db
     const int tr_sub = 4 * (tr_j % 2);
 
-    auto needed = [&](int kb) __attribute__((always_inline)) {
-        const int key0 = kb * kBN;
-        return kb <= kb1 && wave_live && key0 < w_hi && key0 + kBN > w_lo;
-    };
-    // scheduling-group masks: VALU (not transcendental), transcendental, matrix
-    // ops, LDS reads
-    constexpr int VALU = 0x002, TRANS = 0x400, MFMA = 0x008, DSR = 0x100;
+    // A tile's scores per lane: NH halves of 32 keys (one f32x16 MFMA output each),
+    // NP = 8*NH packed bf16 pairs of P, NS = kBN/16 key slices for the PV MFMAs.
+    constexpr int NH = kBN / 32, NP = 8 * NH, NS = kBN / 16;
+    typedef f32x16 Scores[NH];
+    typedef uint32_t Packed[NH][8];
 
-    // S^T = K Q^T for the two 32-key halves of a tile, chains interleaved.  The
-    // per-lane LDS offsets are rebuilt from an opaque copy of the lane index at
-    // each call: hoisted out of the tile loop, the offsets of every stage and
-    // slice would stay live in registers.
-    auto k_frag = [&](const LDS3 char* kbase, int kr, int kk, bf16x8& k0, bf16x8& k1) __attribute__((always_inline)) {
-        const int off = (((2 * kk + half) ^ swz_k<D>(kr)) << 4);
-        k0 = *(const LDS3 bf16x8*)(kbase + off);
-        k1 = *(const LDS3 bf16x8*)(kbase + off + 2 * 32 * D);
+    // S^T = K Q^T, one MFMA chain per 32-key half.  Per-lane LDS byte offsets of
+    // the K reads (one per D-slice kk; the halves add 32 rows) and of the
+    // transposed V reads (one per 32-dim block db; slice m and the upper key half
+    // add constants), computed once: a read then costs one add of the stage base.
+    int kofs[KK], vofs[DB];
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) kofs[kk] = 2 * r32 * D + (((2 * kk + half) ^ swz_k<D>(r32)) << 4);
+    // the swizzle of row 16m + tr_row is that of tr_row
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+        vofs[db] = 2 * (tr_row * D + (((4 * db + tr_chunk) ^ swz_v<D>(tr_row)) << 3) + tr_sub);
+    auto k_frag = [&](uint32_t ks, int kk, bf16x8 (&k)[NH]) __attribute__((always_inline)) {
+        const LDS3 char* p = (const LDS3 char*)(uintptr_t)(ks + kofs[kk]);
+#pragma unroll
+        for (int h = 0; h < NH; ++h) k[h] = *(const LDS3 bf16x8*)(p + 2 * 32 * D * h);
     };
     // mask tile kb's scores in place (only tiles that cross a row's causal or
     // window edge need it)
@@ -306,16 +324,16 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a, const 
         const int key0 = kb * kBN;
         return (key0 + kBN - 1 <= prefix + w_first) && (W == 0 || (prefix + w_last) - key0 < W);
     };
-    auto mask = [&](int kb, f32x16 (&s)[2]) __attribute__((always_inline)) {
+    auto mask = [&](int kb, Scores& s) __attribute__((always_inline)) {
         // distance of this lane's first key in the tile from its row position
         const int d0 = opaque(pos_l - kb * kBN - 4 * half);
 #pragma unroll
-        for (int sb = 0; sb < 2; ++sb)
+        for (int h = 0; h < NH; ++h)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const int dist = d0 - (32 * sb + 8 * (r / 4) + (r % 4));      // pos - key
+                const int dist = d0 - (32 * h + 8 * (r / 4) + (r % 4));      // pos - key
                 const bool vis = dist >= 0 && (W == 0 || dist < W);
-                s[sb][r] = vis ? s[sb][r] : -INFINITY;
+                s[h][r] = vis ? s[h][r] : -INFINITY;
             }
     };
     // Lazy rescale with headroom: the reference max moves only when a row's max
@@ -336,124 +354,110 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a, const 
         }
     };
     // the row max of the raw scores (the scale is positive), then the rescale
-    auto mask_max = [&](int kb, f32x16 (&s)[2]) __attribute__((always_inline)) {
+    auto mask_max = [&](int kb, Scores& s) __attribute__((always_inline)) {
         if (!tile_full(kb)) mask(kb, s);
         float mt = -INFINITY;
 #pragma unroll
-        for (int sb = 0; sb < 2; ++sb)
+        for (int h = 0; h < NH; ++h)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) mt = fmaxf(mt, s[sb][r]);
+            for (int r = 0; r < 16; ++r) mt = fmaxf(mt, s[h][r]);
         rescale(mt);
     };
     // P = 2^(s*c2 - m), packed to bf16 in the B-operand order; l from the rounded P
     // that the PV MFMA uses (a dot2 with (1, 1))
-    auto exp_pair = [&](const f32x16 (&s)[2], uint32_t (&pk)[2][8], int e, float nmu) __attribute__((always_inline)) {
-        const int sb = e / 16, r = e % 16;
-        const float p0 = fast_exp2(fmaf(s[sb][r], c2, nmu));
-        const float p1 = fast_exp2(fmaf(s[sb][r + 1], c2, nmu));
-        pk[sb][r / 2] = pack_bf16_rne(p0, p1);
-        l_run = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(pk[sb][r / 2]), as_bf16x2(0x3F803F80u), l_run, false);
+    auto exp_pair = [&](const Scores& s, Packed& pk, int q, float nmu) __attribute__((always_inline)) {
+        const int h = q / 8, r = 2 * (q % 8);
+        const float p0 = fast_exp2(fmaf(s[h][r], c2, nmu));
+        const float p1 = fast_exp2(fmaf(s[h][r + 1], c2, nmu));
+        pk[h][r / 2] = pack_bf16_rne(p0, p1);
+        l_run = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(pk[h][r / 2]), as_bf16x2(0x3F803F80u), l_run, false);
     };
     // exp_pair pinned in place: the empty asm makes its results exist here, so the
     // optimiser cannot sink the exps out of the bundle they are meant to fill
-    auto exp_pair_here = [&](const f32x16 (&s)[2], uint32_t (&pk)[2][8], int e, float nmu) __attribute__((always_inline)) {
-        exp_pair(s, pk, e, nmu);
-        asm volatile("" : "+v"(pk[e / 16][(e % 16) / 2]), "+v"(l_run));
+    auto exp_pair_here = [&](const Scores& s, Packed& pk, int q, float nmu) __attribute__((always_inline)) {
+        exp_pair(s, pk, q, nmu);
+        asm volatile("" : "+v"(pk[q / 8][q % 8]), "+v"(l_run));
     };
-    auto softmax = [&](const f32x16 (&s)[2], uint32_t (&pk)[2][8]) __attribute__((always_inline)) {
+    auto softmax = [&](const Scores& s, Packed& pk) __attribute__((always_inline)) {
         const float nmu = (m_run == -INFINITY) ? 0.0f : -m_run;
 #pragma unroll
-        for (int e = 0; e < 32; e += 2) exp_pair(s, pk, e, nmu);
+        for (int q = 0; q < NP; ++q) exp_pair(s, pk, q, nmu);
     };
-    // Block 1: S' = K' Q^T (two 32-key chains), optionally with the exps of the
-    // current tile's S interleaved (EXP).  Bundles of one D-slice each: the K reads
-    // of slice kk+1, the two MFMAs of slice kk, 32/KK exps.  A scheduling fence
+    // Block 1: S' = K' Q^T, optionally with pairs [0, P1) of the current tile's
+    // exps interleaved (EXP).  Bundles of one D-slice each: the K reads of slice
+    // kk+1, the NH MFMAs of slice kk, a share of the exps.  A scheduling fence
     // after each bundle keeps the compiler from hoisting every read of the block
     // (which costs registers the scores need).
-    auto qk_block = [&](bool EXP, uint32_t ks, f32x16 (&sn)[2], const f32x16 (&s)[2], uint32_t (&pk)[2][8]) __attribute__((always_inline)) {
+    auto qk_block = [&](bool EXP, int P1, uint32_t ks, Scores& sn, const Scores& s, Packed& pk) __attribute__((always_inline)) {
         const float nmu = (m_run == -INFINITY) ? 0.0f : -m_run;
-        const int kr = opaque(r32);                   // key rows kr and kr + 32 (same swizzle)
-        const LDS3 char* kbase = (const LDS3 char*)(uintptr_t)(ks + 2 * kr * D);
-        bf16x8 k0, k1;
-        k_frag(kbase, kr, 0, k0, k1);
+        // K fragments two D-slices ahead of the MFMAs that use them
+        bf16x8 kq[KK][NH];
+        k_frag(ks, 0, kq[0]);
+        if (KK > 1) k_frag(ks, 1, kq[1]);
 #pragma unroll
         for (int kk = 0; kk < KK; ++kk) {
-            bf16x8 n0, n1;
-            if (kk + 1 < KK) k_frag(kbase, kr, kk + 1, n0, n1);
-            if (kk == 0) {
-                const f32x16 z = {};
-                sn[0] = mfma32(k0, qf[0], z);
-            } else {
-                sn[0] = mfma32(k0, qf[kk], sn[0]);
-            }
-            // score pairs [kk*P1/KK, (kk+1)*P1/KK) of the block's P1, split over the two MFMAs
-            const int pa = kk * kPairs1 / KK, pb = (kk + 1) * kPairs1 / KK, pm = (pa + pb) / 2;
-            if (EXP) {
+            if (kk + 2 < KK) k_frag(ks, kk + 2, kq[kk + 2]);
+            bf16x8 (&k)[NH] = kq[kk];
+            const int pa = kk * P1 / KK, pb = (kk + 1) * P1 / KK;
 #pragma unroll
-                for (int q = pa; q < pm; ++q) exp_pair_here(s, pk, 2 * q, nmu);
-            }
-            if (kk == 0) {
-                const f32x16 z = {};
-                sn[1] = mfma32(k1, qf[0], z);
-            } else {
-                sn[1] = mfma32(k1, qf[kk], sn[1]);
-            }
-            if (EXP) {
+            for (int h = 0; h < NH; ++h) {
+                if (kk == 0) {
+                    const f32x16 z = {};
+                    sn[h] = mfma32(k[h], qf[0], z);
+                } else {
+                    sn[h] = mfma32(k[h], qf[kk], sn[h]);
+                }
+                // this MFMA's share of the bundle's exps
+                if (EXP) {
+                    const int qa = pa + h * (pb - pa) / NH, qb = pa + (h + 1) * (pb - pa) / NH;
 #pragma unroll
-                for (int q = pm; q < pb; ++q) exp_pair_here(s, pk, 2 * q, nmu);
+                    for (int q = qa; q < qb; ++q) exp_pair_here(s, pk, q, nmu);
+                }
             }
-            if (kk + 1 < KK) { k0 = n0; k1 = n1; }
             __builtin_amdgcn_sched_barrier(0);
         }
     };
-    // Block 2: O^T += V^T P^T over the four 16-key slices, optionally with the row
-    // max of the next tile's (masked) scores interleaved (MAX).  Bundles: the
-    // transposed V reads of slice m+1, the DB MFMAs of slice m, 8 max.
-    auto v_offsets = [&](int (&voffs)[DB]) __attribute__((always_inline)) {
-        // the swizzle of row 16m + tr_row is that of tr_row: slice m only adds a constant
-        const int tr = opaque(tr_row);
-#pragma unroll
-        for (int db = 0; db < DB; ++db)
-            voffs[db] = 2 * (tr * D + (((4 * db + tr_chunk) ^ swz_v<D>(tr)) << 3) + tr_sub);
-    };
-    auto v_frag = [&](const LDS3 char* vbase, const int (&voffs)[DB], int m, int db) __attribute__((always_inline)) {
-        const LDS3 char* p = vbase + voffs[db] + 2 * 16 * m * D;
+    // Block 2: O^T += V^T P^T over the NS 16-key slices, optionally (FUSED) with
+    // the exps of pairs [P1, NP) of the tile (the last slice's P, computed during
+    // the slices before it) and the row max of the next tile's scores sn (during
+    // the slices after the first, once their MFMAs have long finished), then the
+    // rescale.
+    auto v_frag = [&](uint32_t vs, int m, int db) __attribute__((always_inline)) {
+        const LDS3 char* p = (const LDS3 char*)(uintptr_t)(vs + vofs[db]) + 2 * 16 * m * D;
         const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS3 s16x4*)p);
         const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS3 s16x4*)(p + 2 * 8 * D));
         return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
     };
-    // FUSED: also the exps of score pairs kPairs1..15 of the current tile (slice 3's
-    // P, computed during slices 0-2) and the row max of the next tile's scores sn
-    // (during slices 1-3, once block 1's MFMAs have long finished), then the rescale.
-    auto pv_block = [&](bool FUSED, uint32_t vs, uint32_t (&pk)[2][8], const f32x16 (&s)[2], const f32x16 (&sn)[2]) __attribute__((always_inline)) {
-        int voffs[DB];
-        v_offsets(voffs);
-        const LDS3 char* vbase = (const LDS3 char*)(uintptr_t)vs;
+    // the slice-0 V fragments of a PV block, read ahead of it
+    typedef bf16x8 VHead[DB];
+    auto pv_head = [&](uint32_t vs, VHead& vh) __attribute__((always_inline)) {
+#pragma unroll
+        for (int db = 0; db < DB; ++db) vh[db] = v_frag(vs, 0, db);
+    };
+    auto pv_block = [&](bool FUSED, int P1, uint32_t vs, VHead& vf, Packed& pk, const Scores& s, const Scores& sn) __attribute__((always_inline)) {
         const float nmu = (m_run == -INFINITY) ? 0.0f : -m_run;
         float mt = -INFINITY;
-        bf16x8 vf[DB];
 #pragma unroll
-        for (int db = 0; db < DB; ++db) vf[db] = v_frag(vbase, voffs, 0, db);
-#pragma unroll
-        for (int m = 0; m < kBN / 16; ++m) {
-            const int sb = m / 2, r0 = 4 * (m % 2);
-            const bf16x8 pf = __builtin_bit_cast(bf16x8, make_uint4(pk[sb][r0], pk[sb][r0 + 1], pk[sb][r0 + 2], pk[sb][r0 + 3]));
+        for (int m = 0; m < NS; ++m) {
+            const int h = m / 2, r0 = 4 * (m % 2);
+            const bf16x8 pf = __builtin_bit_cast(bf16x8, make_uint4(pk[h][r0], pk[h][r0 + 1], pk[h][r0 + 2], pk[h][r0 + 3]));
             // one register set per 32-dim block: slice m+1 is read into it as soon as
             // the MFMA of slice m that reads it has issued
 #pragma unroll
             for (int db = 0; db < DB; ++db) {
                 acc_o[db] = mfma32(vf[db], pf, acc_o[db]);
-                if (m + 1 < kBN / 16) vf[db] = v_frag(vbase, voffs, m + 1, db);
+                if (m + 1 < NS) vf[db] = v_frag(vs, m + 1, db);
             }
             if (FUSED) {
-                if (m < 3) {
-                    const int pa = kPairs1 + m * (16 - kPairs1) / 3, pb = kPairs1 + (m + 1) * (16 - kPairs1) / 3;
+                if (m < NS - 1) {
+                    const int pa = P1 + m * (NP - P1) / (NS - 1), pb = P1 + (m + 1) * (NP - P1) / (NS - 1);
 #pragma unroll
-                    for (int q = pa; q < pb; ++q) exp_pair_here(s, pk, 2 * q, nmu);
+                    for (int q = pa; q < pb; ++q) exp_pair_here(s, pk, q, nmu);
                 }
                 if (m > 0) {
 #pragma unroll
-                    for (int e = 32 * (m - 1) / 3; e < 32 * m / 3; ++e) mt = fmaxf(mt, sn[e / 16][e % 16]);
+                    for (int e = 16 * NH * (m - 1) / (NS - 1); e < 16 * NH * m / (NS - 1); ++e)
+                        mt = fmaxf(mt, sn[e / 16][e % 16]);
                 }
             }
             __builtin_amdgcn_sched_barrier(0);
@@ -469,32 +473,35 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a, const 
         }
     };
 
-    // Software pipeline over the ring, tiles three ahead.  Tile kb sits in stage
-    // (kb - kb0) % kStages.  Every wave runs ring(kb) once for each tile kb0..kb1:
-    // it waits for tile kb+1 (each wave its own direct loads, then the barrier),
-    // refills the stage of tile kb-1 with tile kb+3 (clamped to kb1, so the load
-    // count stays balanced) and zeroes tile kb+1's V rows past the sequence end
-    // (read from the next iteration on).  A wave computes only on the tiles
-    // kw0..kw1 that its rows see; iteration kb of that range holds the masked
-    // scores S of tile kb (row max already folded into m) and runs
-    //   block 1: S' = K_{kb+1} Q^T (MFMA) interleaved with P = exp2(S - m) (VALU);
-    //   block 2: O += P V_kb (MFMA) interleaved with the row max of S' (VALU),
-    //     then the rescale for tile kb+1.
-    // The range's first tile gets its S in the iteration before, its last one
-    // only block 2's PV.
-    auto kst = [&](int kb) { return ring0 + (uint32_t)((kb - kb0) & (kStages - 1)) * (2 * kTileBytes); };
+    // Software pipeline over a 5-stage ring.  Tile kb sits in stage
+    // (kb - kb0) % kStages.  Every wave runs ring(kb) once for each tile kb0..kb1;
+    // ring(kb) makes tile kb+2 visible (each wave waits for its own direct loads,
+    // then the barrier), refills the stage of tile kb-1 with tile kb+4 (clamped to
+    // kb1, so the load count stays balanced) and zeroes tile kb+2's V rows past the
+    // sequence end (visible from the next barrier on).  Because tiles are made
+    // visible two iterations before their PV, the barrier can sit in the middle of
+    // an iteration, where the matrix core still has block 1's MFMAs to run:
+    //   block 1: S' = K_{kb+1} Q^T (MFMA) interleaved with most of P = exp2(S - m);
+    //   ring(kb), with the first V reads of block 2 issued right after the barrier;
+    //   block 2: O += P V_kb (MFMA) interleaved with the rest of the exps and the
+    //     row max of S', then the rescale for tile kb+1.
+    // A wave computes only on the tiles kw0..kw1 its rows see; the range's first
+    // tile gets its S before ring(kw0 - 1), its last one only P and PV.
+    auto kst = [&](int kb) { return ring0 + (uint32_t)((kb - kb0) % kStages) * (2 * kTileBytes); };
     auto vst = [&](int kb) { return kst(kb) + kTileBytes; };
-    int pg_raw;                                // raw page entry of tile min(kb + 3, kb1)
-    auto ring = [&](int kb) __attribute__((always_inline)) {
-        const int pg = clamp_page(pg_raw);     // its load went out one tile ago
-        const uint32_t kd = kst(kb + 3), vd = vst(kb + 3);
-        // in flight: tiles kb+1 and kb+2 (kb+3 is issued below)
-        wait_vmcnt<NL>();                      // this wave's share of tile kb+1 landed
+    int pg_raw;                                // raw page entry of tile min(kb + 4, kb1)
+    // ring in two parts, so that LDS reads can be issued right after the barrier
+    auto ring_pre = [&](int kb) __attribute__((always_inline)) {
+        // in flight: tiles kb+2 and kb+3 (kb+4 is issued below)
+        wait_vmcnt<NL>();                      // this wave's share of tile kb+2 landed
         lds_sync();                            // everyone's; tile kb-1's stage is free
-        issue(pg, kd, vd);                     // tile min(kb + 3, kb1)
-        pg_raw = raw_page(min(kb + 4, kb1));
-        zero_tail(kb + 1, vst(kb + 1));
     };
+    auto ring_post = [&](int kb) __attribute__((always_inline)) {
+        issue(clamp_page(pg_raw), kst(kb + 4), vst(kb + 4));   // tile min(kb + 4, kb1)
+        pg_raw = raw_page(min(kb + 5, kb1));
+        zero_tail(kb + 2, vst(kb + 2));
+    };
+    auto ring = [&](int kb) __attribute__((always_inline)) { ring_pre(kb); ring_post(kb); };
     // this wave's tiles
     int kw0 = kb0, kw1 = kb0 - 1;
     if (wave_live) {
@@ -503,28 +510,32 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a, const 
     }
     const bool any = kw0 <= kw1;
 
-    issue(clamp_page(raw_page(kb0)), kst(kb0), vst(kb0));
-    issue(clamp_page(raw_page(min(kb0 + 1, kb1))), kst(kb0 + 1), vst(kb0 + 1));
-    issue(clamp_page(raw_page(min(kb0 + 2, kb1))), kst(kb0 + 2), vst(kb0 + 2));
-    pg_raw = raw_page(min(kb0 + 3, kb1));
-    wait_vmcnt<2 * NL>();                      // tile kb0 landed (kb0+1, kb0+2 in flight)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) issue(clamp_page(raw_page(min(kb0 + i, kb1))), kst(kb0 + i), vst(kb0 + i));
+    pg_raw = raw_page(min(kb0 + 4, kb1));
+    wait_vmcnt<2 * NL>();                      // tiles kb0, kb0+1 landed (kb0+2, kb0+3 in flight)
     lds_sync();
     zero_tail(kb0, vst(kb0));                  // visible after the next barrier
+    zero_tail(kb0 + 1, vst(kb0 + 1));
 
-    f32x16 s_a[2], s_b[2];                     // scores of the current / next tile
-    uint32_t pk[2][8];
+    Scores s_a, s_b;                           // scores of the current / next tile
+    Packed pk;
+    VHead vh;
     int kb = kb0;
     if (any) {
         for (; kb < kw0 - 1; ++kb) ring(kb);
-        if (kw0 > kb0) ring(kb++);
-        qk_block(false, kst(kw0), s_a, s_b, pk);
+        // tile kw0 became visible at ring(kw0 - 2) or in the prologue
+        qk_block(false, 0, kst(kw0), s_a, s_b, pk);
         mask_max(kw0, s_a);
+        if (kw0 > kb0) ring(kb++);             // ring(kw0 - 1)
         // fused iterations kw0 .. kw1-1, two per round (the score buffers swap)
-        auto fused = [&](int t, f32x16 (&sc)[2], f32x16 (&sn)[2]) __attribute__((always_inline)) {
-            ring(t);
-            qk_block(true, kst(t + 1), sn, sc, pk);
+        auto fused = [&](int t, Scores& sc, Scores& sn) __attribute__((always_inline)) {
+            qk_block(true, kPairs1, kst(t + 1), sn, sc, pk);
             if (!tile_full(t + 1)) mask(t + 1, sn);
-            pv_block(true, vst(t), pk, sc, sn);
+            ring_pre(t);
+            pv_head(vst(t), vh);
+            ring_post(t);
+            pv_block(true, kPairs1, vst(t), vh, pk, sc, sn);
         };
         for (; kb + 1 < kw1; kb += 2) {
             fused(kb, s_a, s_b);
@@ -533,12 +544,16 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a, const 
         if (kb < kw1) {
             fused(kb, s_a, s_b);
 #pragma unroll
-            for (int r = 0; r < 16; ++r) { s_a[0][r] = s_b[0][r]; s_a[1][r] = s_b[1][r]; }
+            for (int h = 0; h < NH; ++h)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) s_a[h][r] = s_b[h][r];
             ++kb;
         }
-        ring(kb++);                            // tile kw1: P and PV only
-        softmax(s_a, pk);
-        pv_block(false, vst(kw1), pk, s_a, s_a);
+        softmax(s_a, pk);                      // tile kw1: P and PV only
+        ring_pre(kb);
+        pv_head(vst(kw1), vh);
+        ring_post(kb++);
+        pv_block(false, NP, vst(kw1), vh, pk, s_a, s_a);
     }
     for (; kb <= kb1; ++kb) ring(kb);
     wait_vmcnt<0>();          // drain the trailing refills before the workgroup retires
@@ -602,7 +617,7 @@ hipError_t launch_d(const PrefillArgs& a, hipStream_t s) {
 
 }  // namespace
 
-hipError_t launch_prefill(const PrefillArgs& a, int head_dim, hipStream_t s) {
+hipError_t PFA_PREFILL_LAUNCH(const PrefillArgs& a, int head_dim, hipStream_t s) {
     if (a.batch == 0 || a.max_q_len == 0) return hipSuccess;
     return head_dim == 128 ? launch_d<128>(a, s) : launch_d<64>(a, s);
 }
