@@ -69,6 +69,16 @@ def decode_bytes(case) -> int:
     return kv + q + out + bt
 
 
+def verify_bytes(case) -> int:
+    """Bytes a verify step (or any chunk) must move at least: every visible K/V byte
+    once per (sequence, KV head), the chunk's q and fp32 out, the block-table entries."""
+    p = case.p
+    vis = visible_keys(case.seq_lens, p.window)
+    kv = int(vis.sum()) * p.num_kv_heads * 2 * p.head_dim * 2
+    T = int(case.q_lens.sum())
+    return kv + T * p.num_q_heads * p.head_dim * (2 + 4) + int((np.asarray(case.seq_lens) + 15).sum() // 16) * 4
+
+
 def kv_write_bytes(case) -> int:
     p = case.p
     T = int(case.q_lens.sum())
@@ -193,13 +203,16 @@ def run_decode(case, torch, pfa, gs, steps, warmup):
                 partial_bytes=int(B * Hq * ms * (D + 1) * 4))
 
 
-def run_prefill(case, torch, pfa, gs, steps, warmup):
+def run_prefill(case, torch, pfa, gs, steps, warmup, verify=False):
+    """Prefill steps (kv_write + prefill), or with verify=True verify steps (kv_write
+    + pfa_paged_attn_verify), on the library's split choice."""
     g, pools, (kn, vn, cun) = setup_case(case, torch, pfa, gs, copies_for_bytes=0)
     p = case.p
     Tq = int(case.cu_q[-1])
     out = torch.empty((Tq, p.num_q_heads, p.head_dim), device="cuda")
     max_q, max_len = int(case.q_lens.max()), int(case.seq_lens.max())
-    ms, sk = pfa.prefill_num_splits(g.desc, case.batch, max_q, max_len)
+    ms, sk = (pfa.verify_num_splits if verify else pfa.prefill_num_splits)(g.desc, case.batch, max_q, max_len)
+    attn = pfa.paged_attn_verify if verify else pfa.paged_attn_prefill
     op = lp = None
     if ms > 1:
         op = torch.empty((Tq, p.num_q_heads, ms, p.head_dim), device="cuda")
@@ -209,8 +222,8 @@ def run_prefill(case, torch, pfa, gs, steps, warmup):
     def step(i):
         pfa.kv_write(g.desc, g.pool, kn, vn, cun, g.seq_lens, g.bt)
         e = tm.mark("prefill")
-        pfa.paged_attn_prefill(g.desc, g.pool, g.q, g.cu_q, g.bt, g.seq_lens, max_q, out, max_seq_len=max_len,
-                               split_keys=sk, max_splits=ms, o_part=op, lse_part=lp)
+        attn(g.desc, g.pool, g.q, g.cu_q, g.bt, g.seq_lens, max_q, out, max_seq_len=max_len,
+             split_keys=sk, max_splits=ms, o_part=op, lse_part=lp)
         tm.close("prefill", e)
 
     for i in range(warmup):
@@ -225,7 +238,7 @@ def run_prefill(case, torch, pfa, gs, steps, warmup):
     t1.record()
     torch.cuda.synchronize()
     return dict(step_ms=t0.elapsed_time(t1) / steps, prefill_ms=tm.mean_ms("prefill"),
-                flops=prefill_flops(case), split_keys=sk, max_splits=ms)
+                flops=prefill_flops(case), split_keys=sk, max_splits=ms, kv_bytes=verify_bytes(case))
 
 
 # ---------------------------------------------------------------------------
@@ -334,6 +347,8 @@ def main():
         "prefill_chunk130_on_8192": lambda: W.prefill_llama8b(prompt=130, prefix=8192),
         "mixed_full_prefill_2x2048": lambda: W.mixed_gptoss(layer="full", part="prefill"),
         "mixed_window_prefill_2x2048": lambda: W.mixed_gptoss(layer="window", part="prefill"),
+        "verify_16tok_batch1_ctx1024": lambda: W.verify_qwen4b(),
+        "verify_8tok_batch32_ctx512_8192": lambda: W.verify_qwen4b(batch=32, tokens=8, lo=512, hi=8192),
     }
     if args.workload not in builders:
         print(f"unknown workload {args.workload}; choose from {sorted(builders)}", file=sys.stderr)
@@ -342,7 +357,13 @@ def main():
     def measure(name, steps, warmup):
         case = builders[name]()
         log(f"[bench] {name}: building + timing {steps} steps")
-        if name.startswith("prefill") or name.endswith("prefill_2x2048"):
+        if name.startswith("verify"):
+            r = run_prefill(case, torch, pfa, gs, steps, warmup, verify=True)
+            tf = r["flops"] / (r["prefill_ms"] * 1e-3) / 1e12
+            gbs = r["kv_bytes"] / (r["prefill_ms"] * 1e-3) / 1e9
+            r.update(metric="verify attn GB/s", kernel_tflops=round(tf, 2), kernel_gbs=round(gbs, 1),
+                     frac_of_mfma_peak=round(tf / BF16_PEAK_TFLOPS, 4), frac_of_hbm_peak=round(gbs / HBM_PEAK_GBS, 4))
+        elif name.startswith("prefill") or name.endswith("prefill_2x2048"):
             r = run_prefill(case, torch, pfa, gs, steps, warmup)
             tf = r["flops"] / (r["prefill_ms"] * 1e-3) / 1e12
             r.update(metric="prefill attn TFLOP/s", kernel_tflops=round(tf, 2),
@@ -356,7 +377,12 @@ def main():
 
     case, r = measure(args.workload, args.steps, args.warmup)
     is_prefill = "prefill_ms" in r
-    if is_prefill:
+    if args.workload.startswith("verify"):
+        value = r["kv_bytes"] / (r["step_ms"] * 1e-3) / 1e9
+        unit, metric = "GB/s", "verify attn GB/s (HBM)"
+        roof = dict(bound="hbm", achieved=r["kernel_gbs"], peak=HBM_PEAK_GBS, unit="GB/s",
+                    frac=r["frac_of_hbm_peak"], traffic=None)
+    elif is_prefill:
         value = r["flops"] / (r["step_ms"] * 1e-3) / 1e12
         unit, metric = "TFLOP/s", "prefill attn TFLOP/s"
         roof = dict(bound="mfma", achieved=r["kernel_tflops"], peak=BF16_PEAK_TFLOPS, unit="TFLOP/s",
@@ -373,10 +399,15 @@ def main():
     if not args.no_extra and args.workload == "decode_batch32_ctx512_8192":
         for name, st in (("decode_batch32_ctx8192", 30), ("decode_int8_batch8_ctx32768", 30),
                          ("mixed_full_decode_b64", 30), ("prefill_causal_8192", 10),
-                         ("prefill_chunk130_on_8192", 20), ("mixed_full_prefill_2x2048", 20)):
+                         ("prefill_chunk130_on_8192", 20), ("mixed_full_prefill_2x2048", 20),
+                         ("verify_16tok_batch1_ctx1024", 50), ("verify_8tok_batch32_ctx512_8192", 30)):
             try:
                 _, rr = measure(name, st, 3)
-                if "prefill_ms" in rr:
+                if name.startswith("verify"):
+                    extra[name] = dict(us=round(rr["prefill_ms"] * 1e3, 2), gbs=rr["kernel_gbs"],
+                                       frac_of_hbm_peak=rr["frac_of_hbm_peak"], tflops=rr["kernel_tflops"],
+                                       split=f"{rr['split_keys']}x{rr['max_splits']}")
+                elif "prefill_ms" in rr:
                     extra[name] = dict(us=round(rr["prefill_ms"] * 1e3, 1), tflops=rr["kernel_tflops"],
                                        frac_of_mfma_peak=rr["frac_of_mfma_peak"])
                 else:

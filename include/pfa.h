@@ -44,7 +44,7 @@
  *
  * Supported shapes: head_dim 64 or 128; page_size 16; Hq % Hkv == 0.
  *  - Decode: group size G = Hq/Hkv in {1,2,4,8}.
- *  - Prefill: G in {1,2,4,8,16,32}.
+ *  - Prefill and verify: G in {1,2,4,8,16,32}; BF16 K/V.
  */
 #ifndef PFA_H
 #define PFA_H
@@ -192,6 +192,36 @@ pfa_status pfa_paged_attn_prefill(const pfa_attn_desc* desc, const pfa_kv_pool* 
  */
 int32_t pfa_prefill_num_splits(const pfa_attn_desc* desc, int32_t batch, int32_t max_q_len,
                                int32_t max_seq_len, int32_t num_cus, int32_t* split_keys);
+
+/*
+ * pfa_paged_attn_verify: attention of a speculative-decoding verify step, the
+ *   2-16 tokens per sequence (the last accepted token plus the drafted ones) that
+ *   one forward pass checks.  TileInfer.jl performance page, section "Speculative
+ *   decoding", paragraph on attention for verify steps: such steps run the
+ *   split-KV kernels rather than the prefill kernel.
+ *
+ *   The result is the one pfa_paged_attn_prefill defines for a chunk of q_len new
+ *   tokens: causal among the new tokens and over the whole cached prefix, with the
+ *   same window and sinks.  Arguments, layouts and the split contract are those of
+ *   pfa_paged_attn_prefill, with max_q_len <= 16 (PFA_ERR_SHAPE otherwise).  The
+ *   work runs on the KV-split kernel build (128-row workgroups, 32-key tiles); use
+ *   pfa_verify_num_splits for split_keys / max_splits.  max_splits == 1 is allowed
+ *   and writes out directly.
+ */
+pfa_status pfa_paged_attn_verify(const pfa_attn_desc* desc, const pfa_kv_pool* pool,
+                                 const void* q, const int32_t* cu_q,
+                                 const int32_t* block_table, int32_t bt_stride,
+                                 const int32_t* seq_lens, int32_t batch, int32_t max_q_len,
+                                 int32_t max_seq_len, int32_t split_keys, int32_t max_splits,
+                                 float* o_part, float* lse_part, float* out, void* stream);
+
+/*
+ * A verify split choice for `num_cus` compute units (0 means 256): split_keys a
+ * multiple of 64, enough ranges for about two workgroups per CU.  Returns
+ * max_splits (1 and *split_keys = 0 when unsplit).  Host-side arithmetic only.
+ */
+int32_t pfa_verify_num_splits(const pfa_attn_desc* desc, int32_t batch, int32_t max_q_len,
+                              int32_t max_seq_len, int32_t num_cus, int32_t* split_keys);
 
 /* ceil(max_seq_len / split_keys), at least 1 (0 when split_keys <= 0). */
 int32_t pfa_decode_num_splits(int32_t max_seq_len, int32_t split_keys);

@@ -26,8 +26,8 @@ KV_DTYPES = {"bf16": 0, "int8": 1}
 
 # every symbol include/pfa.h declares
 EXPORTS = ("pfa_kv_write", "pfa_paged_attn_decode", "pfa_paged_attn_combine",
-           "pfa_paged_attn_prefill", "pfa_decode_num_splits", "pfa_prefill_num_splits",
-           "pfa_status_string", "pfa_last_hip_error")
+           "pfa_paged_attn_prefill", "pfa_paged_attn_verify", "pfa_decode_num_splits",
+           "pfa_prefill_num_splits", "pfa_verify_num_splits", "pfa_status_string", "pfa_last_hip_error")
 
 
 class PfaError(RuntimeError):
@@ -69,6 +69,7 @@ def lib() -> ctypes.CDLL:
         "pfa_paged_attn_decode": [D, PL, P, P, I, P, I, I, I, I, P, P, P, V],
         "pfa_paged_attn_combine": [D, P, P, P, I, I, I, P, V],
         "pfa_paged_attn_prefill": [D, PL, P, P, P, I, P, I, I, I, I, I, P, P, P, V],
+        "pfa_paged_attn_verify": [D, PL, P, P, P, I, P, I, I, I, I, I, P, P, P, V],
     }
     for name, args in sig.items():
         fn = getattr(L, name)
@@ -78,6 +79,8 @@ def lib() -> ctypes.CDLL:
     L.pfa_decode_num_splits.restype = ctypes.c_int32
     L.pfa_prefill_num_splits.argtypes = [D, I, I, I, I, ctypes.POINTER(ctypes.c_int32)]
     L.pfa_prefill_num_splits.restype = ctypes.c_int32
+    L.pfa_verify_num_splits.argtypes = [D, I, I, I, I, ctypes.POINTER(ctypes.c_int32)]
+    L.pfa_verify_num_splits.restype = ctypes.c_int32
     L.pfa_status_string.argtypes = [ctypes.c_int]
     L.pfa_status_string.restype = ctypes.c_char_p
     L.pfa_last_hip_error.argtypes = []
@@ -249,5 +252,36 @@ def paged_attn_prefill(desc: AttnDesc, pool: KVPool, q, cu_q, block_table, seq_l
     _check("pfa_paged_attn_prefill", st)
 
 
+def verify_num_splits(desc: AttnDesc, batch: int, max_q_len: int, max_seq_len: int, num_cus: int = 256):
+    """(max_splits, split_keys) the library suggests for a verify step of this shape."""
+    sk = ctypes.c_int32(0)
+    ms = lib().pfa_verify_num_splits(ctypes.byref(desc.c()), int(batch), int(max_q_len), int(max_seq_len),
+                                     int(num_cus), ctypes.byref(sk))
+    return int(ms), int(sk.value)
+
+
+def paged_attn_verify(desc: AttnDesc, pool: KVPool, q, cu_q, block_table, seq_lens, max_q_len: int,
+                      out, max_seq_len: Optional[int] = None, split_keys: int = 0, max_splits: int = 1,
+                      o_part=None, lse_part=None, stream=None):
+    """Verify step: 2-16 new tokens per sequence, q [Tq, Hq, D] bf16 -> out [Tq, Hq, D]
+    fp32, the same result as paged_attn_prefill for that chunk (see pfa.h)."""
+    _dev(q, torch.bfloat16, "q")
+    _dev(cu_q, torch.int32, "cu_q")
+    _dev(block_table, torch.int32, "block_table")
+    _dev(seq_lens, torch.int32, "seq_lens")
+    _dev(out, torch.float32, "out")
+    _dev(o_part, torch.float32, "o_part")
+    _dev(lse_part, torch.float32, "lse_part")
+    if max_seq_len is None:
+        max_seq_len = int(block_table.shape[1]) * desc.page_size
+    st = lib().pfa_paged_attn_verify(ctypes.byref(desc.c()), ctypes.byref(pool.c()), _ptr(q),
+                                     _ptr(cu_q), _ptr(block_table), int(block_table.shape[1]),
+                                     _ptr(seq_lens), int(seq_lens.numel()), int(max_q_len),
+                                     int(max_seq_len), int(split_keys), int(max_splits),
+                                     _ptr(o_part), _ptr(lse_part), _ptr(out), _stream(stream, q))
+    _check("pfa_paged_attn_verify", st)
+
+
 __all__ = ["AttnDesc", "KVPool", "PfaError", "EXPORTS", "lib", "kv_write", "decode_num_splits",
-           "prefill_num_splits", "paged_attn_decode", "paged_attn_combine", "paged_attn_prefill"]
+           "prefill_num_splits", "verify_num_splits", "paged_attn_decode", "paged_attn_combine",
+           "paged_attn_prefill", "paged_attn_verify"]

@@ -158,12 +158,16 @@ pfa_status pfa_paged_attn_combine(const pfa_attn_desc* desc, const float* o_part
     return hip_status(pfa::launch_combine(a, desc->head_dim, (hipStream_t)stream));
 }
 
-pfa_status pfa_paged_attn_prefill(const pfa_attn_desc* desc, const pfa_kv_pool* pool, const void* q,
-                                  const int32_t* cu_q, const int32_t* block_table,
-                                  int32_t bt_stride, const int32_t* seq_lens, int32_t batch,
-                                  int32_t max_q_len, int32_t max_seq_len, int32_t split_keys,
-                                  int32_t max_splits, float* o_part, float* lse_part, float* out,
-                                  void* stream) {
+namespace {
+
+// The prefill and verify entry points share their checks and launch; `split_build`
+// selects the 128-row / 32-key kernel build (always for verify, and for prefill in
+// split mode).
+pfa_status prefill_like(const pfa_attn_desc* desc, const pfa_kv_pool* pool, const void* q,
+                        const int32_t* cu_q, const int32_t* block_table, int32_t bt_stride,
+                        const int32_t* seq_lens, int32_t batch, int32_t max_q_len,
+                        int32_t max_seq_len, int32_t split_keys, int32_t max_splits, float* o_part,
+                        float* lse_part, float* out, void* stream, bool split_build) {
     PFA_TRY(check_desc(desc));
     PFA_TRY(check_pool(desc, pool));
     if (desc->kv_dtype != PFA_KV_BF16) return PFA_ERR_UNSUPPORTED;
@@ -172,7 +176,7 @@ pfa_status pfa_paged_attn_prefill(const pfa_attn_desc* desc, const pfa_kv_pool* 
     if (batch < 0 || max_q_len < 0 || bt_stride <= 0 || max_seq_len < max_q_len || max_splits < 1)
         return PFA_ERR_SHAPE;
     if (max_seq_len > (int64_t)bt_stride * desc->page_size) return PFA_ERR_SHAPE;
-    const int tpb = (max_splits > 1 ? pfa::kPrefillRowsSplit : pfa::kPrefillRows) / g;
+    const int tpb = (split_build ? pfa::kPrefillRowsSplit : pfa::kPrefillRows) / g;
     const int64_t items =
         (int64_t)batch * desc->num_kv_heads * ((max_q_len + tpb - 1) / tpb) * max_splits;
     if (items > 0x7fffffff - 8) return PFA_ERR_SHAPE;
@@ -205,8 +209,9 @@ pfa_status pfa_paged_attn_prefill(const pfa_attn_desc* desc, const pfa_kv_pool* 
     a.split_keys = max_splits > 1 ? split_keys : 0;
     a.max_splits = max_splits;
     a.sm_scale = desc->sm_scale;
-    if (max_splits == 1) return hip_status(pfa::launch_prefill(a, desc->head_dim, (hipStream_t)stream));
+    if (!split_build) return hip_status(pfa::launch_prefill(a, desc->head_dim, (hipStream_t)stream));
     PFA_TRY(hip_status(pfa::launch_prefill_split(a, desc->head_dim, (hipStream_t)stream)));
+    if (max_splits == 1) return PFA_OK;
     pfa::CombineArgs c;
     c.o_part = o_part;
     c.lse_part = lse_part;
@@ -220,6 +225,50 @@ pfa_status pfa_paged_attn_prefill(const pfa_attn_desc* desc, const pfa_kv_pool* 
     c.max_splits = max_splits;
     c.rows_per_seq = max_q_len;
     return hip_status(pfa::launch_combine(c, desc->head_dim, (hipStream_t)stream));
+}
+
+}  // namespace
+
+pfa_status pfa_paged_attn_prefill(const pfa_attn_desc* desc, const pfa_kv_pool* pool, const void* q,
+                                  const int32_t* cu_q, const int32_t* block_table,
+                                  int32_t bt_stride, const int32_t* seq_lens, int32_t batch,
+                                  int32_t max_q_len, int32_t max_seq_len, int32_t split_keys,
+                                  int32_t max_splits, float* o_part, float* lse_part, float* out,
+                                  void* stream) {
+    return prefill_like(desc, pool, q, cu_q, block_table, bt_stride, seq_lens, batch, max_q_len,
+                        max_seq_len, split_keys, max_splits, o_part, lse_part, out, stream,
+                        max_splits > 1);
+}
+
+pfa_status pfa_paged_attn_verify(const pfa_attn_desc* desc, const pfa_kv_pool* pool, const void* q,
+                                 const int32_t* cu_q, const int32_t* block_table,
+                                 int32_t bt_stride, const int32_t* seq_lens, int32_t batch,
+                                 int32_t max_q_len, int32_t max_seq_len, int32_t split_keys,
+                                 int32_t max_splits, float* o_part, float* lse_part, float* out,
+                                 void* stream) {
+    if (max_q_len > 16) return PFA_ERR_SHAPE;
+    return prefill_like(desc, pool, q, cu_q, block_table, bt_stride, seq_lens, batch, max_q_len,
+                        max_seq_len, split_keys, max_splits, o_part, lse_part, out, stream, true);
+}
+
+int32_t pfa_verify_num_splits(const pfa_attn_desc* desc, int32_t batch, int32_t max_q_len,
+                              int32_t max_seq_len, int32_t num_cus, int32_t* split_keys) {
+    if (split_keys) *split_keys = 0;
+    if (!desc || desc->num_kv_heads <= 0 || desc->num_q_heads % desc->num_kv_heads != 0) return 1;
+    const int g = desc->num_q_heads / desc->num_kv_heads;
+    if (!prefill_group_ok(g) || batch <= 0 || max_q_len <= 0 || max_seq_len <= 0) return 1;
+    if (num_cus <= 0) num_cus = 256;
+    const int tps = pfa::kPrefillRowsSplit / g;
+    const int64_t items = (int64_t)batch * desc->num_kv_heads * ((max_q_len + tps - 1) / tps);
+    const int64_t target = 2 * (int64_t)num_cus;
+    if (items >= target || max_seq_len <= 64) return 1;
+    const int64_t want = (target + items - 1) / items;
+    int64_t sk = (max_seq_len + want - 1) / want;
+    sk = std::max<int64_t>(64, (sk + 63) / 64 * 64);
+    const int64_t ns = (max_seq_len + sk - 1) / sk;
+    if (ns <= 1) return 1;
+    if (split_keys) *split_keys = (int32_t)sk;
+    return (int32_t)ns;
 }
 
 int32_t pfa_prefill_num_splits(const pfa_attn_desc* desc, int32_t batch, int32_t max_q_len,

@@ -372,11 +372,15 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a, const 
         pk[h][r / 2] = pack_bf16_rne(p0, p1);
         l_run = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(pk[h][r / 2]), as_bf16x2(0x3F803F80u), l_run, false);
     };
-    // exp_pair pinned in place: the empty asm makes its results exist here, so the
-    // optimiser cannot sink the exps out of the bundle they are meant to fill
-    auto exp_pair_here = [&](const Scores& s, Packed& pk, int q, float nmu) __attribute__((always_inline)) {
-        exp_pair(s, pk, q, nmu);
-        asm volatile("" : "+v"(pk[q / 8][q % 8]), "+v"(l_run));
+    // exps of pairs [qa, qb) pinned to the current bundle: the empty asm makes their
+    // results exist here, so the optimiser cannot sink the exps out of the bundle
+    // they are meant to fill (within the bundle the pairs' chains interleave)
+    auto exp_pairs_here = [&](const Scores& s, Packed& pk, int qa, int qb, float nmu) __attribute__((always_inline)) {
+#pragma unroll
+        for (int q = qa; q < qb; ++q) exp_pair(s, pk, q, nmu);
+#pragma unroll
+        for (int q = qa; q < qb; ++q) asm volatile("" : "+v"(pk[q / 8][q % 8]));
+        asm volatile("" : "+v"(l_run));
     };
     auto softmax = [&](const Scores& s, Packed& pk) __attribute__((always_inline)) {
         const float nmu = (m_run == -INFINITY) ? 0.0f : -m_run;
@@ -410,8 +414,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a, const 
                 // this MFMA's share of the bundle's exps
                 if (EXP) {
                     const int qa = pa + h * (pb - pa) / NH, qb = pa + (h + 1) * (pb - pa) / NH;
-#pragma unroll
-                    for (int q = qa; q < qb; ++q) exp_pair_here(s, pk, q, nmu);
+                    exp_pairs_here(s, pk, qa, qb, nmu);
                 }
             }
             __builtin_amdgcn_sched_barrier(0);
@@ -451,8 +454,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a, const 
             if (FUSED) {
                 if (m < NS - 1) {
                     const int pa = P1 + m * (NP - P1) / (NS - 1), pb = P1 + (m + 1) * (NP - P1) / (NS - 1);
-#pragma unroll
-                    for (int q = pa; q < pb; ++q) exp_pair_here(s, pk, q, nmu);
+                    exp_pairs_here(s, pk, pa, pb, nmu);
                 }
                 if (m > 0) {
 #pragma unroll

@@ -114,6 +114,29 @@ class GpuCase:
         return out.cpu().numpy()
 
 
+    def verify(self, split="auto"):
+        """A verify step over the case's new tokens (<= 16 per sequence); split as in prefill()."""
+        c = self.case
+        Tq, Hq, D = int(c.cu_q[-1]), c.p.num_q_heads, c.p.head_dim
+        max_q, max_len = int(c.q_lens.max()), int(c.seq_lens.max())
+        if split == "auto":
+            ms, sk = pfa.verify_num_splits(self.desc, c.batch, max_q, max_len)
+        elif split is None:
+            ms, sk = 1, 0
+        else:
+            sk, ms = split
+        out = torch.full((Tq, Hq, D), float("nan"), device="cuda")
+        op = lp = None
+        if ms > 1:
+            op = torch.full((Tq, Hq, ms, D), float("nan"), device="cuda")
+            lp = torch.full((Tq, Hq, ms), float("nan"), device="cuda")
+        pfa.paged_attn_verify(self.desc, self.pool, self.q, self.cu_q, self.bt, self.seq_lens, max_q, out,
+                              max_seq_len=max_len, split_keys=sk, max_splits=ms, o_part=op, lse_part=lp)
+        torch.cuda.synchronize()
+        self.last_split = (sk, ms)
+        return out.cpu().numpy()
+
+
 def oracle_pool(case: W.PagedCase) -> dict:
     p = case.p
     pool = O.empty_pool(case.num_pages, p.num_kv_heads, p.page_size, p.head_dim, p.kv_dtype)

@@ -163,3 +163,33 @@ def test_binding_refuses_host_tensors():
     with pytest.raises(ValueError):
         pfa.paged_attn_combine(d, torch.zeros(1), torch.zeros(1), torch.zeros(1, dtype=torch.int32), 16, 1,
                                torch.zeros(1))
+
+
+def ver(d, p, **kw):
+    a = dict(q=FAKE, cu=FAKE, bt=FAKE, stride=64, sl=FAKE, batch=1, mq=16, ml=1024, S=0, ms=1,
+             op=None, lp=None, out=FAKE)
+    a.update(kw)
+    return pfa.lib().pfa_paged_attn_verify(ctypes.byref(d), ctypes.byref(p), a["q"], a["cu"], a["bt"],
+                                           a["stride"], a["sl"], a["batch"], a["mq"], a["ml"], a["S"],
+                                           a["ms"], a["op"], a["lp"], a["out"], None)
+
+
+def test_verify_validation():
+    assert ver(desc(), pool(), mq=17) == SHAPE                               # more than 16 tokens
+    assert ver(desc(kv_dtype=1), pool(k_scale=FAKE.value, v_scale=FAKE.value)) == UNSUP
+    assert ver(desc(), pool(), out=None) == NULL
+    assert ver(desc(), pool(), S=96, ms=11) == SHAPE                         # not a multiple of 64
+    assert ver(desc(), pool(), S=64, ms=15) == WORKSPACE                     # 1024/64 = 16 ranges
+    assert ver(desc(), pool(), S=64, ms=16) == NULL                          # no partial buffers
+    assert ver(desc(), pool(), mq=0, q=None) == OK
+
+
+def test_verify_split_choice_host_only():
+    L = pfa.lib()
+    sk = ctypes.c_int32(-1)
+    # one sequence, 16 tokens on 1024 positions: 64-key ranges spread it over the chip
+    ms = L.pfa_verify_num_splits(ctypes.byref(desc()), 1, 16, 1040, 256, ctypes.byref(sk))
+    assert ms > 1 and sk.value % 64 == 0 and sk.value >= 64 and ms * sk.value >= 1040
+    # enough sequences fill the chip unsplit
+    assert L.pfa_verify_num_splits(ctypes.byref(desc()), 64, 16, 32768, 256, ctypes.byref(sk)) == 1
+    assert sk.value == 0

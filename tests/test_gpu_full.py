@@ -10,7 +10,9 @@ Workloads:
   and 130 new tokens on a restored 8192-token prefix;
 * INT8-KV decode, Qwen3-30B-A3B attention (32/4, D 128), batch 8 at 32768 positions;
 * gpt-oss-20b attention (64/8, D 64, sinks), window-128 and full layers: batch-64
-  decode with lengths log-uniform in [128, 32768], and two 2048-token prefills.
+  decode with lengths log-uniform in [128, 32768], and two 2048-token prefills;
+* verify steps on Qwen3-4B attention: 16 tokens at 1,024 positions (one sequence),
+  and 8 tokens per sequence on batch 32 with contexts U[512, 8192].
 """
 import numpy as np
 import pytest
@@ -37,10 +39,10 @@ def _decode_check(case, splits=(256,)):
         assert_close(g.decode(S), ref, tol_of(case), f"{case.name} S={S}")
 
 
-def _prefill_check(case, sample=None, seed=0):
+def _prefill_check(case, sample=None, seed=0, verify=False):
     print(f"[full] {case.name}: q_tokens={int(case.cu_q[-1])}", flush=True)
     g = GpuCase(case)
-    got = g.prefill()
+    got = g.verify() if verify else g.prefill()
     Tq = int(case.cu_q[-1])
     if sample is None or sample >= Tq:
         rows = np.arange(Tq)
@@ -93,3 +95,11 @@ def test_mixed_gptoss_decode(layer):
 @pytest.mark.parametrize("layer", ["window", "full"])
 def test_mixed_gptoss_prefill(layer):
     _prefill_check(W.mixed_gptoss(layer=layer, part="prefill"), sample=256)
+
+
+def test_verify_16tok_ctx1024():
+    _prefill_check(W.verify_qwen4b(), verify=True)
+
+
+def test_verify_8tok_batch32_ctx512_8192():
+    _prefill_check(W.verify_qwen4b(batch=32, tokens=8, lo=512, hi=8192), verify=True)

@@ -179,6 +179,34 @@ def test_prefill_split_choice():
     assert pfa.prefill_num_splits(d, 1, 8192, 8192) == (1, 0)
 
 
+VERIFY_CASES = [
+    # (params, seq_lens, q_lens): 2-16 new tokens per sequence on cached contexts
+    (dict(Hq=32, Hkv=8, D=128), [1040], [16]),                           # 16 tokens at 1,024 positions
+    (dict(Hq=32, Hkv=8, D=128), [39, 1002, 300, 2], [2, 2, 2, 2]),       # ragged; a 2-token sequence
+    (dict(Hq=64, Hkv=8, D=64, window=128, sinks=True), [709, 3009], [9, 9]),
+    (dict(Hq=8, Hkv=8, D=128, sinks=True), [518, 777], [5, 16]),
+    (dict(Hq=32, Hkv=2, D=64), [1500], [8]),                             # G = 16: 128 rows
+]
+
+
+@pytest.mark.parametrize("ci", range(len(VERIFY_CASES)))
+def test_verify_parity(ci):
+    prm, lens, qlens = VERIFY_CASES[ci]
+    case = W.make_case(f"ver{ci}", 300 + ci, P(seed=40 + ci, **prm), lens, qlens, split_keys=0)
+    g = GpuCase(case)
+    ref = O.paged_attention(case.q, case.cu_q, oracle_pool(case), case.block_table, case.seq_lens, case.p)
+    for split in ("auto", None, (64, -(-max(lens) // 64)), (320, -(-max(lens) // 320))):
+        got = g.verify(split=split)
+        assert_close(got, ref, BF16_TOL, f"verify case {ci} split={split} ({g.last_split})")
+
+
+def test_verify_split_choice():
+    d = pfa.AttnDesc(32, 8, 128)
+    ms, sk = pfa.verify_num_splits(d, 1, 16, 1040)
+    assert ms > 1 and sk % 64 == 0 and ms * sk >= 1040
+    assert pfa.verify_num_splits(d, 64, 16, 32768) == (1, 0)
+
+
 # ---------------------------------------------------------------------------
 # invariants on the GPU
 # ---------------------------------------------------------------------------

@@ -265,3 +265,20 @@ def mixed_gptoss(seed=5, layer="window", part="decode", batch=64, lo=128, hi=327
                          split_keys=256)
     lens = np.full(chunks, chunk_len, np.int32)
     return make_case(f"mixed_{layer}_prefill_{chunks}x{chunk_len}", seed, p, lens, lens, split_keys=0)
+
+
+def verify_qwen4b(seed=6, batch=1, tokens=16, ctx=1024, lo=None, hi=None):
+    """A speculative-decoding verify step on the Qwen3-4B attention shape (32 q / 8
+    KV heads, D 128): ``tokens`` new tokens per sequence (the last accepted token
+    plus tokens-1 drafted ones) on a cached context of ``ctx`` positions, or of
+    lengths U[lo, hi] when both are given."""
+    p = AttnParams(32, 8, 128)
+    if lo is not None and hi is not None:
+        rng = np.random.default_rng(seed + 13)
+        ctxs = uniform_int_lens(rng, batch, lo, hi)
+        name = f"verify_{tokens}tok_batch{batch}_ctx{lo}_{hi}"
+    else:
+        ctxs = np.full(batch, ctx, np.int32)
+        name = f"verify_{tokens}tok_batch{batch}_ctx{ctx}"
+    q_lens = np.full(batch, tokens, np.int32)
+    return make_case(name, seed, p, ctxs + q_lens, q_lens, split_keys=0)
