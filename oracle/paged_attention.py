@@ -210,7 +210,7 @@ def attend(q: np.ndarray, pos: np.ndarray, K: np.ndarray, V: np.ndarray, params,
         g = h // G
         x = params.sm_scale * (q[:, h, :] @ K[:, g, :].T)          # [rows, n_keys]
         x = np.where(vis, x, NEG_INF)
-        m = np.where(has, x.max(axis=1), NEG_INF)                  # max over visible keys
+        m = np.where(has, x.max(axis=1, initial=NEG_INF), NEG_INF)  # max over visible keys (-inf if none)
         M = np.maximum(m, float(params.sinks[h])) if use_sink else m
         Ms = np.where(np.isfinite(M), M, 0.0)
         p = np.where(vis, np.exp(x - Ms[:, None]), 0.0)            # exp(x_j - M)

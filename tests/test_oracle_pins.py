@@ -188,6 +188,18 @@ def test_one_key_with_sink():
     np.testing.assert_allclose(out[0, 0], w * V[0, 0], rtol=1e-14)
 
 
+def test_no_keys_gives_zero():
+    """A row with no keys at all (an empty sequence) outputs 0, sink or not, and
+    its split statistics are m = -inf, l = 0."""
+    q = np.array([[[1.0, -2.0, 0.5, 3.0]]])
+    K = np.zeros((0, 1, 4))
+    V = np.zeros((0, 1, 4))
+    for sinks in (None, np.array([0.3], np.float32)):
+        out, m, l = O.attend(q, np.array([-1]), K, V, _dense_params(sinks=sinks, scale=1.0))
+        assert np.array_equal(out, np.zeros((1, 1, 4)))
+        assert np.isneginf(m).all() and np.array_equal(l, np.zeros((1, 1)))
+
+
 def test_sink_at_minus_infinity_is_no_sink():
     case = tiny_case(3, [6, 4], [3, 1], sinks=True)
     pool = fill_pool(case)
