@@ -130,7 +130,8 @@ pfa_status pfa_kv_write(const pfa_attn_desc* desc, const pfa_kv_pool* pool,
  *   Otherwise, for every split i < ceil(seq_lens[s]/S), it writes:
  *     o_part   [batch][Hq][max_splits][D] fp32, the softmax-normalised partial output;
  *     lse_part [batch][Hq][max_splits] fp32, the natural log-sum-exp of the split's
- *              visible scores, or -inf when the window hides the whole split.
+ *              visible scores, or -inf when the window hides the whole split;
+ *              the o_part rows of such a split are left unwritten.
  *   Partials never include the sink, and out is left untouched.  Then call
  *   pfa_paged_attn_combine.
  */
@@ -146,6 +147,7 @@ pfa_status pfa_paged_attn_decode(const pfa_attn_desc* desc, const pfa_kv_pool* p
  *     M   = max(max_i lse_i, sink_h)
  *     out = sum_i e^(lse_i - M) o_i / (sum_i e^(lse_i - M) + e^(sink_h - M))
  *   The sink terms appear only when desc->sinks != NULL.  out is [batch][Hq][D] fp32.
+ *   The o_part rows of the leading splits with lse -inf are not read.
  */
 pfa_status pfa_paged_attn_combine(const pfa_attn_desc* desc, const float* o_part,
                                   const float* lse_part, const int32_t* seq_lens, int32_t batch,

@@ -99,6 +99,8 @@ pfa_status pfa_paged_attn_decode(const pfa_attn_desc* desc, const pfa_kv_pool* p
         desc->num_kv_heads > 65535)
         return PFA_ERR_SHAPE;
     if (max_seq_len > (int64_t)bt_stride * desc->page_size) return PFA_ERR_SHAPE;
+    // one 64-lane workgroup per (split run, KV head, sequence) in a 1-D grid
+    if ((int64_t)max_splits * desc->num_kv_heads * batch > (int64_t)1 << 26) return PFA_ERR_SHAPE;
     if (batch == 0) return PFA_OK;
     if (!q || !block_table || !seq_lens) return PFA_ERR_NULL;
     if (max_splits == 1) {

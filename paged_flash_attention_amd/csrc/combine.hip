@@ -9,7 +9,8 @@
 // The sink terms appear only when sinks are given.  For decode a row is a
 // sequence, and its ceil(len/S) splits are merged.  For split prefill a row is a
 // query token, located through cu_rows, and all max_splits are merged; splits with
-// no visible key carry lse = -inf and weigh 0.
+// no visible key carry lse = -inf and weigh 0.  The leading run of such splits
+// is skipped without reading its o rows.
 //
 // One 64-lane wave per (row, h):
 //  * the lanes take the splits' lse values in parallel for the max and the weight
@@ -45,9 +46,17 @@ __global__ __launch_bounds__(64) void combine_kernel(CombineArgs a) {
     const float* lse = a.lse_part + (int64_t)bh * a.max_splits;
     const float* op = a.o_part + (int64_t)bh * a.max_splits * D;
 
+    // max, and the first split with a visible key: decode leaves the o rows of the
+    // splits a window hides (always a prefix) unwritten, so they are never read
     float m = -INFINITY;
-    for (int i = lane; i < ns; i += kWave) m = fmaxf(m, lse[i]);
+    float first = (float)ns;
+    for (int i = lane; i < ns; i += kWave) {
+        const float l = lse[i];
+        m = fmaxf(m, l);
+        if (l != -INFINITY) first = fminf(first, (float)i);
+    }
     m = stride_max<1>(m);
+    const int i_first = (int)-stride_max<1>(-first);
     const bool has_sink = a.sinks != nullptr;
     const float sink = has_sink ? __ldg(a.sinks + h) : -INFINITY;
     m = fmaxf(m, sink);
@@ -58,7 +67,7 @@ __global__ __launch_bounds__(64) void combine_kernel(CombineArgs a) {
 #pragma unroll
     for (int e = 0; e < E; ++e) acc[e] = 0.0f;
     float wsum = 0.0f;
-    for (int base = 0; base < ns; base += kMaxLdsSplits) {
+    for (int base = i_first; base < ns; base += kMaxLdsSplits) {
         const int cnt = min(ns - base, kMaxLdsSplits);
         for (int i = lane; i < cnt; i += kWave) {
             const float w = __expf(lse[base + i] - ms);      // 0 for lse = -inf

@@ -10,14 +10,22 @@
 //
 // MI355X design.  The kernel is HBM-bound, and each K/V element is used by exactly
 // one lane group, so K/V go straight from HBM to registers:
-//  * One wave per (split, KV head, sequence) streams the split's pages.  The kernel
-//    is written for kNW waves per split, taking every kNW-th page and merging
-//    through LDS; kNW = 1 measured fastest.  The G = Hq/Hkv query heads of the
+//  * One wave per (split, KV head, sequence) streams the split's pages, with the
+//    next page always in flight.  The grid is 1-D with the KV head fastest, then
+//    the split, then the sequence: workgroup i runs on XCD i % 8, so each XCD
+//    gets the same share of every sequence, and the KV-head blocks of a page are
+//    read at about the same time.  Measured alternatives, all slower on some
+//    workload: the split fastest (XCD imbalance on ragged batches: split i always
+//    lands on XCD i % 8), the sequence fastest, several waves per split, several
+//    splits per wave, and a balanced persistent schedule over resident waves,
+//    static or through an atomic work counter.  The G = Hq/Hkv query heads of the
 //    group share every page read (GQA packing).
 //  * Page-head block = 16 keys x D.  A lane loads 8 consecutive elements of one key
 //    per load (16 B for bf16, 8 B for int8).  LPK = D/8 lanes cover a key, and one
 //    load instruction covers a contiguous 512*elem-byte run.  The wave's next page
-//    is prefetched while the current one is consumed.
+//    is prefetched while the current one is consumed; two pages in flight (the
+//    loop unrolled over two register buffers) measured no faster, as the
+//    device's HBM is already saturated with one per wave.
 //  * q.k: v_dot2_f32_bf16 on (q, k) bf16 pairs.  INT8 codes are offset to the
 //    unsigned byte c+128 (v_cvt_f32_ubyteN, exact in bf16), and 128*sum(q) is
 //    subtracted from the dot.  A lane's partial dots for the G heads go through a
@@ -34,21 +42,14 @@
 //      - INT8: p*scale_v*2^12 in fp16, with the code pairs built by a byte
 //        permute into fp16 (1024 + u).  The 1152 offset is removed by a packed
 //        fp16 add, which is exact.
-//  * At the end each wave reduces its partial o across key groups.  The waves merge
-//    through LDS, and the workgroup writes o/l with lse = ln(sum e^s) (split mode),
-//    or the final output with the sink (unsplit mode).
+//  * At the end of a split each wave reduces its partial o across key groups and
+//    writes o/l with lse = ln(sum e^s) (split mode), or the final output with the
+//    sink (unsplit mode).
 #include "pfa_device.h"
 
 namespace pfa {
 namespace {
 
-// Waves per workgroup.  Each split is one page stream; measured on MI355X, 2 or 4
-// waves per split (each taking every 2nd/4th page, merged through LDS) were 1-30%
-// slower on every workload: shorter streams expose more first-page latency than
-// they save in the ragged tail.
-constexpr int kNW = 1;
-
-typedef __fp16 h2v __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
 template <bool INT8> struct Chunk;
@@ -154,7 +155,7 @@ __device__ __forceinline__ float lane_read(float v, int l) {
 }
 
 template <int D, int G, bool INT8, bool FINAL>
-__global__ __launch_bounds__(kNW * 64)
+__global__ __launch_bounds__(kWave)
 void decode_kernel(DecodeArgs a) {
     constexpr int EB = INT8 ? 1 : 2;           // bytes per element
     constexpr int LPK = D / 8;                 // lanes per key
@@ -166,51 +167,49 @@ void decode_kernel(DecodeArgs a) {
     static_assert(!PAIRED || NLOAD % 2 == 0, "key pairs");
     typedef typename Chunk<INT8>::T CT;
 
-    __shared__ __attribute__((aligned(16))) float p_buf[kNW][2][kPage][G];
-    __shared__ float m_sh[kNW][G], l_sh[kNW][G];
-    __shared__ float o_sh[kNW][G][D];
+    __shared__ __attribute__((aligned(16))) float p_buf[2][kPage][G];
 
-    const int tid = threadIdx.x;
-    const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
-    const int lane = tid % kWave;
+    const int lane = threadIdx.x;
     const int sub = lane % LPK;
     const int kg = lane / LPK;
     const int myhead = sub / HG;
-    const int split = blockIdx.x;
-    const int kvh = blockIdx.y;
-    const int b = blockIdx.z;
     const int Hq = a.num_q_heads;
+    const int Hkv = a.num_kv_heads;
+    // 1-D grid, KV head fastest, then split, then sequence.  Workgroup i runs on
+    // XCD i % 8, so every XCD gets the same share of every sequence whatever the
+    // lengths; the KV heads of one page are read at about the same time, and a
+    // sequence's splits are dispatched together.
+    const int kvh = blockIdx.x % Hkv;
+    const int sp = FINAL ? 0 : (blockIdx.x / Hkv) % a.max_splits;
+    const int b = FINAL ? blockIdx.x / Hkv : blockIdx.x / (Hkv * a.max_splits);
     const int head0 = kvh * G;
+    const int64_t row0 = (int64_t)b * Hq + head0;                // (b, head0)
 
     int len = __ldg(a.seq_lens + b);
-    len = min(len, a.bt_stride * kPage);
-    int lo = 0, hi = len;
-    if (a.window > 0) lo = max(0, len - a.window);
-    if constexpr (!FINAL) {
-        const int s0 = split * a.split_keys;
-        if (s0 >= len || split >= a.max_splits) return;
+    len = min(max(len, 0), a.bt_stride * kPage);
+    int lo = a.window > 0 ? max(0, len - a.window) : 0;         // first visible key
+    int hi = len;
+    if constexpr (FINAL) {
+        if (lo >= hi) {   // no keys: output 0
+            for (int e = lane; e < G * D; e += kWave) a.out[row0 * D + e] = 0.0f;
+            return;
+        }
+    } else {
+        const int s0 = sp * a.split_keys;
+        if (s0 >= len) return;
+        if (s0 + a.split_keys <= lo) {   // the window hides the whole split
+            if (lane < G) a.lse_part[(row0 + lane) * a.max_splits + sp] = -INFINITY;
+            return;
+        }
         lo = max(lo, s0);
         hi = min(hi, s0 + a.split_keys);
-    }
-    const int64_t part_row = ((int64_t)b * Hq + head0) * a.max_splits + split;  // (b, head0, split)
-
-    if (lo >= hi) {
-        if constexpr (!FINAL) {
-            // the window hides the whole split: empty partial
-            for (int e = tid; e < G * D; e += kNW * kWave) {
-                const int g = e / D, d = e % D;
-                a.o_part[(part_row + (int64_t)g * a.max_splits) * D + d] = 0.0f;
-            }
-            if (tid < G) a.lse_part[part_row + (int64_t)tid * a.max_splits] = -INFINITY;
-        }
-        return;
     }
 
     // q: slot j holds head (j ^ myhead), dims sub*8 .. sub*8+7, as bf16 pairs
     uint32_t q[G][4];
 #pragma unroll
     for (int j = 0; j < G; ++j) {
-        const uint16_t* qp = a.q + ((int64_t)b * Hq + head0 + (j ^ myhead)) * D + sub * 8;
+        const uint16_t* qp = a.q + (row0 + (j ^ myhead)) * D + sub * 8;
         const uint4 v = *reinterpret_cast<const uint4*>(qp);
         q[j][0] = v.x; q[j][1] = v.y; q[j][2] = v.z; q[j][3] = v.w;
     }
@@ -229,6 +228,7 @@ void decode_kernel(DecodeArgs a) {
     const float c2 = a.sm_scale * kLog2e;      // scores kept in log2 units
     // INT8 paired p.v carries p*scale_v*2^12 in fp16; undone at the end
     constexpr float kPScale = 4096.0f;
+    constexpr float kOScale = (INT8 && PAIRED) ? 1.0f / kPScale : 1.0f;
 
     const int p0 = lo / kPage, p1 = (hi - 1) / kPage;
     const int32_t* bt = a.block_table + (int64_t)b * a.bt_stride;
@@ -242,7 +242,7 @@ void decode_kernel(DecodeArgs a) {
     auto load_page = [&](int p) {
         int id = __ldg(bt + p);
         id = min(max(id, 0), a.num_pages - 1);
-        const int64_t blk = (int64_t)id * a.num_kv_heads + kvh;
+        const int64_t blk = (int64_t)id * Hkv + kvh;
         const char* kp = kbase + blk * head_stride * EB + lane_off;
         const char* vp = vbase + blk * head_stride * EB + lane_off;
 #pragma unroll
@@ -268,8 +268,8 @@ void decode_kernel(DecodeArgs a) {
     float l_run = 0.0f;        // this lane's share of sum 2^(s - m_run) (its keys, its head)
 
     int pb = 0;
-    if (p0 + wave <= p1) load_page(p0 + wave);
-    for (int p = p0 + wave; p <= p1; p += kNW) {
+    load_page(p0);
+    for (int p = p0; p <= p1; ++p) {
         CT kcur[NLOAD], vcur[NLOAD];
         float kscur[NLOAD], vscur[NLOAD];
 #pragma unroll
@@ -277,7 +277,7 @@ void decode_kernel(DecodeArgs a) {
             kcur[i] = kc[i]; vcur[i] = vc[i];
             kscur[i] = ksc[i]; vscur[i] = vsc[i];
         }
-        if (p + kNW <= p1) load_page(p + kNW);
+        if (p < p1) load_page(p + 1);
 
         const int kpos0 = p * kPage;
         const bool full = kpos0 >= lo && kpos0 + kPage <= hi;
@@ -329,7 +329,7 @@ void decode_kernel(DecodeArgs a) {
             l_run += pw;
             float pv = pw;
             if constexpr (INT8) pv = valid[i] ? pw * vscur[i] * (PAIRED ? kPScale : 1.0f) : 0.0f;
-            if (sub % HG == 0) p_buf[wave][pb][i * KPL + kg][myhead] = pv;
+            if (sub % HG == 0) p_buf[pb][i * KPL + kg][myhead] = pv;
         }
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
@@ -347,7 +347,7 @@ void decode_kernel(DecodeArgs a) {
             for (int i = 0; i < NLOAD; ++i) {
                 float pw[G];
 #pragma unroll
-                for (int g = 0; g < G; ++g) pw[g] = p_buf[wave][pb][i * KPL + kg][g];
+                for (int g = 0; g < G; ++g) pw[g] = p_buf[pb][i * KPL + kg][g];
                 float x[8];
                 v_floats(vcur[i], x);
 #pragma unroll
@@ -363,8 +363,8 @@ void decode_kernel(DecodeArgs a) {
                 float pa[G], pbv[G];
 #pragma unroll
                 for (int g = 0; g < G; ++g) {
-                    pa[g] = p_buf[wave][pb][i * KPL + kg][g];
-                    pbv[g] = p_buf[wave][pb][(i + 1) * KPL + kg][g];
+                    pa[g] = p_buf[pb][i * KPL + kg][g];
+                    pbv[g] = p_buf[pb][(i + 1) * KPL + kg][g];
                 }
 #pragma unroll
                 for (int g = 0; g < G; ++g) {
@@ -385,60 +385,42 @@ void decode_kernel(DecodeArgs a) {
         pb ^= 1;
     }
 
-    // ---- per wave: reduce across key groups, publish (m, l, o) ----
+    // ---- reduce across key groups; head g's row is written by the lanes of key
+    // group g % KPL ----
 #pragma unroll
     for (int g = 0; g < G; ++g)
 #pragma unroll
         for (int j = 0; j < 8; ++j) o[g][j] = stride_sum<LPK>(o[g][j]);
     const float l_tot = stride_sum<LPK>(l_run);
-    constexpr float kOScale = (INT8 && PAIRED) ? 1.0f / kPScale : 1.0f;
 #pragma unroll
     for (int g = 0; g < G; ++g) {
-        if (g % KPL == kg) {
-            float* dst = &o_sh[wave][g][sub * 8];
-#pragma unroll
-            for (int j = 0; j < 8; ++j) dst[j] = o[g][j] * kOScale;
-        }
-        if (lane == g * HG) {
-            m_sh[wave][g] = m_run;
-            l_sh[wave][g] = l_tot;
-        }
-    }
-    __syncthreads();
-
-    // ---- merge the four waves ----
-    for (int e = tid; e < G * D; e += kNW * kWave) {
-        const int g = e / D, d = e % D;
-        float M = m_sh[0][g];
-#pragma unroll
-        for (int w = 1; w < kNW; ++w) M = fmaxf(M, m_sh[w][g]);
-        const float Ms = (M == -INFINITY) ? 0.0f : M;
-        float num = 0.0f, den = 0.0f;
-#pragma unroll
-        for (int w = 0; w < kNW; ++w) {
-            const float f = fast_exp2(m_sh[w][g] - Ms);      // 0 for a wave with no pages
-            num = fmaf(f, o_sh[w][g][d], num);
-            den = fmaf(f, l_sh[w][g], den);
-        }
+        const float mg = lane_read(m_run, g * HG);
+        const float lg = lane_read(l_tot, g * HG);
+        float den = lg;
         if constexpr (FINAL) {
-            if (a.sinks) den += fast_exp2(__ldg(a.sinks + head0 + g) * kLog2e - Ms);
-            a.out[((int64_t)b * Hq + head0 + g) * D + d] = den > 0.0f ? num / den : 0.0f;
-        } else {
-            a.o_part[(part_row + (int64_t)g * a.max_splits) * D + d] = num / den;
-            if (d == 0) a.lse_part[part_row + (int64_t)g * a.max_splits] = (M + fast_log2(den)) * kLn2;
+            if (a.sinks) den += fast_exp2(__ldg(a.sinks + head0 + g) * kLog2e - mg);
+        }
+        const float f = (FINAL && !(den > 0.0f)) ? 0.0f : kOScale / den;
+        if (g % KPL == kg) {
+            float* dst = FINAL ? a.out + (row0 + g) * D + sub * 8
+                               : a.o_part + ((row0 + g) * a.max_splits + sp) * D + sub * 8;
+            float4* d4 = reinterpret_cast<float4*>(dst);
+            d4[0] = make_float4(o[g][0] * f, o[g][1] * f, o[g][2] * f, o[g][3] * f);
+            d4[1] = make_float4(o[g][4] * f, o[g][5] * f, o[g][6] * f, o[g][7] * f);
+        }
+        if constexpr (!FINAL) {
+            if (lane == 0) a.lse_part[(row0 + g) * a.max_splits + sp] = (mg + fast_log2(lg)) * kLn2;
         }
     }
 }
 
 template <int D, int G, bool INT8>
 hipError_t launch_dg(const DecodeArgs& a, hipStream_t s) {
-    if (a.max_splits == 1) {
-        hipLaunchKernelGGL((decode_kernel<D, G, INT8, true>), dim3(1, a.num_kv_heads, a.batch),
-                           dim3(kNW * kWave), 0, s, a);
-    } else {
-        hipLaunchKernelGGL((decode_kernel<D, G, INT8, false>),
-                           dim3(a.max_splits, a.num_kv_heads, a.batch), dim3(kNW * kWave), 0, s, a);
-    }
+    const int rows = a.num_kv_heads * a.batch;
+    if (a.max_splits == 1)
+        hipLaunchKernelGGL((decode_kernel<D, G, INT8, true>), dim3(rows), dim3(kWave), 0, s, a);
+    else
+        hipLaunchKernelGGL((decode_kernel<D, G, INT8, false>), dim3(a.max_splits * rows), dim3(kWave), 0, s, a);
     return hipGetLastError();
 }
 

@@ -109,6 +109,36 @@ def test_decode_parity(ci):
         assert_close(got, ref, tol_of(case), f"decode case {ci} S={S}")
 
 
+# Many 16-key splits: several times more workgroups than the device holds at once,
+# ragged lengths, and a window that hides a prefix of splits.
+_rng = np.random.default_rng(77)
+MANY_SPLIT_CASES = [
+    (dict(Hq=32, Hkv=8, D=128, window=100, sinks=True), list(_rng.integers(1, 1200, 40)), 16),
+    (dict(Hq=32, Hkv=4, D=128, kv="int8"), list(_rng.integers(1, 2500, 30)), 16),
+    (dict(Hq=64, Hkv=8, D=64, sinks=True), list(_rng.integers(1, 1500, 48)), 16),
+]
+
+
+@pytest.mark.parametrize("ci", range(len(MANY_SPLIT_CASES)))
+def test_decode_many_splits(ci):
+    prm, lens, S = MANY_SPLIT_CASES[ci]
+    case = W.make_case(f"many{ci}", 150 + ci, P(seed=ci, **prm), lens, np.ones(len(lens), np.int32),
+                       outlier_frac=0.01 if prm.get("kv") == "int8" else 0.0)
+    g = GpuCase(case)
+    ref = O.decode(case.q, oracle_pool(case), case.block_table, case.seq_lens, case.p)
+    assert_close(g.decode(split_keys=S), ref, tol_of(case), f"many-split case {ci}")
+
+
+def test_decode_batch_600():
+    """A large batch of short windowed sequences with sinks."""
+    rng = np.random.default_rng(78)
+    lens = list(rng.integers(1, 300, 600))
+    case = W.make_case("bigbatch", 160, P(8, 2, 64, window=90, sinks=True), lens, np.ones(600, np.int32))
+    g = GpuCase(case)
+    ref = O.decode(case.q, oracle_pool(case), case.block_table, case.seq_lens, case.p)
+    assert_close(g.decode(split_keys=64), ref, BF16_TOL, "batch 600")
+
+
 def test_decode_partials_match_oracle():
     prm = dict(Hq=32, Hkv=8, D=128, window=300, sinks=True)
     lens = [10, 256, 257, 900]
