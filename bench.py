@@ -338,6 +338,7 @@ def main():
     builders = {
         "decode_batch32_ctx512_8192": lambda: W.decode_batch32_ctx512_8192(),
         "decode_batch32_ctx8192": lambda: W.decode_batch32_ctx512_8192(fixed_len=8192),
+        "decode_batch32_ctx8192_s1024": lambda: W.decode_batch32_ctx512_8192(fixed_len=8192, split_keys=1024),
         "decode_1seq_ctx1024": lambda: W.decode_1seq_ctx1024(),
         "decode_int8_batch8_ctx32768": lambda: W.decode_int8_qwen30b(),
         "mixed_full_decode_b64": lambda: W.mixed_gptoss(layer="full", part="decode"),
@@ -397,7 +398,8 @@ def main():
 
     extra = {}
     if not args.no_extra and args.workload == "decode_batch32_ctx512_8192":
-        for name, st in (("decode_batch32_ctx8192", 30), ("decode_int8_batch8_ctx32768", 30),
+        for name, st in (("decode_batch32_ctx8192", 30), ("decode_batch32_ctx8192_s1024", 30),
+                         ("decode_int8_batch8_ctx32768", 30),
                          ("mixed_full_decode_b64", 30), ("prefill_causal_8192", 10),
                          ("prefill_chunk130_on_8192", 20), ("mixed_full_prefill_2x2048", 20),
                          ("verify_16tok_batch1_ctx1024", 50), ("verify_8tok_batch32_ctx512_8192", 30)):

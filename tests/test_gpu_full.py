@@ -68,7 +68,8 @@ def test_decode_batch32_ctx512_8192():
 
 
 def test_decode_batch32_ctx8192():
-    _decode_check(W.decode_batch32_ctx512_8192(fixed_len=8192))
+    """256-key splits (the workload's), and 1024-key splits (the bench's target-sweep line)."""
+    _decode_check(W.decode_batch32_ctx512_8192(fixed_len=8192), splits=(256, 1024))
 
 
 def test_prefill_causal_1024():

@@ -223,15 +223,18 @@ def decode_1seq_ctx1024(seed=1, split_keys=256):
                      split_keys=split_keys)
 
 
-def decode_batch32_ctx512_8192(seed=2, batch=32, lo=512, hi=8192, fixed_len=None):
+def decode_batch32_ctx512_8192(seed=2, batch=32, lo=512, hi=8192, fixed_len=None, split_keys=256):
     """Qwen3-4B attention shape (32 q / 8 KV heads, D 128); batch 32, lengths
-    U[512, 8192] (or all ``fixed_len``); 256-key splits."""
+    U[512, 8192] (or all ``fixed_len``); 256-key splits unless ``split_keys`` says
+    otherwise (the name then ends in ``_s<split_keys>``)."""
     rng = np.random.default_rng(seed + 7)
     lens = (np.full(batch, fixed_len, np.int32) if fixed_len
             else uniform_int_lens(rng, batch, lo, hi))
     p = AttnParams(32, 8, 128)
     name = f"decode_batch{batch}_ctx{fixed_len}" if fixed_len else f"decode_batch{batch}_ctx{lo}_{hi}"
-    return make_case(name, seed, p, lens, np.ones(batch, np.int32), split_keys=256)
+    if split_keys != 256:
+        name += f"_s{split_keys}"
+    return make_case(name, seed, p, lens, np.ones(batch, np.int32), split_keys=split_keys)
 
 
 def prefill_llama8b(seed=3, prompt=1024, prefix=0):
