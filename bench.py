@@ -165,7 +165,9 @@ def setup_case(case, torch, pfa, gs, copies_for_bytes=ROTATE_BYTES):
     return g, pools, new
 
 
-def run_decode(case, torch, pfa, gs, steps, warmup):
+def run_decode(case, torch, pfa, gs, steps, warmup, fused=False):
+    """Decode steps: kv_write + split decode + combine, or with fused=True kv_write +
+    pfa_paged_attn_decode_fused (the combine merged into the split kernel)."""
     g, pools, (kn, vn, cun) = setup_case(case, torch, pfa, gs)
     p = case.p
     B, Hq, D = case.batch, p.num_q_heads, p.head_dim
@@ -175,12 +177,17 @@ def run_decode(case, torch, pfa, gs, steps, warmup):
     op = torch.empty((B, Hq, ms, D), device="cuda")
     lp = torch.empty((B, Hq, ms), device="cuda")
     out = torch.empty((B, Hq, D), device="cuda")
+    ctr = torch.zeros(B * p.num_kv_heads, dtype=torch.int32, device="cuda")
     tm = Timer(torch)
 
     def step(i):
         pool = pools[i % len(pools)]
         pfa.kv_write(g.desc, pool, kn, vn, cun, g.seq_lens, g.bt)
         e = tm.mark("decode")
+        if fused:
+            pfa.paged_attn_decode_fused(g.desc, pool, g.q, g.bt, g.seq_lens, max_len, S, ms, op, lp, ctr, out)
+            tm.close("decode", e)
+            return
         pfa.paged_attn_decode(g.desc, pool, g.q, g.bt, g.seq_lens, max_len, S, ms, o_part=op, lse_part=lp)
         tm.close("decode", e)
         pfa.paged_attn_combine(g.desc, op, lp, g.seq_lens, S, ms, out)
@@ -339,6 +346,7 @@ def main():
         "decode_batch32_ctx512_8192": lambda: W.decode_batch32_ctx512_8192(),
         "decode_batch32_ctx8192": lambda: W.decode_batch32_ctx512_8192(fixed_len=8192),
         "decode_batch32_ctx8192_s1024": lambda: W.decode_batch32_ctx512_8192(fixed_len=8192, split_keys=1024),
+        "decode_batch32_ctx512_8192_fused": lambda: W.decode_batch32_ctx512_8192(),
         "decode_1seq_ctx1024": lambda: W.decode_1seq_ctx1024(),
         "decode_int8_batch8_ctx32768": lambda: W.decode_int8_qwen30b(),
         "mixed_full_decode_b64": lambda: W.mixed_gptoss(layer="full", part="decode"),
@@ -370,7 +378,7 @@ def main():
             r.update(metric="prefill attn TFLOP/s", kernel_tflops=round(tf, 2),
                      frac_of_mfma_peak=round(tf / BF16_PEAK_TFLOPS, 4))
         else:
-            r = run_decode(case, torch, pfa, gs, steps, warmup)
+            r = run_decode(case, torch, pfa, gs, steps, warmup, fused=name.endswith("_fused"))
             gbs = r["decode_bytes"] / (r["decode_ms"] * 1e-3) / 1e9
             r.update(metric="decode attn GB/s", kernel_gbs=round(gbs, 1),
                      decode_us=round(r["decode_ms"] * 1e3, 2), frac_of_hbm_peak=round(gbs / HBM_PEAK_GBS, 4))
@@ -398,7 +406,8 @@ def main():
 
     extra = {}
     if not args.no_extra and args.workload == "decode_batch32_ctx512_8192":
-        for name, st in (("decode_batch32_ctx8192", 30), ("decode_batch32_ctx8192_s1024", 30),
+        for name, st in (("decode_batch32_ctx512_8192_fused", 50),
+                         ("decode_batch32_ctx8192", 30), ("decode_batch32_ctx8192_s1024", 30),
                          ("decode_int8_batch8_ctx32768", 30),
                          ("mixed_full_decode_b64", 30), ("prefill_causal_8192", 10),
                          ("prefill_chunk130_on_8192", 20), ("mixed_full_prefill_2x2048", 20),
@@ -414,7 +423,8 @@ def main():
                                        frac_of_mfma_peak=rr["frac_of_mfma_peak"])
                 else:
                     extra[name] = dict(us=rr["decode_us"], gbs=rr["kernel_gbs"],
-                                       frac_of_hbm_peak=rr["frac_of_hbm_peak"])
+                                       frac_of_hbm_peak=rr["frac_of_hbm_peak"],
+                                       step_us=round(rr["step_ms"] * 1e3, 2))
             except Exception as e:   # report, never hide
                 extra[name] = dict(error=str(e)[:200])
             torch.cuda.empty_cache()

@@ -142,6 +142,33 @@ pfa_status pfa_paged_attn_decode(const pfa_attn_desc* desc, const pfa_kv_pool* p
                                  float* o_part, float* lse_part, float* out, void* stream);
 
 /*
+ * pfa_paged_attn_decode_fused: decode with the combine fused into the split
+ *   kernel, through an acquire-release counter per (sequence, KV head): the
+ *   variant the TileInfer.jl performance page ("Fused kernels, FlashAttention and
+ *   PagedAttention") measured and did not keep.  Arguments as
+ *   pfa_paged_attn_decode, plus:
+ *
+ *   counters       device [batch][Hkv] int32, all zero on entry.  The call leaves
+ *                  them zero when it completes, so one zeroed array serves every
+ *                  later call on the same stream.  Calls that may run at the same
+ *                  time (other streams) need arrays of their own.
+ *   out            device [batch][Hq][D] fp32, always written.
+ *
+ *   Each split writes its partial to o_part / lse_part as in pfa_paged_attn_decode,
+ *   then adds one to its counter after an agent-scope release; the split that
+ *   brings the counter to ceil(seq_lens[s]/S) merges the row's partials with
+ *   the combine formula (acquire first), writes out, and resets the counter.  No
+ *   workgroup waits on another.  out equals, bit for bit, that of
+ *   pfa_paged_attn_decode followed by pfa_paged_attn_combine.  seq_lens[s] >= 1.
+ *   With max_splits == 1 this is pfa_paged_attn_decode (counters unused).
+ */
+pfa_status pfa_paged_attn_decode_fused(const pfa_attn_desc* desc, const pfa_kv_pool* pool,
+                                       const void* q, const int32_t* block_table, int32_t bt_stride,
+                                       const int32_t* seq_lens, int32_t batch, int32_t max_seq_len,
+                                       int32_t split_keys, int32_t max_splits, float* o_part,
+                                       float* lse_part, int32_t* counters, float* out, void* stream);
+
+/*
  * pfa_paged_attn_combine: merge the split partials (same page and section as
  *   decode).  For each (b, h), over the ceil(seq_lens[b]/S) splits of b:
  *     M   = max(max_i lse_i, sink_h)

@@ -25,7 +25,7 @@ STATUS_NAMES = {0: "PFA_OK", 1: "PFA_ERR_NULL", 2: "PFA_ERR_SHAPE", 3: "PFA_ERR_
 KV_DTYPES = {"bf16": 0, "int8": 1}
 
 # every symbol include/pfa.h declares
-EXPORTS = ("pfa_kv_write", "pfa_paged_attn_decode", "pfa_paged_attn_combine",
+EXPORTS = ("pfa_kv_write", "pfa_paged_attn_decode", "pfa_paged_attn_decode_fused", "pfa_paged_attn_combine",
            "pfa_paged_attn_prefill", "pfa_paged_attn_verify", "pfa_decode_num_splits",
            "pfa_prefill_num_splits", "pfa_verify_num_splits", "pfa_status_string", "pfa_last_hip_error")
 
@@ -67,6 +67,7 @@ def lib() -> ctypes.CDLL:
     sig = {
         "pfa_kv_write": [D, PL, P, P, P, P, P, I, I, I, V],
         "pfa_paged_attn_decode": [D, PL, P, P, I, P, I, I, I, I, P, P, P, V],
+        "pfa_paged_attn_decode_fused": [D, PL, P, P, I, P, I, I, I, I, P, P, P, P, V],
         "pfa_paged_attn_combine": [D, P, P, P, I, I, I, P, V],
         "pfa_paged_attn_prefill": [D, PL, P, P, P, I, P, I, I, I, I, I, P, P, P, V],
         "pfa_paged_attn_verify": [D, PL, P, P, P, I, P, I, I, I, I, I, P, P, P, V],
@@ -208,6 +209,26 @@ def paged_attn_decode(desc: AttnDesc, pool: KVPool, q, block_table, seq_lens, ma
     _check("pfa_paged_attn_decode", st)
 
 
+def paged_attn_decode_fused(desc: AttnDesc, pool: KVPool, q, block_table, seq_lens, max_seq_len: int,
+                            split_keys: int, max_splits: int, o_part, lse_part, counters, out, stream=None):
+    """Split-KV decode with the combine fused in: out [B, Hq, D] fp32 is written by
+    the last split of each (sequence, KV head).  counters [B * Hkv] int32 must be
+    zero and are left zero."""
+    _dev(q, torch.bfloat16, "q")
+    _dev(block_table, torch.int32, "block_table")
+    _dev(seq_lens, torch.int32, "seq_lens")
+    _dev(o_part, torch.float32, "o_part")
+    _dev(lse_part, torch.float32, "lse_part")
+    _dev(counters, torch.int32, "counters")
+    _dev(out, torch.float32, "out")
+    st = lib().pfa_paged_attn_decode_fused(ctypes.byref(desc.c()), ctypes.byref(pool.c()), _ptr(q),
+                                           _ptr(block_table), int(block_table.shape[1]), _ptr(seq_lens),
+                                           int(q.shape[0]), int(max_seq_len), int(split_keys), int(max_splits),
+                                           _ptr(o_part), _ptr(lse_part), _ptr(counters), _ptr(out),
+                                           _stream(stream, q))
+    _check("pfa_paged_attn_decode_fused", st)
+
+
 def paged_attn_combine(desc: AttnDesc, o_part, lse_part, seq_lens, split_keys: int, max_splits: int,
                        out, stream=None):
     """Merge split partials into out [B, Hq, D] fp32."""
@@ -283,5 +304,6 @@ def paged_attn_verify(desc: AttnDesc, pool: KVPool, q, cu_q, block_table, seq_le
 
 
 __all__ = ["AttnDesc", "KVPool", "PfaError", "EXPORTS", "lib", "kv_write", "decode_num_splits",
-           "prefill_num_splits", "verify_num_splits", "paged_attn_decode", "paged_attn_combine",
+           "prefill_num_splits", "verify_num_splits", "paged_attn_decode", "paged_attn_decode_fused",
+           "paged_attn_combine",
            "paged_attn_prefill", "paged_attn_verify"]

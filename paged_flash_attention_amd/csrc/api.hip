@@ -86,11 +86,15 @@ int32_t pfa_decode_num_splits(int32_t max_seq_len, int32_t split_keys) {
     return (int32_t)(((int64_t)max_seq_len + split_keys - 1) / split_keys);
 }
 
-pfa_status pfa_paged_attn_decode(const pfa_attn_desc* desc, const pfa_kv_pool* pool, const void* q,
-                                 const int32_t* block_table, int32_t bt_stride,
-                                 const int32_t* seq_lens, int32_t batch, int32_t max_seq_len,
-                                 int32_t split_keys, int32_t max_splits, float* o_part,
-                                 float* lse_part, float* out, void* stream) {
+namespace {
+
+// pfa_paged_attn_decode and pfa_paged_attn_decode_fused: shared checks and launch.
+// counters == nullptr is the plain decode.
+pfa_status decode_like(const pfa_attn_desc* desc, const pfa_kv_pool* pool, const void* q,
+                       const int32_t* block_table, int32_t bt_stride, const int32_t* seq_lens,
+                       int32_t batch, int32_t max_seq_len, int32_t split_keys, int32_t max_splits,
+                       float* o_part, float* lse_part, int32_t* counters, float* out, void* stream,
+                       bool fused) {
     PFA_TRY(check_desc(desc));
     PFA_TRY(check_pool(desc, pool));
     const int g = desc->num_q_heads / desc->num_kv_heads;
@@ -99,7 +103,7 @@ pfa_status pfa_paged_attn_decode(const pfa_attn_desc* desc, const pfa_kv_pool* p
         desc->num_kv_heads > 65535)
         return PFA_ERR_SHAPE;
     if (max_seq_len > (int64_t)bt_stride * desc->page_size) return PFA_ERR_SHAPE;
-    // one 64-lane workgroup per (split run, KV head, sequence) in a 1-D grid
+    // one 64-lane workgroup per (split, KV head, sequence) in a 1-D grid
     if ((int64_t)max_splits * desc->num_kv_heads * batch > (int64_t)1 << 26) return PFA_ERR_SHAPE;
     if (batch == 0) return PFA_OK;
     if (!q || !block_table || !seq_lens) return PFA_ERR_NULL;
@@ -109,6 +113,7 @@ pfa_status pfa_paged_attn_decode(const pfa_attn_desc* desc, const pfa_kv_pool* p
         if (split_keys <= 0 || split_keys % desc->page_size != 0) return PFA_ERR_SHAPE;
         if (max_splits < pfa_decode_num_splits(max_seq_len, split_keys)) return PFA_ERR_WORKSPACE;
         if (!o_part || !lse_part) return PFA_ERR_NULL;
+        if (fused && (!counters || !out)) return PFA_ERR_NULL;
     }
     pfa::DecodeArgs a;
     a.q = static_cast<const uint16_t*>(q);
@@ -122,6 +127,7 @@ pfa_status pfa_paged_attn_decode(const pfa_attn_desc* desc, const pfa_kv_pool* p
     a.o_part = o_part;
     a.lse_part = lse_part;
     a.out = out;
+    a.counters = (fused && max_splits > 1) ? counters : nullptr;
     a.bt_stride = bt_stride;
     a.batch = batch;
     a.num_pages = pool->num_pages;
@@ -133,6 +139,26 @@ pfa_status pfa_paged_attn_decode(const pfa_attn_desc* desc, const pfa_kv_pool* p
     a.sm_scale = desc->sm_scale;
     return hip_status(pfa::launch_decode(a, desc->head_dim, desc->kv_dtype == PFA_KV_INT8,
                                          (hipStream_t)stream));
+}
+
+}  // namespace
+
+pfa_status pfa_paged_attn_decode(const pfa_attn_desc* desc, const pfa_kv_pool* pool, const void* q,
+                                 const int32_t* block_table, int32_t bt_stride,
+                                 const int32_t* seq_lens, int32_t batch, int32_t max_seq_len,
+                                 int32_t split_keys, int32_t max_splits, float* o_part,
+                                 float* lse_part, float* out, void* stream) {
+    return decode_like(desc, pool, q, block_table, bt_stride, seq_lens, batch, max_seq_len, split_keys,
+                       max_splits, o_part, lse_part, nullptr, out, stream, false);
+}
+
+pfa_status pfa_paged_attn_decode_fused(const pfa_attn_desc* desc, const pfa_kv_pool* pool,
+                                       const void* q, const int32_t* block_table, int32_t bt_stride,
+                                       const int32_t* seq_lens, int32_t batch, int32_t max_seq_len,
+                                       int32_t split_keys, int32_t max_splits, float* o_part,
+                                       float* lse_part, int32_t* counters, float* out, void* stream) {
+    return decode_like(desc, pool, q, block_table, bt_stride, seq_lens, batch, max_seq_len, split_keys,
+                       max_splits, o_part, lse_part, counters, out, stream, true);
 }
 
 pfa_status pfa_paged_attn_combine(const pfa_attn_desc* desc, const float* o_part,

@@ -12,13 +12,9 @@
 // no visible key carry lse = -inf and weigh 0.  The leading run of such splits
 // is skipped without reading its o rows.
 //
-// One 64-lane wave per (row, h):
-//  * the lanes take the splits' lse values in parallel for the max and the weight
-//    sum, and put the weights in LDS;
-//  * then every lane owns D/64 consecutive elements and walks the splits, 8 rows
-//    in flight, each split's o_part row read as one coalesced D*4-byte access.
+// One 64-lane wave per (row, h) runs merge_splits (merge_splits.h).
 // The work is tiny: rows*Hq*splits*(D+1)*4 bytes read.
-#include "pfa_device.h"
+#include "merge_splits.h"
 
 namespace pfa {
 namespace {
@@ -30,7 +26,6 @@ __global__ __launch_bounds__(64) void combine_kernel(CombineArgs a) {
     __shared__ float w_lds[kMaxLdsSplits];
     const int h = blockIdx.x % a.num_q_heads;
     const int r = blockIdx.x / a.num_q_heads;
-    const int lane = threadIdx.x;
     int row = r;
     int ns = a.max_splits;
     if (a.cu_rows) {
@@ -43,66 +38,8 @@ __global__ __launch_bounds__(64) void combine_kernel(CombineArgs a) {
         ns = min((len + a.split_keys - 1) / a.split_keys, a.max_splits);
     }
     const int64_t bh = (int64_t)row * a.num_q_heads + h;
-    const float* lse = a.lse_part + (int64_t)bh * a.max_splits;
-    const float* op = a.o_part + (int64_t)bh * a.max_splits * D;
-
-    // max, and the first split with a visible key: decode leaves the o rows of the
-    // splits a window hides (always a prefix) unwritten, so they are never read
-    float m = -INFINITY;
-    float first = (float)ns;
-    for (int i = lane; i < ns; i += kWave) {
-        const float l = lse[i];
-        m = fmaxf(m, l);
-        if (l != -INFINITY) first = fminf(first, (float)i);
-    }
-    m = stride_max<1>(m);
-    const int i_first = (int)-stride_max<1>(-first);
-    const bool has_sink = a.sinks != nullptr;
-    const float sink = has_sink ? __ldg(a.sinks + h) : -INFINITY;
-    m = fmaxf(m, sink);
-    const float ms = (m == -INFINITY) ? 0.0f : m;
-
-    constexpr int E = D / kWave;
-    float acc[E];
-#pragma unroll
-    for (int e = 0; e < E; ++e) acc[e] = 0.0f;
-    float wsum = 0.0f;
-    for (int base = i_first; base < ns; base += kMaxLdsSplits) {
-        const int cnt = min(ns - base, kMaxLdsSplits);
-        for (int i = lane; i < cnt; i += kWave) {
-            const float w = __expf(lse[base + i] - ms);      // 0 for lse = -inf
-            w_lds[i] = w;
-            wsum += w;
-        }
-        __syncthreads();
-        const float* row = op + (int64_t)base * D + lane * E;
-        int i = 0;
-        for (; i + 8 <= cnt; i += 8) {
-            float v[8][E];
-#pragma unroll
-            for (int u = 0; u < 8; ++u)
-#pragma unroll
-                for (int e = 0; e < E; ++e) v[u][e] = row[(int64_t)(i + u) * D + e];
-#pragma unroll
-            for (int u = 0; u < 8; ++u) {
-                const float w = w_lds[i + u];
-#pragma unroll
-                for (int e = 0; e < E; ++e) acc[e] = fmaf(w, v[u][e], acc[e]);
-            }
-        }
-        for (; i < cnt; ++i) {
-            const float w = w_lds[i];
-#pragma unroll
-            for (int e = 0; e < E; ++e) acc[e] = fmaf(w, row[(int64_t)i * D + e], acc[e]);
-        }
-        __syncthreads();
-    }
-    wsum = stride_sum<1>(wsum);
-    const float z = wsum + (has_sink ? __expf(sink - ms) : 0.0f);
-    const float inv = z > 0.0f ? 1.0f / z : 0.0f;
-    float* o = a.out + (int64_t)bh * D + lane * E;
-#pragma unroll
-    for (int e = 0; e < E; ++e) o[e] = acc[e] * inv;
+    merge_splits<D, kMaxLdsSplits>(a.lse_part + bh * a.max_splits, a.o_part + bh * a.max_splits * D, ns,
+                                   a.sinks ? a.sinks + h : nullptr, w_lds, a.out + bh * D);
 }
 
 }  // namespace

@@ -45,7 +45,7 @@
 //  * At the end of a split each wave reduces its partial o across key groups and
 //    writes o/l with lse = ln(sum e^s) (split mode), or the final output with the
 //    sink (unsplit mode).
-#include "pfa_device.h"
+#include "merge_splits.h"
 
 namespace pfa {
 namespace {
@@ -154,6 +154,9 @@ __device__ __forceinline__ float lane_read(float v, int l) {
     return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
 }
 
+// Splits whose merge weights sit in LDS at a time, in the fused merge.
+constexpr int kFusedMergeChunk = 256;
+
 template <int D, int G, bool INT8, bool FINAL>
 __global__ __launch_bounds__(kWave)
 void decode_kernel(DecodeArgs a) {
@@ -168,6 +171,7 @@ void decode_kernel(DecodeArgs a) {
     typedef typename Chunk<INT8>::T CT;
 
     __shared__ __attribute__((aligned(16))) float p_buf[2][kPage][G];
+    __shared__ float w_lds[FINAL ? 1 : kFusedMergeChunk];
 
     const int lane = threadIdx.x;
     const int sub = lane % LPK;
@@ -189,6 +193,42 @@ void decode_kernel(DecodeArgs a) {
     len = min(max(len, 0), a.bt_stride * kPage);
     int lo = a.window > 0 ? max(0, len - a.window) : 0;         // first visible key
     int hi = len;
+
+    // Fused merge (counters given).  The partials go out as agent-scope atomic
+    // stores, which write through to the point where all XCDs see them.  After
+    // they complete (vmcnt 0), the split adds one to its (sequence, KV head)
+    // counter; the split that brings it to the split count reads the row's
+    // partials back with agent-scope atomic loads, merges them for its G heads,
+    // writes out, and resets the counter.  No L2 write-back or invalidate is
+    // needed (agent-scope fences would write back or invalidate a whole XCD's L2
+    // for every workgroup), and no wave waits on another.
+    const bool fused = !FINAL && a.counters != nullptr;
+    auto put = [&](float* p, float v) __attribute__((always_inline)) {
+        if (fused) __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        else *p = v;
+    };
+    auto arrive = [&]() __attribute__((always_inline)) {
+        if constexpr (!FINAL) {
+            if (!fused) return;
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            int32_t* ctr = a.counters + (int64_t)b * Hkv + kvh;
+            int old = 0;
+            if (lane == 0) old = __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            old = __builtin_amdgcn_readfirstlane(old);
+            const int nsp = min((len + a.split_keys - 1) / a.split_keys, a.max_splits);
+            if (old != nsp - 1) return;
+            asm volatile("" ::: "memory");
+            for (int g = 0; g < G; ++g) {
+                const int64_t r = row0 + g;
+                merge_splits<D, kFusedMergeChunk, true>(a.lse_part + r * a.max_splits,
+                                                        a.o_part + r * a.max_splits * D, nsp,
+                                                        a.sinks ? a.sinks + head0 + g : nullptr, w_lds,
+                                                        a.out + r * D);
+            }
+            if (lane == 0) __hip_atomic_store(ctr, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+    };
+
     if constexpr (FINAL) {
         if (lo >= hi) {   // no keys: output 0
             for (int e = lane; e < G * D; e += kWave) a.out[row0 * D + e] = 0.0f;
@@ -198,7 +238,8 @@ void decode_kernel(DecodeArgs a) {
         const int s0 = sp * a.split_keys;
         if (s0 >= len) return;
         if (s0 + a.split_keys <= lo) {   // the window hides the whole split
-            if (lane < G) a.lse_part[(row0 + lane) * a.max_splits + sp] = -INFINITY;
+            if (lane < G) put(a.lse_part + (row0 + lane) * a.max_splits + sp, -INFINITY);
+            arrive();
             return;
         }
         lo = max(lo, s0);
@@ -404,14 +445,20 @@ void decode_kernel(DecodeArgs a) {
         if (g % KPL == kg) {
             float* dst = FINAL ? a.out + (row0 + g) * D + sub * 8
                                : a.o_part + ((row0 + g) * a.max_splits + sp) * D + sub * 8;
-            float4* d4 = reinterpret_cast<float4*>(dst);
-            d4[0] = make_float4(o[g][0] * f, o[g][1] * f, o[g][2] * f, o[g][3] * f);
-            d4[1] = make_float4(o[g][4] * f, o[g][5] * f, o[g][6] * f, o[g][7] * f);
+            if (fused) {
+#pragma unroll
+                for (int j = 0; j < 8; ++j) put(dst + j, o[g][j] * f);
+            } else {
+                float4* d4 = reinterpret_cast<float4*>(dst);
+                d4[0] = make_float4(o[g][0] * f, o[g][1] * f, o[g][2] * f, o[g][3] * f);
+                d4[1] = make_float4(o[g][4] * f, o[g][5] * f, o[g][6] * f, o[g][7] * f);
+            }
         }
         if constexpr (!FINAL) {
-            if (lane == 0) a.lse_part[(row0 + g) * a.max_splits + sp] = (mg + fast_log2(lg)) * kLn2;
+            if (lane == 0) put(a.lse_part + (row0 + g) * a.max_splits + sp, (mg + fast_log2(lg)) * kLn2);
         }
     }
+    arrive();
 }
 
 template <int D, int G, bool INT8>

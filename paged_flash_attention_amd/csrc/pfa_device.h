@@ -137,6 +137,7 @@ struct DecodeArgs {
     float* o_part;
     float* lse_part;
     float* out;
+    int32_t* counters;         // split mode, fused merge: [batch * num_kv_heads], zero on entry; else NULL
     int32_t bt_stride, batch, num_pages, num_q_heads, num_kv_heads;
     int32_t split_keys, max_splits, window;
     float sm_scale;

@@ -91,6 +91,25 @@ class GpuCase:
             return out.cpu().numpy(), parts
         return out.cpu().numpy()
 
+    def decode_fused(self, split_keys=256, calls=2):
+        """pfa_paged_attn_decode_fused, `calls` times on one counter array (the later
+        calls check that each call leaves the counters zero).  Returns (out, counters)."""
+        c = self.case
+        B, Hq, D = c.batch, c.p.num_q_heads, c.p.head_dim
+        max_len = int(c.seq_lens.max())
+        ms = pfa.decode_num_splits(max_len, split_keys)
+        ctr = torch.zeros(B * c.p.num_kv_heads, dtype=torch.int32, device="cuda")
+        outs = []
+        for _ in range(calls):
+            out = torch.full((B, Hq, D), float("nan"), device="cuda")
+            op = torch.full((B, Hq, ms, D), float("nan"), device="cuda")
+            lp = torch.full((B, Hq, ms), float("nan"), device="cuda")
+            pfa.paged_attn_decode_fused(self.desc, self.pool, self.q, self.bt, self.seq_lens, max_len,
+                                        split_keys, ms, op, lp, ctr, out)
+            outs.append(out)
+        torch.cuda.synchronize()
+        return [o.cpu().numpy() for o in outs], ctr.cpu().numpy()
+
     def prefill(self, split="auto"):
         """split: "auto" (the library's choice), None (unsplit) or (split_keys, max_splits)."""
         c = self.case

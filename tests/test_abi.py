@@ -107,6 +107,25 @@ def test_decode_validation():
     assert dec(desc(), pool(), batch=0, q=None) == OK
 
 
+def decf(d, p, **kw):
+    a = dict(q=FAKE, bt=FAKE, stride=64, sl=FAKE, batch=4, max_len=1024, S=256, ms=4,
+             op=FAKE, lp=FAKE, ctr=FAKE, out=FAKE)
+    a.update(kw)
+    return pfa.lib().pfa_paged_attn_decode_fused(ctypes.byref(d), ctypes.byref(p), a["q"], a["bt"], a["stride"],
+                                                 a["sl"], a["batch"], a["max_len"], a["S"], a["ms"],
+                                                 a["op"], a["lp"], a["ctr"], a["out"], None)
+
+
+def test_decode_fused_validation():
+    assert decf(desc(), pool(), ctr=None) == NULL
+    assert decf(desc(), pool(), out=None) == NULL
+    assert decf(desc(), pool(), op=None) == NULL
+    assert decf(desc(), pool(), ms=3) == WORKSPACE
+    assert decf(desc(), pool(), S=100) == SHAPE
+    assert decf(desc(num_q_heads=48, num_kv_heads=3), pool()) == UNSUP
+    assert decf(desc(), pool(), batch=0, q=None, ctr=None) == OK
+
+
 def comb(d, **kw):
     a = dict(op=FAKE, lp=FAKE, sl=FAKE, batch=4, S=256, ms=4, out=FAKE)
     a.update(kw)

@@ -139,6 +139,32 @@ def test_decode_batch_600():
     assert_close(g.decode(split_keys=64), ref, BF16_TOL, "batch 600")
 
 
+FUSED_CASES = [
+    (dict(Hq=32, Hkv=8, D=128), [1, 15, 16, 17, 300, 1024, 2049], 256),
+    (dict(Hq=64, Hkv=8, D=64, window=128, sinks=True), [1, 100, 129, 700, 3000], 64),
+    (dict(Hq=32, Hkv=4, D=128, kv="int8", sinks=True), [1, 33, 257, 2000], 256),
+    (dict(Hq=16, Hkv=8, D=64, window=1), [1, 2, 17], 16),
+    (dict(Hq=32, Hkv=8, D=128, window=100, sinks=True), list(np.random.default_rng(79).integers(1, 1200, 40)), 16),
+]
+
+
+@pytest.mark.parametrize("ci", range(len(FUSED_CASES)))
+def test_decode_fused_equals_decode_then_combine(ci):
+    """The fused merge gives the same bits as decode + combine, on repeated calls
+    over one counter array, which it leaves zero; and it meets the oracle."""
+    prm, lens, S = FUSED_CASES[ci]
+    case = W.make_case(f"fused{ci}", 170 + ci, P(seed=ci, **prm), lens, np.ones(len(lens), np.int32),
+                       outlier_frac=0.01 if prm.get("kv") == "int8" else 0.0)
+    g = GpuCase(case)
+    ref = O.decode(case.q, oracle_pool(case), case.block_table, case.seq_lens, case.p)
+    plain = g.decode(split_keys=S)
+    outs, ctr = g.decode_fused(split_keys=S, calls=3)
+    assert not ctr.any(), "counters not reset"
+    for k, got in enumerate(outs):
+        assert np.array_equal(got.view(np.uint32), plain.view(np.uint32)), f"fused call {k} differs from decode+combine"
+    assert_close(outs[-1], ref, tol_of(case), f"fused case {ci}")
+
+
 def test_decode_partials_match_oracle():
     prm = dict(Hq=32, Hkv=8, D=128, window=300, sinks=True)
     lens = [10, 256, 257, 900]
