@@ -210,6 +210,50 @@ def run_decode(case, torch, pfa, gs, steps, warmup, fused=False):
                 partial_bytes=int(B * Hq * ms * (D + 1) * 4))
 
 
+def attn_input_bytes(ic) -> int:
+    """Algorithmic HBM bytes of one fused attention-input launch: the qkv rows, the
+    RoPE table row of each token, q out, and k/v (codes + scales for INT8) in."""
+    c = ic.case
+    p = c.p
+    T = int(c.cu_q[-1])
+    D, Hq, Hkv = p.head_dim, p.num_q_heads, p.num_kv_heads
+    kv = 2 * Hkv * (D * (1 if p.kv_dtype == "int8" else 2) + (4 if p.kv_dtype == "int8" else 0))
+    return T * ((Hq + 2 * Hkv) * D * 2 + (D // 2) * 8 + Hq * D * 2 + kv)
+
+
+def run_attn_input(ic, torch, pfa, gs, steps, warmup):
+    """Fused attention-input launches over rotating qkv copies (>= 1 GiB in all when
+    the rows are large, so the 256 MB MALL does not serve them)."""
+    c = ic.case
+    p = c.p
+    T = int(c.cu_q[-1])
+    desc = gs.desc_of(p)
+    pool = gs.poisoned_pool(c)
+    qkv0 = gs.dev_bf16(ic.qkv)
+    copies = max(1, min(8, -(-(1 << 30) // max(1, qkv0.numel() * 2))))
+    qkvs = [qkv0] + [qkv0.clone() for _ in range(copies - 1)]
+    qw, kw = gs.dev_bf16(ic.q_norm_w), gs.dev_bf16(ic.k_norm_w)
+    rope = torch.from_numpy(ic.rope).cuda()
+    cu, sl, bt = gs.dev_i32(c.cu_q), gs.dev_i32(c.seq_lens), gs.dev_i32(c.block_table)
+    q_out = torch.empty((T, p.num_q_heads, p.head_dim), dtype=torch.bfloat16, device="cuda")
+    tm = Timer(torch)
+
+    def step(i):
+        e = tm.mark("attn_input")
+        pfa.attn_input(desc, pool, qw, kw, rope, ic.eps, qkvs[i % len(qkvs)], cu, sl, bt, q_out)
+        tm.close("attn_input", e)
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    tm.reset()
+    for i in range(steps):
+        step(warmup + i)
+    torch.cuda.synchronize()
+    ms = tm.mean_ms("attn_input")
+    return dict(step_ms=ms, attn_input_ms=ms, bytes=attn_input_bytes(ic), copies=len(qkvs))
+
+
 def run_prefill(case, torch, pfa, gs, steps, warmup, verify=False):
     """Prefill steps (kv_write + prefill), or with verify=True verify steps (kv_write
     + pfa_paged_attn_verify), on the library's split choice."""
@@ -356,6 +400,8 @@ def main():
         "prefill_chunk130_on_8192": lambda: W.prefill_llama8b(prompt=130, prefix=8192),
         "mixed_full_prefill_2x2048": lambda: W.mixed_gptoss(layer="full", part="prefill"),
         "mixed_window_prefill_2x2048": lambda: W.mixed_gptoss(layer="window", part="prefill"),
+        "attn_input_1x8192": lambda: W.attn_input_qwen4b(),
+        "attn_input_32x1_on_4096": lambda: W.attn_input_qwen4b(prompt=1, batch=32, prefix=4095),
         "verify_16tok_batch1_ctx1024": lambda: W.verify_qwen4b(),
         "verify_8tok_batch32_ctx512_8192": lambda: W.verify_qwen4b(batch=32, tokens=8, lo=512, hi=8192),
     }
@@ -366,6 +412,11 @@ def main():
     def measure(name, steps, warmup):
         case = builders[name]()
         log(f"[bench] {name}: building + timing {steps} steps")
+        if name.startswith("attn_input"):
+            r = run_attn_input(case, torch, pfa, gs, steps, warmup)
+            gbs = r["bytes"] / (r["attn_input_ms"] * 1e-3) / 1e9
+            r.update(metric="attn input GB/s", kernel_gbs=round(gbs, 1), frac_of_hbm_peak=round(gbs / HBM_PEAK_GBS, 4))
+            return case, r
         if name.startswith("verify"):
             r = run_prefill(case, torch, pfa, gs, steps, warmup, verify=True)
             tf = r["flops"] / (r["prefill_ms"] * 1e-3) / 1e12
@@ -386,7 +437,14 @@ def main():
 
     case, r = measure(args.workload, args.steps, args.warmup)
     is_prefill = "prefill_ms" in r
-    if args.workload.startswith("verify"):
+    is_attn_input = args.workload.startswith("attn_input")
+    if is_attn_input:
+        value = r["kernel_gbs"]
+        unit, metric = "GB/s", "attn input GB/s (HBM)"
+        roof = dict(bound="hbm", achieved=r["kernel_gbs"], peak=HBM_PEAK_GBS, unit="GB/s",
+                    frac=r["frac_of_hbm_peak"], traffic=None)
+        case = case.case
+    elif args.workload.startswith("verify"):
         value = r["kv_bytes"] / (r["step_ms"] * 1e-3) / 1e9
         unit, metric = "GB/s", "verify attn GB/s (HBM)"
         roof = dict(bound="hbm", achieved=r["kernel_gbs"], peak=HBM_PEAK_GBS, unit="GB/s",
@@ -411,10 +469,14 @@ def main():
                          ("decode_int8_batch8_ctx32768", 30),
                          ("mixed_full_decode_b64", 30), ("prefill_causal_8192", 10),
                          ("prefill_chunk130_on_8192", 20), ("mixed_full_prefill_2x2048", 20),
-                         ("verify_16tok_batch1_ctx1024", 50), ("verify_8tok_batch32_ctx512_8192", 30)):
+                         ("verify_16tok_batch1_ctx1024", 50), ("verify_8tok_batch32_ctx512_8192", 30),
+                         ("attn_input_1x8192", 30), ("attn_input_32x1_on_4096", 50)):
             try:
                 _, rr = measure(name, st, 3)
-                if name.startswith("verify"):
+                if name.startswith("attn_input"):
+                    extra[name] = dict(us=round(rr["attn_input_ms"] * 1e3, 2), gbs=rr["kernel_gbs"],
+                                       frac_of_hbm_peak=rr["frac_of_hbm_peak"])
+                elif name.startswith("verify"):
                     extra[name] = dict(us=round(rr["prefill_ms"] * 1e3, 2), gbs=rr["kernel_gbs"],
                                        frac_of_hbm_peak=rr["frac_of_hbm_peak"], tflops=rr["kernel_tflops"],
                                        split=f"{rr['split_keys']}x{rr['max_splits']}")
@@ -430,7 +492,7 @@ def main():
             torch.cuda.empty_cache()
 
     cpu = None
-    if not args.no_cpu_baseline and not is_prefill:
+    if not args.no_cpu_baseline and not is_prefill and not is_attn_input:
         log("[bench] cpu baseline (oracle)")
         cpu = cpu_baseline_decode(case)
 

@@ -115,6 +115,45 @@ pfa_status pfa_kv_write(const pfa_attn_desc* desc, const pfa_kv_pool* pool,
                         void* stream);
 
 /*
+ * pfa_attn_input: the attention inputs of new tokens, straight from the fused
+ *   q/k/v projection: q/k RMSNorm, RoPE, and the KV-cache write, in one kernel.
+ *   The TileInfer.jl performance page ("Fused kernels, FlashAttention and
+ *   PagedAttention") fuses these, bit-identical to the chain of per-op kernels.
+ *   The chain: each op reads and writes bf16 (round to nearest even); inside an
+ *   op, IEEE fp32 with every product and sum rounded on its own:
+ *     RMSNorm (per head vector x, weight w):
+ *       ss = sum of x_d^2: left to right within each group of 8 consecutive
+ *            elements, then the D/8 group sums pairwise (group j adds group
+ *            j xor m, for m = D/16, ..., 1)
+ *       y  = bf16((x * r) * w),  r = 1 / sqrt(ss / D + eps)
+ *     RoPE (rotate-half), (c, s) = rope_cos_sin[pos][i], i < D/2:
+ *       out_i = bf16(y_i c - y_(i+D/2) s),  out_(i+D/2) = bf16(y_(i+D/2) c + y_i s)
+ *   q heads: RMSNorm(q_norm_weight), RoPE -> q_out.  k heads: RMSNorm(k_norm_weight),
+ *   RoPE -> the pool.  v heads -> the pool unchanged.  INT8 pools receive codes and
+ *   scales of the final k and v as pfa_kv_write computes them.
+ *
+ *   qkv          device [num_tokens][(Hq + 2 Hkv) * D] bf16: per token the Hq q heads,
+ *                then the Hkv k heads, then the Hkv v heads.
+ *   cu_new, seq_lens, block_table, bt_stride, batch: as pfa_kv_write; token i of
+ *                sequence s sits at position seq_lens[s] - n_s + i.
+ *   q_out        device [num_tokens][Hq][D] bf16.
+ *   The positions must be < prm->rope_max_pos (the kernel clamps the table row).
+ *   Tokens whose slot falls outside the block table or the pool write no K/V.
+ */
+typedef struct {
+    const void* q_norm_weight;   /* device [D] bf16 */
+    const void* k_norm_weight;   /* device [D] bf16 */
+    const float* rope_cos_sin;   /* device [rope_max_pos][D/2][2] fp32: (cos, sin) */
+    int32_t rope_max_pos;
+    float eps;                   /* RMSNorm epsilon, 0 <= eps <= 1 */
+} pfa_attn_input_params;
+
+pfa_status pfa_attn_input(const pfa_attn_desc* desc, const pfa_kv_pool* pool,
+                          const pfa_attn_input_params* prm, const void* qkv, const int32_t* cu_new,
+                          const int32_t* seq_lens, const int32_t* block_table, int32_t bt_stride,
+                          int32_t batch, int32_t num_tokens, void* q_out, void* stream);
+
+/*
  * pfa_paged_attn_decode: one query per sequence, at position seq_lens[s]-1.  That
  *   token's K/V must already be written.  Split-KV: the TileInfer.jl performance
  *   page ("Fused kernels, ...") keeps the combine as a separate kernel.

@@ -25,7 +25,7 @@ STATUS_NAMES = {0: "PFA_OK", 1: "PFA_ERR_NULL", 2: "PFA_ERR_SHAPE", 3: "PFA_ERR_
 KV_DTYPES = {"bf16": 0, "int8": 1}
 
 # every symbol include/pfa.h declares
-EXPORTS = ("pfa_kv_write", "pfa_paged_attn_decode", "pfa_paged_attn_decode_fused", "pfa_paged_attn_combine",
+EXPORTS = ("pfa_kv_write", "pfa_attn_input", "pfa_paged_attn_decode", "pfa_paged_attn_decode_fused", "pfa_paged_attn_combine",
            "pfa_paged_attn_prefill", "pfa_paged_attn_verify", "pfa_decode_num_splits",
            "pfa_prefill_num_splits", "pfa_verify_num_splits", "pfa_status_string", "pfa_last_hip_error")
 
@@ -43,6 +43,12 @@ class CAttnDesc(ctypes.Structure):
                 ("head_dim", ctypes.c_int32), ("page_size", ctypes.c_int32),
                 ("kv_dtype", ctypes.c_int32), ("window", ctypes.c_int32),
                 ("sm_scale", ctypes.c_float), ("sinks", ctypes.c_void_p)]
+
+
+class CAttnInputParams(ctypes.Structure):
+    _fields_ = [("q_norm_weight", ctypes.c_void_p), ("k_norm_weight", ctypes.c_void_p),
+                ("rope_cos_sin", ctypes.c_void_p), ("rope_max_pos", ctypes.c_int32),
+                ("eps", ctypes.c_float)]
 
 
 class CKvPool(ctypes.Structure):
@@ -66,6 +72,7 @@ def lib() -> ctypes.CDLL:
     D, PL = ctypes.POINTER(CAttnDesc), ctypes.POINTER(CKvPool)
     sig = {
         "pfa_kv_write": [D, PL, P, P, P, P, P, I, I, I, V],
+        "pfa_attn_input": [D, PL, ctypes.POINTER(CAttnInputParams), P, P, P, P, I, I, I, P, V],
         "pfa_paged_attn_decode": [D, PL, P, P, I, P, I, I, I, I, P, P, P, V],
         "pfa_paged_attn_decode_fused": [D, PL, P, P, I, P, I, I, I, I, P, P, P, P, V],
         "pfa_paged_attn_combine": [D, P, P, P, I, I, I, P, V],
@@ -188,6 +195,25 @@ def kv_write(desc: AttnDesc, pool: KVPool, k_new, v_new, cu_new, seq_lens, block
     _check("pfa_kv_write", st)
 
 
+def attn_input(desc: AttnDesc, pool: KVPool, q_norm_weight, k_norm_weight, rope_cos_sin, eps: float,
+               qkv, cu_new, seq_lens, block_table, q_out, stream=None):
+    """Fused q/k RMSNorm + RoPE + KV write from qkv [T, (Hq + 2 Hkv) * D] bf16.
+    rope_cos_sin [max_pos, D/2, 2] fp32; writes q_out [T, Hq, D] bf16 and the pool."""
+    _dev(qkv, torch.bfloat16, "qkv")
+    _dev(q_norm_weight, torch.bfloat16, "q_norm_weight")
+    _dev(k_norm_weight, torch.bfloat16, "k_norm_weight")
+    _dev(rope_cos_sin, torch.float32, "rope_cos_sin")
+    _dev(q_out, torch.bfloat16, "q_out")
+    for t, n in ((cu_new, "cu_new"), (seq_lens, "seq_lens"), (block_table, "block_table")):
+        _dev(t, torch.int32, n)
+    prm = CAttnInputParams(_ptr(q_norm_weight), _ptr(k_norm_weight), _ptr(rope_cos_sin),
+                           int(rope_cos_sin.shape[0]), float(eps))
+    st = lib().pfa_attn_input(ctypes.byref(desc.c()), ctypes.byref(pool.c()), ctypes.byref(prm), _ptr(qkv),
+                              _ptr(cu_new), _ptr(seq_lens), _ptr(block_table), int(block_table.shape[1]),
+                              int(seq_lens.numel()), int(qkv.shape[0]), _ptr(q_out), _stream(stream, qkv))
+    _check("pfa_attn_input", st)
+
+
 def decode_num_splits(max_seq_len: int, split_keys: int) -> int:
     return int(lib().pfa_decode_num_splits(int(max_seq_len), int(split_keys)))
 
@@ -303,7 +329,7 @@ def paged_attn_verify(desc: AttnDesc, pool: KVPool, q, cu_q, block_table, seq_le
     _check("pfa_paged_attn_verify", st)
 
 
-__all__ = ["AttnDesc", "KVPool", "PfaError", "EXPORTS", "lib", "kv_write", "decode_num_splits",
+__all__ = ["AttnDesc", "KVPool", "PfaError", "EXPORTS", "lib", "kv_write", "attn_input", "decode_num_splits",
            "prefill_num_splits", "verify_num_splits", "paged_attn_decode", "paged_attn_decode_fused",
            "paged_attn_combine",
            "paged_attn_prefill", "paged_attn_verify"]

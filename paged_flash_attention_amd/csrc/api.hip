@@ -80,6 +80,47 @@ pfa_status pfa_kv_write(const pfa_attn_desc* desc, const pfa_kv_pool* pool, cons
     return hip_status(pfa::launch_kv_write(a, desc->kv_dtype == PFA_KV_INT8, (hipStream_t)stream));
 }
 
+pfa_status pfa_attn_input(const pfa_attn_desc* desc, const pfa_kv_pool* pool,
+                          const pfa_attn_input_params* prm, const void* qkv, const int32_t* cu_new,
+                          const int32_t* seq_lens, const int32_t* block_table, int32_t bt_stride,
+                          int32_t batch, int32_t num_tokens, void* q_out, void* stream) {
+    PFA_TRY(check_desc(desc));
+    PFA_TRY(check_pool(desc, pool));
+    if (!prm) return PFA_ERR_NULL;
+    if (batch < 0 || num_tokens < 0 || bt_stride <= 0 || prm->rope_max_pos <= 0) return PFA_ERR_SHAPE;
+    if (!(prm->eps >= 0.0f) || prm->eps > 1.0f) return PFA_ERR_SHAPE;
+    if (num_tokens > 0 && batch == 0) return PFA_ERR_SHAPE;
+    if ((int64_t)num_tokens * pfa::kWave > 0xffffffffLL - 256) return PFA_ERR_SHAPE;   // one wave per token
+    if ((int64_t)desc->num_q_heads + 2 * desc->num_kv_heads > 65536) return PFA_ERR_SHAPE;
+    if (num_tokens == 0) return PFA_OK;
+    if (!qkv || !cu_new || !seq_lens || !block_table || !q_out || !prm->q_norm_weight ||
+        !prm->k_norm_weight || !prm->rope_cos_sin)
+        return PFA_ERR_NULL;
+    pfa::AttnInputArgs a;
+    a.qkv = static_cast<const uint16_t*>(qkv);
+    a.q_norm_w = static_cast<const uint16_t*>(prm->q_norm_weight);
+    a.k_norm_w = static_cast<const uint16_t*>(prm->k_norm_weight);
+    a.rope = prm->rope_cos_sin;
+    a.cu_new = cu_new;
+    a.seq_lens = seq_lens;
+    a.block_table = block_table;
+    a.q_out = static_cast<uint16_t*>(q_out);
+    a.k_pool = pool->k_pool;
+    a.v_pool = pool->v_pool;
+    a.k_scale = pool->k_scale;
+    a.v_scale = pool->v_scale;
+    a.eps = prm->eps;
+    a.bt_stride = bt_stride;
+    a.batch = batch;
+    a.num_tokens = num_tokens;
+    a.num_pages = pool->num_pages;
+    a.num_q_heads = desc->num_q_heads;
+    a.num_kv_heads = desc->num_kv_heads;
+    a.rope_max_pos = prm->rope_max_pos;
+    return hip_status(pfa::launch_attn_input(a, desc->head_dim, desc->kv_dtype == PFA_KV_INT8,
+                                             (hipStream_t)stream));
+}
+
 int32_t pfa_decode_num_splits(int32_t max_seq_len, int32_t split_keys) {
     if (split_keys <= 0) return 0;
     if (max_seq_len <= 0) return 1;

@@ -13,46 +13,10 @@
 // with DPP/swizzle moves.  Loads and stores are 16 B (codes: 8 B) per lane and are
 // contiguous across the lanes of a vector.  The kernel is HBM-bound: it reads
 // 2*D*2 B and writes 2*D*b B (+8 B scales) per (token, head).
-#include "pfa_device.h"
+#include "kv_slot.h"
 
 namespace pfa {
 namespace {
-
-__device__ __forceinline__ int find_seq(const int32_t* __restrict__ cu, int batch, int tok) {
-    // largest s with cu[s] <= tok (cu nondecreasing, cu[0] = 0)
-    int lo = 0, hi = batch - 1;
-    while (lo < hi) {
-        int mid = (lo + hi + 1) >> 1;
-        if (__ldg(cu + mid) <= tok) lo = mid; else hi = mid - 1;
-    }
-    return lo;
-}
-
-template <int D>
-__device__ __forceinline__ float group_absmax(float m) {
-    constexpr int L = D / 8;  // lanes per vector
-    if constexpr (L >= 16) m = xor_max<8>(m);
-    if constexpr (L >= 8) m = xor_max<4>(m);
-    m = xor_max<2>(m);
-    m = xor_max<1>(m);
-    return m;
-}
-
-// Quantise 8 elements whose vector absmax is `amax`; returns the 8 codes packed.
-__device__ __forceinline__ uint2 quantise8(const float (&x)[8], float scale) {
-    uint32_t w[2] = {0u, 0u};
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        float c = 0.0f;
-        if (scale > 0.0f) {
-            c = __builtin_rintf(x[i] / scale);
-            c = fminf(fmaxf(c, -127.0f), 127.0f);
-        }
-        uint32_t b = (uint32_t)((int32_t)c) & 0xffu;
-        w[i >> 2] |= b << (8 * (i & 3));
-    }
-    return make_uint2(w[0], w[1]);
-}
 
 template <int D, bool INT8>
 __global__ __launch_bounds__(256) void kv_write_kernel(KvWriteArgs a) {

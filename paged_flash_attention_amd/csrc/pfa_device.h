@@ -143,6 +143,23 @@ struct DecodeArgs {
     float sm_scale;
 };
 
+struct AttnInputArgs {
+    const uint16_t* qkv;        // [T][(Hq + 2 Hkv) * D] bf16
+    const uint16_t* q_norm_w;   // [D] bf16
+    const uint16_t* k_norm_w;   // [D] bf16
+    const float* rope;          // [rope_max_pos][D/2][2] fp32 (cos, sin)
+    const int32_t* cu_new;
+    const int32_t* seq_lens;
+    const int32_t* block_table;
+    uint16_t* q_out;            // [T][Hq][D] bf16
+    void* k_pool;
+    void* v_pool;
+    float* k_scale;
+    float* v_scale;
+    float eps;
+    int32_t bt_stride, batch, num_tokens, num_pages, num_q_heads, num_kv_heads, rope_max_pos;
+};
+
 struct CombineArgs {
     const float* o_part;
     const float* lse_part;
@@ -171,6 +188,7 @@ struct PrefillArgs {
 };
 
 hipError_t launch_kv_write(const KvWriteArgs& a, bool int8, hipStream_t s);
+hipError_t launch_attn_input(const AttnInputArgs& a, int head_dim, bool int8, hipStream_t s);
 hipError_t launch_decode(const DecodeArgs& a, int head_dim, bool int8, hipStream_t s);
 hipError_t launch_combine(const CombineArgs& a, int head_dim, hipStream_t s);
 hipError_t launch_prefill(const PrefillArgs& a, int head_dim, hipStream_t s);

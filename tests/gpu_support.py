@@ -187,3 +187,40 @@ def assert_close(got, ref, tol, what=""):
 
 def tol_of(case):
     return INT8_TOL if case.p.kv_dtype == "int8" else BF16_TOL
+
+
+def gpu_attn_input(ic: W.AttnInputCase):
+    """pfa_attn_input on a poisoned pool.  Returns (q_out bits, pool)."""
+    c = ic.case
+    p = c.p
+    T = int(c.cu_q[-1])
+    pool = poisoned_pool(c)
+    q_out = torch.empty((T, p.num_q_heads, p.head_dim), dtype=torch.bfloat16, device="cuda")
+    pfa.attn_input(desc_of(p), pool, dev_bf16(ic.q_norm_w), dev_bf16(ic.k_norm_w),
+                   torch.from_numpy(ic.rope).cuda(), ic.eps, dev_bf16(ic.qkv), dev_i32(c.cu_q),
+                   dev_i32(c.seq_lens), dev_i32(c.block_table), q_out)
+    torch.cuda.synchronize()
+    return bits_of(q_out), pool
+
+
+def oracle_attn_input(ic: W.AttnInputCase):
+    """The oracle chain on an empty (poisoned) pool.  Returns (q_out bits, pool dict)."""
+    c = ic.case
+    p = c.p
+    pool = O.empty_pool(c.num_pages, p.num_kv_heads, p.page_size, p.head_dim, p.kv_dtype)
+    q = O.attention_input_to_pool(pool, ic.qkv, ic.q_norm_w, ic.k_norm_w, ic.eps, ic.rope, c.cu_q,
+                                  c.seq_lens, c.block_table, p.num_q_heads, p.num_kv_heads, p.head_dim,
+                                  p.page_size, p.kv_dtype)
+    return q, pool
+
+
+def pool_bits_equal(gpu_pool: pfa.KVPool, ref: dict, kv_dtype: str):
+    """Whole-pool comparison, bit for bit (poison included)."""
+    if kv_dtype == "bf16":
+        return (np.array_equal(bits_of(gpu_pool.k), ref["k"]) and
+                np.array_equal(bits_of(gpu_pool.v), ref["v"]))
+    f32 = lambda t: t.cpu().numpy().view(np.uint32)
+    return (np.array_equal(gpu_pool.k.cpu().numpy(), ref["k"]) and
+            np.array_equal(gpu_pool.v.cpu().numpy(), ref["v"]) and
+            np.array_equal(f32(gpu_pool.k_scale), ref["k_scale"].view(np.uint32)) and
+            np.array_equal(f32(gpu_pool.v_scale), ref["v_scale"].view(np.uint32)))

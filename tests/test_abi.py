@@ -83,6 +83,30 @@ def test_kv_write_validation():
     assert kvw(desc(), pool(), T=0, k=None) == OK              # nothing to do, nothing launched
 
 
+def ain(d, p, prm=True, **kw):
+    a = dict(qkv=FAKE, cu=FAKE, sl=FAKE, bt=FAKE, stride=8, batch=2, T=2, q=FAKE,
+             qw=FAKE.value, kw=FAKE.value, rope=FAKE.value, maxpos=64, eps=1e-6)
+    a.update(kw)
+    pr = pfa.CAttnInputParams(a["qw"], a["kw"], a["rope"], a["maxpos"], a["eps"]) if prm else None
+    return pfa.lib().pfa_attn_input(ctypes.byref(d), ctypes.byref(p), ctypes.byref(pr) if pr else None,
+                                    a["qkv"], a["cu"], a["sl"], a["bt"], a["stride"], a["batch"], a["T"],
+                                    a["q"], None)
+
+
+def test_attn_input_validation():
+    assert ain(desc(), pool(), prm=False) == NULL
+    assert ain(desc(), pool(), qw=None) == NULL
+    assert ain(desc(), pool(), rope=None) == NULL
+    assert ain(desc(), pool(), q=None) == NULL
+    assert ain(desc(), pool(), maxpos=0) == SHAPE
+    assert ain(desc(), pool(), eps=-1.0) == SHAPE
+    assert ain(desc(), pool(), eps=float("nan")) == SHAPE
+    assert ain(desc(head_dim=96), pool()) == UNSUP
+    assert ain(desc(kv_dtype=1), pool()) == NULL                # INT8 without scale pools
+    assert ain(desc(), pool(), batch=0) == SHAPE
+    assert ain(desc(), pool(), T=0, qkv=None) == OK
+
+
 def dec(d, p, **kw):
     a = dict(q=FAKE, bt=FAKE, stride=64, sl=FAKE, batch=4, max_len=1024, S=256, ms=4,
              op=FAKE, lp=FAKE, out=FAKE)

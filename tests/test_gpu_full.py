@@ -104,3 +104,26 @@ def test_verify_16tok_ctx1024():
 
 def test_verify_8tok_batch32_ctx512_8192():
     _prefill_check(W.verify_qwen4b(batch=32, tokens=8, lo=512, hi=8192), verify=True)
+
+
+def test_attn_input_prompt_8192_bitwise():
+    """Fused attention input for an 8192-token prompt (Qwen3-4B shape), bit for bit."""
+    from gpu_support import gpu_attn_input, oracle_attn_input, pool_bits_equal
+    ic = W.attn_input_qwen4b()
+    print(f"[full] {ic.name}", flush=True)
+    q, pool = gpu_attn_input(ic)
+    q_ref, pool_ref = oracle_attn_input(ic)
+    assert np.array_equal(q, q_ref), f"q_out differs in {np.sum(q != q_ref)} elements"
+    assert pool_bits_equal(pool, pool_ref, "bf16")
+
+
+def test_attn_input_decode_batch32_int8_bitwise():
+    """One new token for each of 32 sequences at 4096 positions, INT8 pool."""
+    from gpu_support import gpu_attn_input, oracle_attn_input, pool_bits_equal
+    ic = W.attn_input_case("attn_input_32x1_int8", 9, W.AttnParams(32, 8, 128, kv_dtype="int8"),
+                           np.full(32, 4096, np.int32), np.ones(32, np.int32))
+    q, pool = gpu_attn_input(ic)
+    q_ref, pool_ref = oracle_attn_input(ic)
+    assert np.array_equal(q, q_ref)
+    assert pool_bits_equal(pool, pool_ref, "int8")
+

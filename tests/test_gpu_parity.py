@@ -18,7 +18,7 @@ import oracle as O
 import paged_flash_attention_amd as pfa
 import workloads as W
 from gpu_support import (BF16_TOL, INT8_TOL, GpuCase, assert_close, bits_of, dev_bf16, dev_i32,
-                         oracle_pool, tol_of)
+                         gpu_attn_input, oracle_attn_input, oracle_pool, pool_bits_equal, tol_of)
 
 pytestmark = pytest.mark.gpu
 
@@ -35,6 +35,30 @@ def _need_gpu():
 def P(Hq, Hkv, D, window=0, sinks=False, kv="bf16", seed=0):
     return W.AttnParams(Hq, Hkv, D, kv_dtype=kv, window=window,
                         sinks=W.sinks_normal(seed + 31, Hq) if sinks else None)
+
+
+# ---------------------------------------------------------------------------
+# fused attention input (q/k RMSNorm + RoPE + KV write): bit for bit
+# ---------------------------------------------------------------------------
+
+ATTN_INPUT_CASES = [
+    # (params, seq_lens, new_lens, qkv_scale)
+    (dict(Hq=32, Hkv=8, D=128), [1, 40, 300], [1, 17, 300], 1.0),
+    (dict(Hq=32, Hkv=8, D=128, kv="int8"), [5, 70, 33], [5, 3, 33], 1.0),
+    (dict(Hq=64, Hkv=8, D=64), [2, 130, 17], [2, 130, 1], 4.0),
+    (dict(Hq=16, Hkv=4, D=64, kv="int8"), [9, 1, 600], [9, 1, 64], 0.25),
+    (dict(Hq=8, Hkv=8, D=128), [31, 16], [15, 16], 30.0),
+]
+
+
+@pytest.mark.parametrize("ci", range(len(ATTN_INPUT_CASES)))
+def test_attn_input_bitwise(ci):
+    prm, lens, new, scale = ATTN_INPUT_CASES[ci]
+    ic = W.attn_input_case(f"ain{ci}", 180 + ci, P(seed=ci, **prm), lens, new, qkv_scale=scale)
+    q, pool = gpu_attn_input(ic)
+    q_ref, pool_ref = oracle_attn_input(ic)
+    assert np.array_equal(q, q_ref), f"q_out differs in {np.sum(q != q_ref)} elements"
+    assert pool_bits_equal(pool, pool_ref, ic.case.p.kv_dtype), "pool differs"
 
 
 # ---------------------------------------------------------------------------

@@ -285,3 +285,61 @@ def verify_qwen4b(seed=6, batch=1, tokens=16, ctx=1024, lo=None, hi=None):
         name = f"verify_{tokens}tok_batch{batch}_ctx{ctx}"
     q_lens = np.full(batch, tokens, np.int32)
     return make_case(name, seed, p, ctxs + q_lens, q_lens, split_keys=0)
+
+
+# ---------------------------------------------------------------------------
+# Attention-input inputs: the fused q/k/v projection output of new tokens, the
+# q/k RMSNorm weights and the rotary table a model holds.
+# ---------------------------------------------------------------------------
+
+def rope_table(max_pos: int, head_dim: int, theta: float) -> np.ndarray:
+    """Rotary cos/sin table [max_pos, D/2, 2] float32, as a model holds it: the
+    angle of position p and pair i is p * theta^(-2i/D), evaluated in float64 and
+    rounded to float32 (Qwen3 uses theta = 1e6)."""
+    i = np.arange(head_dim // 2, dtype=np.float64)
+    inv = theta ** (-2.0 * i / head_dim)
+    ang = np.arange(max_pos, dtype=np.float64)[:, None] * inv[None, :]
+    return np.stack([np.cos(ang), np.sin(ang)], axis=-1).astype(np.float32)
+
+
+@dataclass
+class AttnInputCase:
+    """New tokens' fused qkv rows over a paged pool (``case`` gives the sequences,
+    the block table and the pool size; its own K/V draws are not used)."""
+    name: str
+    case: PagedCase
+    qkv: np.ndarray          # bf16 bits [T_new, (Hq + 2 Hkv) * D]
+    q_norm_w: np.ndarray     # bf16 bits [D]
+    k_norm_w: np.ndarray     # bf16 bits [D]
+    rope: np.ndarray         # float32 [max_pos, D/2, 2]
+    eps: float
+
+
+def attn_input_case(name, seed, p: AttnParams, seq_lens, new_lens, theta=1e6, eps=1e-6,
+                    qkv_scale=1.0) -> AttnInputCase:
+    """qkv ~ N(0, qkv_scale^2) rounded to bf16; norm weights 1 + 0.1 N(0,1) in bf16."""
+    case = make_case(name, seed, p, seq_lens, new_lens, split_keys=0)
+    rng = np.random.default_rng(seed + 11)
+    T = int(case.cu_q[-1])
+    width = (p.num_q_heads + 2 * p.num_kv_heads) * p.head_dim
+    qkv = normal_bf16(rng, (T, width)) if qkv_scale == 1.0 else _scaled_bf16(rng, (T, width), qkv_scale)
+    q_w = _scaled_bf16(rng, (p.head_dim,), 0.1, offset=1.0)
+    k_w = _scaled_bf16(rng, (p.head_dim,), 0.1, offset=1.0)
+    return AttnInputCase(name, case, qkv, q_w, k_w,
+                         rope_table(int(np.max(seq_lens)) + 1, p.head_dim, theta), eps)
+
+
+def _scaled_bf16(rng, shape, scale, offset=0.0):
+    x = (offset + scale * rng.standard_normal(shape)).astype(np.float32)
+    u = x.view(np.uint32).astype(np.uint64)
+    return ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+
+
+def attn_input_qwen4b(seed=8, prompt=8192, batch=1, prefix=0):
+    """Qwen3-4B attention shape (32 q / 8 KV heads, D 128): ``batch`` sequences of
+    ``prompt`` new tokens each on a ``prefix``-token prefix."""
+    p = AttnParams(32, 8, 128)
+    lens = np.full(batch, prefix + prompt, np.int32)
+    name = f"attn_input_{batch}x{prompt}" + (f"_on_{prefix}" if prefix else "")
+    return attn_input_case(name, seed, p, lens, np.full(batch, prompt, np.int32))
+
