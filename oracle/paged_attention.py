@@ -63,12 +63,15 @@ def bf16_to_f64(bits: np.ndarray) -> np.ndarray:
 # a2: the INT8 quantiser (numpy float32, the precision the stored scale has)
 # ---------------------------------------------------------------------------
 
-def quantize_int8(x_bits: np.ndarray):
+def quantize_int8(x_bits: np.ndarray, smooth=None):
     """Quantise bf16 vectors along the last axis to int8 codes + one float32 scale.
 
     Follows the TileInfer page, section "INT8 KV cache": one Int8 scale for each
     cached vector.  The steps, all in IEEE float32:
 
+    * with a per-channel ``smooth`` vector s (float32 [D], all > 0), the vector
+      quantised is ``x / s`` (the same section smooths keys by the key norm's
+      weight; a query then meets ``q * s``, leaving q.k unchanged);
     * ``scale = absmax / 127``;
     * ``code = clamp(rint(x / scale), -127, 127)``, where rint rounds ties to even;
     * an all-zero vector gets scale 0 and codes 0.
@@ -76,6 +79,8 @@ def quantize_int8(x_bits: np.ndarray):
     Returns ``(codes int8 [..., D], scale float32 [...])``.
     """
     x = bf16_to_f32(x_bits)
+    if smooth is not None:
+        x = (x / np.asarray(smooth, dtype=np.float32)).astype(np.float32)
     absmax = np.max(np.abs(x), axis=-1)
     scale = (absmax / np.float32(127.0)).astype(np.float32)
     safe = np.where(scale > 0, scale, np.float32(1.0)).astype(np.float32)
@@ -85,27 +90,36 @@ def quantize_int8(x_bits: np.ndarray):
     return codes, scale
 
 
-def dequantize_int8(codes: np.ndarray, scale: np.ndarray) -> np.ndarray:
-    """code * scale, exact in float64."""
-    return codes.astype(np.float64) * scale.astype(np.float64)[..., None]
+def dequantize_int8(codes: np.ndarray, scale: np.ndarray, smooth=None) -> np.ndarray:
+    """code * scale (* s per channel when smoothed), exact in float64."""
+    x = codes.astype(np.float64) * scale.astype(np.float64)[..., None]
+    if smooth is not None:
+        x = x * np.asarray(smooth, dtype=np.float32).astype(np.float64)
+    return x
 
 
 # ---------------------------------------------------------------------------
 # the page pool and a1/a2: writing new tokens
 # ---------------------------------------------------------------------------
 
-def empty_pool(num_pages: int, num_kv_heads: int, page_size: int, head_dim: int, kv_dtype: str):
+def empty_pool(num_pages: int, num_kv_heads: int, page_size: int, head_dim: int, kv_dtype: str,
+               k_smooth=None):
     """A pool whose every slot is poison.
 
     BF16 slots hold NaN.  INT8 slots hold code 0 with a NaN scale.
-    Layout: ``[num_pages, Hkv, P, D]``; scales ``[num_pages, Hkv, P]``.
+    Layout: ``[num_pages, Hkv, P, D]``; scales ``[num_pages, Hkv, P]``.  An INT8 pool
+    may carry ``k_smooth`` (float32 [D]): its keys are stored smoothed by it.
     """
     shape = (num_pages, num_kv_heads, page_size, head_dim)
     if kv_dtype == "bf16":
+        assert k_smooth is None, "key smoothing is an INT8 cache feature"
         return {"k": np.full(shape, 0x7FC0, np.uint16), "v": np.full(shape, 0x7FC0, np.uint16)}
-    return {"k": np.zeros(shape, np.int8), "v": np.zeros(shape, np.int8),
+    pool = {"k": np.zeros(shape, np.int8), "v": np.zeros(shape, np.int8),
             "k_scale": np.full(shape[:3], np.nan, np.float32),
             "v_scale": np.full(shape[:3], np.nan, np.float32)}
+    if k_smooth is not None:
+        pool["k_smooth"] = np.asarray(k_smooth, dtype=np.float32).copy()
+    return pool
 
 
 def slot_of(block_table_row: np.ndarray, pos: int, page_size: int):
@@ -120,7 +134,8 @@ def kv_write(pool: dict, k_new: np.ndarray, v_new: np.ndarray, cu_new: np.ndarra
     Token i of sequence s (rows ``cu_new[s]..cu_new[s+1]`` of ``k_new``/``v_new``,
     bf16 bits ``[T, Hkv, D]``) goes to position ``seq_lens[s] - n_s + i``.  Here
     ``seq_lens`` counts the tokens after the append.  BF16 pools take a copy of the
-    bits.  INT8 pools take the quantised codes and scales.  The TileInfer page
+    bits.  INT8 pools take the quantised codes and scales (keys divided by the
+    pool's ``k_smooth`` first, when it has one).  The TileInfer page
     (section "Fused kernels, ...") names the KV write as one of the engine's kernels.
     """
     B = len(seq_lens)
@@ -136,7 +151,7 @@ def kv_write(pool: dict, k_new: np.ndarray, v_new: np.ndarray, cu_new: np.ndarra
         pool["k"][pg, :, off, :] = k_new[:T]
         pool["v"][pg, :, off, :] = v_new[:T]
     else:
-        kc, ks = quantize_int8(k_new[:T])
+        kc, ks = quantize_int8(k_new[:T], pool.get("k_smooth"))
         vc, vs = quantize_int8(v_new[:T])
         pool["k"][pg, :, off, :] = kc
         pool["v"][pg, :, off, :] = vc
@@ -155,7 +170,7 @@ def gather(pool: dict, block_table_row: np.ndarray, n: int, page_size: int, kv_d
         K = bf16_to_f64(pool["k"][pg, :, off, :])
         V = bf16_to_f64(pool["v"][pg, :, off, :])
     else:
-        K = dequantize_int8(pool["k"][pg, :, off, :], pool["k_scale"][pg, :, off])
+        K = dequantize_int8(pool["k"][pg, :, off, :], pool["k_scale"][pg, :, off], pool.get("k_smooth"))
         V = dequantize_int8(pool["v"][pg, :, off, :], pool["v_scale"][pg, :, off])
     return K, V
 

@@ -431,3 +431,83 @@ def test_quantiser_bounds_and_argmax():
     assert np.all(err <= bound)
     # scale is the float32 quotient absmax/127
     np.testing.assert_array_equal(scale, (np.abs(x).max(axis=1).astype(np.float32) / np.float32(127)))
+
+
+# ---------------------------------------------------------------------------
+# INT8 key smoothing (keys stored as k / s per channel; queries meet q * s)
+# ---------------------------------------------------------------------------
+
+def test_smoothing_by_ones_is_no_smoothing():
+    rng = np.random.default_rng(21)
+    bits = W.normal_bf16(rng, (300, 128), outlier_frac=0.01)
+    c0, s0 = O.quantize_int8(bits)
+    c1, s1 = O.quantize_int8(bits, np.ones(128, np.float32))
+    assert np.array_equal(c0, c1) and np.array_equal(s0, s1)
+
+
+def test_smoothing_by_a_power_of_two_divides_the_scale_only():
+    rng = np.random.default_rng(22)
+    bits = W.normal_bf16(rng, (300, 64))
+    c0, s0 = O.quantize_int8(bits)
+    c1, s1 = O.quantize_int8(bits, np.full(64, 4.0, np.float32))
+    assert np.array_equal(c0, c1)
+    assert np.array_equal(s1, (s0 / np.float32(4)).astype(np.float32))
+
+
+def test_smoothed_dequantisation_bound():
+    rng = np.random.default_rng(23)
+    bits = W.normal_bf16(rng, (500, 64), outlier_frac=0.02)
+    s = (0.2 + rng.random(64) * 5).astype(np.float32)
+    codes, scale = O.quantize_int8(bits, s)
+    x = O.bf16_to_f64(bits)
+    err = np.abs(O.dequantize_int8(codes, scale, s) - x)
+    bound = scale.astype(np.float64)[:, None] * s.astype(np.float64)[None, :] * (0.5 + 2.0 ** -15) \
+        + np.abs(x) * 2.0 ** -22
+    assert np.all(err <= bound)
+
+
+def test_smoothed_attention_is_scaled_query_on_unsmoothed_codes():
+    """q . (code * scale * s) = (q * s) . (code * scale): the smoothing vector sits on
+    channels, so a brute force with the query scaled instead must agree."""
+    rng = np.random.default_rng(24)
+    p = W.AttnParams(4, 2, 8, page_size=2, kv_dtype="int8")
+    case = W.make_case("smooth", 24, p, [5, 3], [1, 1])
+    s = (0.5 + rng.random(8) * 3).astype(np.float32)
+    pool = O.empty_pool(case.num_pages, 2, 2, 8, "int8", k_smooth=s)
+    k, v, cu = case.k_tok, case.v_tok, case.cu_tok
+    O.kv_write(pool, k, v, cu, case.seq_lens, case.block_table, 2, "int8")
+    got = O.decode(case.q, pool, case.block_table, case.seq_lens, p)
+    for b in range(case.batch):
+        n = int(case.seq_lens[b])
+        for h in range(4):
+            g = h // 2
+            q = [bf16_bits_to_float(x) * float(s[d]) for d, x in enumerate(case.q[b, h])]
+            xs, vs = [], []
+            for j in range(n):
+                pg, off = int(case.block_table[b][j // 2]), j % 2
+                kc = pool["k"][pg, g, off].astype(np.float64) * float(pool["k_scale"][pg, g, off])
+                vc = pool["v"][pg, g, off].astype(np.float64) * float(pool["v_scale"][pg, g, off])
+                xs.append(p.sm_scale * math.fsum(qd * kd for qd, kd in zip(q, kc)))
+                vs.append(vc)
+            M = max(xs)
+            w = [math.exp(x - M) for x in xs]
+            Z = math.fsum(w)
+            ref = [math.fsum(wj * vj[d] for wj, vj in zip(w, vs)) / Z for d in range(8)]
+            np.testing.assert_allclose(got[b, h], ref, rtol=1e-12, atol=1e-13)
+
+
+def test_smoothing_by_the_channel_weight_helps_outlier_channels():
+    """Keys shaped like k_norm output (a unit-RMS vector times a per-channel weight with
+    a few large channels) quantise with less error when smoothed by that weight."""
+    rng = np.random.default_rng(25)
+    w = np.ones(128, np.float32)
+    w[[3, 77]] = 12.0
+    base = rng.standard_normal((2000, 128)).astype(np.float32)
+    bits = W.f32_to_bf16_bits((base * w).astype(np.float32))
+    x = O.bf16_to_f64(bits)
+    e0 = np.abs(O.dequantize_int8(*O.quantize_int8(bits)) - x)
+    c1, s1 = O.quantize_int8(bits, w)
+    e1 = np.abs(O.dequantize_int8(c1, s1, w) - x)
+    others = np.ones(128, bool)
+    others[[3, 77]] = False
+    assert e1[:, others].mean() < 0.5 * e0[:, others].mean()
