@@ -393,6 +393,7 @@ def main():
         "decode_batch32_ctx512_8192_fused": lambda: W.decode_batch32_ctx512_8192(),
         "decode_1seq_ctx1024": lambda: W.decode_1seq_ctx1024(),
         "decode_int8_batch8_ctx32768": lambda: W.decode_int8_qwen30b(),
+        "decode_int8_batch8_ctx32768_smooth": lambda: W.decode_int8_qwen30b(smooth=True),
         "mixed_full_decode_b64": lambda: W.mixed_gptoss(layer="full", part="decode"),
         "mixed_window_decode_b64": lambda: W.mixed_gptoss(layer="window", part="decode"),
         "prefill_causal_8192": lambda: W.prefill_llama8b(prompt=8192),
@@ -466,7 +467,7 @@ def main():
     if not args.no_extra and args.workload == "decode_batch32_ctx512_8192":
         for name, st in (("decode_batch32_ctx512_8192_fused", 50),
                          ("decode_batch32_ctx8192", 30), ("decode_batch32_ctx8192_s1024", 30),
-                         ("decode_int8_batch8_ctx32768", 30),
+                         ("decode_int8_batch8_ctx32768", 30), ("decode_int8_batch8_ctx32768_smooth", 30),
                          ("mixed_full_decode_b64", 30), ("prefill_causal_8192", 10),
                          ("prefill_chunk130_on_8192", 20), ("mixed_full_prefill_2x2048", 20),
                          ("verify_16tok_batch1_ctx1024", 50), ("verify_8tok_batch32_ctx512_8192", 30),

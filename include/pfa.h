@@ -79,13 +79,21 @@ typedef struct {
     const float* sinks;        /* device [Hq] fp32 sink logits, or NULL               */
 } pfa_attn_desc;
 
-/* The page pool. */
+/* The page pool.
+ *   k_smooth (INT8 only, optional): the key smoothing of the TileInfer.jl
+ *   performance page ("INT8 KV cache": keys smoothed by the key norm's weight).
+ *   A device [D] fp32 vector s, every s_d > 0 (e.g. |k_norm weight|).  The KV
+ *   writes quantise k/s (IEEE fp32 divide) per vector; decode meets q*s (rounded
+ *   to bf16), so q.k is unchanged in exact arithmetic.  The cache then
+ *   dequantises to code * scale * s.  NULL: no smoothing.  A BF16 pool with
+ *   k_smooth set is PFA_ERR_UNSUPPORTED. */
 typedef struct {
     void* k_pool;              /* device [num_pages][Hkv][P][D], bf16 or int8         */
     void* v_pool;              /* same                                                */
     float* k_scale;            /* device [num_pages][Hkv][P] fp32; INT8 only, else NULL */
     float* v_scale;            /* same                                                */
     int32_t num_pages;
+    const float* k_smooth;     /* device [D] fp32 key smoothing (INT8 only), or NULL  */
 } pfa_kv_pool;
 
 /*

@@ -54,7 +54,7 @@ class CAttnInputParams(ctypes.Structure):
 class CKvPool(ctypes.Structure):
     _fields_ = [("k_pool", ctypes.c_void_p), ("v_pool", ctypes.c_void_p),
                 ("k_scale", ctypes.c_void_p), ("v_scale", ctypes.c_void_p),
-                ("num_pages", ctypes.c_int32)]
+                ("num_pages", ctypes.c_int32), ("k_smooth", ctypes.c_void_p)]
 
 
 _lib = None
@@ -131,11 +131,13 @@ class AttnDesc:
 
 @dataclass
 class KVPool:
-    """k/v: [num_pages, Hkv, P, D] (bf16 or int8); scales [num_pages, Hkv, P] fp32 for INT8."""
+    """k/v: [num_pages, Hkv, P, D] (bf16 or int8); scales [num_pages, Hkv, P] fp32 for INT8.
+    k_smooth: optional [D] fp32 key smoothing of an INT8 pool (keys stored as k / s)."""
     k: torch.Tensor
     v: torch.Tensor
     k_scale: Optional[torch.Tensor] = None
     v_scale: Optional[torch.Tensor] = None
+    k_smooth: Optional[torch.Tensor] = None
 
     @property
     def num_pages(self) -> int:
@@ -153,7 +155,10 @@ class KVPool:
                 raise ValueError("an INT8 pool needs k_scale and v_scale")
             ks = _dev(self.k_scale, torch.float32, "k_scale").data_ptr()
             vs = _dev(self.v_scale, torch.float32, "v_scale").data_ptr()
-        return CKvPool(self.k.data_ptr(), self.v.data_ptr(), ks, vs, self.num_pages)
+        sm = None
+        if self.k_smooth is not None:
+            sm = _dev(self.k_smooth, torch.float32, "k_smooth").data_ptr()
+        return CKvPool(self.k.data_ptr(), self.v.data_ptr(), ks, vs, self.num_pages, sm)
 
 
 def _dev(t: Optional[torch.Tensor], dtype, name: str):

@@ -31,6 +31,7 @@ pfa_status check_desc(const pfa_attn_desc* d) {
 pfa_status check_pool(const pfa_attn_desc* d, const pfa_kv_pool* p) {
     if (!p || !p->k_pool || !p->v_pool) return PFA_ERR_NULL;
     if (d->kv_dtype == PFA_KV_INT8 && (!p->k_scale || !p->v_scale)) return PFA_ERR_NULL;
+    if (d->kv_dtype != PFA_KV_INT8 && p->k_smooth) return PFA_ERR_UNSUPPORTED;
     if (p->num_pages <= 0) return PFA_ERR_SHAPE;
     return PFA_OK;
 }
@@ -71,6 +72,7 @@ pfa_status pfa_kv_write(const pfa_attn_desc* desc, const pfa_kv_pool* pool, cons
     a.v_pool = pool->v_pool;
     a.k_scale = pool->k_scale;
     a.v_scale = pool->v_scale;
+    a.k_smooth = pool->k_smooth;
     a.bt_stride = bt_stride;
     a.batch = batch;
     a.num_tokens = num_tokens;
@@ -109,6 +111,7 @@ pfa_status pfa_attn_input(const pfa_attn_desc* desc, const pfa_kv_pool* pool,
     a.v_pool = pool->v_pool;
     a.k_scale = pool->k_scale;
     a.v_scale = pool->v_scale;
+    a.k_smooth = pool->k_smooth;
     a.eps = prm->eps;
     a.bt_stride = bt_stride;
     a.batch = batch;
@@ -162,6 +165,7 @@ pfa_status decode_like(const pfa_attn_desc* desc, const pfa_kv_pool* pool, const
     a.v_pool = pool->v_pool;
     a.k_scale = pool->k_scale;
     a.v_scale = pool->v_scale;
+    a.k_smooth = pool->k_smooth;
     a.block_table = block_table;
     a.seq_lens = seq_lens;
     a.sinks = desc->sinks;

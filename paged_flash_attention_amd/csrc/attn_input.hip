@@ -16,7 +16,8 @@
 //     out_i = bf16(a*c - b*s),  out_(i+D/2) = bf16(b*c + a*s),  a = y_i, b = y_(i+D/2)
 // q heads get RMSNorm(q_norm_w) + RoPE and go to q_out; k heads get
 // RMSNorm(k_norm_w) + RoPE and go to the pool; v heads go to the pool unchanged.
-// INT8 pools quantise the final k and v vectors as the KV write does.
+// INT8 pools quantise the final k and v vectors as the KV write does (keys
+// divided by the pool's smoothing vector first, when it has one).
 //
 // MI355X layout: one wave per token.  The token's sequence (a lane-parallel count
 // over cu_new), position, pool slot, RoPE row and both weight vectors are read
@@ -93,6 +94,16 @@ __global__ __launch_bounds__(256) void attn_input_kernel(AttnInputArgs a) {
             kw[2 * i] = bf16_lo(ka[i]); kw[2 * i + 1] = bf16_hi(ka[i]);
         }
     }
+    float ks[8];                    // INT8 key smoothing of the lane's 8 channels (1 = none)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) ks[e] = 1.0f;
+    const bool smooth = INT8 && a.k_smooth != nullptr;
+    if (smooth) {
+        const float4* sp = reinterpret_cast<const float4*>(a.k_smooth + chunk * 8);
+        const float4 s0 = __ldg(sp), s1 = __ldg(sp + 1);
+        ks[0] = s0.x; ks[1] = s0.y; ks[2] = s0.z; ks[3] = s0.w;
+        ks[4] = s1.x; ks[5] = s1.y; ks[6] = s1.z; ks[7] = s1.w;
+    }
     const uint16_t* row = a.qkv + (int64_t)tok * heads * D + chunk * 8;
     const bool lower = chunk < HALF;
 
@@ -145,6 +156,10 @@ __global__ __launch_bounds__(256) void attn_input_kernel(AttnInputArgs a) {
             for (int i = 0; i < 4; ++i) {
                 qv[2 * i] = is_v ? x[2 * i] : bf16_lo(ow[i]);
                 qv[2 * i + 1] = is_v ? x[2 * i + 1] : bf16_hi(ow[i]);
+            }
+            if (smooth && is_k) {   // keys smoothed per channel: quantise k / s
+#pragma unroll
+                for (int e = 0; e < 8; ++e) qv[e] = qv[e] / ks[e];
             }
             float m = 0.0f;
 #pragma unroll

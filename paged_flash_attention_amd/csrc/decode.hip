@@ -28,7 +28,9 @@
 //    device's HBM is already saturated with one per wave.
 //  * q.k: v_dot2_f32_bf16 on (q, k) bf16 pairs.  INT8 codes are offset to the
 //    unsigned byte c+128 (v_cvt_f32_ubyteN, exact in bf16), and 128*sum(q) is
-//    subtracted from the dot.  A lane's partial dots for the G heads go through a
+//    subtracted from the dot.  With key smoothing (keys stored as k/s per
+//    channel, the "INT8 KV cache" section's smoothing by the key norm's weight),
+//    q is first scaled by s and rounded to bf16.  A lane's partial dots for the G heads go through a
 //    transposed butterfly over the LPK lanes (DPP / swizzle moves).  Slot j of a
 //    lane holds head (j ^ myhead), so each stage adds a partner's upper half to its
 //    own lower half with no selects, and ends with the lane holding its own head's
@@ -253,6 +255,18 @@ void decode_kernel(DecodeArgs a) {
         const uint16_t* qp = a.q + (row0 + (j ^ myhead)) * D + sub * 8;
         const uint4 v = *reinterpret_cast<const uint4*>(qp);
         q[j][0] = v.x; q[j][1] = v.y; q[j][2] = v.z; q[j][3] = v.w;
+    }
+    if constexpr (INT8) {
+        if (a.k_smooth) {   // keys stored smoothed (k / s): the query meets q * s, rounded to bf16
+            const float4* sp = reinterpret_cast<const float4*>(a.k_smooth + sub * 8);
+            const float4 s0 = __ldg(sp), s1 = __ldg(sp + 1);
+            const float sv[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+#pragma unroll
+            for (int j = 0; j < G; ++j)
+#pragma unroll
+                for (int w = 0; w < 4; ++w)
+                    q[j][w] = pack_bf16_rne(bf16_lo(q[j][w]) * sv[2 * w], bf16_hi(q[j][w]) * sv[2 * w + 1]);
+        }
     }
     float qbias = 0.0f;   // INT8: 128 * sum_d q[myhead][d]
     if constexpr (INT8) {

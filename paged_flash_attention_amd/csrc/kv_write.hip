@@ -7,6 +7,8 @@
 //   scale = absmax/127 in IEEE fp32;
 //   code  = clamp(rint(x/scale), +-127), ties to even;
 //   a zero vector gets scale 0.
+// With a key smoothing vector s (same section: keys smoothed by the key norm's
+// weight), a key vector is divided by s per channel (IEEE fp32) before that.
 //
 // Each thread owns 8 consecutive elements (16 B of bf16 input) of one vector for
 // both K and V, so D/8 lanes share a vector.  The absmax is a max over those lanes
@@ -66,6 +68,13 @@ __global__ __launch_bounds__(256) void kv_write_kernel(KvWriteArgs a) {
             kx[2 * i + 1] = bf16_hi(kw[i]);
             vx[2 * i] = bf16_lo(vw[i]);
             vx[2 * i + 1] = bf16_hi(vw[i]);
+        }
+        if (a.k_smooth) {   // keys smoothed per channel: quantise k / s (IEEE divide)
+            const float4* sp = reinterpret_cast<const float4*>(a.k_smooth + chunk * 8);
+            const float4 s0 = __ldg(sp), s1 = __ldg(sp + 1);
+            const float sv[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+#pragma unroll
+            for (int i = 0; i < 8; ++i) kx[i] = kx[i] / sv[i];
         }
 #pragma unroll
         for (int i = 0; i < 8; ++i) {

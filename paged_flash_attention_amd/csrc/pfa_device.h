@@ -122,6 +122,7 @@ struct KvWriteArgs {
     void* v_pool;
     float* k_scale;
     float* v_scale;
+    const float* k_smooth;      // INT8: [D] per-channel key smoothing, or NULL
     int32_t bt_stride, batch, num_tokens, num_pages, num_kv_heads, head_dim;
 };
 
@@ -131,6 +132,7 @@ struct DecodeArgs {
     const void* v_pool;
     const float* k_scale;
     const float* v_scale;
+    const float* k_smooth;      // INT8: [D] per-channel key smoothing (q is scaled by it), or NULL
     const int32_t* block_table;
     const int32_t* seq_lens;
     const float* sinks;
@@ -156,6 +158,7 @@ struct AttnInputArgs {
     void* v_pool;
     float* k_scale;
     float* v_scale;
+    const float* k_smooth;      // INT8: [D] per-channel key smoothing, or NULL
     float eps;
     int32_t bt_stride, batch, num_tokens, num_pages, num_q_heads, num_kv_heads, rope_max_pos;
 };

@@ -40,7 +40,8 @@ def poisoned_pool(case: W.PagedCase) -> pfa.KVPool:
         return pfa.KVPool(k, k.clone())
     k = torch.zeros(shape, dtype=torch.int8, device="cuda")
     s = torch.full(shape[:3], float("nan"), dtype=torch.float32, device="cuda")
-    return pfa.KVPool(k, k.clone(), s, s.clone())
+    sm = None if case.k_smooth is None else torch.from_numpy(np.asarray(case.k_smooth, np.float32)).cuda()
+    return pfa.KVPool(k, k.clone(), s, s.clone(), sm)
 
 
 class GpuCase:
@@ -158,7 +159,8 @@ class GpuCase:
 
 def oracle_pool(case: W.PagedCase) -> dict:
     p = case.p
-    pool = O.empty_pool(case.num_pages, p.num_kv_heads, p.page_size, p.head_dim, p.kv_dtype)
+    pool = O.empty_pool(case.num_pages, p.num_kv_heads, p.page_size, p.head_dim, p.kv_dtype,
+                        k_smooth=case.k_smooth)
     k, v, cu = case.prefix_tokens()
     O.kv_write(pool, k, v, cu, case.prefix_lens(), case.block_table, p.page_size, p.kv_dtype)
     k, v, cu = case.new_tokens()
@@ -207,7 +209,8 @@ def oracle_attn_input(ic: W.AttnInputCase):
     """The oracle chain on an empty (poisoned) pool.  Returns (q_out bits, pool dict)."""
     c = ic.case
     p = c.p
-    pool = O.empty_pool(c.num_pages, p.num_kv_heads, p.page_size, p.head_dim, p.kv_dtype)
+    pool = O.empty_pool(c.num_pages, p.num_kv_heads, p.page_size, p.head_dim, p.kv_dtype,
+                        k_smooth=c.k_smooth)
     q = O.attention_input_to_pool(pool, ic.qkv, ic.q_norm_w, ic.k_norm_w, ic.eps, ic.rope, c.cu_q,
                                   c.seq_lens, c.block_table, p.num_q_heads, p.num_kv_heads, p.head_dim,
                                   p.page_size, p.kv_dtype)

@@ -53,7 +53,7 @@ def desc(**kw):
 
 
 def pool(**kw):
-    p = dict(k_pool=FAKE.value, v_pool=FAKE.value, k_scale=None, v_scale=None, num_pages=64)
+    p = dict(k_pool=FAKE.value, v_pool=FAKE.value, k_scale=None, v_scale=None, num_pages=64, k_smooth=None)
     p.update(kw)
     return pfa.CKvPool(**p)
 
@@ -64,6 +64,11 @@ def kvw(d, p, **kw):
     return pfa.lib().pfa_kv_write(ctypes.byref(d) if d is not None else None,
                                   ctypes.byref(p) if p is not None else None,
                                   a["k"], a["v"], a["cu"], a["sl"], a["bt"], a["stride"], a["batch"], a["T"], None)
+
+
+def test_key_smoothing_is_int8_only():
+    assert kvw(desc(), pool(k_smooth=FAKE.value)) == UNSUP
+    assert dec(desc(), pool(k_smooth=FAKE.value)) == UNSUP
 
 
 def test_kv_write_validation():

@@ -104,6 +104,65 @@ def test_kv_write_int8_bitwise(D):
     assert np.array_equal(vs.view(np.uint32), ref["v_scale"].view(np.uint32))
 
 
+@pytest.mark.parametrize("D", [64, 128])
+def test_kv_write_int8_smoothed_bitwise(D):
+    """Keys smoothed per channel (quantised as k / s): codes and scales bit-exact."""
+    w = W.key_norm_weight(90 + D, D)
+    case = W.make_case("kvw8s", 3, P(8, 2, D, kv="int8"), [3, 30, 70], [3, 30, 9], outlier_frac=0.01,
+                       key_weight=w)
+    g = GpuCase(case)
+    ref = oracle_pool(case)
+    torch.cuda.synchronize()
+    assert np.array_equal(g.pool.k.cpu().numpy(), ref["k"])
+    assert np.array_equal(g.pool.v.cpu().numpy(), ref["v"])
+    ks, vs = g.pool.k_scale.cpu().numpy(), g.pool.v_scale.cpu().numpy()
+    assert np.array_equal(ks.view(np.uint32), ref["k_scale"].view(np.uint32))
+    assert np.array_equal(vs.view(np.uint32), ref["v_scale"].view(np.uint32))
+
+
+def test_attn_input_int8_smoothed_bitwise():
+    ic = W.attn_input_case("ain_s", 186, P(32, 8, 128, kv="int8"), [9, 200, 40], [9, 100, 1], smooth=True)
+    q, pool = gpu_attn_input(ic)
+    q_ref, pool_ref = oracle_attn_input(ic)
+    assert np.array_equal(q, q_ref)
+    assert pool_bits_equal(pool, pool_ref, "int8")
+
+
+SMOOTH_CASES = [
+    (dict(Hq=32, Hkv=4, D=128, kv="int8"), [1, 33, 257, 2000], [256, 0]),
+    (dict(Hq=16, Hkv=4, D=64, kv="int8", window=50, sinks=True), [7, 64, 300], [32, 0]),
+]
+
+
+@pytest.mark.parametrize("ci", range(len(SMOOTH_CASES)))
+def test_decode_int8_smoothed(ci):
+    """Decode over a key-smoothed INT8 cache meets the oracle on that cache.  Beside
+    it, reported: the error against the BF16-cache oracle with and without smoothing,
+    on keys shaped by a key-norm weight with large channels (smoothing must help)."""
+    prm, lens, splits = SMOOTH_CASES[ci]
+    w = W.key_norm_weight(95 + ci, prm["D"])
+    kw = dict(outlier_frac=0.0, key_weight=w)
+    case_s = W.make_case(f"sm{ci}", 190 + ci, P(seed=ci, **prm), lens, np.ones(len(lens), np.int32), **kw)
+    g = GpuCase(case_s)
+    ref = O.decode(case_s.q, oracle_pool(case_s), case_s.block_table, case_s.seq_lens, case_s.p)
+    outs = {}
+    for S in splits:
+        outs[S] = g.decode(split_keys=S)
+        assert_close(outs[S], ref, INT8_TOL, f"smoothed decode case {ci} S={S}")
+    # the same keys in a BF16 cache and in an unsmoothed INT8 cache
+    prm_bf = dict(prm, kv="bf16")
+    case_bf = W.make_case(f"sm{ci}b", 190 + ci, P(seed=ci, **prm_bf), lens, np.ones(len(lens), np.int32), **kw)
+    case_bf.k_smooth = None
+    exact = O.decode(case_bf.q, oracle_pool(case_bf), case_bf.block_table, case_bf.seq_lens, case_bf.p)
+    case_u = W.make_case(f"sm{ci}u", 190 + ci, P(seed=ci, **prm), lens, np.ones(len(lens), np.int32), **kw)
+    case_u.k_smooth = None
+    plain = GpuCase(case_u).decode(split_keys=splits[0])
+    e_s = float(np.sqrt(np.mean((outs[splits[0]] - exact) ** 2)))
+    e_u = float(np.sqrt(np.mean((plain - exact) ** 2)))
+    print(f"rms error vs the BF16 cache: smoothed {e_s:.3e}, unsmoothed {e_u:.3e}", flush=True)
+    assert e_s < e_u
+
+
 # ---------------------------------------------------------------------------
 # decode + combine
 # ---------------------------------------------------------------------------

@@ -141,6 +141,7 @@ class PagedCase:
     q: np.ndarray
     split_keys: int = 256
     meta: dict = field(default_factory=dict)
+    k_smooth: Optional[np.ndarray] = None   # INT8 pools: [D] float32 key smoothing, or None
 
     @property
     def batch(self) -> int:
@@ -184,8 +185,13 @@ class PagedCase:
 
 
 def make_case(name, seed, p: AttnParams, seq_lens, q_lens, pool_pages=None,
-              outlier_frac=0.0, split_keys=256, sink_seed_offset=1000, meta=None) -> PagedCase:
-    """Draw K/V for every token, queries for the new tokens, and a page assignment."""
+              outlier_frac=0.0, split_keys=256, sink_seed_offset=1000, meta=None,
+              key_weight=None) -> PagedCase:
+    """Draw K/V for every token, queries for the new tokens, and a page assignment.
+
+    ``key_weight`` (float32 [D], INT8 cases): keys are drawn as N(0,1) times this
+    per-channel weight (the shape a key-norm weight gives them), and the pool
+    smooths keys by it."""
     rng = np.random.default_rng(seed)
     seq_lens = np.asarray(seq_lens, dtype=np.int32)
     q_lens = np.asarray(q_lens, dtype=np.int32)
@@ -196,12 +202,16 @@ def make_case(name, seed, p: AttnParams, seq_lens, q_lens, pool_pages=None,
     T = int(cu_tok[-1])
     k_tok = normal_bf16(rng, (T, p.num_kv_heads, p.head_dim), outlier_frac)
     v_tok = normal_bf16(rng, (T, p.num_kv_heads, p.head_dim), outlier_frac)
+    if key_weight is not None:
+        kf = (k_tok.astype(np.uint32) << np.uint32(16)).view(np.float32)
+        k_tok = f32_to_bf16_bits((kf * np.asarray(key_weight, np.float32)).astype(np.float32))
     cu_q = np.zeros(len(seq_lens) + 1, dtype=np.int32)
     cu_q[1:] = np.cumsum(q_lens)
     q = normal_bf16(rng, (int(cu_q[-1]), p.num_q_heads, p.head_dim))
     return PagedCase(name=name, p=p, seq_lens=seq_lens, q_lens=q_lens, cu_q=cu_q,
                      cu_tok=cu_tok, block_table=bt, num_pages=num_pages, spare_page=spare,
-                     k_tok=k_tok, v_tok=v_tok, q=q, split_keys=split_keys, meta=meta or {})
+                     k_tok=k_tok, v_tok=v_tok, q=q, split_keys=split_keys, meta=meta or {},
+                     k_smooth=None if key_weight is None else np.asarray(key_weight, np.float32))
 
 
 def sinks_normal(seed, n):
@@ -245,12 +255,24 @@ def prefill_llama8b(seed=3, prompt=1024, prefix=0):
     return make_case(name, seed, p, [prefix + prompt], [prompt], split_keys=0)
 
 
-def decode_int8_qwen30b(seed=4, batch=8, ctx=32768):
+def key_norm_weight(seed: int, head_dim: int, n_large: int = 4, large: float = 8.0) -> np.ndarray:
+    """A synthetic key-norm weight (float32 [D], > 0): 1 + |N(0, 0.3)| per channel,
+    with ``n_large`` channels at ``large`` (the few large channels such weights have)."""
+    rng = np.random.default_rng(seed)
+    w = (1.0 + np.abs(0.3 * rng.standard_normal(head_dim))).astype(np.float32)
+    w[rng.choice(head_dim, n_large, replace=False)] = large
+    return (f32_to_bf16_bits(w).astype(np.uint32) << np.uint32(16)).view(np.float32)   # bf16 values
+
+
+def decode_int8_qwen30b(seed=4, batch=8, ctx=32768, smooth=False):
     """Qwen3-30B-A3B attention shape (32 q / 4 KV heads, D 128), INT8 KV, batch 8 at
-    32768 positions; raw K/V N(0,1) with 1% outliers at +-8."""
+    32768 positions; raw K/V N(0,1) with 1% outliers at +-8.  ``smooth``: keys
+    shaped by a synthetic key-norm weight and the pool smoothing keys by it."""
     p = AttnParams(32, 4, 128, kv_dtype="int8")
-    return make_case(f"decode_int8_batch{batch}_ctx{ctx}", seed, p, np.full(batch, ctx, np.int32),
-                     np.ones(batch, np.int32), outlier_frac=0.01, split_keys=256)
+    name = f"decode_int8_batch{batch}_ctx{ctx}" + ("_smooth" if smooth else "")
+    return make_case(name, seed, p, np.full(batch, ctx, np.int32), np.ones(batch, np.int32),
+                     outlier_frac=0.01, split_keys=256,
+                     key_weight=key_norm_weight(seed + 50, 128) if smooth else None)
 
 
 def mixed_gptoss(seed=5, layer="window", part="decode", batch=64, lo=128, hi=32768,
@@ -316,8 +338,9 @@ class AttnInputCase:
 
 
 def attn_input_case(name, seed, p: AttnParams, seq_lens, new_lens, theta=1e6, eps=1e-6,
-                    qkv_scale=1.0) -> AttnInputCase:
-    """qkv ~ N(0, qkv_scale^2) rounded to bf16; norm weights 1 + 0.1 N(0,1) in bf16."""
+                    qkv_scale=1.0, smooth=False) -> AttnInputCase:
+    """qkv ~ N(0, qkv_scale^2) rounded to bf16; norm weights 1 + 0.1 N(0,1) in bf16.
+    ``smooth`` (INT8): the pool smooths keys by |k norm weight|."""
     case = make_case(name, seed, p, seq_lens, new_lens, split_keys=0)
     rng = np.random.default_rng(seed + 11)
     T = int(case.cu_q[-1])
@@ -325,6 +348,8 @@ def attn_input_case(name, seed, p: AttnParams, seq_lens, new_lens, theta=1e6, ep
     qkv = normal_bf16(rng, (T, width)) if qkv_scale == 1.0 else _scaled_bf16(rng, (T, width), qkv_scale)
     q_w = _scaled_bf16(rng, (p.head_dim,), 0.1, offset=1.0)
     k_w = _scaled_bf16(rng, (p.head_dim,), 0.1, offset=1.0)
+    if smooth:
+        case.k_smooth = np.abs((k_w.astype(np.uint32) << np.uint32(16)).view(np.float32))
     return AttnInputCase(name, case, qkv, q_w, k_w,
                          rope_table(int(np.max(seq_lens)) + 1, p.head_dim, theta), eps)
 
