@@ -212,6 +212,17 @@ def test_decode_many_splits(ci):
     assert_close(g.decode(split_keys=S), ref, tol_of(case), f"many-split case {ci}")
 
 
+def test_decode_batch_2048_short():
+    """Many short sequences: far more rows than splits, one page or less each."""
+    rng = np.random.default_rng(81)
+    lens = list(rng.integers(1, 40, 2048))
+    case = W.make_case("b2048", 161, P(8, 2, 128), lens, np.ones(2048, np.int32))
+    g = GpuCase(case)
+    ref = O.decode(case.q, oracle_pool(case), case.block_table, case.seq_lens, case.p)
+    for S in (0, 16):
+        assert_close(g.decode(split_keys=S), ref, BF16_TOL, f"batch 2048 S={S}")
+
+
 def test_decode_batch_600():
     """A large batch of short windowed sequences with sinks."""
     rng = np.random.default_rng(78)
@@ -296,6 +307,10 @@ PREFILL_CASES = [
     (dict(Hq=4, Hkv=2, D=64, window=7), [90, 33], [90, 20]),
     (dict(Hq=32, Hkv=2, D=64), [77], [77]),                              # G = 16
     (dict(Hq=32, Hkv=1, D=128, window=64), [150], [150]),                # G = 32
+    (dict(Hq=32, Hkv=8, D=128), [63, 64, 65, 128, 255, 256, 257], [63, 64, 65, 128, 255, 256, 257]),  # tile edges
+    (dict(Hq=16, Hkv=4, D=128, sinks=True), [100, 50, 200, 9], [10, 0, 64, 0]),  # sequences with no new tokens
+    (dict(Hq=8, Hkv=4, D=64, window=1, sinks=True), [70, 33], [70, 5]),  # window 1: each row sees itself
+    (dict(Hq=32, Hkv=8, D=128, window=100), [1037, 16], [37, 16]),       # prefix not page-aligned
 ]
 
 
