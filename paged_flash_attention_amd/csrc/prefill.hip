@@ -10,15 +10,12 @@
 //  * A workgroup is 8 waves and owns 256 query rows of one (sequence, KV head).
 //    A row is one (token, head-of-group) pair, so the G query heads sharing a KV
 //    head share every K/V tile (GQA packing).  Each wave owns 32 rows.
-//  * K/V go HBM -> LDS with global_load_lds_dwordx4, with no register staging, as
-//    64-key tiles (4 pages) in two rings, one for K (5 tiles) and one for V (4).
-//    A tile's K is read an iteration before its V, so split rings give every
-//    load three iterations to land, in less LDS than a joint K+V ring allowing
-//    two.  One barrier per tile (after each wave's own vmcnt wait) publishes the
-//    K tile of the iteration after next and the V tile of this iteration's PV,
-//    so it sits in the middle of an iteration while the matrix core still has
-//    queued work.  The page ids of later tiles are read (wave-uniform, scalar
-//    loads) a tile before they are needed.
+//  * K/V go HBM -> LDS with global_load_lds_dwordx4, with no register staging, in
+//    a 5-stage ring of 64-key tiles (4 pages).  A tile is made visible (each wave
+//    waits on its own vmcnt, then the one barrier per tile) two iterations before
+//    its PV, so the barrier sits in the middle of an iteration while the matrix
+//    core still has queued work.  The page ids of later tiles are read
+//    (wave-uniform, scalar loads) a tile before they are needed.
 //  * The loop is software-pipelined within each wave, so that the matrix cores
 //    and the VALU work at the same time (on gfx950 each MFMA issue also takes
 //    VALU issue cycles, so the VALU work is spread evenly): the QK^T MFMAs of
@@ -49,8 +46,8 @@
 //        (log2 units), so p <= 2^8.
 //  * Causal/window masking costs nothing on tiles that are fully visible.  A wave
 //    skips the MFMAs of tiles that lie entirely outside its rows' ranges.  V rows
-//    past the sequence end are loaded from a written row of the same page, so
-//    poison in unwritten page slots never meets a zero weight.
+//    past the sequence end are zeroed in LDS, so poison in unwritten page slots
+//    never meets a zero weight.
 //  * Workgroups map to XCDs so that each XCD's L2 holds the K/V of the heads it
 //    serves.  Within an XCD the longest (latest) query tiles go first.
 //  * Split mode covers a short chunk on a long prefix, such as 130 new tokens on
@@ -60,10 +57,10 @@
 //    log-sum-exp, and the combine kernel then merges them with the sink.
 #include "pfa_device.h"
 
-// Two builds of this file: the default one (256-row workgroups, 64-key tiles,
-// 144 KB of LDS at D = 128, one workgroup per CU) and, from prefill_split.hip, the
-// KV-split one (128-row workgroups, 32-key tiles, 72 KB, two workgroups per CU),
-// which fills the chip better when a short chunk is spread over key splits.
+// Two builds of this file: the default one (256-row workgroups, 64-key tiles, one
+// workgroup per CU) and, from prefill_split.hip, the KV-split one (128-row
+// workgroups, 32-key tiles, 64 KB of LDS, two workgroups per CU), which fills the
+// chip better when a short chunk is spread over key splits.
 #ifndef PFA_PREFILL_BN
 #define PFA_PREFILL_BN 64
 #define PFA_PREFILL_ROWS_WG kPrefillRows
@@ -77,11 +74,7 @@ constexpr int kRowsPerWave = 32;
 constexpr int kWaves = PFA_PREFILL_ROWS_WG / kRowsPerWave;
 constexpr int kThreads = kWaves * kWave;
 constexpr int kBN = PFA_PREFILL_BN;   // keys per tile
-// K and V tiles sit in two LDS rings.  A tile's K is read one iteration before its
-// V, so the K ring holds one more tile; both rings run kLook iterations ahead.
-constexpr int kLook = 3;             // iterations between a tile's load and its use
-constexpr int kKSlots = kLook + 2;   // K ring: tiles kb+1 .. kb+5 around ring(kb)
-constexpr int kVSlots = kLook + 1;   // V ring: tiles kb-1 .. kb+3
+constexpr int kStages = 5;        // LDS ring depth: tiles kb-1 .. kb+3 around tile kb
 constexpr int kPairs1 = kBN == 64 ? 12 : 6;   // of a tile's 8*kBN/32 score pairs per lane,
                                   // those whose exps run beside the QK^T MFMAs (the rest beside PV)
 constexpr int kXcds = 8;
@@ -163,8 +156,8 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a, const 
     constexpr int NL = 2 * DMA_PER_WAVE;                // vector-memory ops per tile per wave
     static_assert(DMA_PER_WAVE >= 1, "tile split");
 
-    // the K ring then the V ring, kBN x D tiles each (swizzled)
-    __shared__ __attribute__((aligned(1024))) uint16_t ring_lds[(kKSlots + kVSlots) * kBN * D];
+    // ring of kStages stages, each a K tile then a V tile (keys x D, swizzled)
+    __shared__ __attribute__((aligned(1024))) uint16_t ring_lds[kStages * 2 * kBN * D];
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);   // wave-uniform
@@ -263,42 +256,28 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a, const 
     auto clamp_page = [&](int v) __attribute__((always_inline)) { return min(max(v, 0), a.num_pages - 1); };
     const int lrow = lane / CPR;                          // row within one direct load
     const int lchunk = lane % CPR;                        // physical chunk this lane fills
-    // per-lane byte offsets within a page-head block (the same for every tile);
-    // vfirst is the page's first row in the chunk order of this lane's V row
-    uint32_t koff[DMA_PER_WAVE], voff[DMA_PER_WAVE], vfirst[DMA_PER_WAVE];
-    int vrow[DMA_PER_WAVE];                               // the V row's place in the tile
+    // per-lane byte offsets within a page-head block (the same for every tile)
+    uint32_t koff[DMA_PER_WAVE], voff[DMA_PER_WAVE];
 #pragma unroll
     for (int i = 0; i < DMA_PER_WAVE; ++i) {
         const int row = (wave * DMA_PER_WAVE + i) * ROWS_PER_DMA + lrow;
         koff[i] = 2u * ((row % kPage) * D + (lchunk ^ swz_k<D>(row)) * 8);
-        vfirst[i] = 2u * ((lchunk ^ swz_v<D>(row)) * 8);
-        voff[i] = 2u * ((row % kPage) * D) + vfirst[i];
-        vrow[i] = row;
+        voff[i] = 2u * ((row % kPage) * D + (lchunk ^ swz_v<D>(row)) * 8);
     }
     const uint16_t* kpool_h = uniform_ptr(a.k_pool + (int64_t)kvh * hblk);
     const uint16_t* vpool_h = uniform_ptr(a.v_pool + (int64_t)kvh * hblk);
     const int64_t page_stride = (int64_t)a.num_kv_heads * hblk;
-    // LDS byte addresses of the rings' slots
+    // LDS byte addresses: the ring's stages, each a K tile then a V tile
     const uint32_t ring0 = lds_addr(ring_lds);
     constexpr uint32_t kTileBytes = kBN * D * 2;
-    // this wave's rows of one tile's K (or V), from page pg into the slot at dst
-    auto issue_k = [&](int pg, uint32_t dst) __attribute__((always_inline)) {
+    auto issue = [&](int pg, uint32_t kdst, uint32_t vdst) __attribute__((always_inline)) {
         const int64_t pbase = (int64_t)pg * page_stride;
 #pragma unroll
-        for (int i = 0; i < DMA_PER_WAVE; ++i)
-            dma16(kpool_h + pbase, koff[i], dst + (wave * DMA_PER_WAVE + i) * ROWS_PER_DMA * D * 2);
-    };
-    // V rows of tile kb past the sequence end come from the page's first row (a
-    // written key): the unwritten slots may hold anything, and 0 * NaN would reach
-    // the output, while a finite row under a zero weight adds nothing.  (K rows
-    // past the end only feed scores that the mask replaces.)
-    auto issue_v = [&](int pg, uint32_t dst, int kb) __attribute__((always_inline)) {
-        const int64_t pbase = (int64_t)pg * page_stride;
-        const int lim = n - kb * kBN;
-#pragma unroll
-        for (int i = 0; i < DMA_PER_WAVE; ++i)
-            dma16(vpool_h + pbase, vrow[i] < lim ? voff[i] : vfirst[i],
-                  dst + (wave * DMA_PER_WAVE + i) * ROWS_PER_DMA * D * 2);
+        for (int i = 0; i < DMA_PER_WAVE; ++i) {
+            const uint32_t row0 = (wave * DMA_PER_WAVE + i) * ROWS_PER_DMA;
+            dma16(kpool_h + pbase, koff[i], kdst + row0 * D * 2);
+            dma16(vpool_h + pbase, voff[i], vdst + row0 * D * 2);
+        }
     };
 
     // ---- accumulators ----
@@ -487,35 +466,42 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a, const 
         }
         if (FUSED) rescale(mt);
     };
-    // Software pipeline over the two rings.  Tile kb's K sits in K slot
-    // (kb - kb0) % kKSlots, its V in V slot (kb - kb0) % kVSlots.  Every wave runs
-    // ring(kb) once for each tile kb0..kb1.  ring(kb) waits for this wave's loads of
-    // K_{kb+2} and V_kb, and the barrier then makes everyone's visible.  It then
-    // issues K_{kb+2+kLook} into the slot of K_kb and V_{kb+kLook} into that of
-    // V_{kb-1}, both read before the barrier (tiles clamped to kb1, so the load
-    // count stays balanced): a load has kLook iterations to land.  K runs two tiles
-    // ahead of V, so the barrier can sit in the middle of an iteration, where the
-    // matrix core still has block 1's MFMAs to run:
+    // rows of a tile past the sequence end hold whatever the page slots hold: zero V
+    auto zero_tail = [&](int kb, uint32_t vs) __attribute__((always_inline)) {
+        if (kb <= kb1 && kb * kBN + kBN > n) {
+            const int r0 = max(0, n - kb * kBN);
+            for (int e = tid; e < (kBN - r0) * CPR; e += kThreads)
+                *(LDS3 u32x4*)(uintptr_t)(vs + 2 * ((r0 + e / CPR) * D + (e % CPR) * 8)) = u32x4{0u, 0u, 0u, 0u};
+        }
+    };
+
+    // Software pipeline over a 5-stage ring.  Tile kb sits in stage
+    // (kb - kb0) % kStages.  Every wave runs ring(kb) once for each tile kb0..kb1;
+    // ring(kb) makes tile kb+2 visible (each wave waits for its own direct loads,
+    // then the barrier), refills the stage of tile kb-1 with tile kb+4 (clamped to
+    // kb1, so the load count stays balanced) and zeroes tile kb+2's V rows past the
+    // sequence end (visible from the next barrier on).  Because tiles are made
+    // visible two iterations before their PV, the barrier can sit in the middle of
+    // an iteration, where the matrix core still has block 1's MFMAs to run:
     //   block 1: S' = K_{kb+1} Q^T (MFMA) interleaved with most of P = exp2(S - m);
     //   ring(kb), with the first V reads of block 2 issued right after the barrier;
     //   block 2: O += P V_kb (MFMA) interleaved with the rest of the exps and the
     //     row max of S', then the rescale for tile kb+1.
     // A wave computes only on the tiles kw0..kw1 its rows see; the range's first
     // tile gets its S before ring(kw0 - 1), its last one only P and PV.
-    auto kst = [&](int kb) { return ring0 + (uint32_t)((kb - kb0) % kKSlots) * kTileBytes; };
-    auto vst = [&](int kb) { return ring0 + (uint32_t)(kKSlots + (kb - kb0) % kVSlots) * kTileBytes; };
-    int pgk_raw, pgv_raw;                      // raw page entries of the next ring's K and V tiles
+    auto kst = [&](int kb) { return ring0 + (uint32_t)((kb - kb0) % kStages) * (2 * kTileBytes); };
+    auto vst = [&](int kb) { return kst(kb) + kTileBytes; };
+    int pg_raw;                                // raw page entry of tile min(kb + 4, kb1)
     // ring in two parts, so that LDS reads can be issued right after the barrier
     auto ring_pre = [&](int kb) __attribute__((always_inline)) {
-        // in flight: the loads of ring(kb - kLook) .. ring(kb - 1)
-        wait_vmcnt<(kLook - 1) * NL>();        // this wave's share of K_{kb+2} and V_kb landed
-        lds_sync();                            // everyone's
+        // in flight: tiles kb+2 and kb+3 (kb+4 is issued below)
+        wait_vmcnt<NL>();                      // this wave's share of tile kb+2 landed
+        lds_sync();                            // everyone's; tile kb-1's stage is free
     };
     auto ring_post = [&](int kb) __attribute__((always_inline)) {
-        issue_k(clamp_page(pgk_raw), kst(kb + 2 + kLook));
-        issue_v(clamp_page(pgv_raw), vst(kb + kLook), min(kb + kLook, kb1));
-        pgk_raw = raw_page(min(kb + 3 + kLook, kb1));
-        pgv_raw = raw_page(min(kb + 1 + kLook, kb1));
+        issue(clamp_page(pg_raw), kst(kb + 4), vst(kb + 4));   // tile min(kb + 4, kb1)
+        pg_raw = raw_page(min(kb + 5, kb1));
+        zero_tail(kb + 2, vst(kb + 2));
     };
     auto ring = [&](int kb) __attribute__((always_inline)) { ring_pre(kb); ring_post(kb); };
     // this wave's tiles
@@ -526,19 +512,13 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a, const 
     }
     const bool any = kw0 <= kw1;
 
-    // prologue: K_{kb0} and K_{kb0+1}, then the loads that ring(kb0 - kLook) ..
-    // ring(kb0 - 1) would have issued
-    issue_k(clamp_page(raw_page(kb0)), kst(kb0));
-    issue_k(clamp_page(raw_page(min(kb0 + 1, kb1))), kst(kb0 + 1));
 #pragma unroll
-    for (int i = 0; i < kLook; ++i) {
-        issue_k(clamp_page(raw_page(min(kb0 + 2 + i, kb1))), kst(kb0 + 2 + i));
-        issue_v(clamp_page(raw_page(min(kb0 + i, kb1))), vst(kb0 + i), min(kb0 + i, kb1));
-    }
-    pgk_raw = raw_page(min(kb0 + 2 + kLook, kb1));
-    pgv_raw = raw_page(min(kb0 + kLook, kb1));
-    wait_vmcnt<kLook * NL>();                  // K_{kb0} and K_{kb0+1} landed
+    for (int i = 0; i < 4; ++i) issue(clamp_page(raw_page(min(kb0 + i, kb1))), kst(kb0 + i), vst(kb0 + i));
+    pg_raw = raw_page(min(kb0 + 4, kb1));
+    wait_vmcnt<2 * NL>();                      // tiles kb0, kb0+1 landed (kb0+2, kb0+3 in flight)
     lds_sync();
+    zero_tail(kb0, vst(kb0));                  // visible after the next barrier
+    zero_tail(kb0 + 1, vst(kb0 + 1));
 
     Scores s_a, s_b;                           // scores of the current / next tile
     Packed pk;
