@@ -57,10 +57,10 @@
 //    log-sum-exp, and the combine kernel then merges them with the sink.
 #include "pfa_device.h"
 
-// Two builds of this file: the default one (256-row workgroups, 64-key tiles, one
-// workgroup per CU) and, from prefill_split.hip, the KV-split one (128-row
-// workgroups, 32-key tiles, 64 KB of LDS, two workgroups per CU), which fills the
-// chip better when a short chunk is spread over key splits.
+// Two builds of this file: the default one (256-row workgroups, 64-key tiles,
+// 160 KB of LDS at D = 128, one workgroup per CU) and, from prefill_split.hip, the
+// KV-split one (128-row workgroups, 32-key tiles, 80 KB, two workgroups per CU),
+// which fills the chip better when a short chunk is spread over key splits.
 #ifndef PFA_PREFILL_BN
 #define PFA_PREFILL_BN 64
 #define PFA_PREFILL_ROWS_WG kPrefillRows
