@@ -376,7 +376,7 @@ const char* pfa_status_string(pfa_status s) {
         case PFA_OK: return "ok";
         case PFA_ERR_NULL: return "a required pointer is NULL";
         case PFA_ERR_SHAPE: return "sizes inconsistent or out of range";
-        case PFA_ERR_UNSUPPORTED: return "shape or dtype not supported by this build";
+        case PFA_ERR_UNSUPPORTED: return "shape or dtype not supported by the library";
         case PFA_ERR_WORKSPACE: return "split buffers too small (max_splits < ceil(max_seq_len/split_keys))";
         case PFA_ERR_HIP: return "HIP launch failed";
     }
