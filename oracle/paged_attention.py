@@ -42,6 +42,8 @@ import math
 
 import numpy as np
 
+from . import tq3
+
 NEG_INF = -math.inf
 
 
@@ -106,14 +108,21 @@ def empty_pool(num_pages: int, num_kv_heads: int, page_size: int, head_dim: int,
                k_smooth=None):
     """A pool whose every slot is poison.
 
-    BF16 slots hold NaN.  INT8 slots hold code 0 with a NaN scale.
-    Layout: ``[num_pages, Hkv, P, D]``; scales ``[num_pages, Hkv, P]``.  An INT8 pool
-    may carry ``k_smooth`` (float32 [D]): its keys are stored smoothed by it.
+    BF16 slots hold NaN.  INT8 and 3-bit slots hold code 0 with a NaN scale.
+    Layout: ``[num_pages, Hkv, P, D]``; scales ``[num_pages, Hkv, P]``.  A 3-bit
+    ("tq3") pool holds bit planes ``[num_pages, Hkv, P, 3, D/8]`` (see ``tq3``).  An
+    INT8 pool may carry ``k_smooth`` (float32 [D]): its keys are stored smoothed by it.
     """
     shape = (num_pages, num_kv_heads, page_size, head_dim)
     if kv_dtype == "bf16":
         assert k_smooth is None, "key smoothing is an INT8 cache feature"
         return {"k": np.full(shape, 0x7FC0, np.uint16), "v": np.full(shape, 0x7FC0, np.uint16)}
+    if kv_dtype == "tq3":
+        assert k_smooth is None, "key smoothing is an INT8 cache feature"
+        pshape = shape[:3] + (3, head_dim // 8)
+        return {"k": np.zeros(pshape, np.uint8), "v": np.zeros(pshape, np.uint8),
+                "k_scale": np.full(shape[:3], np.nan, np.float32),
+                "v_scale": np.full(shape[:3], np.nan, np.float32)}
     pool = {"k": np.zeros(shape, np.int8), "v": np.zeros(shape, np.int8),
             "k_scale": np.full(shape[:3], np.nan, np.float32),
             "v_scale": np.full(shape[:3], np.nan, np.float32)}
@@ -135,7 +144,8 @@ def kv_write(pool: dict, k_new: np.ndarray, v_new: np.ndarray, cu_new: np.ndarra
     bf16 bits ``[T, Hkv, D]``) goes to position ``seq_lens[s] - n_s + i``.  Here
     ``seq_lens`` counts the tokens after the append.  BF16 pools take a copy of the
     bits.  INT8 pools take the quantised codes and scales (keys divided by the
-    pool's ``k_smooth`` first, when it has one).  The TileInfer page
+    pool's ``k_smooth`` first, when it has one), 3-bit pools the bit planes and
+    scales of ``tq3.quantize_tq3``.  The TileInfer page
     (section "Fused kernels, ...") names the KV write as one of the engine's kernels.
     """
     B = len(seq_lens)
@@ -150,6 +160,13 @@ def kv_write(pool: dict, k_new: np.ndarray, v_new: np.ndarray, cu_new: np.ndarra
     if kv_dtype == "bf16":
         pool["k"][pg, :, off, :] = k_new[:T]
         pool["v"][pg, :, off, :] = v_new[:T]
+    elif kv_dtype == "tq3":
+        kc, ks = tq3.quantize_tq3(k_new[:T])
+        vc, vs = tq3.quantize_tq3(v_new[:T])
+        pool["k"][pg, :, off] = kc
+        pool["v"][pg, :, off] = vc
+        pool["k_scale"][pg, :, off] = ks
+        pool["v_scale"][pg, :, off] = vs
     else:
         kc, ks = quantize_int8(k_new[:T], pool.get("k_smooth"))
         vc, vs = quantize_int8(v_new[:T])
@@ -169,6 +186,9 @@ def gather(pool: dict, block_table_row: np.ndarray, n: int, page_size: int, kv_d
     if kv_dtype == "bf16":
         K = bf16_to_f64(pool["k"][pg, :, off, :])
         V = bf16_to_f64(pool["v"][pg, :, off, :])
+    elif kv_dtype == "tq3":
+        K = tq3.dequantize_tq3(pool["k"][pg, :, off], pool["k_scale"][pg, :, off])
+        V = tq3.dequantize_tq3(pool["v"][pg, :, off], pool["v_scale"][pg, :, off])
     else:
         K = dequantize_int8(pool["k"][pg, :, off, :], pool["k_scale"][pg, :, off], pool.get("k_smooth"))
         V = dequantize_int8(pool["v"][pg, :, off, :], pool["v_scale"][pg, :, off])
