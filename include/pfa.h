@@ -65,7 +65,27 @@ typedef enum {
     PFA_ERR_HIP = 5            /* a HIP call failed; see pfa_last_hip_error()         */
 } pfa_status;
 
-typedef enum { PFA_KV_BF16 = 0, PFA_KV_INT8 = 1 } pfa_kv_dtype;
+/*
+ * KV cache element formats.
+ *   PFA_KV_TQ3: the 3-bit rotated cache the qengine README lists (feature list:
+ *   "3-bit KV cache: Walsh-Hadamard rotation + Lloyd-Max scalar quant").  Each
+ *   cached K or V vector x of D elements is stored as:
+ *     y = H_D x          (Walsh-Hadamard, Sylvester order, unnormalised)
+ *     s = sqrt(sum(y^2) / D)                        (fp32 scale, one per vector)
+ *     t = y / s  (t = 0 when s = 0), coded by the symmetric 8-level Lloyd-Max
+ *     quantiser of N(0, 1) (pfa_tq3_codebook): bits 0-1 of a code are the
+ *     magnitude index m = #{k : |t| >= T[k]}, bit 2 is 1 when t >= 0;
+ *     three bit planes of D/8 bytes: element 8j+i is bit i of byte j of plane b,
+ *     which holds bit b of the codes.
+ *   The cache stands for x^ = H_D (s * c) / D with c = +-M[m].  kv_write and
+ *   decode (split or not; not the fused merge) take it; prefill, verify and
+ *   attn_input return PFA_ERR_UNSUPPORTED.  The encoder's decisions are made in
+ *   fp32 in a fixed order: butterflies of stride 1, 2, ..., D/2, each (a+b, a-b);
+ *   the squares summed over consecutive groups of 8 in order, then the groups in
+ *   a pairwise tree (group g with g^1, then g^2, ...); a correctly rounded sqrt
+ *   and division.
+ */
+typedef enum { PFA_KV_BF16 = 0, PFA_KV_INT8 = 1, PFA_KV_TQ3 = 2 } pfa_kv_dtype;
 
 /* Attention shape and options. */
 typedef struct {
@@ -88,13 +108,26 @@ typedef struct {
  *   dequantises to code * scale * s.  NULL: no smoothing.  A BF16 pool with
  *   k_smooth set is PFA_ERR_UNSUPPORTED. */
 typedef struct {
-    void* k_pool;              /* device [num_pages][Hkv][P][D], bf16 or int8         */
+    void* k_pool;              /* device [num_pages][Hkv][P][D], bf16 or int8;        */
+                               /* TQ3: [num_pages][Hkv][P][3][D/8] bytes (bit planes) */
     void* v_pool;              /* same                                                */
-    float* k_scale;            /* device [num_pages][Hkv][P] fp32; INT8 only, else NULL */
+    float* k_scale;            /* device [num_pages][Hkv][P] fp32; INT8/TQ3, else NULL */
     float* v_scale;            /* same                                                */
     int32_t num_pages;
     const float* k_smooth;     /* device [D] fp32 key smoothing (INT8 only), or NULL  */
 } pfa_kv_pool;
+
+/*
+ * pfa_tq3_codebook: the codebook of PFA_KV_TQ3 as the kernels use it.
+ *   magnitudes  host float[4]: M[0..3], ascending, the positive levels;
+ *   thresholds  host float[3]: T[0..2], the magnitude thresholds.
+ *   It is the 8-level Lloyd-Max (minimum mean-square error) quantiser of the unit
+ *   normal: Lloyd's iteration in double precision (thresholds at the midpoints of
+ *   adjacent levels, levels at the centroids of their cells) until no level moves
+ *   by more than 1e-13, then each value rounded to float.  Host-only; no GPU call.
+ *   Returns PFA_ERR_NULL for a NULL pointer.
+ */
+pfa_status pfa_tq3_codebook(float* magnitudes, float* thresholds);
 
 /*
  * pfa_kv_write: append new tokens' K and V to their sequences' pages.
@@ -113,8 +146,9 @@ typedef struct {
  *   For each (token, KV head) vector x, computed separately for K and V:
  *     scale = absmax(x) / 127                         (IEEE fp32 division)
  *     code  = clamp(rint(x / scale), -127, 127)       (ties to even)
- *   An all-zero vector gets scale 0 and codes 0.  Tokens whose slot falls outside
- *   the block table or the pool are skipped.
+ *   An all-zero vector gets scale 0 and codes 0.  TQ3 pools receive bit planes and
+ *   scales as described at pfa_kv_dtype.  Tokens whose slot falls outside the block
+ *   table or the pool are skipped.
  */
 pfa_status pfa_kv_write(const pfa_attn_desc* desc, const pfa_kv_pool* pool,
                         const void* k_new, const void* v_new, const int32_t* cu_new,
@@ -181,6 +215,10 @@ pfa_status pfa_attn_input(const pfa_attn_desc* desc, const pfa_kv_pool* pool,
  *              the o_part rows of such a split are left unwritten.
  *   Partials never include the sink, and out is left untouched.  Then call
  *   pfa_paged_attn_combine.
+ *
+ *   A TQ3 pool is attended as the cache it stands for (pfa_kv_dtype).  The kernel
+ *   works in the rotated domain: q . x^ = s * ((H_D q / D) . c), and the split's
+ *   sum of p * s * c is rotated back by H_D / D at its end.
  */
 pfa_status pfa_paged_attn_decode(const pfa_attn_desc* desc, const pfa_kv_pool* pool,
                                  const void* q, const int32_t* block_table, int32_t bt_stride,

@@ -22,12 +22,13 @@ LIB_PATH = os.path.join(_HERE, "libpfa.so")
 PFA_OK = 0
 STATUS_NAMES = {0: "PFA_OK", 1: "PFA_ERR_NULL", 2: "PFA_ERR_SHAPE", 3: "PFA_ERR_UNSUPPORTED",
                 4: "PFA_ERR_WORKSPACE", 5: "PFA_ERR_HIP"}
-KV_DTYPES = {"bf16": 0, "int8": 1}
+KV_DTYPES = {"bf16": 0, "int8": 1, "tq3": 2}
 
 # every symbol include/pfa.h declares
 EXPORTS = ("pfa_kv_write", "pfa_attn_input", "pfa_paged_attn_decode", "pfa_paged_attn_decode_fused", "pfa_paged_attn_combine",
            "pfa_paged_attn_prefill", "pfa_paged_attn_verify", "pfa_decode_num_splits",
-           "pfa_prefill_num_splits", "pfa_verify_num_splits", "pfa_status_string", "pfa_last_hip_error")
+           "pfa_prefill_num_splits", "pfa_verify_num_splits", "pfa_tq3_codebook", "pfa_status_string",
+           "pfa_last_hip_error")
 
 
 class PfaError(RuntimeError):
@@ -89,6 +90,8 @@ def lib() -> ctypes.CDLL:
     L.pfa_prefill_num_splits.restype = ctypes.c_int32
     L.pfa_verify_num_splits.argtypes = [D, I, I, I, I, ctypes.POINTER(ctypes.c_int32)]
     L.pfa_verify_num_splits.restype = ctypes.c_int32
+    L.pfa_tq3_codebook.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.POINTER(ctypes.c_float)]
+    L.pfa_tq3_codebook.restype = ctypes.c_int
     L.pfa_status_string.argtypes = [ctypes.c_int]
     L.pfa_status_string.restype = ctypes.c_char_p
     L.pfa_last_hip_error.argtypes = []
@@ -131,7 +134,8 @@ class AttnDesc:
 
 @dataclass
 class KVPool:
-    """k/v: [num_pages, Hkv, P, D] (bf16 or int8); scales [num_pages, Hkv, P] fp32 for INT8.
+    """k/v: [num_pages, Hkv, P, D] (bf16 or int8), or uint8 bit planes [num_pages, Hkv, P, 3, D/8]
+    for the 3-bit rotated format; scales [num_pages, Hkv, P] fp32 for INT8 and 3-bit pools.
     k_smooth: optional [D] fp32 key smoothing of an INT8 pool (keys stored as k / s)."""
     k: torch.Tensor
     v: torch.Tensor
@@ -145,14 +149,14 @@ class KVPool:
 
     def c(self) -> CKvPool:
         dt = self.k.dtype
-        if dt not in (torch.bfloat16, torch.int8) or self.v.dtype != dt:
-            raise TypeError("pool tensors must both be bfloat16 or both int8")
+        if dt not in (torch.bfloat16, torch.int8, torch.uint8) or self.v.dtype != dt:
+            raise TypeError("pool tensors must both be bfloat16, both int8 or both uint8 (3-bit planes)")
         _dev(self.k, dt, "k_pool")
         _dev(self.v, dt, "v_pool")
         ks = vs = None
-        if dt == torch.int8:
+        if dt != torch.bfloat16:
             if self.k_scale is None or self.v_scale is None:
-                raise ValueError("an INT8 pool needs k_scale and v_scale")
+                raise ValueError("an INT8 or 3-bit pool needs k_scale and v_scale")
             ks = _dev(self.k_scale, torch.float32, "k_scale").data_ptr()
             vs = _dev(self.v_scale, torch.float32, "v_scale").data_ptr()
         sm = None
@@ -217,6 +221,14 @@ def attn_input(desc: AttnDesc, pool: KVPool, q_norm_weight, k_norm_weight, rope_
                               _ptr(cu_new), _ptr(seq_lens), _ptr(block_table), int(block_table.shape[1]),
                               int(seq_lens.numel()), int(qkv.shape[0]), _ptr(q_out), _stream(stream, qkv))
     _check("pfa_attn_input", st)
+
+
+def tq3_codebook():
+    """The 3-bit format's codebook as the library computes it: (magnitudes [4], thresholds [3])."""
+    m = (ctypes.c_float * 4)()
+    t = (ctypes.c_float * 3)()
+    _check("pfa_tq3_codebook", lib().pfa_tq3_codebook(m, t))
+    return list(m), list(t)
 
 
 def decode_num_splits(max_seq_len: int, split_keys: int) -> int:
@@ -335,6 +347,7 @@ def paged_attn_verify(desc: AttnDesc, pool: KVPool, q, cu_q, block_table, seq_le
 
 
 __all__ = ["AttnDesc", "KVPool", "PfaError", "EXPORTS", "lib", "kv_write", "attn_input", "decode_num_splits",
+           "tq3_codebook",
            "prefill_num_splits", "verify_num_splits", "paged_attn_decode", "paged_attn_decode_fused",
            "paged_attn_combine",
            "paged_attn_prefill", "paged_attn_verify"]

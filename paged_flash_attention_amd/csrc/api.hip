@@ -4,6 +4,7 @@
 #include "pfa.h"
 
 #include <algorithm>
+#include <cmath>
 
 #include "pfa_device.h"
 
@@ -24,13 +25,14 @@ pfa_status check_desc(const pfa_attn_desc* d) {
     if (d->window < 0) return PFA_ERR_SHAPE;
     if (d->head_dim != 64 && d->head_dim != 128) return PFA_ERR_UNSUPPORTED;
     if (d->page_size != 16) return PFA_ERR_UNSUPPORTED;
-    if (d->kv_dtype != PFA_KV_BF16 && d->kv_dtype != PFA_KV_INT8) return PFA_ERR_UNSUPPORTED;
+    if (d->kv_dtype != PFA_KV_BF16 && d->kv_dtype != PFA_KV_INT8 && d->kv_dtype != PFA_KV_TQ3)
+        return PFA_ERR_UNSUPPORTED;
     return PFA_OK;
 }
 
 pfa_status check_pool(const pfa_attn_desc* d, const pfa_kv_pool* p) {
     if (!p || !p->k_pool || !p->v_pool) return PFA_ERR_NULL;
-    if (d->kv_dtype == PFA_KV_INT8 && (!p->k_scale || !p->v_scale)) return PFA_ERR_NULL;
+    if (d->kv_dtype != PFA_KV_BF16 && (!p->k_scale || !p->v_scale)) return PFA_ERR_NULL;
     if (d->kv_dtype != PFA_KV_INT8 && p->k_smooth) return PFA_ERR_UNSUPPORTED;
     if (p->num_pages <= 0) return PFA_ERR_SHAPE;
     return PFA_OK;
@@ -40,6 +42,36 @@ bool decode_group_ok(int g) { return g == 1 || g == 2 || g == 4 || g == 8; }
 
 bool prefill_group_ok(int g) {
     return g == 1 || g == 2 || g == 4 || g == 8 || g == 16 || g == 32;
+}
+
+// The 3-bit rotated cache's codebook: the symmetric 8-level Lloyd-Max quantiser
+// of N(0, 1) (qengine README, feature list: "Lloyd-Max scalar quant").  Lloyd's
+// iteration on the positive half in double precision: thresholds at midpoints of
+// adjacent levels (the first at 0), levels at the centroids of their cells,
+// E[X | a < X < b] = (phi(a) - phi(b)) / (Phi(b) - Phi(a)), from 0.25, 0.75, 1.25,
+// 2.0 until no level moves by more than 1e-13.  Then rounded to float.
+const pfa::Tq3Book& tq3_book() {
+    static const pfa::Tq3Book book = [] {
+        auto phi = [](double x) { return std::isinf(x) ? 0.0 : std::exp(-0.5 * x * x) / std::sqrt(2.0 * M_PI); };
+        auto cdf = [](double x) { return std::isinf(x) ? 1.0 : 0.5 * (1.0 + std::erf(x / std::sqrt(2.0))); };
+        double m[4] = {0.25, 0.75, 1.25, 2.0};
+        for (int it = 0; it < 100000; ++it) {
+            const double e[5] = {0.0, 0.5 * (m[0] + m[1]), 0.5 * (m[1] + m[2]), 0.5 * (m[2] + m[3]), INFINITY};
+            double moved = 0.0;
+            double n[4];
+            for (int k = 0; k < 4; ++k) {
+                n[k] = (phi(e[k]) - phi(e[k + 1])) / (cdf(e[k + 1]) - cdf(e[k]));
+                moved = std::max(moved, std::fabs(n[k] - m[k]));
+            }
+            for (int k = 0; k < 4; ++k) m[k] = n[k];
+            if (moved <= 1e-13) break;
+        }
+        pfa::Tq3Book b;
+        for (int k = 0; k < 4; ++k) b.m[k] = (float)m[k];
+        for (int k = 0; k < 3; ++k) b.t[k] = (float)(0.5 * (m[k] + m[k + 1]));
+        return b;
+    }();
+    return book;
 }
 
 #define PFA_TRY(expr)                    \
@@ -79,7 +111,8 @@ pfa_status pfa_kv_write(const pfa_attn_desc* desc, const pfa_kv_pool* pool, cons
     a.num_pages = pool->num_pages;
     a.num_kv_heads = desc->num_kv_heads;
     a.head_dim = desc->head_dim;
-    return hip_status(pfa::launch_kv_write(a, desc->kv_dtype == PFA_KV_INT8, (hipStream_t)stream));
+    a.book = tq3_book();
+    return hip_status(pfa::launch_kv_write(a, desc->kv_dtype, (hipStream_t)stream));
 }
 
 pfa_status pfa_attn_input(const pfa_attn_desc* desc, const pfa_kv_pool* pool,
@@ -88,6 +121,7 @@ pfa_status pfa_attn_input(const pfa_attn_desc* desc, const pfa_kv_pool* pool,
                           int32_t batch, int32_t num_tokens, void* q_out, void* stream) {
     PFA_TRY(check_desc(desc));
     PFA_TRY(check_pool(desc, pool));
+    if (desc->kv_dtype == PFA_KV_TQ3) return PFA_ERR_UNSUPPORTED;
     if (!prm) return PFA_ERR_NULL;
     if (batch < 0 || num_tokens < 0 || bt_stride <= 0 || prm->rope_max_pos <= 0) return PFA_ERR_SHAPE;
     if (!(prm->eps >= 0.0f) || prm->eps > 1.0f) return PFA_ERR_SHAPE;
@@ -124,6 +158,14 @@ pfa_status pfa_attn_input(const pfa_attn_desc* desc, const pfa_kv_pool* pool,
                                              (hipStream_t)stream));
 }
 
+pfa_status pfa_tq3_codebook(float* magnitudes, float* thresholds) {
+    if (!magnitudes || !thresholds) return PFA_ERR_NULL;
+    const pfa::Tq3Book& b = tq3_book();
+    for (int k = 0; k < 4; ++k) magnitudes[k] = b.m[k];
+    for (int k = 0; k < 3; ++k) thresholds[k] = b.t[k];
+    return PFA_OK;
+}
+
 int32_t pfa_decode_num_splits(int32_t max_seq_len, int32_t split_keys) {
     if (split_keys <= 0) return 0;
     if (max_seq_len <= 0) return 1;
@@ -143,6 +185,7 @@ pfa_status decode_like(const pfa_attn_desc* desc, const pfa_kv_pool* pool, const
     PFA_TRY(check_pool(desc, pool));
     const int g = desc->num_q_heads / desc->num_kv_heads;
     if (!decode_group_ok(g)) return PFA_ERR_UNSUPPORTED;
+    if (fused && desc->kv_dtype == PFA_KV_TQ3) return PFA_ERR_UNSUPPORTED;
     if (batch < 0 || batch > 65535 || bt_stride <= 0 || max_seq_len < 0 || max_splits < 1 ||
         desc->num_kv_heads > 65535)
         return PFA_ERR_SHAPE;
@@ -182,6 +225,8 @@ pfa_status decode_like(const pfa_attn_desc* desc, const pfa_kv_pool* pool, const
     a.max_splits = max_splits;
     a.window = desc->window;
     a.sm_scale = desc->sm_scale;
+    if (desc->kv_dtype == PFA_KV_TQ3)
+        return hip_status(pfa::launch_decode_tq3(a, desc->head_dim, tq3_book(), (hipStream_t)stream));
     return hip_status(pfa::launch_decode(a, desc->head_dim, desc->kv_dtype == PFA_KV_INT8,
                                          (hipStream_t)stream));
 }

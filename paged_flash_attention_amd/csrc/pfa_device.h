@@ -112,6 +112,13 @@ __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_lo
 // ---- launchers exported by each kernel file to the C-ABI layer ---------------
 namespace pfa {
 
+// The 3-bit rotated cache's codebook as the kernels use it (fp32): magnitudes
+// M[0..3] (ascending) and the magnitude thresholds T[0..2].
+struct Tq3Book {
+    float m[4];
+    float t[3];
+};
+
 struct KvWriteArgs {
     const uint16_t* k_new;
     const uint16_t* v_new;
@@ -124,6 +131,7 @@ struct KvWriteArgs {
     float* v_scale;
     const float* k_smooth;      // INT8: [D] per-channel key smoothing, or NULL
     int32_t bt_stride, batch, num_tokens, num_pages, num_kv_heads, head_dim;
+    Tq3Book book;               // 3-bit pools only
 };
 
 struct DecodeArgs {
@@ -190,9 +198,11 @@ struct PrefillArgs {
     float sm_scale;
 };
 
-hipError_t launch_kv_write(const KvWriteArgs& a, bool int8, hipStream_t s);
+// kv_dtype: 0 bf16, 1 int8, 2 3-bit rotated
+hipError_t launch_kv_write(const KvWriteArgs& a, int kv_dtype, hipStream_t s);
 hipError_t launch_attn_input(const AttnInputArgs& a, int head_dim, bool int8, hipStream_t s);
 hipError_t launch_decode(const DecodeArgs& a, int head_dim, bool int8, hipStream_t s);
+hipError_t launch_decode_tq3(const DecodeArgs& a, int head_dim, const Tq3Book& bk, hipStream_t s);
 hipError_t launch_combine(const CombineArgs& a, int head_dim, hipStream_t s);
 hipError_t launch_prefill(const PrefillArgs& a, int head_dim, hipStream_t s);
 hipError_t launch_prefill_split(const PrefillArgs& a, int head_dim, hipStream_t s);

@@ -241,3 +241,29 @@ def test_verify_split_choice_host_only():
     # enough sequences fill the chip unsplit
     assert L.pfa_verify_num_splits(ctypes.byref(desc()), 64, 16, 32768, 256, ctypes.byref(sk)) == 1
     assert sk.value == 0
+
+
+def test_tq3_codebook_matches_the_oracle():
+    """The library computes the 3-bit codebook itself (host code, no GPU); it must
+    round to the oracle's float32 codebook exactly."""
+    import numpy as np
+    import oracle as O
+    m, t = pfa.tq3_codebook()
+    M, T = O.codebook_f32()
+    assert np.array_equal(np.array(m, np.float32), M)
+    assert np.array_equal(np.array(t, np.float32), T)
+    assert pfa.lib().pfa_tq3_codebook(None, None) == NULL
+
+
+def test_tq3_pool_validation():
+    tq = dict(k_scale=FAKE.value, v_scale=FAKE.value)
+    assert kvw(desc(kv_dtype=2), pool()) == NULL                           # 3-bit pool without scales
+    assert dec(desc(kv_dtype=2), pool()) == NULL
+    assert kvw(desc(kv_dtype=2), pool(k_smooth=FAKE.value, **tq)) == UNSUP  # smoothing is INT8-only
+    assert pre(desc(kv_dtype=2), pool(**tq)) == UNSUP                      # prefill: BF16 only
+    assert ver(desc(kv_dtype=2), pool(**tq)) == UNSUP
+    assert ain(desc(kv_dtype=2), pool(**tq)) == UNSUP
+    assert decf(desc(kv_dtype=2), pool(**tq)) == UNSUP                     # no fused merge
+    assert dec(desc(kv_dtype=2, num_q_heads=48, num_kv_heads=3), pool(**tq)) == UNSUP   # G = 16
+    assert dec(desc(kv_dtype=2), pool(**tq), batch=0) == OK                # nothing launched
+    assert kvw(desc(kv_dtype=2), pool(**tq), T=0, k=None) == OK

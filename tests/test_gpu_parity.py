@@ -3,7 +3,9 @@
 Bars, from the target tolerances:
 * BF16 KV: max-abs 1e-2 and rel-L2 5e-3 over each call's whole output.
 * INT8 KV: max-abs 3e-2, graded against the oracle on the dequantised cache.
-* The INT8 quantiser and the BF16 KV write: bit-exact.
+* 3-bit rotated KV: the BF16 bars, against the oracle on the dequantised cache (the
+  GPU computes the same function in fp32, in the rotated domain).
+* The INT8 and 3-bit quantisers and the BF16 KV write: bit-exact.
 
 Every pool starts poisoned, with NaN in BF16 slots and NaN scales in INT8 ones,
 so a read of an unwritten slot shows up as a non-finite output.
@@ -166,6 +168,61 @@ def test_decode_int8_smoothed(ci):
 # ---------------------------------------------------------------------------
 # decode + combine
 # ---------------------------------------------------------------------------
+
+def _tq3_special_rows(D, n):
+    """bf16 rows for the 3-bit encoder: a zero vector, spikes, signed zeros,
+    large and tiny magnitudes, a constant row (one nonzero rotated coordinate)."""
+    rows = np.zeros((n, D), np.float32)
+    rows[1, 3] = 5.0
+    rows[2, D - 1] = -0.75
+    rows[3] = -0.0
+    rows[3, 0] = 2.0
+    rows[4] = np.linspace(-300, 300, D)
+    rows[5] = 1e-30 * np.arange(D)
+    rows[6] = 1.0
+    rows[7, ::2] = 1.0
+    rows[7, 1::2] = -1.0
+    return W.f32_to_bf16_bits(rows[:n])
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_kv_write_tq3_bitwise(D):
+    """3-bit rotated KV write: bit planes and scales equal the oracle's, whole pool,
+    poison included."""
+    case = W.make_case("kvw3", 5, P(8, 2, D, kv="tq3"), [3, 30, 70], [3, 30, 9], outlier_frac=0.01)
+    sp = _tq3_special_rows(D, 8)
+    case.k_tok[:8, 0] = sp
+    case.v_tok[-8:, 1] = sp
+    g = GpuCase(case)
+    ref = oracle_pool(case)
+    torch.cuda.synchronize()
+    assert pool_bits_equal(g.pool, ref, "tq3")
+
+
+TQ3_DECODE_CASES = [
+    # (params, lens, split_keys list): G = 8, 1, 2, 4 at D = 128 and 64, window and sinks
+    (dict(Hq=32, Hkv=4, D=128, kv="tq3"), [1, 33, 257, 2000], [256, 0]),
+    (dict(Hq=8, Hkv=8, D=128, kv="tq3", sinks=True), [1, 90, 16], [16, 0]),
+    (dict(Hq=16, Hkv=8, D=128, kv="tq3"), [15, 16, 17, 1024], [64, 0]),
+    (dict(Hq=16, Hkv=4, D=64, kv="tq3", window=50, sinks=True), [7, 64, 300], [32, 0]),
+    (dict(Hq=64, Hkv=8, D=64, kv="tq3", window=128, sinks=True), [1, 128, 129, 700], [256, 0]),
+    (dict(Hq=16, Hkv=8, D=64, kv="tq3"), list(np.random.default_rng(78).integers(1, 1500, 24)), [16]),
+]
+
+
+@pytest.mark.parametrize("ci", range(len(TQ3_DECODE_CASES)))
+def test_decode_tq3(ci):
+    prm, lens, splits = TQ3_DECODE_CASES[ci]
+    case = W.make_case(f"dec3_{ci}", 140 + ci, P(seed=ci, **prm), lens, np.ones(len(lens), np.int32),
+                       outlier_frac=0.01)
+    g = GpuCase(case)
+    pool = oracle_pool(case)
+    assert pool_bits_equal(g.pool, pool, "tq3")
+    ref = O.decode(case.q, pool, case.block_table, case.seq_lens, case.p)
+    for S in splits:
+        got = g.decode(split_keys=S)
+        assert_close(got, ref, BF16_TOL, f"tq3 decode case {ci} S={S}")
+
 
 DECODE_CASES = [
     # (params, lens, split_keys list)

@@ -107,7 +107,7 @@ class AttnParams:
     num_kv_heads: int
     head_dim: int
     page_size: int = 16
-    kv_dtype: str = "bf16"          # "bf16" or "int8"
+    kv_dtype: str = "bf16"          # "bf16", "int8" or "tq3" (3-bit rotated)
     window: int = 0                 # 0 = full attention
     sm_scale: float = 0.0           # 0 -> 1/sqrt(head_dim)
     sinks: Optional[np.ndarray] = None  # float32 [num_q_heads] or None
@@ -273,6 +273,14 @@ def decode_int8_qwen30b(seed=4, batch=8, ctx=32768, smooth=False):
     return make_case(name, seed, p, np.full(batch, ctx, np.int32), np.ones(batch, np.int32),
                      outlier_frac=0.01, split_keys=256,
                      key_weight=key_norm_weight(seed + 50, 128) if smooth else None)
+
+
+def decode_tq3_qwen30b(seed=4, batch=8, ctx=32768):
+    """The INT8 decode shape above (32 q / 4 KV heads, D 128, batch 8 at 32768
+    positions, N(0,1) with 1% outliers at +-8) on the 3-bit rotated cache."""
+    p = AttnParams(32, 4, 128, kv_dtype="tq3")
+    return make_case(f"decode_tq3_batch{batch}_ctx{ctx}", seed, p, np.full(batch, ctx, np.int32),
+                     np.ones(batch, np.int32), outlier_frac=0.01, split_keys=256)
 
 
 def mixed_gptoss(seed=5, layer="window", part="decode", batch=64, lo=128, hi=32768,
