@@ -54,12 +54,21 @@ def visible_keys(lens, window):
     return np.minimum(lens, window) if window > 0 else lens
 
 
+def kv_bytes_per_key_head(p) -> int:
+    """Cached bytes of one key and its value for one KV head: bf16 elements, or int8
+    codes + two fp32 scales, or 3-bit planes (3D/8 bytes) + two fp32 scales."""
+    if p.kv_dtype == "int8":
+        return 2 * p.head_dim + 8
+    if p.kv_dtype == "tq3":
+        return 2 * (3 * p.head_dim // 8 + 4)
+    return 2 * p.head_dim * 2
+
+
 def decode_bytes(case) -> int:
-    """Visible K/V (+ scales for INT8) + q + out + block-table entries of the decode."""
+    """Visible K/V (+ scales for INT8 and 3-bit) + q + out + block-table entries of the decode."""
     p = case.p
     vis = visible_keys(case.seq_lens, p.window)
-    elem = 1 if p.kv_dtype == "int8" else 2
-    per_key = p.num_kv_heads * (2 * p.head_dim * elem + (8 if p.kv_dtype == "int8" else 0))
+    per_key = p.num_kv_heads * kv_bytes_per_key_head(p)
     kv = int(vis.sum()) * per_key
     q = case.batch * p.num_q_heads * p.head_dim * 2
     out = case.batch * p.num_q_heads * p.head_dim * 4
@@ -82,9 +91,8 @@ def verify_bytes(case) -> int:
 def kv_write_bytes(case) -> int:
     p = case.p
     T = int(case.q_lens.sum())
-    elem = 1 if p.kv_dtype == "int8" else 2
     rd = T * p.num_kv_heads * p.head_dim * 2 * 2
-    wr = T * p.num_kv_heads * (2 * p.head_dim * elem + (8 if p.kv_dtype == "int8" else 0))
+    wr = T * p.num_kv_heads * kv_bytes_per_key_head(p)
     return rd + wr
 
 
@@ -394,6 +402,7 @@ def main():
         "decode_1seq_ctx1024": lambda: W.decode_1seq_ctx1024(),
         "decode_int8_batch8_ctx32768": lambda: W.decode_int8_qwen30b(),
         "decode_int8_batch8_ctx32768_smooth": lambda: W.decode_int8_qwen30b(smooth=True),
+        "decode_tq3_batch8_ctx32768": lambda: W.decode_tq3_qwen30b(),
         "mixed_full_decode_b64": lambda: W.mixed_gptoss(layer="full", part="decode"),
         "mixed_window_decode_b64": lambda: W.mixed_gptoss(layer="window", part="decode"),
         "prefill_causal_8192": lambda: W.prefill_llama8b(prompt=8192),
@@ -468,6 +477,7 @@ def main():
         for name, st in (("decode_batch32_ctx512_8192_fused", 50),
                          ("decode_batch32_ctx8192", 30), ("decode_batch32_ctx8192_s1024", 30),
                          ("decode_int8_batch8_ctx32768", 30), ("decode_int8_batch8_ctx32768_smooth", 30),
+                         ("decode_tq3_batch8_ctx32768", 30),
                          ("mixed_full_decode_b64", 30), ("prefill_causal_8192", 10),
                          ("prefill_chunk130_on_8192", 20), ("mixed_full_prefill_2x2048", 20),
                          ("verify_16tok_batch1_ctx1024", 50), ("verify_8tok_batch32_ctx512_8192", 30),
@@ -502,7 +512,7 @@ def main():
         "metric": metric, "value": round(value, 2), "unit": unit, "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(r["step_ms"], 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "bf16" if p.kv_dtype == "bf16" else "int8", "data": "synthetic",
+        "dtype": {"bf16": "bf16", "int8": "int8", "tq3": "fp32"}[p.kv_dtype], "data": "synthetic",
         "config": {"workload": case.name, "batch": case.batch, "q_heads": p.num_q_heads,
                    "kv_heads": p.num_kv_heads, "head_dim": p.head_dim, "page_size": p.page_size,
                    "split_keys": case.split_keys if not is_prefill else None,

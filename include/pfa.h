@@ -75,8 +75,8 @@ typedef enum {
  *     t = y / s  (t = 0 when s = 0), coded by the symmetric 8-level Lloyd-Max
  *     quantiser of N(0, 1) (pfa_tq3_codebook): bits 0-1 of a code are the
  *     magnitude index m = #{k : |t| >= T[k]}, bit 2 is 1 when t >= 0;
- *     three bit planes of D/8 bytes: element 8j+i is bit i of byte j of plane b,
- *     which holds bit b of the codes.
+ *     packed as D/8 little-endian 24-bit fields of 3 bytes: field j holds the
+ *     codes of elements 8j .. 8j+7, element 8j+i in bits 3i .. 3i+2.
  *   The cache stands for x^ = H_D (s * c) / D with c = +-M[m].  kv_write and
  *   decode (split or not; not the fused merge) take it; prefill, verify and
  *   attn_input return PFA_ERR_UNSUPPORTED.  The encoder's decisions are made in
@@ -109,7 +109,7 @@ typedef struct {
  *   k_smooth set is PFA_ERR_UNSUPPORTED. */
 typedef struct {
     void* k_pool;              /* device [num_pages][Hkv][P][D], bf16 or int8;        */
-                               /* TQ3: [num_pages][Hkv][P][3][D/8] bytes (bit planes) */
+                               /* TQ3: [num_pages][Hkv][P][3D/8] bytes (packed codes) */
     void* v_pool;              /* same                                                */
     float* k_scale;            /* device [num_pages][Hkv][P] fp32; INT8/TQ3, else NULL */
     float* v_scale;            /* same                                                */
@@ -146,7 +146,7 @@ pfa_status pfa_tq3_codebook(float* magnitudes, float* thresholds);
  *   For each (token, KV head) vector x, computed separately for K and V:
  *     scale = absmax(x) / 127                         (IEEE fp32 division)
  *     code  = clamp(rint(x / scale), -127, 127)       (ties to even)
- *   An all-zero vector gets scale 0 and codes 0.  TQ3 pools receive bit planes and
+ *   An all-zero vector gets scale 0 and codes 0.  TQ3 pools receive packed codes and
  *   scales as described at pfa_kv_dtype.  Tokens whose slot falls outside the block
  *   table or the pool are skipped.
  */

@@ -110,7 +110,7 @@ def empty_pool(num_pages: int, num_kv_heads: int, page_size: int, head_dim: int,
 
     BF16 slots hold NaN.  INT8 and 3-bit slots hold code 0 with a NaN scale.
     Layout: ``[num_pages, Hkv, P, D]``; scales ``[num_pages, Hkv, P]``.  A 3-bit
-    ("tq3") pool holds bit planes ``[num_pages, Hkv, P, 3, D/8]`` (see ``tq3``).  An
+    ("tq3") pool holds packed codes ``[num_pages, Hkv, P, 3D/8]`` (see ``tq3``).  An
     INT8 pool may carry ``k_smooth`` (float32 [D]): its keys are stored smoothed by it.
     """
     shape = (num_pages, num_kv_heads, page_size, head_dim)
@@ -119,7 +119,7 @@ def empty_pool(num_pages: int, num_kv_heads: int, page_size: int, head_dim: int,
         return {"k": np.full(shape, 0x7FC0, np.uint16), "v": np.full(shape, 0x7FC0, np.uint16)}
     if kv_dtype == "tq3":
         assert k_smooth is None, "key smoothing is an INT8 cache feature"
-        pshape = shape[:3] + (3, head_dim // 8)
+        pshape = shape[:3] + (3 * head_dim // 8,)
         return {"k": np.zeros(pshape, np.uint8), "v": np.zeros(pshape, np.uint8),
                 "k_scale": np.full(shape[:3], np.nan, np.float32),
                 "v_scale": np.full(shape[:3], np.nan, np.float32)}
@@ -144,7 +144,7 @@ def kv_write(pool: dict, k_new: np.ndarray, v_new: np.ndarray, cu_new: np.ndarra
     bf16 bits ``[T, Hkv, D]``) goes to position ``seq_lens[s] - n_s + i``.  Here
     ``seq_lens`` counts the tokens after the append.  BF16 pools take a copy of the
     bits.  INT8 pools take the quantised codes and scales (keys divided by the
-    pool's ``k_smooth`` first, when it has one), 3-bit pools the bit planes and
+    pool's ``k_smooth`` first, when it has one), 3-bit pools the packed codes and
     scales of ``tq3.quantize_tq3``.  The TileInfer page
     (section "Fused kernels, ...") names the KV write as one of the engine's kernels.
     """

@@ -22,8 +22,8 @@ works (each is also listed in the design notes):
 * Codes are sign-magnitude: bits 0-1 hold the index m of the magnitude M[m]
   (ascending), bit 2 is 1 for a positive level.  ``t = y/s >= 0`` counts as
   positive, and ``m = #{k : |t| >= T[k]}``.  A zero vector (s = 0) takes t = 0.
-* The codes are stored as three bit planes per vector: byte j of plane b holds
-  bit b of the codes of elements 8j .. 8j+7 (element 8j+i in bit i).
+* The codes of a vector are stored as D/8 little-endian 24-bit fields, 3 bytes
+  each: field j holds elements 8j .. 8j+7, element 8j+i in bits 3i .. 3i+2.
 * The decisions (codes and the stored scale) are made in float32, in a fixed order
   of operations, so that a GPU quantiser can match them bit for bit: the rotation
   by butterflies of stride 1, 2, 4, ..., D/2 (each ``(a + b, a - b)``); the sum of
@@ -145,7 +145,7 @@ def sum_squares_f32(y: np.ndarray) -> np.ndarray:
 def quantize_tq3(x_bits: np.ndarray, codebook=None):
     """Quantise bf16 vectors (uint16 bits) along the last axis.
 
-    Returns ``(planes uint8 [..., 3, D/8], scale float32 [...])``.
+    Returns ``(packed uint8 [..., 3D/8], scale float32 [...])``.
     """
     M, T = codebook_f32() if codebook is None else codebook
     x = bf16_to_f32(np.asarray(x_bits, dtype=np.uint16))
@@ -160,39 +160,36 @@ def quantize_tq3(x_bits: np.ndarray, codebook=None):
     a = np.abs(t)
     mag = ((a >= T[0]).astype(np.uint8) + (a >= T[1]).astype(np.uint8) + (a >= T[2]).astype(np.uint8))
     codes = (mag | (sign << 2)).astype(np.uint8)
-    return pack_planes(codes), scale
+    return pack_codes(codes), scale
 
 
-def pack_planes(codes: np.ndarray) -> np.ndarray:
-    """3-bit codes [..., D] -> bit planes [..., 3, D/8] (element 8j+i in bit i of byte j)."""
+def pack_codes(codes: np.ndarray) -> np.ndarray:
+    """3-bit codes [..., D] -> packed bytes [..., 3D/8]: field j (bytes 3j .. 3j+2,
+    little-endian) holds element 8j+i in bits 3i .. 3i+2."""
     codes = np.asarray(codes, dtype=np.uint8)
     D = codes.shape[-1]
-    c = codes.reshape(codes.shape[:-1] + (D // 8, 8))
-    planes = []
-    for b in range(3):
-        bits = (c >> b) & 1
-        byte = np.zeros(c.shape[:-1], dtype=np.uint8)
-        for i in range(8):
-            byte |= (bits[..., i] << i).astype(np.uint8)
-        planes.append(byte)
-    return np.stack(planes, axis=-2)
+    c = codes.reshape(codes.shape[:-1] + (D // 8, 8)).astype(np.uint32)
+    field = np.zeros(c.shape[:-1], dtype=np.uint32)
+    for i in range(8):
+        field |= c[..., i] << np.uint32(3 * i)
+    out = np.stack([(field >> np.uint32(8 * k)) & np.uint32(0xFF) for k in range(3)], axis=-1)
+    return out.astype(np.uint8).reshape(codes.shape[:-1] + (3 * D // 8,))
 
 
-def unpack_planes(planes: np.ndarray) -> np.ndarray:
-    """Bit planes [..., 3, D/8] -> 3-bit codes [..., D]."""
-    planes = np.asarray(planes, dtype=np.uint8)
-    n = planes.shape[-1]
-    codes = np.zeros(planes.shape[:-2] + (n, 8), dtype=np.uint8)
-    for b in range(3):
-        for i in range(8):
-            codes[..., i] |= ((planes[..., b, :] >> i) & 1) << b
-    return codes.reshape(planes.shape[:-2] + (8 * n,))
+def unpack_codes(packed: np.ndarray) -> np.ndarray:
+    """Packed bytes [..., 3D/8] -> 3-bit codes [..., D]."""
+    packed = np.asarray(packed, dtype=np.uint8)
+    n = packed.shape[-1] // 3
+    b = packed.reshape(packed.shape[:-1] + (n, 3)).astype(np.uint32)
+    field = b[..., 0] | (b[..., 1] << np.uint32(8)) | (b[..., 2] << np.uint32(16))
+    codes = np.stack([(field >> np.uint32(3 * i)) & np.uint32(7) for i in range(8)], axis=-1)
+    return codes.astype(np.uint8).reshape(packed.shape[:-1] + (8 * n,))
 
 
-def dequantize_tq3(planes: np.ndarray, scale: np.ndarray, codebook=None) -> np.ndarray:
+def dequantize_tq3(packed: np.ndarray, scale: np.ndarray, codebook=None) -> np.ndarray:
     """``x^ = H_D (s * c) / D`` in float64, with ``c = +-M[m]`` from the codes."""
     M, _ = codebook_f32() if codebook is None else codebook
-    codes = unpack_planes(planes)
+    codes = unpack_codes(packed)
     D = codes.shape[-1]
     mag = M.astype(np.float64)[codes & 3]
     c = np.where((codes >> 2) & 1, mag, -mag)

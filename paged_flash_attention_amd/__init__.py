@@ -134,7 +134,7 @@ class AttnDesc:
 
 @dataclass
 class KVPool:
-    """k/v: [num_pages, Hkv, P, D] (bf16 or int8), or uint8 bit planes [num_pages, Hkv, P, 3, D/8]
+    """k/v: [num_pages, Hkv, P, D] (bf16 or int8), or uint8 packed codes [num_pages, Hkv, P, 3D/8]
     for the 3-bit rotated format; scales [num_pages, Hkv, P] fp32 for INT8 and 3-bit pools.
     k_smooth: optional [D] fp32 key smoothing of an INT8 pool (keys stored as k / s)."""
     k: torch.Tensor
@@ -150,7 +150,7 @@ class KVPool:
     def c(self) -> CKvPool:
         dt = self.k.dtype
         if dt not in (torch.bfloat16, torch.int8, torch.uint8) or self.v.dtype != dt:
-            raise TypeError("pool tensors must both be bfloat16, both int8 or both uint8 (3-bit planes)")
+            raise TypeError("pool tensors must both be bfloat16, both int8 or both uint8 (3-bit codes)")
         _dev(self.k, dt, "k_pool")
         _dev(self.v, dt, "v_pool")
         ks = vs = None

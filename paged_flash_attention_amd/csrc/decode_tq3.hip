@@ -14,15 +14,20 @@
 // merges them.
 //
 // One wave per (split, KV head, sequence), in the BF16/INT8 decode's 1-D grid
-// order (KV head fastest, then split, then sequence).  A lane owns 8 elements
-// (group g) of one key: L = D/8 lanes cover a key, and one step handles
-// R = 64/L keys of a page (NS = 16/R steps per page).  Every lane keeps the rotated
-// q of its 8 elements for all G heads, so a key's G scores come from one 8-term
-// dot per head and a butterfly over its L lanes.  The softmax max is taken per
-// step and the rescale is lazy (only when some head's max grows).  The next page's
-// plane bytes and scales are loaded step by step into the registers the current
-// step has just unpacked.  Unwritten slots may hold a NaN scale: masked keys are
-// removed by selects, never by a multiplication by zero.
+// order (KV head fastest, then split, then sequence), and with its lane layout: a
+// lane owns 8 elements (group sub) of one key, L = D/8 lanes cover a key, and one
+// step handles R = 64/L keys of a page (NS = 16/R steps per page).  q is rotated
+// in head order (the rotation runs across the L lanes of one head), then re-read
+// through LDS so that slot j of a lane holds head j ^ myhead: one transposed
+// butterfly then leaves each lane with its own head's score (myhead = sub/(L/G)).
+// The softmax max is taken per page, the rescale is lazy (only when some head's
+// max grows), and the weights of a page's keys are shared through LDS for p.v,
+// which accumulates all G heads in every lane.  A code's level is one bit-field
+// extract and one read of an 8-entry level table in LDS.  The next page's code
+// bytes and scales are loaded step by step into the registers the current step
+// has just unpacked.  Unwritten slots may hold a NaN scale: masked keys are removed by
+// selects, never by a multiplication by zero.
+#include "group_reduce.h"
 #include "tq3.h"
 
 namespace pfa {
@@ -33,13 +38,19 @@ __global__ __launch_bounds__(kWave) void decode_tq3_kernel(DecodeArgs a, Tq3Book
     constexpr int L = D / 8;          // lanes per key
     constexpr int R = kWave / L;      // keys per step
     constexpr int NS = kPage / R;     // steps per page
-    constexpr int PB = D / 8;         // bytes per plane
-    constexpr int VB = 3 * PB;        // bytes per vector
+    constexpr int HG = L / G;         // lanes holding each head after the reduce
+    constexpr int VB = 3 * D / 8;     // bytes per vector
     constexpr float kInvD = 1.0f / D;
+    static_assert(G <= L, "group size");
+
+    __shared__ __attribute__((aligned(16))) float q_lds[G][D];
+    __shared__ __attribute__((aligned(16))) float p_buf[NS][R][G];
+    __shared__ float lv[8];                    // level of each 3-bit code
 
     const int lane = threadIdx.x;
-    const int g = lane % L;
+    const int sub = lane % L;
     const int kr = lane / L;
+    const int myhead = sub / HG;
     const int Hq = a.num_q_heads;
     const int Hkv = a.num_kv_heads;
     const int kvh = blockIdx.x % Hkv;
@@ -68,20 +79,34 @@ __global__ __launch_bounds__(kWave) void decode_tq3_kernel(DecodeArgs a, Tq3Book
         hi = min(hi, s0 + a.split_keys);
     }
 
-    // rotated query: qr[j] = (H_D q_j / D), elements 8g .. 8g+7
+    // rotated query H_D q / D: in head order across the L lanes of a key group,
+    // then re-read in slot order (slot j = head j ^ myhead)
     float qr[G][8];
 #pragma unroll
-    for (int j = 0; j < G; ++j) {
-        const uint4 v = *reinterpret_cast<const uint4*>(a.q + (row0 + j) * D + g * 8);
+    for (int h = 0; h < G; ++h) {
+        const uint4 v = *reinterpret_cast<const uint4*>(a.q + (row0 + h) * D + sub * 8);
         const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+        float x[8];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            qr[j][2 * i] = bf16_lo(w[i]);
-            qr[j][2 * i + 1] = bf16_hi(w[i]);
+            x[2 * i] = bf16_lo(w[i]);
+            x[2 * i + 1] = bf16_hi(w[i]);
         }
-        fwht_lanes<L>(qr[j], g);
+        fwht_lanes<L>(x, sub);
+        if (kr == 0) {
+            float4* d = reinterpret_cast<float4*>(&q_lds[h][sub * 8]);
+            d[0] = make_float4(x[0] * kInvD, x[1] * kInvD, x[2] * kInvD, x[3] * kInvD);
+            d[1] = make_float4(x[4] * kInvD, x[5] * kInvD, x[6] * kInvD, x[7] * kInvD);
+        }
+    }
+    if (lane < 8) lv[lane] = tq3_level_of(lane, bk);
+    __syncthreads();
 #pragma unroll
-        for (int i = 0; i < 8; ++i) qr[j][i] *= kInvD;
+    for (int j = 0; j < G; ++j) {
+        const float4* s4 = reinterpret_cast<const float4*>(&q_lds[j ^ myhead][sub * 8]);
+        const float4 x0 = s4[0], x1 = s4[1];
+        qr[j][0] = x0.x; qr[j][1] = x0.y; qr[j][2] = x0.z; qr[j][3] = x0.w;
+        qr[j][4] = x1.x; qr[j][5] = x1.y; qr[j][6] = x1.z; qr[j][7] = x1.w;
     }
     const float c2 = a.sm_scale * kLog2e;      // scores in log2 units
 
@@ -90,7 +115,7 @@ __global__ __launch_bounds__(kWave) void decode_tq3_kernel(DecodeArgs a, Tq3Book
     const uint8_t* kpool = static_cast<const uint8_t*>(a.k_pool);
     const uint8_t* vpool = static_cast<const uint8_t*>(a.v_pool);
 
-    // raw plane bytes and scales of one page, by step
+    // raw code bytes and scales of one page, by step
     uint32_t kb[NS][3], vb[NS][3];
     float ks[NS], vs[NS];
     auto page_block = [&](int p) __attribute__((always_inline)) {
@@ -99,26 +124,24 @@ __global__ __launch_bounds__(kWave) void decode_tq3_kernel(DecodeArgs a, Tq3Book
     };
     auto load_step = [&](int64_t blk, int r) __attribute__((always_inline)) {
         const int64_t vec = blk + r * R + kr;
-        const uint8_t* kp = kpool + vec * VB + g;
-        const uint8_t* vp = vpool + vec * VB + g;
+        const uint8_t* kp = kpool + vec * VB + 3 * sub;
+        const uint8_t* vp = vpool + vec * VB + 3 * sub;
 #pragma unroll
-        for (int pl = 0; pl < 3; ++pl) {
-            kb[r][pl] = kp[pl * PB];
-            vb[r][pl] = vp[pl * PB];
+        for (int k = 0; k < 3; ++k) {
+            kb[r][k] = kp[k];
+            vb[r][k] = vp[k];
         }
         ks[r] = __ldg(a.k_scale + vec);
         vs[r] = __ldg(a.v_scale + vec);
     };
 
     float o[G][8];
-    float m_run[G], l_run[G];
 #pragma unroll
-    for (int j = 0; j < G; ++j) {
-        m_run[j] = -INFINITY;
-        l_run[j] = 0.0f;
+    for (int g = 0; g < G; ++g)
 #pragma unroll
-        for (int i = 0; i < 8; ++i) o[j][i] = 0.0f;
-    }
+        for (int i = 0; i < 8; ++i) o[g][i] = 0.0f;
+    float m_run = -INFINITY;   // running max (log2 units) of this lane's head
+    float l_run = 0.0f;        // this lane's share of sum 2^(s - m_run) (its row's keys, its head)
 
     {
         const int64_t blk = page_block(p0);
@@ -128,84 +151,108 @@ __global__ __launch_bounds__(kWave) void decode_tq3_kernel(DecodeArgs a, Tq3Book
     for (int p = p0; p <= p1; ++p) {
         const bool more = p < p1;
         const int64_t nblk = more ? page_block(p + 1) : 0;
+        // ---- scores of the page: one per lane and step (this lane's head) ----
+        float s[NS];
+        bool valid[NS];
+        uint32_t vw[NS];
+        float vsc[NS];
 #pragma unroll
         for (int r = 0; r < NS; ++r) {
             const uint32_t kw = kb[r][0] | (kb[r][1] << 8) | (kb[r][2] << 16);
-            const uint32_t vw = vb[r][0] | (vb[r][1] << 8) | (vb[r][2] << 16);
-            const float ksr = ks[r], vsr = vs[r];
+            vw[r] = vb[r][0] | (vb[r][1] << 8) | (vb[r][2] << 16);
+            const float ksr = ks[r];
+            vsc[r] = vs[r];
             if (more) load_step(nblk, r);
-
-            const int key = p * kPage + r * R + kr;
-            const bool valid = key >= lo && key < hi;
             float c[8];
-            tq3_levels8(kw, bk, c);
-            float s[G];
+            tq3_levels8(kw, lv, c);
+            float acc[G];
 #pragma unroll
             for (int j = 0; j < G; ++j) {
                 float d = qr[j][0] * c[0];
 #pragma unroll
                 for (int i = 1; i < 8; ++i) d = fmaf(qr[j][i], c[i], d);
-                if constexpr (L >= 2) d = xor_sum<1>(d);
-                if constexpr (L >= 4) d = xor_sum<2>(d);
-                if constexpr (L >= 8) d = xor_sum<4>(d);
-                if constexpr (L >= 16) d = xor_sum<8>(d);
-                s[j] = valid ? d * (ksr * c2) : -INFINITY;
+                acc[j] = d;
             }
-            // the step's max over its R keys; lazy rescale
+            const float dot = transpose_reduce<L, G>(acc);
+            const int key = p * kPage + r * R + kr;
+            valid[r] = key >= lo && key < hi;
+            s[r] = valid[r] ? dot * (ksr * c2) : -INFINITY;
+        }
+        // ---- running max, lazy rescale ----
+        float pm = s[0];
 #pragma unroll
-            for (int j = 0; j < G; ++j) {
-                const float mt = stride_max<L>(s[j]);
-                if (mt > m_run[j]) {          // uniform: every lane holds the same mt and m_run
-                    const float alpha = fast_exp2(m_run[j] - mt);   // 0 when m_run is -inf
-                    l_run[j] *= alpha;
+        for (int r = 1; r < NS; ++r) pm = fmaxf(pm, s[r]);
+        pm = stride_max<L>(pm);
+        const float m_new = fmaxf(m_run, pm);
+        if (__any(m_new > m_run)) {
+            const float alpha = fast_exp2(m_run - m_new);   // 0 on the first page
+            l_run *= alpha;
 #pragma unroll
-                    for (int i = 0; i < 8; ++i) o[j][i] *= alpha;
-                    m_run[j] = mt;
-                }
+            for (int g = 0; g < G; ++g) {
+                const float ag = lane_read(alpha, g * HG);
+#pragma unroll
+                for (int i = 0; i < 8; ++i) o[g][i] *= ag;
             }
+            m_run = m_new;
+        }
+        // ---- weights, shared within the wave ----
+#pragma unroll
+        for (int r = 0; r < NS; ++r) {
+            const float pw = fast_exp2(s[r] - m_run);      // 0 for masked keys
+            l_run += pw;
+            const float pv = valid[r] ? pw * vsc[r] : 0.0f;   // the scale of a masked slot may be NaN
+            if (sub % HG == 0) p_buf[r][kr][myhead] = pv;
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        // ---- p.v in the rotated domain, all G heads ----
+#pragma unroll
+        for (int r = 0; r < NS; ++r) {
             float cv[8];
-            tq3_levels8(vw, bk, cv);
+            tq3_levels8(vw[r], lv, cv);
 #pragma unroll
-            for (int j = 0; j < G; ++j) {
-                const float mu = m_run[j] == -INFINITY ? 0.0f : m_run[j];
-                const float pj = fast_exp2(s[j] - mu);            // 0 for masked keys
-                l_run[j] += pj;
-                const float w = valid ? pj * vsr : 0.0f;          // vsr may be NaN when masked
+            for (int g = 0; g < G; ++g) {
+                const float w = p_buf[r][kr][g];
 #pragma unroll
-                for (int i = 0; i < 8; ++i) o[j][i] = fmaf(w, cv[i], o[j][i]);
+                for (int i = 0; i < 8; ++i) o[g][i] = fmaf(w, cv[i], o[g][i]);
             }
         }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     }
 
-    // sum over the key rows of a step, rotate back, normalise, write
+    // sum over the key rows, rotate back, normalise, write
+    const float l_tot = stride_sum<L>(l_run);
 #pragma unroll
-    for (int j = 0; j < G; ++j) {
-        // l_run counts each key once per lane of its row: sum over rows only
-        l_run[j] = stride_sum<L>(l_run[j]);
+    for (int g = 0; g < G; ++g) {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) o[j][i] = stride_sum<L>(o[j][i]);
-        fwht_lanes<L>(o[j], g);
+        for (int i = 0; i < 8; ++i) o[g][i] = stride_sum<L>(o[g][i]);
+        fwht_lanes<L>(o[g], sub);
     }
     if (kr != 0) return;
 #pragma unroll
-    for (int j = 0; j < G; ++j) {
-        const float mu = m_run[j] == -INFINITY ? 0.0f : m_run[j];
+    for (int g = 0; g < G; ++g) {
+        const float mg = lane_read(m_run, g * HG);
+        const float lg = lane_read(l_tot, g * HG);
+        const float mu = mg == -INFINITY ? 0.0f : mg;
         float* dst;
         float inv;
         if constexpr (FINAL) {
-            float z = l_run[j];
-            if (a.sinks) z += fast_exp2(__ldg(a.sinks + head0 + j) * kLog2e - mu);
+            float z = lg;
+            if (a.sinks) z += fast_exp2(__ldg(a.sinks + head0 + g) * kLog2e - mu);
             inv = z > 0.0f ? 1.0f / z : 0.0f;
-            dst = a.out + (row0 + j) * D + g * 8;
+            dst = a.out + (row0 + g) * D + sub * 8;
         } else {
-            const int64_t pr = (row0 + j) * a.max_splits + sp;
-            inv = l_run[j] > 0.0f ? 1.0f / l_run[j] : 0.0f;
-            if (g == 0) a.lse_part[pr] = l_run[j] > 0.0f ? (m_run[j] + fast_log2(l_run[j])) * kLn2 : -INFINITY;
-            dst = a.o_part + pr * D + g * 8;
+            const int64_t pr = (row0 + g) * a.max_splits + sp;
+            inv = lg > 0.0f ? 1.0f / lg : 0.0f;
+            if (sub == 0) a.lse_part[pr] = lg > 0.0f ? (mg + fast_log2(lg)) * kLn2 : -INFINITY;
+            dst = a.o_part + pr * D + sub * 8;
         }
         const float f = inv * kInvD;
-        *reinterpret_cast<float4*>(dst) = make_float4(o[j][0] * f, o[j][1] * f, o[j][2] * f, o[j][3] * f);
-        *reinterpret_cast<float4*>(dst + 4) = make_float4(o[j][4] * f, o[j][5] * f, o[j][6] * f, o[j][7] * f);
+        *reinterpret_cast<float4*>(dst) = make_float4(o[g][0] * f, o[g][1] * f, o[g][2] * f, o[g][3] * f);
+        *reinterpret_cast<float4*>(dst + 4) = make_float4(o[g][4] * f, o[g][5] * f, o[g][6] * f, o[g][7] * f);
     }
 }
 

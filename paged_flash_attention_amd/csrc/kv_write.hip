@@ -11,8 +11,8 @@
 // weight), a key vector is divided by s per channel (IEEE fp32) before that.
 //
 // For 3-bit rotated pools (tq3.h) it rotates each vector by the Walsh-Hadamard
-// transform, takes its RMS as the scale and writes the 3-bit codes as bit planes,
-// with the decisions in fp32 in the fixed order tq3.h gives.
+// transform, takes its RMS as the scale and writes the 3-bit codes in 24-bit
+// fields, with the decisions in fp32 in the fixed order tq3.h gives.
 //
 // Each thread owns 8 consecutive elements (16 B of bf16 input) of one vector for
 // both K and V, so D/8 lanes share a vector.  The absmax is a max over those lanes
@@ -103,12 +103,12 @@ __global__ __launch_bounds__(256) void kv_write_kernel(KvWriteArgs a) {
     }
 }
 
-// 3-bit rotated pools: same lane layout as above.  Planes of a vector are
-// [3][D/8] bytes; lane g writes byte g of each plane.
+// 3-bit rotated pools: same lane layout as above.  A vector's codes are 3D/8
+// bytes; lane g writes its 24-bit field, bytes 3g .. 3g+2.
 template <int D>
 __global__ __launch_bounds__(256) void kv_write_tq3_kernel(KvWriteArgs a) {
     constexpr int L = D / 8;
-    constexpr int PB = D / 8;               // bytes per plane
+    constexpr int VB = 3 * D / 8;           // bytes per vector
     const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     const int64_t vec = t / L;
     const int g = (int)(t % L);
@@ -144,12 +144,12 @@ __global__ __launch_bounds__(256) void kv_write_tq3_kernel(KvWriteArgs a) {
         }
         fwht_lanes<L>(y, g);
         const float sc = __builtin_sqrtf(sum_squares_lanes<L>(y) / (float)D);
-        const uint32_t planes = tq3_codes8(y, sc, a.book);
+        const uint32_t field = tq3_codes8(y, sc, a.book);
         if (ok) {
-            uint8_t* dst = pool + sdst * (3 * PB) + g;
-            dst[0] = (uint8_t)planes;
-            dst[PB] = (uint8_t)(planes >> 8);
-            dst[2 * PB] = (uint8_t)(planes >> 16);
+            uint8_t* dst = pool + sdst * VB + 3 * g;
+            dst[0] = (uint8_t)field;
+            dst[1] = (uint8_t)(field >> 8);
+            dst[2] = (uint8_t)(field >> 16);
             if (g == 0) scale[sdst] = sc;
         }
     };

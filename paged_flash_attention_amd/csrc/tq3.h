@@ -9,8 +9,9 @@
 //    normal: levels +-M[0..3], thresholds 0, +-T[0..2].  Code bits 0-1 are the
 //    magnitude index m = #{k : |t| >= T[k]}, bit 2 is 1 when t >= 0 (a zero vector
 //    takes t = 0);
-//  * the codes are kept as three bit planes of D/8 bytes: element 8j+i of the
-//    vector is bit i of byte j of each plane ([3][D/8] bytes per vector);
+//  * the codes of a vector are packed as D/8 little-endian 24-bit fields of 3
+//    bytes: field j holds elements 8j .. 8j+7, element 8j+i in bits 3i .. 3i+2
+//    (3D/8 bytes per vector), so a lane's 8 codes are its own 3 bytes;
 //  * the cache holds x^ = H_D (s * c) / D with c = +-M[m].
 // The code decisions are made in fp32 in one fixed order (butterflies by stride 1,
 // 2, ..., D/2; squares summed by 8 in order, then the groups in a pairwise tree;
@@ -68,8 +69,7 @@ __device__ __forceinline__ float sum_squares_lanes(const float (&y)[8]) {
     return s;
 }
 
-// Quantise the lane's 8 rotated elements at scale s; returns the three plane
-// bytes (plane b in bits 8b .. 8b+7).
+// Quantise the lane's 8 rotated elements at scale s; returns their 24-bit field.
 __device__ __forceinline__ uint32_t tq3_codes8(const float (&y)[8], float s, const Tq3Book& bk) {
     uint32_t w = 0;
 #pragma unroll
@@ -78,21 +78,23 @@ __device__ __forceinline__ uint32_t tq3_codes8(const float (&y)[8], float s, con
         const float a = fabsf(t);
         const uint32_t m = (uint32_t)(a >= bk.t[0]) + (uint32_t)(a >= bk.t[1]) + (uint32_t)(a >= bk.t[2]);
         const uint32_t pos = t >= 0.0f ? 1u : 0u;
-        w |= ((m & 1u) << i) | (((m >> 1) & 1u) << (8 + i)) | (pos << (16 + i));
+        w |= (m | (pos << 2)) << (3 * i);
     }
     return w;
 }
 
-// The 8 levels (+-M[m]) of the codes in plane word w (as returned by tq3_codes8).
-__device__ __forceinline__ void tq3_levels8(uint32_t w, const Tq3Book& bk, float (&c)[8]) {
+// The level of a code: codes 0..3 are -M[0..3], codes 4..7 are +M[0..3].
+__device__ __forceinline__ float tq3_level_of(int code, const Tq3Book& bk) {
+    const float lo = (code & 1) ? bk.m[1] : bk.m[0];
+    const float hi = (code & 1) ? bk.m[3] : bk.m[2];
+    const float mag = (code & 2) ? hi : lo;
+    return (code & 4) ? mag : -mag;
+}
+
+// The 8 levels of a field, looked up in a level table in LDS.
+__device__ __forceinline__ void tq3_levels8(uint32_t w, const float* table, float (&c)[8]) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const bool b0 = (w >> i) & 1u, b1 = (w >> (8 + i)) & 1u, pos = (w >> (16 + i)) & 1u;
-        const float lo = b0 ? bk.m[1] : bk.m[0];
-        const float hi = b0 ? bk.m[3] : bk.m[2];
-        const float mag = b1 ? hi : lo;
-        c[i] = pos ? mag : -mag;
-    }
+    for (int i = 0; i < 8; ++i) c[i] = table[(w >> (3 * i)) & 7u];
 }
 
 }  // namespace pfa

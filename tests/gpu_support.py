@@ -39,7 +39,7 @@ def poisoned_pool(case: W.PagedCase) -> pfa.KVPool:
         k = torch.full(shape, float("nan"), dtype=torch.bfloat16, device="cuda")
         return pfa.KVPool(k, k.clone())
     if p.kv_dtype == "tq3":
-        k = torch.zeros(shape[:3] + (3, p.head_dim // 8), dtype=torch.uint8, device="cuda")
+        k = torch.zeros(shape[:3] + (3 * p.head_dim // 8,), dtype=torch.uint8, device="cuda")
         s = torch.full(shape[:3], float("nan"), dtype=torch.float32, device="cuda")
         return pfa.KVPool(k, k.clone(), s, s.clone())
     k = torch.zeros(shape, dtype=torch.int8, device="cuda")

@@ -8,7 +8,8 @@ Workloads:
 * batched decode, Qwen3-4B attention (32/8, D 128), batch 32, lengths U[512, 8192];
 * causal prefill, Llama-3.1-8B attention (32/8, D 128): 1024 and 8192 tokens,
   and 130 new tokens on a restored 8192-token prefix;
-* INT8-KV decode, Qwen3-30B-A3B attention (32/4, D 128), batch 8 at 32768 positions;
+* INT8-KV decode, Qwen3-30B-A3B attention (32/4, D 128), batch 8 at 32768 positions,
+  and the same shape on the 3-bit rotated cache (pool bit-exact, then decode);
 * gpt-oss-20b attention (64/8, D 64, sinks), window-128 and full layers: batch-64
   decode with lengths log-uniform in [128, 32768], and two 2048-token prefills;
 * verify steps on Qwen3-4B attention: 16 tokens at 1,024 positions (one sequence),
@@ -20,7 +21,7 @@ import torch
 
 import oracle as O
 import workloads as W
-from gpu_support import BF16_TOL, GpuCase, assert_close, oracle_pool, tol_of
+from gpu_support import BF16_TOL, GpuCase, assert_close, oracle_pool, pool_bits_equal, tol_of
 
 pytestmark = [pytest.mark.gpu, pytest.mark.slow]
 
@@ -86,6 +87,32 @@ def test_prefill_chunk130_on_8192():
 
 def test_decode_int8_batch8_ctx32768():
     _decode_check(W.decode_int8_qwen30b())
+
+
+def test_decode_tq3_batch8_ctx32768():
+    """The whole batch runs on the GPU; the oracle (whose fp32 rotation takes about a
+    minute for all 8 x 32768 x 4 vectors) checks sequences 0 and 5: their pages bit
+    for bit, then their decode outputs."""
+    case = W.decode_tq3_qwen30b()
+    seqs = [0, 5]
+    print(f"[full] {case.name}: B={case.batch} max_len={int(case.seq_lens.max())}, oracle on {seqs}", flush=True)
+    g = GpuCase(case)
+    got = g.decode(256)
+    p = case.p
+    pool = O.empty_pool(case.num_pages, p.num_kv_heads, p.page_size, p.head_dim, "tq3")
+    bt = case.block_table[seqs]
+    lens = case.seq_lens[seqs]
+    k = np.concatenate([case.k_tok[case.token_slice(s, 0, int(case.seq_lens[s]))] for s in seqs])
+    v = np.concatenate([case.v_tok[case.token_slice(s, 0, int(case.seq_lens[s]))] for s in seqs])
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    O.kv_write(pool, k, v, cu, lens, bt, p.page_size, "tq3")
+    pages = np.unique(np.concatenate([bt[i, : -(-int(lens[i]) // p.page_size)] for i in range(len(seqs))]))
+    for name in ("k", "v"):
+        assert np.array_equal(getattr(g.pool, name).cpu().numpy()[pages], pool[name][pages]), name
+        sc = getattr(g.pool, name + "_scale").cpu().numpy()[pages]
+        assert np.array_equal(sc.view(np.uint32), pool[name + "_scale"][pages].view(np.uint32)), name
+    ref = O.decode(case.q[seqs], pool, bt, lens, p)
+    assert_close(got[seqs], ref, BF16_TOL, f"{case.name} S=256, sequences {seqs}")
 
 
 @pytest.mark.parametrize("layer", ["window", "full"])

@@ -187,8 +187,8 @@ def _tq3_special_rows(D, n):
 
 @pytest.mark.parametrize("D", [64, 128])
 def test_kv_write_tq3_bitwise(D):
-    """3-bit rotated KV write: bit planes and scales equal the oracle's, whole pool,
-    poison included."""
+    """3-bit rotated KV write: packed codes and scales equal the oracle's, whole
+    pool, poison included."""
     case = W.make_case("kvw3", 5, P(8, 2, D, kv="tq3"), [3, 30, 70], [3, 30, 9], outlier_frac=0.01)
     sp = _tq3_special_rows(D, 8)
     case.k_tok[:8, 0] = sp

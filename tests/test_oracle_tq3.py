@@ -95,8 +95,8 @@ def test_quantiser_against_brute_force(D):
     scale is ||x||."""
     rng = np.random.default_rng(D + 3)
     bits = _bf16_bits(rng.standard_normal((300, D)).astype(np.float32) * rng.uniform(0.01, 10, (300, 1)))
-    planes, scale = O.quantize_tq3(bits)
-    codes = O.unpack_planes(planes)
+    packed, scale = O.quantize_tq3(bits)
+    codes = O.unpack_codes(packed)
     x = O.bf16_to_f64(bits)
     y = x @ scipy.linalg.hadamard(D).T
     rms = np.sqrt((y ** 2).mean(-1))
@@ -114,10 +114,10 @@ def test_quantiser_against_brute_force(D):
 
 
 def test_zero_vector():
-    planes, scale = O.quantize_tq3(np.zeros((2, 128), np.uint16))
+    packed, scale = O.quantize_tq3(np.zeros((2, 128), np.uint16))
     assert np.all(scale == 0)
-    assert np.all(O.unpack_planes(planes) == 4)                      # t = 0: positive, magnitude 0
-    assert np.all(O.dequantize_tq3(planes, scale) == 0)
+    assert np.all(O.unpack_codes(packed) == 4)                      # t = 0: positive, magnitude 0
+    assert np.all(O.dequantize_tq3(packed, scale) == 0)
 
 
 @pytest.mark.parametrize("k", [0, 5, 127])
@@ -127,12 +127,12 @@ def test_spike_reconstructs_closed_form(k):
     a = np.float32(-3.5)
     x = np.zeros((1, 128), np.float32)
     x[0, k] = a
-    planes, scale = O.quantize_tq3(_bf16_bits(x))
-    assert np.all(O.unpack_planes(planes) & 3 == 1)
+    packed, scale = O.quantize_tq3(_bf16_bits(x))
+    assert np.all(O.unpack_codes(packed) & 3 == 1)
     M, _ = O.codebook_f32()
     expect = np.zeros(128)
     expect[k] = float(M[1]) * float(a)
-    assert np.allclose(O.dequantize_tq3(planes, scale)[0], expect, atol=1e-6)
+    assert np.allclose(O.dequantize_tq3(packed, scale)[0], expect, atol=1e-6)
 
 
 def test_sign_symmetry():
@@ -141,21 +141,22 @@ def test_sign_symmetry():
     pa, sa = O.quantize_tq3(_bf16_bits(x))
     pb, sb = O.quantize_tq3(_bf16_bits(-x))
     assert np.array_equal(sa, sb)
-    assert np.array_equal(O.unpack_planes(pb), O.unpack_planes(pa) ^ 4)
+    assert np.array_equal(O.unpack_codes(pb), O.unpack_codes(pa) ^ 4)
 
 
-def test_planes_roundtrip():
+def test_packed_codes_roundtrip_and_layout():
     rng = np.random.default_rng(6)
     codes = rng.integers(0, 8, size=(3, 5, 128)).astype(np.uint8)
-    planes = O.pack_planes(codes)
-    assert planes.shape == (3, 5, 3, 16)
-    assert np.array_equal(O.unpack_planes(planes), codes)
-    # element 8j+i sits in bit i of byte j of each plane
+    packed = O.pack_codes(codes)
+    assert packed.shape == (3, 5, 48)
+    assert np.array_equal(O.unpack_codes(packed), codes)
+    # element 8j+i sits in bits 3i .. 3i+2 of the little-endian 24-bit field j
     one = np.zeros(128, np.uint8)
-    one[8 * 3 + 5] = 6                                               # bits 1 and 2
-    p = O.pack_planes(one)
-    assert p[0, 3] == 0 and p[1, 3] == 1 << 5 and p[2, 3] == 1 << 5
-    assert p.sum() == 2 << 5
+    one[8 * 3 + 5] = 6                                               # field 3, bits 15..17 = 0b110
+    p = O.pack_codes(one)
+    field = int(p[9]) | (int(p[10]) << 8) | (int(p[11]) << 16)
+    assert field == 6 << 15
+    assert p.sum() == p[9] + p[10] + p[11]
 
 
 def test_gaussian_round_trip_distortion():
@@ -163,9 +164,9 @@ def test_gaussian_round_trip_distortion():
     trip is the quantiser's distortion, 0.0345 (Max's table), up to sampling."""
     rng = np.random.default_rng(7)
     bits = _bf16_bits(rng.standard_normal((3000, 128)).astype(np.float32))
-    planes, scale = O.quantize_tq3(bits)
+    packed, scale = O.quantize_tq3(bits)
     x = O.bf16_to_f64(bits)
-    err = ((O.dequantize_tq3(planes, scale) - x) ** 2).sum() / (x ** 2).sum()
+    err = ((O.dequantize_tq3(packed, scale) - x) ** 2).sum() / (x ** 2).sum()
     assert 0.031 < err < 0.037
 
 
