@@ -468,7 +468,8 @@ def main():
         value = r["step_bytes"] / (r["step_ms"] * 1e-3) / 1e9
         unit, metric = "GB/s", "decode attn GB/s (HBM)"
         kernel = "decode_kernel"
-        traffic = measured_traffic(f"{kernel}:{args.workload}", src_digest("decode.hip", "pfa_device.h"))
+        traffic = measured_traffic(f"{kernel}:{args.workload}",
+                                   src_digest("decode.hip", "pfa_device.h", "group_reduce.h", "merge_splits.h"))
         roof = dict(bound="hbm", achieved=r["kernel_gbs"], peak=HBM_PEAK_GBS, unit="GB/s",
                     frac=r["frac_of_hbm_peak"], traffic=traffic)
 
