@@ -198,7 +198,9 @@ def run_decode(case, torch, pfa, gs, steps, warmup, fused=False):
             return
         pfa.paged_attn_decode(g.desc, pool, g.q, g.bt, g.seq_lens, max_len, S, ms, o_part=op, lse_part=lp)
         tm.close("decode", e)
+        e = tm.mark("combine")
         pfa.paged_attn_combine(g.desc, op, lp, g.seq_lens, S, ms, out)
+        tm.close("combine", e)
 
     for i in range(warmup):
         step(i)
@@ -213,9 +215,57 @@ def run_decode(case, torch, pfa, gs, steps, warmup, fused=False):
     torch.cuda.synchronize()
     step_ms = t0.elapsed_time(t1) / steps
     dec_ms = tm.mean_ms("decode")
-    return dict(step_ms=step_ms, decode_ms=dec_ms, pool_copies=len(pools),
-                decode_bytes=decode_bytes(case), step_bytes=decode_bytes(case) + kv_write_bytes(case),
-                partial_bytes=int(B * Hq * ms * (D + 1) * 4))
+    r = dict(step_ms=step_ms, decode_ms=dec_ms, pool_copies=len(pools),
+             decode_bytes=decode_bytes(case), step_bytes=decode_bytes(case) + kv_write_bytes(case),
+             partial_bytes=int(B * Hq * ms * (D + 1) * 4))
+    if not fused:
+        cms = tm.mean_ms("combine")
+        cb = combine_bytes(case)
+        r.update(combine_us=round(cms * 1e3, 2), combine_bytes=cb,
+                 combine_gbs=round(cb / (cms * 1e-3) / 1e9, 1))
+    return r
+
+
+def combine_bytes(case) -> int:
+    """The combine's algorithmic bytes: per (sequence, q head), the lse and o row of
+    each split its length covers, read once, and the fp32 output row written."""
+    p = case.p
+    S = case.split_keys
+    ns = (np.asarray(case.seq_lens, np.int64) + S - 1) // S
+    return int(ns.sum()) * p.num_q_heads * (p.head_dim + 1) * 4 + case.batch * p.num_q_heads * p.head_dim * 4
+
+
+def run_kv_write(case, torch, pfa, gs, steps, warmup):
+    """KV writes of the case's new tokens alone, each into the next of a set of poisoned
+    pools and from the next of a set of input copies (together >= 1 GiB, so the 256 MB
+    MALL serves neither side)."""
+    g = gs.GpuCase(case, fill=False)
+    k, v, cu = case.new_tokens()
+    per_call = sum(t.numel() * t.element_size() for t in (g.pool.k, g.pool.v, g.pool.k_scale, g.pool.v_scale)
+                   if t is not None) + 2 * k.size * 2
+    n = max(2, min(16, int(math.ceil((1 << 30) / per_call))))
+    pools = [g.pool] + [pfa.KVPool(*(None if t is None else t.clone() for t in
+                                     (g.pool.k, g.pool.v, g.pool.k_scale, g.pool.v_scale)))
+                        for _ in range(n - 1)]
+    ins = [(gs.dev_bf16(k), gs.dev_bf16(v)) for _ in range(n)]
+    cun = gs.dev_i32(cu)
+    tm = Timer(torch)
+
+    def step(i):
+        kn, vn = ins[i % n]
+        e = tm.mark("kv_write")
+        pfa.kv_write(g.desc, pools[i % n], kn, vn, cun, g.seq_lens, g.bt)
+        tm.close("kv_write", e)
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    tm.reset()
+    for i in range(steps):
+        step(warmup + i)
+    torch.cuda.synchronize()
+    ms = tm.mean_ms("kv_write")
+    return dict(step_ms=ms, kv_write_ms=ms, kv_write_bytes=kv_write_bytes(case), copies=n)
 
 
 def attn_input_bytes(ic) -> int:
@@ -403,6 +453,9 @@ def main():
         "decode_int8_batch8_ctx32768": lambda: W.decode_int8_qwen30b(),
         "decode_int8_batch8_ctx32768_smooth": lambda: W.decode_int8_qwen30b(smooth=True),
         "decode_tq3_batch8_ctx32768": lambda: W.decode_tq3_qwen30b(),
+        "kv_write_bf16_8192": lambda: W.kv_write_prompt("bf16"),
+        "kv_write_int8_8192": lambda: W.kv_write_prompt("int8"),
+        "kv_write_tq3_8192": lambda: W.kv_write_prompt("tq3"),
         "mixed_full_decode_b64": lambda: W.mixed_gptoss(layer="full", part="decode"),
         "mixed_window_decode_b64": lambda: W.mixed_gptoss(layer="window", part="decode"),
         "prefill_causal_8192": lambda: W.prefill_llama8b(prompt=8192),
@@ -427,6 +480,11 @@ def main():
             gbs = r["bytes"] / (r["attn_input_ms"] * 1e-3) / 1e9
             r.update(metric="attn input GB/s", kernel_gbs=round(gbs, 1), frac_of_hbm_peak=round(gbs / HBM_PEAK_GBS, 4))
             return case, r
+        if name.startswith("kv_write"):
+            r = run_kv_write(case, torch, pfa, gs, steps, warmup)
+            gbs = r["kv_write_bytes"] / (r["kv_write_ms"] * 1e-3) / 1e9
+            r.update(metric="kv write GB/s", kernel_gbs=round(gbs, 1), frac_of_hbm_peak=round(gbs / HBM_PEAK_GBS, 4))
+            return case, r
         if name.startswith("verify"):
             r = run_prefill(case, torch, pfa, gs, steps, warmup, verify=True)
             tf = r["flops"] / (r["prefill_ms"] * 1e-3) / 1e12
@@ -448,7 +506,13 @@ def main():
     case, r = measure(args.workload, args.steps, args.warmup)
     is_prefill = "prefill_ms" in r
     is_attn_input = args.workload.startswith("attn_input")
-    if is_attn_input:
+    is_kv_write = args.workload.startswith("kv_write")
+    if is_kv_write:
+        value = r["kernel_gbs"]
+        unit, metric = "GB/s", "kv write GB/s (HBM)"
+        roof = dict(bound="hbm", achieved=r["kernel_gbs"], peak=HBM_PEAK_GBS, unit="GB/s",
+                    frac=r["frac_of_hbm_peak"], traffic=None)
+    elif is_attn_input:
         value = r["kernel_gbs"]
         unit, metric = "GB/s", "attn input GB/s (HBM)"
         roof = dict(bound="hbm", achieved=r["kernel_gbs"], peak=HBM_PEAK_GBS, unit="GB/s",
@@ -479,6 +543,7 @@ def main():
                          ("decode_batch32_ctx8192", 30), ("decode_batch32_ctx8192_s1024", 30),
                          ("decode_int8_batch8_ctx32768", 30), ("decode_int8_batch8_ctx32768_smooth", 30),
                          ("decode_tq3_batch8_ctx32768", 30),
+                         ("kv_write_bf16_8192", 40), ("kv_write_int8_8192", 40), ("kv_write_tq3_8192", 40),
                          ("mixed_full_decode_b64", 30), ("prefill_causal_8192", 10),
                          ("prefill_chunk130_on_8192", 20), ("mixed_full_prefill_2x2048", 20),
                          ("verify_16tok_batch1_ctx1024", 50), ("verify_8tok_batch32_ctx512_8192", 30),
@@ -487,6 +552,9 @@ def main():
                 _, rr = measure(name, st, 3)
                 if name.startswith("attn_input"):
                     extra[name] = dict(us=round(rr["attn_input_ms"] * 1e3, 2), gbs=rr["kernel_gbs"],
+                                       frac_of_hbm_peak=rr["frac_of_hbm_peak"])
+                elif name.startswith("kv_write"):
+                    extra[name] = dict(us=round(rr["kv_write_ms"] * 1e3, 2), gbs=rr["kernel_gbs"],
                                        frac_of_hbm_peak=rr["frac_of_hbm_peak"])
                 elif name.startswith("verify"):
                     extra[name] = dict(us=round(rr["prefill_ms"] * 1e3, 2), gbs=rr["kernel_gbs"],
@@ -504,7 +572,7 @@ def main():
             torch.cuda.empty_cache()
 
     cpu = None
-    if not args.no_cpu_baseline and not is_prefill and not is_attn_input:
+    if not args.no_cpu_baseline and not is_prefill and not is_attn_input and not is_kv_write:
         log("[bench] cpu baseline (oracle)")
         cpu = cpu_baseline_decode(case)
 

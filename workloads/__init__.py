@@ -255,6 +255,15 @@ def prefill_llama8b(seed=3, prompt=1024, prefix=0):
     return make_case(name, seed, p, [prefix + prompt], [prompt], split_keys=0)
 
 
+def kv_write_prompt(kv_dtype="bf16", seed=12, prompt=8192):
+    """The KV write of one ``prompt``-token prompt in the Llama-3.1-8B attention shape
+    (8 KV heads, D 128), into a BF16, INT8 or 3-bit pool; raw K/V N(0,1) with 1%
+    outliers at +-8 for the quantised pools."""
+    p = AttnParams(32, 8, 128, kv_dtype=kv_dtype)
+    return make_case(f"kv_write_{kv_dtype}_{prompt}", seed, p, [prompt], [prompt], split_keys=0,
+                     outlier_frac=0.0 if kv_dtype == "bf16" else 0.01)
+
+
 def key_norm_weight(seed: int, head_dim: int, n_large: int = 4, large: float = 8.0) -> np.ndarray:
     """A synthetic key-norm weight (float32 [D], > 0): 1 + |N(0, 0.3)| per channel,
     with ``n_large`` channels at ``large`` (the few large channels such weights have)."""
