@@ -6,8 +6,9 @@ rows of the chunk plus seeded random ones.
 Workloads:
 * decode, 1 sequence at 1024 positions (16 q / 8 KV heads, D 128): split and unsplit;
 * batched decode, Qwen3-4B attention (32/8, D 128), batch 32, lengths U[512, 8192];
-* causal prefill, Llama-3.1-8B attention (32/8, D 128): 1024 and 8192 tokens,
-  and 130 new tokens on a restored 8192-token prefix;
+* causal prefill, Llama-3.1-8B attention (32/8, D 128): 1024, 8192 and 32768
+  tokens, and 130 new tokens on a restored 8192-token prefix;
+* one sequence decoding at 131072 positions (the longest context here);
 * INT8-KV decode, Qwen3-30B-A3B attention (32/4, D 128), batch 8 at 32768 positions,
   and the same shape on the 3-bit rotated cache (pool bit-exact, then decode);
 * gpt-oss-20b attention (64/8, D 64, sinks), window-128 and full layers: batch-64
@@ -83,6 +84,18 @@ def test_prefill_causal_8192_sampled():
 
 def test_prefill_chunk130_on_8192():
     _prefill_check(W.prefill_llama8b(prompt=130, prefix=8192))
+
+
+def test_decode_1seq_ctx131072():
+    """The longest context here: one sequence at 131072 positions (32 q / 8 KV heads,
+    D 128), as 512 splits of 256 keys and unsplit (one wave per KV head)."""
+    case = W.make_case("decode_1seq_ctx131072", 201, W.AttnParams(32, 8, 128), [131072], [1])
+    _decode_check(case, splits=(256, 0))
+
+
+def test_prefill_causal_32768_sampled():
+    """A 32768-token causal prompt (Llama-3.1-8B attention), sampled rows."""
+    _prefill_check(W.prefill_llama8b(prompt=32768), sample=256, seed=5)
 
 
 def test_decode_int8_batch8_ctx32768():
