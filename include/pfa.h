@@ -148,7 +148,8 @@ pfa_status pfa_tq3_codebook(float* magnitudes, float* thresholds);
  *     code  = clamp(rint(x / scale), -127, 127)       (ties to even)
  *   An all-zero vector gets scale 0 and codes 0.  TQ3 pools receive packed codes and
  *   scales as described at pfa_kv_dtype.  Tokens whose slot falls outside the block
- *   table or the pool are skipped.
+ *   table or the pool are skipped.  PFA_ERR_SHAPE if num_tokens * Hkv * D/8 exceeds
+ *   (2^31 - 1) * 256 (one thread per 8 elements).
  */
 pfa_status pfa_kv_write(const pfa_attn_desc* desc, const pfa_kv_pool* pool,
                         const void* k_new, const void* v_new, const int32_t* cu_new,

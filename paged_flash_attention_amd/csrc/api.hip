@@ -92,6 +92,9 @@ pfa_status pfa_kv_write(const pfa_attn_desc* desc, const pfa_kv_pool* pool, cons
     PFA_TRY(check_pool(desc, pool));
     if (batch < 0 || num_tokens < 0 || bt_stride <= 0) return PFA_ERR_SHAPE;
     if (num_tokens > 0 && batch == 0) return PFA_ERR_SHAPE;
+    // one thread per 8 elements of a (token, KV head) vector, 256 per workgroup
+    if ((int64_t)num_tokens * desc->num_kv_heads * (desc->head_dim / 8) > (int64_t)0x7fffffff * 256)
+        return PFA_ERR_SHAPE;
     if (num_tokens == 0) return PFA_OK;
     if (!k_new || !v_new || !cu_new || !seq_lens || !block_table) return PFA_ERR_NULL;
     pfa::KvWriteArgs a;

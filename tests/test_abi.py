@@ -86,6 +86,7 @@ def test_kv_write_validation():
     assert kvw(desc(), pool(), T=-1) == SHAPE
     assert kvw(desc(), pool(), batch=0) == SHAPE                # tokens but no sequences
     assert kvw(desc(), pool(), T=0, k=None) == OK              # nothing to do, nothing launched
+    assert kvw(desc(num_q_heads=65535 * 2, num_kv_heads=65535), pool(), T=2**31 - 1) == SHAPE   # grid too large
 
 
 def ain(d, p, prm=True, **kw):
