@@ -472,3 +472,53 @@ def test_decode_equals_last_prefill_row():
     for S in (0, 256):
         dec = gd.decode(S)
         assert np.max(np.abs(dec[0] - pre[-1])) < 1e-2
+
+
+# ---------------------------------------------------------------------------
+# a decode step under HIP graph capture: every replay equals the eager step
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("kv", ["bf16", "int8", "tq3"])
+def test_decode_step_replays_in_a_graph(kv):
+    """kv_write + split decode + combine captured once and replayed four times, with
+    eager work and synchronisations between the replays; each replay is bit-identical
+    to the eager step (the calls record no memset nodes)."""
+    case = W.make_case(f"graph_{kv}", 310, P(32, 8, 128, kv=kv, window=0), [100, 700, 1500, 33],
+                       np.ones(4, np.int32), outlier_frac=0.01 if kv != "bf16" else 0.0)
+    g = GpuCase(case)
+    k, v, cu = case.new_tokens()
+    kn, vn, cun = dev_bf16(k), dev_bf16(v), dev_i32(cu)
+    B, Hq, D = case.batch, case.p.num_q_heads, case.p.head_dim
+    max_len = int(case.seq_lens.max())
+    S = 256
+    ms = pfa.decode_num_splits(max_len, S)
+    op = torch.zeros((B, Hq, ms, D), device="cuda")
+    lp = torch.zeros((B, Hq, ms), device="cuda")
+    out = torch.zeros((B, Hq, D), device="cuda")
+
+    def step():
+        pfa.kv_write(g.desc, g.pool, kn, vn, cun, g.seq_lens, g.bt)
+        pfa.paged_attn_decode(g.desc, g.pool, g.q, g.bt, g.seq_lens, max_len, S, ms, o_part=op, lse_part=lp)
+        pfa.paged_attn_combine(g.desc, op, lp, g.seq_lens, S, ms, out)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):          # warm-up off the capture
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    ref = out.clone()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    torch.cuda.synchronize()
+    scratch = torch.randn(1 << 20, device="cuda")
+    for i in range(4):
+        out.fill_(float("nan"))
+        scratch.mul_(1.0001)               # eager work between replays
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref), f"replay {i} differs from the eager step"
+    assert_close(ref.cpu().numpy(), O.decode(case.q, oracle_pool(case), case.block_table, case.seq_lens, case.p),
+                 tol_of(case), f"graph step ({kv})")
