@@ -350,6 +350,48 @@ def run_prefill(case, torch, pfa, gs, steps, warmup, verify=False):
                 flops=prefill_flops(case), split_keys=sk, max_splits=ms, kv_bytes=verify_bytes(case))
 
 
+def run_verify_graph(case, torch, pfa, gs, steps, warmup):
+    """The verify step (kv_write + pfa_paged_attn_verify on the library's split, with
+    its combine) captured once in a HIP graph and replayed: the step as a serving loop
+    that replays graphs runs it, without host launch gaps."""
+    g, _, (kn, vn, cun) = setup_case(case, torch, pfa, gs, copies_for_bytes=0)
+    p = case.p
+    Tq = int(case.cu_q[-1])
+    out = torch.empty((Tq, p.num_q_heads, p.head_dim), device="cuda")
+    max_q, max_len = int(case.q_lens.max()), int(case.seq_lens.max())
+    ms, sk = pfa.verify_num_splits(g.desc, case.batch, max_q, max_len)
+    op = lp = None
+    if ms > 1:
+        op = torch.empty((Tq, p.num_q_heads, ms, p.head_dim), device="cuda")
+        lp = torch.empty((Tq, p.num_q_heads, ms), device="cuda")
+
+    def step():
+        pfa.kv_write(g.desc, g.pool, kn, vn, cun, g.seq_lens, g.bt)
+        pfa.paged_attn_verify(g.desc, g.pool, g.q, g.cu_q, g.bt, g.seq_lens, max_q, out,
+                              max_seq_len=max_len, split_keys=sk, max_splits=ms, o_part=op, lse_part=lp)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    for _ in range(warmup):
+        graph.replay()
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(steps):
+        graph.replay()
+    t1.record()
+    torch.cuda.synchronize()
+    return dict(step_ms=t0.elapsed_time(t1) / steps, split_keys=sk, max_splits=ms, kv_bytes=verify_bytes(case))
+
+
 # ---------------------------------------------------------------------------
 # CPU baseline: the oracle as it stands
 # ---------------------------------------------------------------------------
@@ -466,6 +508,7 @@ def main():
         "attn_input_1x8192": lambda: W.attn_input_qwen4b(),
         "attn_input_32x1_on_4096": lambda: W.attn_input_qwen4b(prompt=1, batch=32, prefix=4095),
         "verify_16tok_batch1_ctx1024": lambda: W.verify_qwen4b(),
+        "verify_16tok_batch1_ctx1024_graph": lambda: W.verify_qwen4b(),
         "verify_8tok_batch32_ctx512_8192": lambda: W.verify_qwen4b(batch=32, tokens=8, lo=512, hi=8192),
     }
     if args.workload not in builders:
@@ -484,6 +527,10 @@ def main():
             r = run_kv_write(case, torch, pfa, gs, steps, warmup)
             gbs = r["kv_write_bytes"] / (r["kv_write_ms"] * 1e-3) / 1e9
             r.update(metric="kv write GB/s", kernel_gbs=round(gbs, 1), frac_of_hbm_peak=round(gbs / HBM_PEAK_GBS, 4))
+            return case, r
+        if name.endswith("_graph"):
+            r = run_verify_graph(case, torch, pfa, gs, steps, warmup)
+            r.update(metric="verify step us (graph replay)")
             return case, r
         if name.startswith("verify"):
             r = run_prefill(case, torch, pfa, gs, steps, warmup, verify=True)
@@ -504,7 +551,7 @@ def main():
         return case, r
 
     case, r = measure(args.workload, args.steps, args.warmup)
-    is_prefill = "prefill_ms" in r
+    is_prefill = "prefill_ms" in r or args.workload.endswith("_graph")
     is_attn_input = args.workload.startswith("attn_input")
     is_kv_write = args.workload.startswith("kv_write")
     if is_kv_write:
@@ -518,6 +565,11 @@ def main():
         roof = dict(bound="hbm", achieved=r["kernel_gbs"], peak=HBM_PEAK_GBS, unit="GB/s",
                     frac=r["frac_of_hbm_peak"], traffic=None)
         case = case.case
+    elif args.workload.endswith("_graph"):
+        value = r["kv_bytes"] / (r["step_ms"] * 1e-3) / 1e9
+        unit, metric = "GB/s", "verify step GB/s (HBM, graph replay)"
+        roof = dict(bound="hbm", achieved=round(value, 1), peak=HBM_PEAK_GBS, unit="GB/s",
+                    frac=round(value / HBM_PEAK_GBS, 4), traffic=None)
     elif args.workload.startswith("verify"):
         value = r["kv_bytes"] / (r["step_ms"] * 1e-3) / 1e9
         unit, metric = "GB/s", "verify attn GB/s (HBM)"
@@ -546,13 +598,17 @@ def main():
                          ("kv_write_bf16_8192", 40), ("kv_write_int8_8192", 40), ("kv_write_tq3_8192", 40),
                          ("mixed_full_decode_b64", 30), ("prefill_causal_8192", 10),
                          ("prefill_chunk130_on_8192", 20), ("mixed_full_prefill_2x2048", 20),
-                         ("verify_16tok_batch1_ctx1024", 50), ("verify_8tok_batch32_ctx512_8192", 30),
+                         ("verify_16tok_batch1_ctx1024", 50), ("verify_16tok_batch1_ctx1024_graph", 200),
+                         ("verify_8tok_batch32_ctx512_8192", 30),
                          ("attn_input_1x8192", 30), ("attn_input_32x1_on_4096", 50)):
             try:
                 _, rr = measure(name, st, 3)
                 if name.startswith("attn_input"):
                     extra[name] = dict(us=round(rr["attn_input_ms"] * 1e3, 2), gbs=rr["kernel_gbs"],
                                        frac_of_hbm_peak=rr["frac_of_hbm_peak"])
+                elif name.endswith("_graph"):
+                    extra[name] = dict(step_us=round(rr["step_ms"] * 1e3, 2),
+                                       split=f"{rr['split_keys']}x{rr['max_splits']}")
                 elif name.startswith("kv_write"):
                     extra[name] = dict(us=round(rr["kv_write_ms"] * 1e3, 2), gbs=rr["kernel_gbs"],
                                        frac_of_hbm_peak=rr["frac_of_hbm_peak"])
