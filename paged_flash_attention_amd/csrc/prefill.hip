@@ -37,8 +37,12 @@
 //    ds_read_b64_tr_b16.  In each 16-lane group, lane j points at
 //    V[k0 + j/4][d0 + 4(j%4)], and lane i gets V[k0..k0+3][d0 + i].
 //  * Softmax arithmetic is trimmed for the VALU:
-//      - the row max is taken on raw scores;
-//      - p = exp2(s*c - m) is one FMA plus v_exp_f32, with c = sm_scale*log2 e;
+//      - c = sm_scale*log2 e is folded into Q (rounded to bf16) and -m into the
+//        QK accumulators' initial value, so a score leaves the MFMA as s*c - m and
+//        p = exp2 of it is one v_exp_f32 (64-key build; the 32-key build keeps
+//        one FMA per score, as its registers are tighter);
+//      - the row max is taken on those scores; when the reference m moves, the
+//        tile's scores move with it;
 //      - P is rounded to bf16 (RNE) for the PV MFMA;
 //      - the row sum is a dot2 of those rounded pairs with (1, 1), so l matches the
 //        numerator exactly;
