@@ -596,13 +596,15 @@ def main():
                          ("decode_int8_batch8_ctx32768", 30), ("decode_int8_batch8_ctx32768_smooth", 30),
                          ("decode_tq3_batch8_ctx32768", 30),
                          ("kv_write_bf16_8192", 40), ("kv_write_int8_8192", 40), ("kv_write_tq3_8192", 40),
-                         ("mixed_full_decode_b64", 30), ("prefill_causal_8192", 10),
+                         ("mixed_full_decode_b64", 30), ("prefill_causal_8192", 30),
                          ("prefill_chunk130_on_8192", 20), ("mixed_full_prefill_2x2048", 20),
                          ("verify_16tok_batch1_ctx1024", 50), ("verify_16tok_batch1_ctx1024_graph", 200),
                          ("verify_8tok_batch32_ctx512_8192", 30),
                          ("attn_input_1x8192", 30), ("attn_input_32x1_on_4096", 50)):
             try:
-                _, rr = measure(name, st, 3)
+                # the long MFMA-bound prompt gets a longer warmup: its first ~10 launches
+                # on a cold device run through a clock transient (up to ~20% slower)
+                _, rr = measure(name, st, 20 if name == "prefill_causal_8192" else 3)
                 if name.startswith("attn_input"):
                     extra[name] = dict(us=round(rr["attn_input_ms"] * 1e3, 2), gbs=rr["kernel_gbs"],
                                        frac_of_hbm_peak=rr["frac_of_hbm_peak"])
