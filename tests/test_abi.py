@@ -268,3 +268,13 @@ def test_tq3_pool_validation():
     assert dec(desc(kv_dtype=2, num_q_heads=48, num_kv_heads=3), pool(**tq)) == UNSUP   # G = 16
     assert dec(desc(kv_dtype=2), pool(**tq), batch=0) == OK                # nothing launched
     assert kvw(desc(kv_dtype=2), pool(**tq), T=0, k=None) == OK
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    """With no built library the binding raises; there is no fallback path."""
+    monkeypatch.setattr(pfa, "LIB_PATH", str(tmp_path / "libpfa.so"))
+    monkeypatch.setattr(pfa, "_lib", None)
+    with pytest.raises(RuntimeError, match="missing"):
+        pfa.lib()
+    with pytest.raises(RuntimeError, match="missing"):
+        pfa.decode_num_splits(1024, 256)
