@@ -181,7 +181,7 @@ def run_decode(case, torch, pfa, gs, steps, warmup, fused=False):
     B, Hq, D = case.batch, p.num_q_heads, p.head_dim
     max_len = int(case.seq_lens.max())
     S = case.split_keys
-    ms = pfa.decode_num_splits(max_len, S)
+    ms = pfa.decode_num_splits(max_len, S) if S > 0 else 1   # S = 0: unsplit, no combine
     op = torch.empty((B, Hq, ms, D), device="cuda")
     lp = torch.empty((B, Hq, ms), device="cuda")
     out = torch.empty((B, Hq, D), device="cuda")
@@ -194,6 +194,10 @@ def run_decode(case, torch, pfa, gs, steps, warmup, fused=False):
         e = tm.mark("decode")
         if fused:
             pfa.paged_attn_decode_fused(g.desc, pool, g.q, g.bt, g.seq_lens, max_len, S, ms, op, lp, ctr, out)
+            tm.close("decode", e)
+            return
+        if S == 0:
+            pfa.paged_attn_decode(g.desc, pool, g.q, g.bt, g.seq_lens, max_len, 0, 1, out=out)
             tm.close("decode", e)
             return
         pfa.paged_attn_decode(g.desc, pool, g.q, g.bt, g.seq_lens, max_len, S, ms, o_part=op, lse_part=lp)
@@ -218,7 +222,7 @@ def run_decode(case, torch, pfa, gs, steps, warmup, fused=False):
     r = dict(step_ms=step_ms, decode_ms=dec_ms, pool_copies=len(pools),
              decode_bytes=decode_bytes(case), step_bytes=decode_bytes(case) + kv_write_bytes(case),
              partial_bytes=int(B * Hq * ms * (D + 1) * 4))
-    if not fused:
+    if not fused and S > 0:
         cms = tm.mean_ms("combine")
         cb = combine_bytes(case)
         r.update(combine_us=round(cms * 1e3, 2), combine_bytes=cb,
@@ -596,8 +600,10 @@ def main():
                          ("decode_int8_batch8_ctx32768", 30), ("decode_int8_batch8_ctx32768_smooth", 30),
                          ("decode_tq3_batch8_ctx32768", 30),
                          ("kv_write_bf16_8192", 40), ("kv_write_int8_8192", 40), ("kv_write_tq3_8192", 40),
-                         ("mixed_full_decode_b64", 30), ("prefill_causal_8192", 30),
+                         ("mixed_full_decode_b64", 30), ("mixed_window_decode_b64", 50),
+                         ("prefill_causal_8192", 30),
                          ("prefill_chunk130_on_8192", 20), ("mixed_full_prefill_2x2048", 20),
+                         ("mixed_window_prefill_2x2048", 30),
                          ("verify_16tok_batch1_ctx1024", 50), ("verify_16tok_batch1_ctx1024_graph", 200),
                          ("verify_8tok_batch32_ctx512_8192", 30),
                          ("attn_input_1x8192", 30), ("attn_input_32x1_on_4096", 50)):

@@ -130,7 +130,8 @@ def test_decode_tq3_batch8_ctx32768():
 
 @pytest.mark.parametrize("layer", ["window", "full"])
 def test_mixed_gptoss_decode(layer):
-    _decode_check(W.mixed_gptoss(layer=layer, part="decode"), splits=(256,))
+    # the window layer is benchmarked unsplit
+    _decode_check(W.mixed_gptoss(layer=layer, part="decode"), splits=(256, 0) if layer == "window" else (256,))
 
 
 @pytest.mark.parametrize("layer", ["window", "full"])

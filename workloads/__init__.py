@@ -296,7 +296,9 @@ def mixed_gptoss(seed=5, layer="window", part="decode", batch=64, lo=128, hi=327
                  chunks=2, chunk_len=2048):
     """gpt-oss-20b attention shape (64 q / 8 KV heads, D 64, one sink logit per q
     head).  Window layers see the last 128 positions, full layers all of them.
-    ``part`` = "decode": 64 sequences, lengths log-uniform in [128, 32768];
+    ``part`` = "decode": 64 sequences, lengths log-uniform in [128, 32768], 256-key
+    splits for full layers and no split for window layers (a sequence sees at most
+    128 keys there, and splits of the hidden prefix would only write lse = -inf);
     ``part`` = "prefill": fresh prompts of ``chunk_len`` tokens."""
     window = 128 if layer == "window" else 0
     p = AttnParams(64, 8, 64, window=window, sinks=sinks_normal(seed + 99, 64))
@@ -304,7 +306,7 @@ def mixed_gptoss(seed=5, layer="window", part="decode", batch=64, lo=128, hi=327
         rng = np.random.default_rng(seed + 11)
         lens = log_uniform_lens(rng, batch, lo, hi)
         return make_case(f"mixed_{layer}_decode_b{batch}", seed, p, lens, np.ones(batch, np.int32),
-                         split_keys=256)
+                         split_keys=0 if window else 256)
     lens = np.full(chunks, chunk_len, np.int32)
     return make_case(f"mixed_{layer}_prefill_{chunks}x{chunk_len}", seed, p, lens, lens, split_keys=0)
 
