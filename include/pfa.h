@@ -291,6 +291,11 @@ pfa_status pfa_paged_attn_combine(const pfa_attn_desc* desc, const float* o_part
  *   A range with no visible key writes lse -inf.  A second kernel on the same
  *   stream then merges the partials into out, as pfa_paged_attn_combine does.
  *   When max_splits == 1, split_keys, o_part and lse_part are ignored.
+ *
+ *   With a sliding window of at most 512 keys, the work runs on the KV-split
+ *   kernel build (128-row workgroups, 32-key tiles) whether or not the key range
+ *   is split: each workgroup then sees only a few tiles, and the smaller
+ *   workgroups keep more of them resident per CU.
  */
 pfa_status pfa_paged_attn_prefill(const pfa_attn_desc* desc, const pfa_kv_pool* pool,
                                   const void* q, const int32_t* cu_q,

@@ -356,9 +356,13 @@ pfa_status pfa_paged_attn_prefill(const pfa_attn_desc* desc, const pfa_kv_pool* 
                                   int32_t max_q_len, int32_t max_seq_len, int32_t split_keys,
                                   int32_t max_splits, float* o_part, float* lse_part, float* out,
                                   void* stream) {
+    // A short sliding window gives each workgroup a few key tiles at most, so the
+    // kernel is its prologue and epilogue: the 128-row build, with more workgroups
+    // resident per CU, hides more of that latency.
+    const bool short_window = desc && desc->window > 0 && desc->window <= 512;
     return prefill_like(desc, pool, q, cu_q, block_table, bt_stride, seq_lens, batch, max_q_len,
                         max_seq_len, split_keys, max_splits, o_part, lse_part, out, stream,
-                        max_splits > 1);
+                        max_splits > 1 || short_window);
 }
 
 pfa_status pfa_paged_attn_verify(const pfa_attn_desc* desc, const pfa_kv_pool* pool, const void* q,
