@@ -217,6 +217,11 @@ pfa_status pfa_attn_input(const pfa_attn_desc* desc, const pfa_kv_pool* pool,
  *   Partials never include the sink, and out is left untouched.  Then call
  *   pfa_paged_attn_combine.
  *
+ *   The grid has one 64-lane workgroup per (split, KV head, sequence) for
+ *   max_splits splits.  With a short sliding window, most splits of a long
+ *   sequence are hidden and only write lse = -inf, so unsplit is the faster
+ *   launch there: each wave then reads at most the window's pages.
+ *
  *   A TQ3 pool is attended as the cache it stands for (pfa_kv_dtype).  The kernel
  *   works in the rotated domain: q . x^ = s * ((H_D q / D) . c), and the split's
  *   sum of p * s * c is rotated back by H_D / D at its end.
