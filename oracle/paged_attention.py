@@ -65,15 +65,28 @@ def bf16_to_f64(bits: np.ndarray) -> np.ndarray:
 # a2: the INT8 quantiser (numpy float32, the precision the stored scale has)
 # ---------------------------------------------------------------------------
 
+def smoothing_factors(smooth) -> np.ndarray:
+    """The per-channel factors an INT8 cache smooths keys by: for each given weight
+    s > 0 (float32, a normal number), the largest power of two not above it,
+    2^(e-1) where s = m * 2^e with 0.5 <= m < 1.  A power of two keeps k / s and
+    q * s exact (a reading: the page names the key norm's weight as the smoothing,
+    not how it is applied)."""
+    s = np.asarray(smooth, dtype=np.float32)
+    assert np.all(s > 0), "smoothing weights must be positive"
+    _, e = np.frexp(s.astype(np.float64))
+    return np.ldexp(1.0, e - 1).astype(np.float32)
+
+
 def quantize_int8(x_bits: np.ndarray, smooth=None):
     """Quantise bf16 vectors along the last axis to int8 codes + one float32 scale.
 
     Follows the TileInfer page, section "INT8 KV cache": one Int8 scale for each
     cached vector.  The steps, all in IEEE float32:
 
-    * with a per-channel ``smooth`` vector s (float32 [D], all > 0), the vector
-      quantised is ``x / s`` (the same section smooths keys by the key norm's
-      weight; a query then meets ``q * s``, leaving q.k unchanged);
+    * with a per-channel ``smooth`` weight (float32 [D], all > 0), the vector
+      quantised is ``x / s`` with s = ``smoothing_factors(smooth)`` (the same
+      section smooths keys by the key norm's weight; a query then meets ``q * s``,
+      leaving q.k unchanged);
     * ``scale = absmax / 127``;
     * ``code = clamp(rint(x / scale), -127, 127)``, where rint rounds ties to even;
     * an all-zero vector gets scale 0 and codes 0.
@@ -82,7 +95,7 @@ def quantize_int8(x_bits: np.ndarray, smooth=None):
     """
     x = bf16_to_f32(x_bits)
     if smooth is not None:
-        x = (x / np.asarray(smooth, dtype=np.float32)).astype(np.float32)
+        x = (x / smoothing_factors(smooth)).astype(np.float32)
     absmax = np.max(np.abs(x), axis=-1)
     scale = (absmax / np.float32(127.0)).astype(np.float32)
     safe = np.where(scale > 0, scale, np.float32(1.0)).astype(np.float32)
@@ -93,10 +106,11 @@ def quantize_int8(x_bits: np.ndarray, smooth=None):
 
 
 def dequantize_int8(codes: np.ndarray, scale: np.ndarray, smooth=None) -> np.ndarray:
-    """code * scale (* s per channel when smoothed), exact in float64."""
+    """code * scale (* s per channel when smoothed, s = smoothing_factors(smooth)),
+    exact in float64."""
     x = codes.astype(np.float64) * scale.astype(np.float64)[..., None]
     if smooth is not None:
-        x = x * np.asarray(smooth, dtype=np.float32).astype(np.float64)
+        x = x * smoothing_factors(smooth).astype(np.float64)
     return x
 
 

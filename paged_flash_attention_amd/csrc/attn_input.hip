@@ -94,7 +94,7 @@ __global__ __launch_bounds__(256) void attn_input_kernel(AttnInputArgs a) {
             kw[2 * i] = bf16_lo(ka[i]); kw[2 * i + 1] = bf16_hi(ka[i]);
         }
     }
-    float ks[8];                    // INT8 key smoothing of the lane's 8 channels (1 = none)
+    float ks[8];                    // INT8 key smoothing of the lane's 8 channels, powers of two (1 = none)
 #pragma unroll
     for (int e = 0; e < 8; ++e) ks[e] = 1.0f;
     const bool smooth = INT8 && a.k_smooth != nullptr;
@@ -103,6 +103,8 @@ __global__ __launch_bounds__(256) void attn_input_kernel(AttnInputArgs a) {
         const float4 s0 = __ldg(sp), s1 = __ldg(sp + 1);
         ks[0] = s0.x; ks[1] = s0.y; ks[2] = s0.z; ks[3] = s0.w;
         ks[4] = s1.x; ks[5] = s1.y; ks[6] = s1.z; ks[7] = s1.w;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) ks[e] = smooth_pow2(ks[e]);
     }
     const uint16_t* row = a.qkv + (int64_t)tok * heads * D + chunk * 8;
     const bool lower = chunk < HALF;
@@ -157,7 +159,7 @@ __global__ __launch_bounds__(256) void attn_input_kernel(AttnInputArgs a) {
                 qv[2 * i] = is_v ? x[2 * i] : bf16_lo(ow[i]);
                 qv[2 * i + 1] = is_v ? x[2 * i + 1] : bf16_hi(ow[i]);
             }
-            if (smooth && is_k) {   // keys smoothed per channel: quantise k / s
+            if (smooth && is_k) {   // keys smoothed per channel: quantise k / s (exact)
 #pragma unroll
                 for (int e = 0; e < 8; ++e) qv[e] = qv[e] / ks[e];
             }

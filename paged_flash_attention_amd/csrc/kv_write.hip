@@ -74,12 +74,12 @@ __global__ __launch_bounds__(256) void kv_write_kernel(KvWriteArgs a) {
             vx[2 * i] = bf16_lo(vw[i]);
             vx[2 * i + 1] = bf16_hi(vw[i]);
         }
-        if (a.k_smooth) {   // keys smoothed per channel: quantise k / s (IEEE divide)
+        if (a.k_smooth) {   // keys smoothed per channel: quantise k / s, s a power of two (exact)
             const float4* sp = reinterpret_cast<const float4*>(a.k_smooth + chunk * 8);
             const float4 s0 = __ldg(sp), s1 = __ldg(sp + 1);
             const float sv[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
 #pragma unroll
-            for (int i = 0; i < 8; ++i) kx[i] = kx[i] / sv[i];
+            for (int i = 0; i < 8; ++i) kx[i] = kx[i] / smooth_pow2(sv[i]);
         }
 #pragma unroll
         for (int i = 0; i < 8; ++i) {

@@ -104,6 +104,11 @@ __device__ __forceinline__ float stride_max(float x) {
     return x;
 }
 
+// INT8 key smoothing uses, per channel, the largest power of two not above the
+// given weight s (the weight with its mantissa bits cleared), so that k / s and
+// q * s are exact.
+__device__ __forceinline__ float smooth_pow2(float s) { return __uint_as_float(__float_as_uint(s) & 0xff800000u); }
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 

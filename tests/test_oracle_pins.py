@@ -437,6 +437,14 @@ def test_quantiser_bounds_and_argmax():
 # INT8 key smoothing (keys stored as k / s per channel; queries meet q * s)
 # ---------------------------------------------------------------------------
 
+def test_smoothing_factor_is_the_largest_power_of_two_not_above_the_weight():
+    w = np.array([1.0, 1.5, 1.999, 2.0, 0.75, 0.5, 12.0, 8.0, 3e-30, 1e30], np.float32)
+    want = np.array([2.0 ** math.floor(math.log2(float(x))) for x in w], np.float32)
+    np.testing.assert_array_equal(O.smoothing_factors(w), want)
+    f = O.smoothing_factors(w).astype(np.float64)
+    assert np.all((f <= w) & (w < 2 * f))
+
+
 def test_smoothing_by_ones_is_no_smoothing():
     rng = np.random.default_rng(21)
     bits = W.normal_bf16(rng, (300, 128), outlier_frac=0.01)
@@ -468,7 +476,8 @@ def test_smoothed_dequantisation_bound():
 
 def test_smoothed_attention_is_scaled_query_on_unsmoothed_codes():
     """q . (code * scale * s) = (q * s) . (code * scale): the smoothing vector sits on
-    channels, so a brute force with the query scaled instead must agree."""
+    channels, so a brute force with the query scaled instead must agree.  s is the
+    power of two at or below each given weight."""
     rng = np.random.default_rng(24)
     p = W.AttnParams(4, 2, 8, page_size=2, kv_dtype="int8")
     case = W.make_case("smooth", 24, p, [5, 3], [1, 1])
@@ -481,7 +490,8 @@ def test_smoothed_attention_is_scaled_query_on_unsmoothed_codes():
         n = int(case.seq_lens[b])
         for h in range(4):
             g = h // 2
-            q = [bf16_bits_to_float(x) * float(s[d]) for d, x in enumerate(case.q[b, h])]
+            q = [bf16_bits_to_float(x) * 2.0 ** math.floor(math.log2(float(s[d])))
+                 for d, x in enumerate(case.q[b, h])]
             xs, vs = [], []
             for j in range(n):
                 pg, off = int(case.block_table[b][j // 2]), j % 2
