@@ -29,9 +29,9 @@
 //  * q.k: v_dot2_f32_bf16 on (q, k) bf16 pairs.  INT8 codes are offset to the
 //    unsigned byte c+128 (v_cvt_f32_ubyteN, exact in bf16), and 128*sum(q) is
 //    subtracted from the dot.  With key smoothing (keys stored as k/s per
-//    channel, the "INT8 KV cache" section's smoothing by the key norm's weight),
-//    q is first scaled by s and rounded to bf16.  A lane's partial dots for the G heads go through a
-//    transposed butterfly over the LPK lanes (DPP / swizzle moves).  Slot j of a
+//    channel, the "INT8 KV cache" section's smoothing by the key norm's weight,
+//    s taken as a power of two), q is first scaled by s, which is exact in bf16.
+//    A lane's partial dots for the G heads go through a transposed butterfly over the LPK lanes (DPP / swizzle moves).  Slot j of a
 //    lane holds head (j ^ myhead), so each stage adds a partner's upper half to its
 //    own lower half with no selects, and ends with the lane holding its own head's
 //    full score.
@@ -39,11 +39,15 @@
 //    rescaled only when some head's running max grows.  The weights p are shared
 //    within the wave through LDS.
 //  * p.v: for G <= 4, fp32 FMAs on the lane's 8 elements for all G heads.  For
-//    G = 8, the VALU budget forces dot2 on key pairs from two loads:
-//      - BF16: p rounded to bf16, with the (v_a, v_b) pairs built by v_perm;
-//      - INT8: p*scale_v*2^12 in fp16, with the code pairs built by a byte
-//        permute into fp16 (1024 + u).  The 1152 offset is removed by a packed
-//        fp16 add, which is exact.
+//    G = 8, the VALU budget forces dot2 on key pairs from two loads.  The lane
+//    that computes a head's weights w (p, or p*scale_v for INT8) for two keys
+//    rounds them to a bf16 pair once (nearest even; bf16 has fp32's range, so no
+//    weight can overflow or flush) and shares the pair through LDS:
+//      - BF16: the (v_a, v_b) pairs are built by v_perm; l sums the same rounded
+//        weights (a dot2 with (1, 1)), so numerator and denominator agree;
+//      - INT8: the code pairs are u = c + 128 (exact in bf16, from
+//        v_cvt_f32_ubyteN), and 128 * (the sum of the same rounded weights) is
+//        subtracted at the end.
 //  * At the end of a split each wave reduces its partial o across key groups and
 //    writes o/l with lse = ln(sum e^s) (split mode), or the final output with the
 //    sink (unsplit mode).
@@ -52,8 +56,6 @@
 
 namespace pfa {
 namespace {
-
-typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
 template <bool INT8> struct Chunk;
 template <> struct Chunk<false> { typedef uint4 T; };   // 8 bf16
@@ -97,10 +99,9 @@ __device__ __forceinline__ void v_floats(const uint2& c, float (&x)[8]) {
     }
 }
 
-// Element pairs (a[d], b[d]) of two keys' chunks, d = 0..7 (paired p.v).
-// BF16: bf16 pairs by byte permute.  INT8: fp16 pairs of the codes, exact: the
-// byte permute forms 1024 + (c ^ 0x80) = 1152 + c, then a packed fp16 add of
-// -1152 leaves c.
+// Element pairs (a[d], b[d]) of two keys' chunks as bf16, d = 0..7 (paired p.v).
+// BF16: by byte permute.  INT8: u = c + 128 of each code, exact in bf16 (the
+// caller removes the offset).
 __device__ __forceinline__ void v_pairs(const uint4& a, const uint4& b, uint32_t (&v)[8]) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -109,17 +110,13 @@ __device__ __forceinline__ void v_pairs(const uint4& a, const uint4& b, uint32_t
     }
 }
 __device__ __forceinline__ void v_pairs(const uint2& a, const uint2& b, uint32_t (&v)[8]) {
-    const f16x2 off = {(_Float16)-1152.0f, (_Float16)-1152.0f};
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            // bytes: [a_k, 0, b_k, 0]  (selector 0x0c yields zero)
-            const uint32_t sel = (uint32_t)k | (0x0cu << 8) | ((uint32_t)(4 + k) << 16) | (0x0cu << 24);
-            const uint32_t w = __builtin_amdgcn_perm(dw(b, h), dw(a, h), sel) ^ 0x64806480u;
-            f16x2 f = __builtin_bit_cast(f16x2, w) + off;
-            v[4 * h + k] = __builtin_bit_cast(uint32_t, f);
-        }
+        const uint32_t ua = dw(a, h) ^ 0x80808080u, ub = dw(b, h) ^ 0x80808080u;
+        v[4 * h + 0] = pack_hi16((float)(ua & 0xffu), (float)(ub & 0xffu));
+        v[4 * h + 1] = pack_hi16((float)((ua >> 8) & 0xffu), (float)((ub >> 8) & 0xffu));
+        v[4 * h + 2] = pack_hi16((float)((ua >> 16) & 0xffu), (float)((ub >> 16) & 0xffu));
+        v[4 * h + 3] = pack_hi16((float)(ua >> 24), (float)(ub >> 24));
     }
 }
 
@@ -139,6 +136,8 @@ void decode_kernel(DecodeArgs a) {
     static_assert(!PAIRED || NLOAD % 2 == 0, "key pairs");
     typedef typename Chunk<INT8>::T CT;
 
+    // weights of a page, double-buffered: [key][head] floats (G <= 4), or for
+    // G = 8 [key pair][key group][head] bf16 pairs
     __shared__ __attribute__((aligned(16))) float p_buf[2][kPage][G];
     __shared__ float w_lds[FINAL ? 1 : kFusedMergeChunk];
 
@@ -224,7 +223,7 @@ void decode_kernel(DecodeArgs a) {
         q[j][0] = v.x; q[j][1] = v.y; q[j][2] = v.z; q[j][3] = v.w;
     }
     if constexpr (INT8) {
-        if (a.k_smooth) {   // keys stored smoothed (k / s): the query meets q * s, rounded to bf16
+        if (a.k_smooth) {   // keys stored smoothed (k / s): the query meets q * s (s a power of two: exact)
             const float4* sp = reinterpret_cast<const float4*>(a.k_smooth + sub * 8);
             const float4 s0 = __ldg(sp), s1 = __ldg(sp + 1);
             const float sv[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
@@ -232,7 +231,8 @@ void decode_kernel(DecodeArgs a) {
             for (int j = 0; j < G; ++j)
 #pragma unroll
                 for (int w = 0; w < 4; ++w)
-                    q[j][w] = pack_bf16_rne(bf16_lo(q[j][w]) * sv[2 * w], bf16_hi(q[j][w]) * sv[2 * w + 1]);
+                    q[j][w] = pack_bf16_rne(bf16_lo(q[j][w]) * smooth_pow2(sv[2 * w]),
+                                            bf16_hi(q[j][w]) * smooth_pow2(sv[2 * w + 1]));
         }
     }
     float qbias = 0.0f;   // INT8: 128 * sum_d q[myhead][d]
@@ -248,9 +248,6 @@ void decode_kernel(DecodeArgs a) {
         qbias = 128.0f * transpose_reduce<LPK, G>(part);
     }
     const float c2 = a.sm_scale * kLog2e;      // scores kept in log2 units
-    // INT8 paired p.v carries p*scale_v*2^12 in fp16; undone at the end
-    constexpr float kPScale = 4096.0f;
-    constexpr float kOScale = (INT8 && PAIRED) ? 1.0f / kPScale : 1.0f;
 
     const int p0 = lo / kPage, p1 = (hi - 1) / kPage;
     const int32_t* bt = a.block_table + (int64_t)b * a.bt_stride;
@@ -288,6 +285,7 @@ void decode_kernel(DecodeArgs a) {
         for (int j = 0; j < 8; ++j) o[g][j] = 0.0f;
     float m_run = -INFINITY;   // running max (log2 units) of this lane's head
     float l_run = 0.0f;        // this lane's share of sum 2^(s - m_run) (its keys, its head)
+    float w_run = 0.0f;        // INT8 paired: this lane's share of the sum of the rounded weights
 
     int pb = 0;
     load_page(p0);
@@ -336,6 +334,7 @@ void decode_kernel(DecodeArgs a) {
         if (__any(m_new > m_run)) {
             const float alpha = fast_exp2(m_run - m_new);   // 0 on the first page
             l_run *= alpha;
+            if constexpr (INT8 && PAIRED) w_run *= alpha;
 #pragma unroll
             for (int g = 0; g < G; ++g) {
                 const float ag = lane_read(alpha, g * HG);
@@ -345,13 +344,32 @@ void decode_kernel(DecodeArgs a) {
             m_run = m_new;
         }
         // ---- weights, shared within the wave ----
+        if constexpr (!PAIRED) {
 #pragma unroll
-        for (int i = 0; i < NLOAD; ++i) {
-            const float pw = fast_exp2(s[i] - m_run);      // 0 for masked keys
-            l_run += pw;
-            float pv = pw;
-            if constexpr (INT8) pv = valid[i] ? pw * vscur[i] * (PAIRED ? kPScale : 1.0f) : 0.0f;
-            if (sub % HG == 0) p_buf[pb][i * KPL + kg][myhead] = pv;
+            for (int i = 0; i < NLOAD; ++i) {
+                const float pw = fast_exp2(s[i] - m_run);      // 0 for masked keys
+                l_run += pw;
+                float pv = pw;
+                if constexpr (INT8) pv = valid[i] ? pw * vscur[i] : 0.0f;
+                if (sub % HG == 0) p_buf[pb][i * KPL + kg][myhead] = pv;
+            }
+        } else {
+            // the weights of keys (i, i+1) as one bf16 pair, at [i/2][kg][head]
+            uint32_t* pp_buf = reinterpret_cast<uint32_t*>(&p_buf[pb][0][0]);
+#pragma unroll
+            for (int i = 0; i < NLOAD; i += 2) {
+                const float p0 = fast_exp2(s[i] - m_run), p1 = fast_exp2(s[i + 1] - m_run);
+                uint32_t pr;
+                if constexpr (INT8) {
+                    l_run += p0 + p1;
+                    pr = pack_bf16_rne(valid[i] ? p0 * vscur[i] : 0.0f, valid[i + 1] ? p1 * vscur[i + 1] : 0.0f);
+                    w_run = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(pr), as_bf16x2(0x3F803F80u), w_run, false);
+                } else {
+                    pr = pack_bf16_rne(p0, p1);
+                    l_run = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(pr), as_bf16x2(0x3F803F80u), l_run, false);
+                }
+                if (sub % HG == 0) pp_buf[((i / 2) * KPL + kg) * G + myhead] = pr;
+            }
         }
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
@@ -378,30 +396,23 @@ void decode_kernel(DecodeArgs a) {
                     for (int j = 0; j < 8; ++j) o[g][j] = fmaf(pw[g], x[j], o[g][j]);
             }
         } else {
+            const uint4* pp4 = reinterpret_cast<const uint4*>(&p_buf[pb][0][0]);
 #pragma unroll
             for (int i = 0; i < NLOAD; i += 2) {
                 uint32_t vv[8];
                 v_pairs(vcur[i], vcur[i + 1], vv);
-                float pa[G], pbv[G];
+                // the G weight pairs of keys (i, i+1) of this key group
+                uint32_t pp[G];
 #pragma unroll
-                for (int g = 0; g < G; ++g) {
-                    pa[g] = p_buf[pb][i * KPL + kg][g];
-                    pbv[g] = p_buf[pb][(i + 1) * KPL + kg][g];
+                for (int q4 = 0; q4 < G / 4; ++q4) {
+                    const uint4 w = pp4[((i / 2) * KPL + kg) * (G / 4) + q4];
+                    pp[4 * q4] = w.x; pp[4 * q4 + 1] = w.y; pp[4 * q4 + 2] = w.z; pp[4 * q4 + 3] = w.w;
                 }
 #pragma unroll
-                for (int g = 0; g < G; ++g) {
-                    if constexpr (INT8) {
-                        const f16x2 pp = __builtin_bit_cast(f16x2, __builtin_amdgcn_cvt_pkrtz(pa[g], pbv[g]));
+                for (int g = 0; g < G; ++g)
 #pragma unroll
-                        for (int j = 0; j < 8; ++j)
-                            o[g][j] = __builtin_amdgcn_fdot2(pp, __builtin_bit_cast(f16x2, vv[j]), o[g][j], false);
-                    } else {
-                        const bf16x2 pp = as_bf16x2(pack_bf16_rne(pa[g], pbv[g]));
-#pragma unroll
-                        for (int j = 0; j < 8; ++j)
-                            o[g][j] = __builtin_amdgcn_fdot2_f32_bf16(pp, as_bf16x2(vv[j]), o[g][j], false);
-                    }
-                }
+                    for (int j = 0; j < 8; ++j)
+                        o[g][j] = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(pp[g]), as_bf16x2(vv[j]), o[g][j], false);
             }
         }
         pb ^= 1;
@@ -414,15 +425,22 @@ void decode_kernel(DecodeArgs a) {
 #pragma unroll
         for (int j = 0; j < 8; ++j) o[g][j] = stride_sum<LPK>(o[g][j]);
     const float l_tot = stride_sum<LPK>(l_run);
+    float w_tot = 0.0f;
+    if constexpr (INT8 && PAIRED) w_tot = stride_sum<LPK>(w_run);
 #pragma unroll
     for (int g = 0; g < G; ++g) {
         const float mg = lane_read(m_run, g * HG);
         const float lg = lane_read(l_tot, g * HG);
+        if constexpr (INT8 && PAIRED) {   // the codes entered as c + 128
+            const float off = 128.0f * lane_read(w_tot, g * HG);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) o[g][j] -= off;
+        }
         float den = lg;
         if constexpr (FINAL) {
             if (a.sinks) den += fast_exp2(__ldg(a.sinks + head0 + g) * kLog2e - mg);
         }
-        const float f = (FINAL && !(den > 0.0f)) ? 0.0f : kOScale / den;
+        const float f = (FINAL && !(den > 0.0f)) ? 0.0f : 1.0f / den;
         if (g % KPL == kg) {
             float* dst = FINAL ? a.out + (row0 + g) * D + sub * 8
                                : a.o_part + ((row0 + g) * a.max_splits + sp) * D + sub * 8;

@@ -37,12 +37,11 @@
 //    ds_read_b64_tr_b16.  In each 16-lane group, lane j points at
 //    V[k0 + j/4][d0 + 4(j%4)], and lane i gets V[k0..k0+3][d0 + i].
 //  * Softmax arithmetic is trimmed for the VALU:
-//      - c = sm_scale*log2 e is folded into Q (rounded to bf16) and -m into the
-//        QK accumulators' initial value, so a score leaves the MFMA as s*c - m and
-//        p = exp2 of it is one v_exp_f32 (64-key build; the 32-key build keeps
-//        one FMA per score, as its registers are tighter);
-//      - the row max is taken on those scores; when the reference m moves, the
-//        tile's scores move with it;
+//      - Q and K enter the MFMA as they are (bf16), so q.k is exact up to fp32
+//        summation; p = exp2(c*s - m) with c = sm_scale*log2 e is one FMA and one
+//        v_exp_f32 per score.  (Folding c into Q would save the FMA but round Q*c
+//        to bf16, an error that grows with the logits.)
+//      - the row max is taken on the raw scores (c > 0);
 //      - P is rounded to bf16 (RNE) for the PV MFMA;
 //      - the row sum is a dot2 of those rounded pairs with (1, 1), so l matches the
 //        numerator exactly;
@@ -82,10 +81,6 @@ constexpr int kStages = 5;        // LDS ring depth: tiles kb-1 .. kb+3 around t
 constexpr int kPairs1 = kBN == 64 ? 12 : 6;   // of a tile's 8*kBN/32 score pairs per lane,
                                   // those whose exps run beside the QK^T MFMAs (the rest beside PV)
 constexpr int kXcds = 8;
-// Fold the softmax scale into Q and the running max into the QK accumulators (see
-// the Q fragment below).  Only the 64-key build gains from it: in the 32-key build
-// the extra registers cost more than the VALU work saved.
-constexpr bool kFold = kBN == 64;
 
 #define LDS3 __attribute__((address_space(3)))
 typedef short s16x4 __attribute__((ext_vector_type(4)));
@@ -229,10 +224,8 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a, const 
     const int w_lo = W > 0 ? max(0, prefix + w_first - W + 1) : 0;
 
     // ---- Q fragment (B operand of S^T = K Q^T) ----
-    // With kFold, scores come out of the MFMA in log2 units, s' = c2 q.k - mu:
-    // c2 = sm_scale * log2 e is folded into Q (rounded to bf16), and -mu, the row's
-    // reference max, is the accumulator's initial value.  Then p = 2^s' needs no
-    // arithmetic before the exp.  Otherwise s' = q.k and p = 2^(c2 s' - mu).
+    // Scores leave the MFMA as s = q.k; p = 2^(c2 s - mu) with c2 = sm_scale * log2 e
+    // and mu the row's reference max (log2 units).
     const float c2 = a.sm_scale * kLog2e;
     bf16x8 qf[KK];
     {
@@ -241,13 +234,6 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a, const 
         for (int kk = 0; kk < KK; ++kk) {
             uint4 v = make_uint4(0, 0, 0, 0);
             if (row_ok) v = *reinterpret_cast<const uint4*>(qp + 16 * kk);
-            if constexpr (kFold) {
-                const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-                uint32_t o[4];
-#pragma unroll
-                for (int i = 0; i < 4; ++i) o[i] = pack_bf16_rne(bf16_lo(w[i]) * c2, bf16_hi(w[i]) * c2);
-                v = make_uint4(o[0], o[1], o[2], o[3]);
-            }
             qf[kk] = __builtin_bit_cast(bf16x8, v);
         }
         // The direct loads below are invisible to the compiler's vmcnt tracking.
@@ -308,11 +294,6 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a, const 
         for (int r = 0; r < 16; ++r) acc_o[db][r] = 0.0f;
     float m_run = -INFINITY;   // log2 units
     float l_run = 0.0f;        // this lane's share (its 16 keys of each 32)
-    // kFold: -mu splat, the QK accumulators' initial value (mu is m_run, or 0
-    // while no key has been seen)
-    f32x16 negm;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) negm[r] = 0.0f;
 
     // per-lane constants of the transposed V reads
     const int tr_g = lane / 16, tr_j = lane % 16;
@@ -363,11 +344,9 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a, const 
     // Lazy rescale with headroom: the reference max moves only when a row's max
     // exceeds it by more than 8, so p <= 2^8 (exact enough in bf16, no overflow in
     // the fp32 sums).  O and l share the reference, so o/l is unchanged.  mt is
-    // the lane's max of the tile's scores s'.  With kFold they carry the reference
-    // mu they were computed with, and when it moves, s' moves with it.
-    auto rescale = [&](float mt, Scores& s) __attribute__((always_inline)) {
-        const float mu_old = (m_run == -INFINITY) ? 0.0f : m_run;
-        mt = kFold ? xor32_max(mt) + mu_old : xor32_max(mt) * c2;
+    // the lane's max of the tile's raw scores.
+    auto rescale = [&](float mt) __attribute__((always_inline)) {
+        mt = xor32_max(mt) * c2;
         if (__any(mt > m_run + 8.0f)) {
             const float m_new = fmaxf(m_run, mt);
             const float mu = (m_new == -INFINITY) ? 0.0f : m_new;
@@ -378,15 +357,6 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a, const 
 #pragma unroll
                 for (int r = 0; r < 16; ++r) acc_o[db][r] *= alpha;
             m_run = m_new;
-            if constexpr (kFold) {
-                const float delta = mu - mu_old;
-#pragma unroll
-                for (int h = 0; h < NH; ++h)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) s[h][r] -= delta;
-#pragma unroll
-                for (int r = 0; r < 16; ++r) negm[r] = -mu;
-            }
         }
     };
     // the row max of the raw scores (the scale is positive), then the rescale
@@ -397,14 +367,14 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a, const 
         for (int h = 0; h < NH; ++h)
 #pragma unroll
             for (int r = 0; r < 16; ++r) mt = fmaxf(mt, s[h][r]);
-        rescale(mt, s);
+        rescale(mt);
     };
-    // P = 2^s' (kFold) or 2^(c2 s' - mu), packed to bf16 in the B-operand order;
-    // l from the rounded P that the PV MFMA uses (a dot2 with (1, 1))
+    // P = 2^(c2 s - mu), packed to bf16 in the B-operand order; l from the rounded
+    // P that the PV MFMA uses (a dot2 with (1, 1))
     auto exp_pair = [&](const Scores& s, Packed& pk, int q, float nmu) __attribute__((always_inline)) {
         const int h = q / 8, r = 2 * (q % 8);
-        const float p0 = fast_exp2(kFold ? s[h][r] : fmaf(s[h][r], c2, nmu));
-        const float p1 = fast_exp2(kFold ? s[h][r + 1] : fmaf(s[h][r + 1], c2, nmu));
+        const float p0 = fast_exp2(fmaf(s[h][r], c2, nmu));
+        const float p1 = fast_exp2(fmaf(s[h][r + 1], c2, nmu));
         pk[h][r / 2] = pack_bf16_rne(p0, p1);
         l_run = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(pk[h][r / 2]), as_bf16x2(0x3F803F80u), l_run, false);
     };
@@ -442,12 +412,8 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a, const 
 #pragma unroll
             for (int h = 0; h < NH; ++h) {
                 if (kk == 0) {
-                    if constexpr (kFold) {
-                        sn[h] = mfma32(k[h], qf[0], negm);
-                    } else {
-                        const f32x16 z = {};
-                        sn[h] = mfma32(k[h], qf[0], z);
-                    }
+                    const f32x16 z = {};
+                    sn[h] = mfma32(k[h], qf[0], z);
                 } else {
                     sn[h] = mfma32(k[h], qf[kk], sn[h]);
                 }
@@ -504,7 +470,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a, const 
             }
             __builtin_amdgcn_sched_barrier(0);
         }
-        if (FUSED) rescale(mt, sn);
+        if (FUSED) rescale(mt);
     };
     // rows of a tile past the sequence end hold whatever the page slots hold: zero V
     auto zero_tail = [&](int kb, uint32_t vs) __attribute__((always_inline)) {

@@ -184,14 +184,29 @@ class PagedCase:
         return max(1, int(-(-int(self.seq_lens.max()) // self.split_keys)))
 
 
+def _scale_bf16(bits: np.ndarray, factor) -> np.ndarray:
+    """bf16 bits times a float32 factor (broadcast), rounded back to bf16."""
+    x = (bits.astype(np.uint32) << np.uint32(16)).view(np.float32)
+    return f32_to_bf16_bits((x * np.asarray(factor, np.float32)).astype(np.float32))
+
+
 def make_case(name, seed, p: AttnParams, seq_lens, q_lens, pool_pages=None,
               outlier_frac=0.0, split_keys=256, sink_seed_offset=1000, meta=None,
-              key_weight=None) -> PagedCase:
+              key_weight=None, q_scale=1.0, k_ramp=None, v_mags=None) -> PagedCase:
     """Draw K/V for every token, queries for the new tokens, and a page assignment.
 
     ``key_weight`` (float32 [D], INT8 cases): keys are drawn as N(0,1) times this
     per-channel weight (the shape a key-norm weight gives them), and the pool
-    smooths keys by it."""
+    smooths keys by it.
+
+    Value ranges beyond N(0,1) logits and values:
+    * ``q_scale``: queries times this factor (a power of two keeps them exact), so
+      the logits have standard deviation ``q_scale`` (with the 1/sqrt(D) scale);
+    * ``k_ramp``: the key at position j of a sequence of n tokens is multiplied
+      by ``k_ramp ** (j / (n - 1))``, so key norms grow along the sequence and a
+      row's maximum logit jumps as later keys arrive;
+    * ``v_mags``: each token's value vectors are multiplied by one of these
+      magnitudes, drawn uniformly per token."""
     rng = np.random.default_rng(seed)
     seq_lens = np.asarray(seq_lens, dtype=np.int32)
     q_lens = np.asarray(q_lens, dtype=np.int32)
@@ -208,6 +223,17 @@ def make_case(name, seed, p: AttnParams, seq_lens, q_lens, pool_pages=None,
     cu_q = np.zeros(len(seq_lens) + 1, dtype=np.int32)
     cu_q[1:] = np.cumsum(q_lens)
     q = normal_bf16(rng, (int(cu_q[-1]), p.num_q_heads, p.head_dim))
+    if q_scale != 1.0:
+        q = _scale_bf16(q, q_scale)
+    if k_ramp is not None:
+        f = np.empty(T, np.float32)
+        for s_, n in enumerate(seq_lens):
+            j = np.arange(int(n), dtype=np.float64)
+            f[cu_tok[s_]:cu_tok[s_ + 1]] = (float(k_ramp) ** (j / max(int(n) - 1, 1))).astype(np.float32)
+        k_tok = _scale_bf16(k_tok, f[:, None, None])
+    if v_mags is not None:
+        mags = np.asarray(v_mags, np.float32)[rng.integers(0, len(v_mags), size=T)]
+        v_tok = _scale_bf16(v_tok, mags[:, None, None])
     return PagedCase(name=name, p=p, seq_lens=seq_lens, q_lens=q_lens, cu_q=cu_q,
                      cu_tok=cu_tok, block_table=bt, num_pages=num_pages, spare_page=spare,
                      k_tok=k_tok, v_tok=v_tok, q=q, split_keys=split_keys, meta=meta or {},
