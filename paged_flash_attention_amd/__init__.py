@@ -177,8 +177,57 @@ def _dev(t: Optional[torch.Tensor], dtype, name: str):
     return t
 
 
+def _expect(t: Optional[torch.Tensor], shape, dtype, name: str, optional: bool = False):
+    """Check a tensor's dtype and shape (None in ``shape`` matches any size).  The
+    device and contiguity checks follow when its pointer is taken (``_ptr``); both
+    raise before anything is launched."""
+    if t is None:
+        if optional:
+            return None
+        raise ValueError(f"{name} is required")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.dim() != len(shape) or any(w is not None and int(n) != int(w) for n, w in zip(t.shape, shape)):
+        want = "(" + ", ".join("*" if w is None else str(int(w)) for w in shape) + ")"
+        raise ValueError(f"{name} must have shape {want}, got {tuple(t.shape)}")
+    return t
+
+
+def _check_pool(desc: "AttnDesc", pool: "KVPool"):
+    """The pool's tensors against the descriptor: dtype of kv_dtype, shape
+    [num_pages, Hkv, P, D] (3-bit codes: 3D/8 bytes), scales [num_pages, Hkv, P]."""
+    want = {"bf16": torch.bfloat16, "int8": torch.int8, "tq3": torch.uint8}.get(desc.kv_dtype)
+    if want is None:
+        raise ValueError(f"unknown kv_dtype {desc.kv_dtype!r}")
+    last = 3 * desc.head_dim // 8 if desc.kv_dtype == "tq3" else desc.head_dim
+    shape = (None, desc.num_kv_heads, desc.page_size, last)
+    _expect(pool.k, shape, want, "k_pool")
+    _expect(pool.v, tuple(pool.k.shape), want, "v_pool")
+    if desc.kv_dtype != "bf16":
+        sshape = tuple(pool.k.shape[:3])
+        _expect(pool.k_scale, sshape, torch.float32, "k_scale")
+        _expect(pool.v_scale, sshape, torch.float32, "v_scale")
+    if pool.k_smooth is not None:
+        if desc.kv_dtype != "int8":
+            raise ValueError("k_smooth is an INT8 pool option")
+        _expect(pool.k_smooth, (desc.head_dim,), torch.float32, "k_smooth")
+
+
+def _check_table(block_table, seq_lens, name="seq_lens"):
+    _expect(block_table, (None, None), torch.int32, "block_table")
+    batch = int(block_table.shape[0])
+    _expect(seq_lens, (batch,), torch.int32, name)
+    return batch
+
+
 def _ptr(t: Optional[torch.Tensor]):
-    return None if t is None else t.data_ptr()
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError(f"a {tuple(t.shape)} {t.dtype} argument must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"a {tuple(t.shape)} {t.dtype} argument must be contiguous")
+    return t.data_ptr()
 
 
 def _stream(stream, ref: torch.Tensor):
@@ -193,11 +242,11 @@ def _stream(stream, ref: torch.Tensor):
 
 def kv_write(desc: AttnDesc, pool: KVPool, k_new, v_new, cu_new, seq_lens, block_table, stream=None):
     """Append k_new/v_new [T, Hkv, D] bf16 to their sequences' pages (pfa_kv_write)."""
-    for t, n in ((k_new, "k_new"), (v_new, "v_new")):
-        _dev(t, torch.bfloat16, n)
-    for t, n in ((cu_new, "cu_new"), (seq_lens, "seq_lens"), (block_table, "block_table")):
-        _dev(t, torch.int32, n)
-    batch = int(seq_lens.numel())
+    _check_pool(desc, pool)
+    batch = _check_table(block_table, seq_lens)
+    _expect(k_new, (None, desc.num_kv_heads, desc.head_dim), torch.bfloat16, "k_new")
+    _expect(v_new, tuple(k_new.shape), torch.bfloat16, "v_new")
+    _expect(cu_new, (batch + 1,), torch.int32, "cu_new")
     st = lib().pfa_kv_write(ctypes.byref(desc.c()), ctypes.byref(pool.c()), _ptr(k_new), _ptr(v_new),
                             _ptr(cu_new), _ptr(seq_lens), _ptr(block_table), int(block_table.shape[1]),
                             batch, int(k_new.shape[0]), _stream(stream, k_new))
@@ -208,13 +257,15 @@ def attn_input(desc: AttnDesc, pool: KVPool, q_norm_weight, k_norm_weight, rope_
                qkv, cu_new, seq_lens, block_table, q_out, stream=None):
     """Fused q/k RMSNorm + RoPE + KV write from qkv [T, (Hq + 2 Hkv) * D] bf16.
     rope_cos_sin [max_pos, D/2, 2] fp32; writes q_out [T, Hq, D] bf16 and the pool."""
-    _dev(qkv, torch.bfloat16, "qkv")
-    _dev(q_norm_weight, torch.bfloat16, "q_norm_weight")
-    _dev(k_norm_weight, torch.bfloat16, "k_norm_weight")
-    _dev(rope_cos_sin, torch.float32, "rope_cos_sin")
-    _dev(q_out, torch.bfloat16, "q_out")
-    for t, n in ((cu_new, "cu_new"), (seq_lens, "seq_lens"), (block_table, "block_table")):
-        _dev(t, torch.int32, n)
+    D = desc.head_dim
+    _check_pool(desc, pool)
+    batch = _check_table(block_table, seq_lens)
+    _expect(qkv, (None, (desc.num_q_heads + 2 * desc.num_kv_heads) * D), torch.bfloat16, "qkv")
+    _expect(q_norm_weight, (D,), torch.bfloat16, "q_norm_weight")
+    _expect(k_norm_weight, (D,), torch.bfloat16, "k_norm_weight")
+    _expect(rope_cos_sin, (None, D // 2, 2), torch.float32, "rope_cos_sin")
+    _expect(q_out, (qkv.shape[0], desc.num_q_heads, D), torch.bfloat16, "q_out")
+    _expect(cu_new, (batch + 1,), torch.int32, "cu_new")
     prm = CAttnInputParams(_ptr(q_norm_weight), _ptr(k_norm_weight), _ptr(rope_cos_sin),
                            int(rope_cos_sin.shape[0]), float(eps))
     st = lib().pfa_attn_input(ctypes.byref(desc.c()), ctypes.byref(pool.c()), ctypes.byref(prm), _ptr(qkv),
@@ -231,6 +282,18 @@ def tq3_codebook():
     return list(m), list(t)
 
 
+def _check_decode(desc, pool, q, block_table, seq_lens, max_splits, o_part, lse_part, out,
+                  need_out: bool, need_parts: bool) -> int:
+    Hq, D = desc.num_q_heads, desc.head_dim
+    _check_pool(desc, pool)
+    batch = _check_table(block_table, seq_lens)
+    _expect(q, (batch, Hq, D), torch.bfloat16, "q")
+    _expect(o_part, (batch, Hq, max_splits, D), torch.float32, "o_part", optional=not need_parts)
+    _expect(lse_part, (batch, Hq, max_splits), torch.float32, "lse_part", optional=not need_parts)
+    _expect(out, (batch, Hq, D), torch.float32, "out", optional=not need_out)
+    return batch
+
+
 def decode_num_splits(max_seq_len: int, split_keys: int) -> int:
     return int(lib().pfa_decode_num_splits(int(max_seq_len), int(split_keys)))
 
@@ -239,12 +302,8 @@ def paged_attn_decode(desc: AttnDesc, pool: KVPool, q, block_table, seq_lens, ma
                       split_keys: int, max_splits: int, o_part=None, lse_part=None, out=None,
                       stream=None):
     """Split-KV decode partials, or the final output when max_splits == 1."""
-    _dev(q, torch.bfloat16, "q")
-    _dev(block_table, torch.int32, "block_table")
-    _dev(seq_lens, torch.int32, "seq_lens")
-    _dev(o_part, torch.float32, "o_part")
-    _dev(lse_part, torch.float32, "lse_part")
-    _dev(out, torch.float32, "out")
+    _check_decode(desc, pool, q, block_table, seq_lens, max_splits, o_part, lse_part, out,
+                  need_out=max_splits == 1, need_parts=max_splits > 1)
     st = lib().pfa_paged_attn_decode(ctypes.byref(desc.c()), ctypes.byref(pool.c()), _ptr(q),
                                      _ptr(block_table), int(block_table.shape[1]), _ptr(seq_lens),
                                      int(q.shape[0]), int(max_seq_len), int(split_keys), int(max_splits),
@@ -257,13 +316,9 @@ def paged_attn_decode_fused(desc: AttnDesc, pool: KVPool, q, block_table, seq_le
     """Split-KV decode with the combine fused in: out [B, Hq, D] fp32 is written by
     the last split of each (sequence, KV head).  counters [B * Hkv] int32 must be
     zero and are left zero."""
-    _dev(q, torch.bfloat16, "q")
-    _dev(block_table, torch.int32, "block_table")
-    _dev(seq_lens, torch.int32, "seq_lens")
-    _dev(o_part, torch.float32, "o_part")
-    _dev(lse_part, torch.float32, "lse_part")
-    _dev(counters, torch.int32, "counters")
-    _dev(out, torch.float32, "out")
+    batch = _check_decode(desc, pool, q, block_table, seq_lens, max_splits, o_part, lse_part, out,
+                          need_out=True, need_parts=max_splits > 1)
+    _expect(counters, (batch * desc.num_kv_heads,), torch.int32, "counters", optional=max_splits == 1)
     st = lib().pfa_paged_attn_decode_fused(ctypes.byref(desc.c()), ctypes.byref(pool.c()), _ptr(q),
                                            _ptr(block_table), int(block_table.shape[1]), _ptr(seq_lens),
                                            int(q.shape[0]), int(max_seq_len), int(split_keys), int(max_splits),
@@ -275,14 +330,28 @@ def paged_attn_decode_fused(desc: AttnDesc, pool: KVPool, q, block_table, seq_le
 def paged_attn_combine(desc: AttnDesc, o_part, lse_part, seq_lens, split_keys: int, max_splits: int,
                        out, stream=None):
     """Merge split partials into out [B, Hq, D] fp32."""
-    _dev(o_part, torch.float32, "o_part")
-    _dev(lse_part, torch.float32, "lse_part")
-    _dev(seq_lens, torch.int32, "seq_lens")
-    _dev(out, torch.float32, "out")
+    Hq, D = desc.num_q_heads, desc.head_dim
+    _expect(seq_lens, (None,), torch.int32, "seq_lens")
+    batch = int(seq_lens.shape[0])
+    _expect(o_part, (batch, Hq, max_splits, D), torch.float32, "o_part")
+    _expect(lse_part, (batch, Hq, max_splits), torch.float32, "lse_part")
+    _expect(out, (batch, Hq, D), torch.float32, "out")
     st = lib().pfa_paged_attn_combine(ctypes.byref(desc.c()), _ptr(o_part), _ptr(lse_part),
                                       _ptr(seq_lens), int(seq_lens.numel()), int(split_keys),
                                       int(max_splits), _ptr(out), _stream(stream, out))
     _check("pfa_paged_attn_combine", st)
+
+
+def _check_chunk(desc, pool, q, cu_q, block_table, seq_lens, out, max_splits, o_part, lse_part):
+    Hq, D = desc.num_q_heads, desc.head_dim
+    _check_pool(desc, pool)
+    batch = _check_table(block_table, seq_lens)
+    _expect(cu_q, (batch + 1,), torch.int32, "cu_q")
+    _expect(q, (None, Hq, D), torch.bfloat16, "q")
+    T = int(q.shape[0])
+    _expect(out, (T, Hq, D), torch.float32, "out")
+    _expect(o_part, (T, Hq, max_splits, D), torch.float32, "o_part", optional=max_splits == 1)
+    _expect(lse_part, (T, Hq, max_splits), torch.float32, "lse_part", optional=max_splits == 1)
 
 
 def prefill_num_splits(desc: AttnDesc, batch: int, max_q_len: int, max_seq_len: int, num_cus: int = 256):
@@ -299,13 +368,7 @@ def paged_attn_prefill(desc: AttnDesc, pool: KVPool, q, cu_q, block_table, seq_l
     """Causal prefill of the new tokens q [Tq, Hq, D] bf16 into out [Tq, Hq, D] fp32.
     With max_splits > 1 the key range is split (o_part [Tq, Hq, max_splits, D] and
     lse_part [Tq, Hq, max_splits] fp32 are the caller's workspace)."""
-    _dev(q, torch.bfloat16, "q")
-    _dev(cu_q, torch.int32, "cu_q")
-    _dev(block_table, torch.int32, "block_table")
-    _dev(seq_lens, torch.int32, "seq_lens")
-    _dev(out, torch.float32, "out")
-    _dev(o_part, torch.float32, "o_part")
-    _dev(lse_part, torch.float32, "lse_part")
+    _check_chunk(desc, pool, q, cu_q, block_table, seq_lens, out, max_splits, o_part, lse_part)
     if max_seq_len is None:
         max_seq_len = int(block_table.shape[1]) * desc.page_size
     st = lib().pfa_paged_attn_prefill(ctypes.byref(desc.c()), ctypes.byref(pool.c()), _ptr(q),
@@ -329,13 +392,7 @@ def paged_attn_verify(desc: AttnDesc, pool: KVPool, q, cu_q, block_table, seq_le
                       o_part=None, lse_part=None, stream=None):
     """Verify step: 2-16 new tokens per sequence, q [Tq, Hq, D] bf16 -> out [Tq, Hq, D]
     fp32, the same result as paged_attn_prefill for that chunk (see pfa.h)."""
-    _dev(q, torch.bfloat16, "q")
-    _dev(cu_q, torch.int32, "cu_q")
-    _dev(block_table, torch.int32, "block_table")
-    _dev(seq_lens, torch.int32, "seq_lens")
-    _dev(out, torch.float32, "out")
-    _dev(o_part, torch.float32, "o_part")
-    _dev(lse_part, torch.float32, "lse_part")
+    _check_chunk(desc, pool, q, cu_q, block_table, seq_lens, out, max_splits, o_part, lse_part)
     if max_seq_len is None:
         max_seq_len = int(block_table.shape[1]) * desc.page_size
     st = lib().pfa_paged_attn_verify(ctypes.byref(desc.c()), ctypes.byref(pool.c()), _ptr(q),
