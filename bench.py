@@ -318,8 +318,10 @@ def run_attn_input(ic, torch, pfa, gs, steps, warmup):
 
 def run_prefill(case, torch, pfa, gs, steps, warmup, verify=False):
     """Prefill steps (kv_write + prefill), or with verify=True verify steps (kv_write
-    + pfa_paged_attn_verify), on the library's split choice."""
-    g, pools, (kn, vn, cun) = setup_case(case, torch, pfa, gs, copies_for_bytes=0)
+    + pfa_paged_attn_verify), on the library's split choice.  Steps rotate over pool
+    copies (about 2 GiB in all, at most 16), so a short chunk on a long prefix reads
+    its prefix from HBM rather than from the 256 MB MALL."""
+    g, pools, (kn, vn, cun) = setup_case(case, torch, pfa, gs)
     p = case.p
     Tq = int(case.cu_q[-1])
     out = torch.empty((Tq, p.num_q_heads, p.head_dim), device="cuda")
@@ -333,9 +335,10 @@ def run_prefill(case, torch, pfa, gs, steps, warmup, verify=False):
     tm = Timer(torch)
 
     def step(i):
-        pfa.kv_write(g.desc, g.pool, kn, vn, cun, g.seq_lens, g.bt)
+        pool = pools[i % len(pools)]
+        pfa.kv_write(g.desc, pool, kn, vn, cun, g.seq_lens, g.bt)
         e = tm.mark("prefill")
-        attn(g.desc, g.pool, g.q, g.cu_q, g.bt, g.seq_lens, max_q, out, max_seq_len=max_len,
+        attn(g.desc, pool, g.q, g.cu_q, g.bt, g.seq_lens, max_q, out, max_seq_len=max_len,
              split_keys=sk, max_splits=ms, o_part=op, lse_part=lp)
         tm.close("prefill", e)
 
@@ -347,11 +350,12 @@ def run_prefill(case, torch, pfa, gs, steps, warmup, verify=False):
     t1 = torch.cuda.Event(enable_timing=True)
     t0.record()
     for i in range(steps):
-        step(i)
+        step(warmup + i)
     t1.record()
     torch.cuda.synchronize()
     return dict(step_ms=t0.elapsed_time(t1) / steps, prefill_ms=tm.mean_ms("prefill"),
-                flops=prefill_flops(case), split_keys=sk, max_splits=ms, kv_bytes=verify_bytes(case))
+                flops=prefill_flops(case), split_keys=sk, max_splits=ms, kv_bytes=verify_bytes(case),
+                pool_copies=len(pools))
 
 
 def run_verify_graph(case, torch, pfa, gs, steps, warmup):
@@ -400,6 +404,17 @@ def run_verify_graph(case, torch, pfa, gs, steps, warmup):
 # CPU baseline: the oracle as it stands
 # ---------------------------------------------------------------------------
 
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline_decode(case, min_s=10.0, budget_s=25.0):
     import oracle as O
     try:
@@ -444,6 +459,7 @@ def cpu_baseline_decode(case, min_s=10.0, budget_s=25.0):
             break
     elapsed = time.perf_counter() - t_start
     return dict(value=round(nbytes / elapsed / 1e9, 4), unit="GB/s", cores=int(cores), kind="oracle",
+                cpu_count=os.cpu_count(), affinity=len(os.sched_getaffinity(0)), cpu_model=cpu_model(),
                 sample=f"{seqs} sequence-steps ({passes} pass(es) over the {case.batch} sequences of the same "
                        f"batch; kv_write of the new token + materialised-softmax decode, float64 numpy), "
                        f"{elapsed:.1f} s")
@@ -471,8 +487,7 @@ def main():
     import torch
     import paged_flash_attention_amd as pfa
     import workloads as W
-    sys.path.insert(0, os.path.join(ROOT, "tests"))
-    import gpu_support as gs
+    import workloads.device as gs
 
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
@@ -595,13 +610,13 @@ def main():
 
     extra = {}
     if not args.no_extra and args.workload == "decode_batch32_ctx512_8192":
-        for name, st in (("decode_batch32_ctx512_8192_fused", 50),
+        for name, st in (("decode_1seq_ctx1024", 100), ("decode_batch32_ctx512_8192_fused", 50),
                          ("decode_batch32_ctx8192", 30), ("decode_batch32_ctx8192_s1024", 30),
                          ("decode_int8_batch8_ctx32768", 30), ("decode_int8_batch8_ctx32768_smooth", 30),
                          ("decode_tq3_batch8_ctx32768", 30),
                          ("kv_write_bf16_8192", 40), ("kv_write_int8_8192", 40), ("kv_write_tq3_8192", 40),
                          ("mixed_full_decode_b64", 30), ("mixed_window_decode_b64", 50),
-                         ("prefill_causal_8192", 30),
+                         ("prefill_causal_8192", 30), ("prefill_causal_1024", 50),
                          ("prefill_chunk130_on_8192", 20), ("mixed_full_prefill_2x2048", 20),
                          ("mixed_window_prefill_2x2048", 30),
                          ("verify_16tok_batch1_ctx1024", 50), ("verify_16tok_batch1_ctx1024_graph", 200),
