@@ -67,9 +67,9 @@ typedef enum {
 
 /*
  * KV cache element formats.
- *   PFA_KV_TQ3: the 3-bit rotated cache the qengine README lists (feature list:
- *   "3-bit KV cache: Walsh-Hadamard rotation + Lloyd-Max scalar quant").  Each
- *   cached K or V vector x of D elements is stored as:
+ *   PFA_KV_TQ3: the 3-bit rotated cache of the qengine README's feature list (a
+ *   Walsh-Hadamard rotation followed by an 8-level Lloyd-Max scalar quantiser).
+ *   Each cached K or V vector x of D elements is stored as:
  *     y = H_D x          (Walsh-Hadamard, Sylvester order, unnormalised)
  *     s = sqrt(sum(y^2) / D)                        (fp32 scale, one per vector)
  *     t = y / s  (t = 0 when s = 0), coded by the symmetric 8-level Lloyd-Max
@@ -102,10 +102,11 @@ typedef struct {
 /* The page pool.
  *   k_smooth (INT8 only, optional): the key smoothing of the TileInfer.jl
  *   performance page ("INT8 KV cache": keys smoothed by the key norm's weight).
- *   A device [D] fp32 vector s, every s_d > 0 (e.g. |k_norm weight|).  The KV
- *   writes quantise k/s (IEEE fp32 divide) per vector; decode meets q*s (rounded
- *   to bf16), so q.k is unchanged in exact arithmetic.  The cache then
- *   dequantises to code * scale * s.  NULL: no smoothing.  A BF16 pool with
+ *   A device [D] fp32 vector w, every w_d a positive normal float (e.g. |k_norm
+ *   weight|).  The cache smooths channel d by s_d, the largest power of two not
+ *   above w_d (w_d with its mantissa bits cleared).  The KV writes quantise k/s
+ *   per vector and decode meets q*s; both are exact, so q.k is unchanged.  The
+ *   cache dequantises to code * scale * s.  NULL: no smoothing.  A BF16 pool with
  *   k_smooth set is PFA_ERR_UNSUPPORTED. */
 typedef struct {
     void* k_pool;              /* device [num_pages][Hkv][P][D], bf16 or int8;        */
@@ -234,10 +235,10 @@ pfa_status pfa_paged_attn_decode(const pfa_attn_desc* desc, const pfa_kv_pool* p
 
 /*
  * pfa_paged_attn_decode_fused: decode with the combine fused into the split
- *   kernel, through an acquire-release counter per (sequence, KV head): the
- *   variant the TileInfer.jl performance page ("Fused kernels, FlashAttention and
- *   PagedAttention") measured and did not keep.  Arguments as
- *   pfa_paged_attn_decode, plus:
+ *   kernel, through an arrival counter per (sequence, KV head): the variant the
+ *   TileInfer.jl performance page ("Fused kernels, FlashAttention and
+ *   PagedAttention") measured, with an acquire-release counter, and did not keep.
+ *   Arguments as pfa_paged_attn_decode, plus:
  *
  *   counters       device [batch][Hkv] int32, all zero on entry.  The call leaves
  *                  them zero when it completes, so one zeroed array serves every
@@ -246,9 +247,13 @@ pfa_status pfa_paged_attn_decode(const pfa_attn_desc* desc, const pfa_kv_pool* p
  *   out            device [batch][Hq][D] fp32, always written.
  *
  *   Each split writes its partial to o_part / lse_part as in pfa_paged_attn_decode,
- *   then adds one to its counter after an agent-scope release; the split that
- *   brings the counter to ceil(seq_lens[s]/S) merges the row's partials with
- *   the combine formula (acquire first), writes out, and resets the counter.  No
+ *   with agent-scope atomic stores (written through to the device-coherent level),
+ *   waits until those stores have completed, then adds one to its counter with an
+ *   agent-scope atomic.  The split that brings the counter to ceil(seq_lens[s]/S)
+ *   reads the row's partials back with agent-scope atomic loads, merges them with
+ *   the combine formula, writes out, and resets the counter.  The ordering rests on
+ *   the completed stores and the coherent loads rather than on release/acquire
+ *   fences (which would write back or invalidate a whole L2 per workgroup).  No
  *   workgroup waits on another.  out equals, bit for bit, that of
  *   pfa_paged_attn_decode followed by pfa_paged_attn_combine.  seq_lens[s] >= 1.
  *   With max_splits == 1 this is pfa_paged_attn_decode (counters unused).
@@ -350,6 +355,16 @@ int32_t pfa_verify_num_splits(const pfa_attn_desc* desc, int32_t batch, int32_t 
 
 /* ceil(max_seq_len / split_keys), at least 1 (0 when split_keys <= 0). */
 int32_t pfa_decode_num_splits(int32_t max_seq_len, int32_t split_keys);
+
+/*
+ * Bytes of the split buffers pfa_paged_attn_decode needs for `batch` sequences
+ * and `max_splits` splits: o_part [batch][Hq][max_splits][D] fp32 plus lse_part
+ * [batch][Hq][max_splits] fp32, i.e. batch*Hq*max_splits*(D+1)*4.  0 when
+ * max_splits <= 1 (unsplit decode writes out directly), batch <= 0, or desc is
+ * NULL or invalid.  The caller allocates them as two arrays.  Host-side
+ * arithmetic only.
+ */
+size_t pfa_decode_workspace_bytes(const pfa_attn_desc* desc, int32_t batch, int32_t max_splits);
 
 /* Static description of a status code; never NULL. */
 const char* pfa_status_string(pfa_status status);

@@ -27,6 +27,7 @@ KV_DTYPES = {"bf16": 0, "int8": 1, "tq3": 2}
 # every symbol include/pfa.h declares
 EXPORTS = ("pfa_kv_write", "pfa_attn_input", "pfa_paged_attn_decode", "pfa_paged_attn_decode_fused", "pfa_paged_attn_combine",
            "pfa_paged_attn_prefill", "pfa_paged_attn_verify", "pfa_decode_num_splits",
+           "pfa_decode_workspace_bytes",
            "pfa_prefill_num_splits", "pfa_verify_num_splits", "pfa_tq3_codebook", "pfa_status_string",
            "pfa_last_hip_error")
 
@@ -86,6 +87,8 @@ def lib() -> ctypes.CDLL:
         fn.restype = ctypes.c_int
     L.pfa_decode_num_splits.argtypes = [I, I]
     L.pfa_decode_num_splits.restype = ctypes.c_int32
+    L.pfa_decode_workspace_bytes.argtypes = [D, I, I]
+    L.pfa_decode_workspace_bytes.restype = ctypes.c_size_t
     L.pfa_prefill_num_splits.argtypes = [D, I, I, I, I, ctypes.POINTER(ctypes.c_int32)]
     L.pfa_prefill_num_splits.restype = ctypes.c_int32
     L.pfa_verify_num_splits.argtypes = [D, I, I, I, I, ctypes.POINTER(ctypes.c_int32)]
@@ -282,6 +285,11 @@ def tq3_codebook():
     return list(m), list(t)
 
 
+def decode_workspace_bytes(desc: AttnDesc, batch: int, max_splits: int) -> int:
+    """Bytes of o_part + lse_part for a split decode (0 when unsplit)."""
+    return int(lib().pfa_decode_workspace_bytes(ctypes.byref(desc.c()), int(batch), int(max_splits)))
+
+
 def _check_decode(desc, pool, q, block_table, seq_lens, max_splits, o_part, lse_part, out,
                   need_out: bool, need_parts: bool) -> int:
     Hq, D = desc.num_q_heads, desc.head_dim
@@ -404,6 +412,7 @@ def paged_attn_verify(desc: AttnDesc, pool: KVPool, q, cu_q, block_table, seq_le
 
 
 __all__ = ["AttnDesc", "KVPool", "PfaError", "EXPORTS", "lib", "kv_write", "attn_input", "decode_num_splits",
+           "decode_workspace_bytes",
            "tq3_codebook",
            "prefill_num_splits", "verify_num_splits", "paged_attn_decode", "paged_attn_decode_fused",
            "paged_attn_combine",

@@ -45,7 +45,7 @@ bool prefill_group_ok(int g) {
 }
 
 // The 3-bit rotated cache's codebook: the symmetric 8-level Lloyd-Max quantiser
-// of N(0, 1) (qengine README, feature list: "Lloyd-Max scalar quant").  Lloyd's
+// of N(0, 1) (the qengine README's feature list names a Lloyd-Max quantiser).  Lloyd's
 // iteration on the positive half in double precision: thresholds at midpoints of
 // adjacent levels (the first at 0), levels at the centroids of their cells,
 // E[X | a < X < b] = (phi(a) - phi(b)) / (Phi(b) - Phi(a)), from 0.25, 0.75, 1.25,
@@ -173,6 +173,12 @@ int32_t pfa_decode_num_splits(int32_t max_seq_len, int32_t split_keys) {
     if (split_keys <= 0) return 0;
     if (max_seq_len <= 0) return 1;
     return (int32_t)(((int64_t)max_seq_len + split_keys - 1) / split_keys);
+}
+
+size_t pfa_decode_workspace_bytes(const pfa_attn_desc* desc, int32_t batch, int32_t max_splits) {
+    if (check_desc(desc) != PFA_OK || batch <= 0 || max_splits <= 1) return 0;
+    return (size_t)batch * (size_t)desc->num_q_heads * (size_t)max_splits * ((size_t)desc->head_dim + 1) *
+           sizeof(float);
 }
 
 namespace {

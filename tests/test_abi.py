@@ -45,6 +45,17 @@ def test_status_strings_and_splits():
     assert L.pfa_last_hip_error() == 0
 
 
+def test_decode_workspace_bytes():
+    L = pfa.lib()
+    d = desc()
+    assert L.pfa_decode_workspace_bytes(ctypes.byref(d), 32, 33) == 32 * 32 * 33 * 129 * 4
+    assert L.pfa_decode_workspace_bytes(ctypes.byref(d), 32, 1) == 0        # unsplit: no buffers
+    assert L.pfa_decode_workspace_bytes(ctypes.byref(d), 0, 33) == 0
+    assert L.pfa_decode_workspace_bytes(None, 32, 33) == 0
+    assert L.pfa_decode_workspace_bytes(ctypes.byref(desc(head_dim=96)), 32, 33) == 0
+    assert pfa.decode_workspace_bytes(pfa.AttnDesc(64, 8, 64), 64, 128) == 64 * 64 * 128 * 65 * 4
+
+
 def desc(**kw):
     d = dict(num_q_heads=32, num_kv_heads=8, head_dim=128, page_size=16, kv_dtype=0, window=0,
              sm_scale=0.088, sinks=None)
