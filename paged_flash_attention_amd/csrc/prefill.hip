@@ -19,8 +19,9 @@
 //  * The loop is software-pipelined within each wave, so that the matrix cores
 //    and the VALU work at the same time (on gfx950 each MFMA issue also takes
 //    VALU issue cycles, so the VALU work is spread evenly): the QK^T MFMAs of
-//    tile j+1 are interleaved with three quarters of the exps of tile j, and the
-//    PV MFMAs of tile j with the last quarter and the row max of tile j+1.
+//    tile j+1 are interleaved with the exps of tile j (64-key build; the 32-key
+//    build puts three quarters of them there), and the PV MFMAs of tile j with
+//    the rest and the row max of tile j+1.
 //    Scheduling fences bound how far the compiler hoists LDS reads (registers);
 //    K fragments are read two D-slices ahead, and the per-lane LDS offsets are
 //    computed once, so a read costs one add of the stage base.
@@ -78,7 +79,7 @@ constexpr int kWaves = PFA_PREFILL_ROWS_WG / kRowsPerWave;
 constexpr int kThreads = kWaves * kWave;
 constexpr int kBN = PFA_PREFILL_BN;   // keys per tile
 constexpr int kStages = 5;        // LDS ring depth: tiles kb-1 .. kb+3 around tile kb
-constexpr int kPairs1 = kBN == 64 ? 12 : 6;   // of a tile's 8*kBN/32 score pairs per lane,
+constexpr int kPairs1 = kBN == 64 ? 16 : 6;   // of a tile's 8*kBN/32 score pairs per lane,
                                   // those whose exps run beside the QK^T MFMAs (the rest beside PV)
 constexpr int kXcds = 8;
 
