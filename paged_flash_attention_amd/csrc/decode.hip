@@ -23,18 +23,18 @@
 //  * Page-head block = 16 keys x D.  A lane loads 8 consecutive elements of one key
 //    per load (16 B for bf16, 8 B for int8).  LPK = D/8 lanes cover a key, and one
 //    load instruction covers a contiguous 512*elem-byte run.  The wave's next page
-//    is prefetched while the current one is consumed; two pages in flight (the
-//    loop unrolled over two register buffers) measured no faster, as the
-//    device's HBM is already saturated with one per wave.
+//    is prefetched while the current one is consumed; two or three pages in
+//    flight (a ring of register sets) measured no faster.  For INT8 and for G = 8
+//    the page ids are scalar loads issued a page ahead (see kScalarIds).
 //  * q.k: v_dot2_f32_bf16 on (q, k) bf16 pairs.  INT8 codes are offset to the
 //    unsigned byte c+128 (v_cvt_f32_ubyteN, exact in bf16), and 128*sum(q) is
 //    subtracted from the dot.  With key smoothing (keys stored as k/s per
 //    channel, the "INT8 KV cache" section's smoothing by the key norm's weight,
 //    s taken as a power of two), q is first scaled by s, which is exact in bf16.
-//    A lane's partial dots for the G heads go through a transposed butterfly over the LPK lanes (DPP / swizzle moves).  Slot j of a
-//    lane holds head (j ^ myhead), so each stage adds a partner's upper half to its
-//    own lower half with no selects, and ends with the lane holding its own head's
-//    full score.
+//    A lane's partial dots for the G heads go through a transposed butterfly over
+//    the LPK lanes, on DPP moves only (group_reduce.h).  Slot j of a lane holds
+//    head (j ^ myhead), so each stage adds a partner's slots to its own lower half
+//    with no selects, and ends with the lane holding its own head's full score.
 //  * The softmax max is taken per page and the rescale is lazy: o and l are
 //    rescaled only when some head's running max grows.  The weights p are shared
 //    within the wave through LDS.
@@ -123,9 +123,20 @@ __device__ __forceinline__ void v_pairs(const uint2& a, const uint2& b, uint32_t
 // Splits whose merge weights sit in LDS at a time, in the fused merge.
 constexpr int kFusedMergeChunk = 256;
 
+// Page ids.  The block table also comes in as a __restrict__ argument of its own:
+// reads of it with a wave-uniform index then become scalar loads, counted apart
+// from the K/V loads, and each is issued a page ahead of its use.  As a vector
+// load issued just before the page's K/V loads, a page id waits for every load in
+// flight.  Measured on one MI355X (us per launch, vector -> scalar ids): INT8 at
+// G = 8 (batch 8 x 32768) 102 -> 93, BF16 at G = 8 (gpt-oss full layer) 201 ->
+// 192, but BF16 at G = 4 on the ragged batch 131 -> 136; so BF16 at G <= 4 keeps
+// the vector form.
+template <int G, bool INT8>
+constexpr bool kScalarIds = INT8 || G >= 8;
+
 template <int D, int G, bool INT8, bool FINAL>
 __global__ __launch_bounds__(kWave)
-void decode_kernel(DecodeArgs a) {
+void decode_kernel(DecodeArgs a, const int32_t* __restrict__ block_table) {
     constexpr int EB = INT8 ? 1 : 2;           // bytes per element
     constexpr int LPK = D / 8;                 // lanes per key
     constexpr int KPL = kWave / LPK;           // keys per load instruction
@@ -250,30 +261,36 @@ void decode_kernel(DecodeArgs a) {
     const float c2 = a.sm_scale * kLog2e;      // scores kept in log2 units
 
     const int p0 = lo / kPage, p1 = (hi - 1) / kPage;
-    const int32_t* bt = a.block_table + (int64_t)b * a.bt_stride;
+    const int32_t* bt = block_table + (int64_t)b * a.bt_stride;
     const int64_t head_stride = (int64_t)kPage * D;              // elements per page-head block
     const char* kbase = static_cast<const char*>(a.k_pool);
     const char* vbase = static_cast<const char*>(a.v_pool);
     const int lane_off = lane * 8 * EB;
 
-    CT kc[NLOAD], vc[NLOAD];
-    float ksc[NLOAD], vsc[NLOAD];
-    auto load_page = [&](int p) {
-        int id = __ldg(bt + p);
-        id = min(max(id, 0), a.num_pages - 1);
+    // a page's K/V (and INT8 scales) as this lane loads them
+    struct PageRegs {
+        CT k[NLOAD], v[NLOAD];
+        float ks[NLOAD], vs[NLOAD];
+    };
+    // a page's block-table entry (a scalar load; the index is clamped to the
+    // split's last page so that the read stays inside the row), read one page
+    // ahead of the loads that use it
+    auto page_id = [&](int p) __attribute__((always_inline)) { return __ldg(bt + min(p, p1)); };
+    auto load_page = [&](int raw_id, PageRegs& r) __attribute__((always_inline)) {
+        const int id = min(max(raw_id, 0), a.num_pages - 1);
         const int64_t blk = (int64_t)id * Hkv + kvh;
         const char* kp = kbase + blk * head_stride * EB + lane_off;
         const char* vp = vbase + blk * head_stride * EB + lane_off;
 #pragma unroll
         for (int i = 0; i < NLOAD; ++i) {
-            kc[i] = *reinterpret_cast<const CT*>(kp + i * 512 * EB);
-            vc[i] = *reinterpret_cast<const CT*>(vp + i * 512 * EB);
+            r.k[i] = *reinterpret_cast<const CT*>(kp + i * 512 * EB);
+            r.v[i] = *reinterpret_cast<const CT*>(vp + i * 512 * EB);
         }
         if constexpr (INT8) {
 #pragma unroll
             for (int i = 0; i < NLOAD; ++i) {
-                ksc[i] = __ldg(a.k_scale + blk * kPage + i * KPL + kg);
-                vsc[i] = __ldg(a.v_scale + blk * kPage + i * KPL + kg);
+                r.ks[i] = __ldg(a.k_scale + blk * kPage + i * KPL + kg);
+                r.vs[i] = __ldg(a.v_scale + blk * kPage + i * KPL + kg);
             }
         }
     };
@@ -288,19 +305,9 @@ void decode_kernel(DecodeArgs a) {
     float w_run = 0.0f;        // INT8 paired: this lane's share of the sum of the rounded weights
 
     int pb = 0;
-    load_page(p0);
-    for (int p = p0; p <= p1; ++p) {
-        CT kcur[NLOAD], vcur[NLOAD];
-        float kscur[NLOAD], vscur[NLOAD];
-#pragma unroll
-        for (int i = 0; i < NLOAD; ++i) {
-            kcur[i] = kc[i]; vcur[i] = vc[i];
-            kscur[i] = ksc[i]; vscur[i] = vsc[i];
-        }
-        if (p < p1) load_page(p + 1);
-
+    // one page: scores, lazy rescale, weights, p.v
+    auto page = [&](int p, PageRegs& r) __attribute__((always_inline)) {
         const int kpos0 = p * kPage;
-        const bool full = kpos0 >= lo && kpos0 + kPage <= hi;
 
         // ---- scores ----
         float s[NLOAD];
@@ -308,21 +315,29 @@ void decode_kernel(DecodeArgs a) {
 #pragma unroll
         for (int i = 0; i < NLOAD; ++i) {
             uint32_t kp[4];
-            k_pairs(kcur[i], kp);
+            k_pairs(r.k[i], kp);
             float acc[G];
 #pragma unroll
             for (int j = 0; j < G; ++j) {
                 float t = 0.0f;
+                int w0 = 0;
+                if constexpr (INT8 && PAIRED) {
+                    // the chain's first product in the three-operand form with a zero
+                    // addend (the compiler otherwise zeroes a register and accumulates
+                    // in place: one more VALU op per head and key)
+                    asm("v_dot2_f32_bf16 %0, %1, %2, 0" : "=v"(t) : "v"(q[j][0]), "v"(kp[0]));
+                    w0 = 1;
+                }
 #pragma unroll
-                for (int w = 0; w < 4; ++w)
+                for (int w = w0; w < 4; ++w)
                     t = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(q[j][w]), as_bf16x2(kp[w]), t, false);
                 acc[j] = t;
             }
             float dot = transpose_reduce<LPK, G>(acc);
             if constexpr (INT8) dot -= qbias;
+            const float sc = INT8 ? c2 * r.ks[i] : c2;
             const int key = kpos0 + i * KPL + kg;
             valid[i] = key >= lo && key < hi;
-            const float sc = INT8 ? c2 * kscur[i] : c2;
             s[i] = valid[i] ? dot * sc : -INFINITY;
         }
         // ---- running max, lazy rescale ----
@@ -343,14 +358,15 @@ void decode_kernel(DecodeArgs a) {
             }
             m_run = m_new;
         }
-        // ---- weights, shared within the wave ----
+        // ---- weights, shared within the wave (masked keys weigh 0; an INT8 scale
+        // of a masked slot may be poison, so it is selected away) ----
         if constexpr (!PAIRED) {
 #pragma unroll
             for (int i = 0; i < NLOAD; ++i) {
                 const float pw = fast_exp2(s[i] - m_run);      // 0 for masked keys
                 l_run += pw;
                 float pv = pw;
-                if constexpr (INT8) pv = valid[i] ? pw * vscur[i] : 0.0f;
+                if constexpr (INT8) pv = valid[i] ? pw * r.vs[i] : 0.0f;
                 if (sub % HG == 0) p_buf[pb][i * KPL + kg][myhead] = pv;
             }
         } else {
@@ -362,7 +378,7 @@ void decode_kernel(DecodeArgs a) {
                 uint32_t pr;
                 if constexpr (INT8) {
                     l_run += p0 + p1;
-                    pr = pack_bf16_rne(valid[i] ? p0 * vscur[i] : 0.0f, valid[i + 1] ? p1 * vscur[i + 1] : 0.0f);
+                    pr = pack_bf16_rne(valid[i] ? p0 * r.vs[i] : 0.0f, valid[i + 1] ? p1 * r.vs[i + 1] : 0.0f);
                     w_run = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(pr), as_bf16x2(0x3F803F80u), w_run, false);
                 } else {
                     pr = pack_bf16_rne(p0, p1);
@@ -375,11 +391,16 @@ void decode_kernel(DecodeArgs a) {
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
         // ---- p.v ----
+        CT vcur[NLOAD];
+#pragma unroll
+        for (int i = 0; i < NLOAD; ++i) vcur[i] = r.v[i];
         if constexpr (!INT8) {
-            if (!full) {
+            // BF16 values past the sequence end may be poison: zero them (weight 0 *
+            // NaN), on the pages that cross [lo, hi) only
+            if (!(kpos0 >= lo && kpos0 + kPage <= hi)) {
 #pragma unroll
                 for (int i = 0; i < NLOAD; ++i)
-                    if (!valid[i]) vcur[i] = CT{};          // poison past the sequence end
+                    if (!valid[i]) vcur[i] = CT{};
             }
         }
         if constexpr (!PAIRED) {
@@ -416,6 +437,28 @@ void decode_kernel(DecodeArgs a) {
             }
         }
         pb ^= 1;
+    };
+    // page p is consumed from one register set while page p+1 loads into the other
+    PageRegs rn;
+    if constexpr (kScalarIds<G, INT8>) {
+        load_page(page_id(p0), rn);
+        int nid = page_id(p0 + 1);
+        for (int p = p0; p <= p1; ++p) {
+            PageRegs rc = rn;
+            if (p < p1) {
+                load_page(nid, rn);
+                nid = page_id(p + 2);
+            }
+            page(p, rc);
+        }
+    } else {
+        const int32_t* vbt = a.block_table + (int64_t)b * a.bt_stride;
+        load_page(__ldg(vbt + p0), rn);
+        for (int p = p0; p <= p1; ++p) {
+            PageRegs rc = rn;
+            if (p < p1) load_page(__ldg(vbt + p + 1), rn);
+            page(p, rc);
+        }
     }
 
     // ---- reduce across key groups; head g's row is written by the lanes of key
@@ -464,9 +507,10 @@ template <int D, int G, bool INT8>
 hipError_t launch_dg(const DecodeArgs& a, hipStream_t s) {
     const int rows = a.num_kv_heads * a.batch;
     if (a.max_splits == 1)
-        hipLaunchKernelGGL((decode_kernel<D, G, INT8, true>), dim3(rows), dim3(kWave), 0, s, a);
+        hipLaunchKernelGGL((decode_kernel<D, G, INT8, true>), dim3(rows), dim3(kWave), 0, s, a, a.block_table);
     else
-        hipLaunchKernelGGL((decode_kernel<D, G, INT8, false>), dim3(a.max_splits * rows), dim3(kWave), 0, s, a);
+        hipLaunchKernelGGL((decode_kernel<D, G, INT8, false>), dim3(a.max_splits * rows), dim3(kWave), 0, s, a,
+                           a.block_table);
     return hipGetLastError();
 }
 

@@ -34,7 +34,10 @@ namespace pfa {
 namespace {
 
 template <int D, int G, bool FINAL>
-__global__ __launch_bounds__(kWave) void decode_tq3_kernel(DecodeArgs a, Tq3Book bk) {
+// (the block table is a __restrict__ argument of its own, so that page ids are
+// scalar loads, counted apart from the K/V loads)
+__global__ __launch_bounds__(kWave) void decode_tq3_kernel(DecodeArgs a, Tq3Book bk,
+                                                           const int32_t* __restrict__ block_table) {
     constexpr int L = D / 8;          // lanes per key
     constexpr int R = kWave / L;      // keys per step
     constexpr int NS = kPage / R;     // steps per page
@@ -111,7 +114,7 @@ __global__ __launch_bounds__(kWave) void decode_tq3_kernel(DecodeArgs a, Tq3Book
     const float c2 = a.sm_scale * kLog2e;      // scores in log2 units
 
     const int p0 = lo / kPage, p1 = (hi - 1) / kPage;
-    const int32_t* bt = a.block_table + (int64_t)b * a.bt_stride;
+    const int32_t* bt = block_table + (int64_t)b * a.bt_stride;
     const uint8_t* kpool = static_cast<const uint8_t*>(a.k_pool);
     const uint8_t* vpool = static_cast<const uint8_t*>(a.v_pool);
 
@@ -260,9 +263,10 @@ template <int D, int G>
 hipError_t launch_dg(const DecodeArgs& a, const Tq3Book& bk, hipStream_t s) {
     const int rows = a.batch * a.num_kv_heads;
     if (a.max_splits == 1)
-        hipLaunchKernelGGL((decode_tq3_kernel<D, G, true>), dim3(rows), dim3(kWave), 0, s, a, bk);
+        hipLaunchKernelGGL((decode_tq3_kernel<D, G, true>), dim3(rows), dim3(kWave), 0, s, a, bk, a.block_table);
     else
-        hipLaunchKernelGGL((decode_tq3_kernel<D, G, false>), dim3(a.max_splits * rows), dim3(kWave), 0, s, a, bk);
+        hipLaunchKernelGGL((decode_tq3_kernel<D, G, false>), dim3(a.max_splits * rows), dim3(kWave), 0, s, a, bk,
+                           a.block_table);
     return hipGetLastError();
 }
 

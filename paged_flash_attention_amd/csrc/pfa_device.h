@@ -76,10 +76,31 @@ __device__ __forceinline__ float group_bcast(float x, int src) {
         (int)(((__lane_id() & ~(W - 1)) | src) << 2), __float_as_int(x)));
 }
 
+// max / sum of x over lanes i and i ^ 16, on the VALU: v_permlane16_swap with x in
+// both operands leaves (x of row 2r, x of row 2r+1) in the two results.
+__device__ __forceinline__ float xor16_max(float x) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xor16_sum(float x) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// x + / max with x of lane (lane ^ M).  M = 16 and 32 use the permlane swaps (VALU);
+// the others a DPP or swizzle move.
 template <int M>
-__device__ __forceinline__ float xor_sum(float x) { return x + xor_lane<M>(x); }
+__device__ __forceinline__ float xor_sum(float x) {
+    if constexpr (M == 16) return xor16_sum(x);
+    else if constexpr (M == 32) return xor32_sum(x);
+    else return x + xor_lane<M>(x);
+}
 template <int M>
-__device__ __forceinline__ float xor_max(float x) { return fmaxf(x, xor_lane<M>(x)); }
+__device__ __forceinline__ float xor_max(float x) {
+    if constexpr (M == 16) return xor16_max(x);
+    else if constexpr (M == 32) return xor32_max(x);
+    else return fmaxf(x, xor_lane<M>(x));
+}
 
 // Sum / max over all lanes whose ids differ only in bits [LO, 64): lane groups
 // of stride LO.  LO is a power of two < 64.
