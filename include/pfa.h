@@ -265,6 +265,31 @@ pfa_status pfa_paged_attn_decode_fused(const pfa_attn_desc* desc, const pfa_kv_p
                                        float* lse_part, int32_t* counters, float* out, void* stream);
 
 /*
+ * pfa_paged_attn_decode_static: pfa_paged_attn_decode followed by
+ *   pfa_paged_attn_combine, allocating nothing: the split partials live in a
+ *   device array the library holds.  For callers that cannot allocate device
+ *   memory: code under HIP graph capture, tight serving loops, harnesses that
+ *   forbid hipMalloc.
+ *
+ *   Arguments as pfa_paged_attn_decode.  split_keys == 0 runs unsplit (out written
+ *   directly, the array unused); otherwise max_splits = ceil(max_seq_len /
+ *   split_keys), and o_part/lse_part take batch*Hq*max_splits*(D+1)*4 bytes (plus
+ *   alignment) of the array.  PFA_ERR_WORKSPACE, with nothing launched, when that
+ *   exceeds PFA_STATIC_SCRATCH_BYTES.  out [batch][Hq][D] fp32 is always written.
+ *
+ *   The array is per device (the current device, which must own `stream`), is
+ *   looked up on the first call on that device and lasts until the process ends.
+ *   It keeps the last call's partials; nothing in it needs to start at zero.
+ *   Calls that can overlap on one device (other streams, other threads) race on
+ *   it and must be serialised by the caller.
+ */
+#define PFA_STATIC_SCRATCH_BYTES (32u << 20)
+pfa_status pfa_paged_attn_decode_static(const pfa_attn_desc* desc, const pfa_kv_pool* pool,
+                                        const void* q, const int32_t* block_table, int32_t bt_stride,
+                                        const int32_t* seq_lens, int32_t batch, int32_t max_seq_len,
+                                        int32_t split_keys, float* out, void* stream);
+
+/*
  * pfa_paged_attn_combine: merge the split partials (same page and section as
  *   decode).  For each (b, h), over the ceil(seq_lens[b]/S) splits of b:
  *     M   = max(max_i lse_i, sink_h)

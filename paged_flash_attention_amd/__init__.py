@@ -25,7 +25,8 @@ STATUS_NAMES = {0: "PFA_OK", 1: "PFA_ERR_NULL", 2: "PFA_ERR_SHAPE", 3: "PFA_ERR_
 KV_DTYPES = {"bf16": 0, "int8": 1, "tq3": 2}
 
 # every symbol include/pfa.h declares
-EXPORTS = ("pfa_kv_write", "pfa_attn_input", "pfa_paged_attn_decode", "pfa_paged_attn_decode_fused", "pfa_paged_attn_combine",
+EXPORTS = ("pfa_kv_write", "pfa_attn_input", "pfa_paged_attn_decode", "pfa_paged_attn_decode_fused",
+           "pfa_paged_attn_decode_static", "pfa_paged_attn_combine",
            "pfa_paged_attn_prefill", "pfa_paged_attn_verify", "pfa_decode_num_splits",
            "pfa_decode_workspace_bytes",
            "pfa_prefill_num_splits", "pfa_verify_num_splits", "pfa_tq3_codebook", "pfa_status_string",
@@ -77,6 +78,7 @@ def lib() -> ctypes.CDLL:
         "pfa_attn_input": [D, PL, ctypes.POINTER(CAttnInputParams), P, P, P, P, I, I, I, P, V],
         "pfa_paged_attn_decode": [D, PL, P, P, I, P, I, I, I, I, P, P, P, V],
         "pfa_paged_attn_decode_fused": [D, PL, P, P, I, P, I, I, I, I, P, P, P, P, V],
+        "pfa_paged_attn_decode_static": [D, PL, P, P, I, P, I, I, I, P, V],
         "pfa_paged_attn_combine": [D, P, P, P, I, I, I, P, V],
         "pfa_paged_attn_prefill": [D, PL, P, P, P, I, P, I, I, I, I, I, P, P, P, V],
         "pfa_paged_attn_verify": [D, PL, P, P, P, I, P, I, I, I, I, I, P, P, P, V],
@@ -335,6 +337,21 @@ def paged_attn_decode_fused(desc: AttnDesc, pool: KVPool, q, block_table, seq_le
     _check("pfa_paged_attn_decode_fused", st)
 
 
+STATIC_SCRATCH_BYTES = 32 << 20   # PFA_STATIC_SCRATCH_BYTES
+
+
+def paged_attn_decode_static(desc: AttnDesc, pool: KVPool, q, block_table, seq_lens, max_seq_len: int,
+                             split_keys: int, out, stream=None):
+    """Decode + combine with the split partials in the library's own device array
+    (pfa_paged_attn_decode_static): nothing is allocated.  out [B, Hq, D] fp32."""
+    _check_decode(desc, pool, q, block_table, seq_lens, 1, None, None, out, need_out=True, need_parts=False)
+    st = lib().pfa_paged_attn_decode_static(ctypes.byref(desc.c()), ctypes.byref(pool.c()), _ptr(q),
+                                            _ptr(block_table), int(block_table.shape[1]), _ptr(seq_lens),
+                                            int(q.shape[0]), int(max_seq_len), int(split_keys), _ptr(out),
+                                            _stream(stream, q))
+    _check("pfa_paged_attn_decode_static", st)
+
+
 def paged_attn_combine(desc: AttnDesc, o_part, lse_part, seq_lens, split_keys: int, max_splits: int,
                        out, stream=None):
     """Merge split partials into out [B, Hq, D] fp32."""
@@ -413,7 +430,7 @@ def paged_attn_verify(desc: AttnDesc, pool: KVPool, q, cu_q, block_table, seq_le
 
 __all__ = ["AttnDesc", "KVPool", "PfaError", "EXPORTS", "lib", "kv_write", "attn_input", "decode_num_splits",
            "decode_workspace_bytes",
-           "tq3_codebook",
+           "tq3_codebook", "paged_attn_decode_static", "STATIC_SCRATCH_BYTES",
            "prefill_num_splits", "verify_num_splits", "paged_attn_decode", "paged_attn_decode_fused",
            "paged_attn_combine",
            "paged_attn_prefill", "paged_attn_verify"]

@@ -1,10 +1,12 @@
 // The C ABI of include/pfa.h: host-side argument checks, then one launch on the
-// caller's stream.  Nothing here allocates or keeps state beyond the thread-local
-// last HIP error.
+// caller's stream.  Nothing here allocates.  State: the thread-local last HIP
+// error, and for pfa_paged_attn_decode_static a file-scope device array whose
+// per-device address is looked up once.
 #include "pfa.h"
 
 #include <algorithm>
 #include <cmath>
+#include <mutex>
 
 #include "pfa_device.h"
 
@@ -79,6 +81,33 @@ const pfa::Tq3Book& tq3_book() {
         pfa_status st_ = (expr);         \
         if (st_ != PFA_OK) return st_;   \
     } while (0)
+
+// The split partials of pfa_paged_attn_decode_static.  Every GPU the library
+// runs on holds its own copy of this array from the code object's load until the
+// process ends.  In host code `scratch` names a host-side stand-in, never a device
+// address: the device address comes from hipGetSymbolAddress, once per device.
+constexpr size_t kStaticScratchBytes = (size_t)PFA_STATIC_SCRATCH_BYTES;
+constexpr int kMaxDevices = 64;
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
+pfa_status static_scratch(void** ptr) {
+    static std::mutex mu;
+    static void* addr[kMaxDevices] = {};
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_status(e);
+    if (dev < 0 || dev >= kMaxDevices) return PFA_ERR_UNSUPPORTED;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!addr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return hip_status(e);
+        if (!p) return PFA_ERR_HIP;
+        addr[dev] = p;
+    }
+    *ptr = addr[dev];
+    return PFA_OK;
+}
 
 }  // namespace
 
@@ -258,6 +287,30 @@ pfa_status pfa_paged_attn_decode_fused(const pfa_attn_desc* desc, const pfa_kv_p
                                        float* lse_part, int32_t* counters, float* out, void* stream) {
     return decode_like(desc, pool, q, block_table, bt_stride, seq_lens, batch, max_seq_len, split_keys,
                        max_splits, o_part, lse_part, counters, out, stream, true);
+}
+
+pfa_status pfa_paged_attn_decode_static(const pfa_attn_desc* desc, const pfa_kv_pool* pool,
+                                        const void* q, const int32_t* block_table, int32_t bt_stride,
+                                        const int32_t* seq_lens, int32_t batch, int32_t max_seq_len,
+                                        int32_t split_keys, float* out, void* stream) {
+    PFA_TRY(check_desc(desc));
+    if (split_keys < 0 || batch < 0 || max_seq_len < 0) return PFA_ERR_SHAPE;
+    const int32_t ms = split_keys == 0 ? 1 : pfa_decode_num_splits(max_seq_len, split_keys);
+    const size_t o_bytes = (size_t)batch * desc->num_q_heads * ms * desc->head_dim * sizeof(float);
+    const size_t lse_off = (o_bytes + 255) / 256 * 256;
+    const size_t need = lse_off + (size_t)batch * desc->num_q_heads * ms * sizeof(float);
+    if (ms > 1 && need > kStaticScratchBytes) return PFA_ERR_WORKSPACE;
+    if (ms == 1 || batch == 0)   // unsplit: the kernel writes out directly, no partials
+        return decode_like(desc, pool, q, block_table, bt_stride, seq_lens, batch, max_seq_len, 0, 1,
+                           nullptr, nullptr, nullptr, out, stream, false);
+    if (!out) return PFA_ERR_NULL;
+    void* base = nullptr;
+    PFA_TRY(static_scratch(&base));
+    float* o_part = static_cast<float*>(base);
+    float* lse_part = reinterpret_cast<float*>(static_cast<unsigned char*>(base) + lse_off);
+    PFA_TRY(decode_like(desc, pool, q, block_table, bt_stride, seq_lens, batch, max_seq_len, split_keys, ms,
+                        o_part, lse_part, nullptr, out, stream, false));
+    return pfa_paged_attn_combine(desc, o_part, lse_part, seq_lens, batch, split_keys, ms, out, stream);
 }
 
 pfa_status pfa_paged_attn_combine(const pfa_attn_desc* desc, const float* o_part,

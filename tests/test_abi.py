@@ -56,6 +56,20 @@ def test_decode_workspace_bytes():
     assert pfa.decode_workspace_bytes(pfa.AttnDesc(64, 8, 64), 64, 128) == 64 * 64 * 128 * 65 * 4
 
 
+def test_decode_static_rejects_partials_beyond_its_array():
+    """pfa_paged_attn_decode_static: partials larger than PFA_STATIC_SCRATCH_BYTES
+    return PFA_ERR_WORKSPACE before any HIP call (no GPU needed)."""
+    L = pfa.lib()
+    d, p = desc(), pool()
+    call = lambda B, ml, S, out=FAKE: L.pfa_paged_attn_decode_static(
+        ctypes.byref(d), ctypes.byref(p), FAKE, FAKE, 4096, FAKE, B, ml, S, out, None)
+    # 64 x 32 heads x 128 splits x 129 x 4 B = 135 MB > 32 MiB
+    assert call(64, 32768, 256) == WORKSPACE
+    assert pfa.STATIC_SCRATCH_BYTES == 32 << 20
+    assert call(8, 1024, -16) == SHAPE
+    assert call(-1, 1024, 256) == SHAPE
+
+
 def desc(**kw):
     d = dict(num_q_heads=32, num_kv_heads=8, head_dim=128, page_size=16, kv_dtype=0, window=0,
              sm_scale=0.088, sinks=None)
