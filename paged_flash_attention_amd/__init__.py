@@ -60,17 +60,34 @@ class CKvPool(ctypes.Structure):
                 ("num_pages", ctypes.c_int32), ("k_smooth", ctypes.c_void_p)]
 
 
+AUDIT_LIB_PATH = os.path.join(_HERE, "libpfa_audit.so")   # prefill barrier-audit build (tests)
+
 _lib = None
 
 
 def lib() -> ctypes.CDLL:
     """Load libpfa.so (built in-tree) and declare its signatures."""
     global _lib
-    if _lib is not None:
-        return _lib
-    if not os.path.exists(LIB_PATH):
-        raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m paged_flash_attention_amd.build`")
-    L = ctypes.CDLL(LIB_PATH)
+    if _lib is None:
+        _lib = load_library(LIB_PATH)
+    return _lib
+
+
+def use_library(L: Optional[ctypes.CDLL]) -> Optional[ctypes.CDLL]:
+    """Route the entry points below through another loaded build (e.g. the audit
+    build, from load_library(AUDIT_LIB_PATH)); None restores libpfa.so.  Returns
+    the build used before."""
+    global _lib
+    prev = _lib
+    _lib = L
+    return prev
+
+
+def load_library(path: str) -> ctypes.CDLL:
+    """Load a build of the library and declare its signatures."""
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with `python -m paged_flash_attention_amd.build`")
+    L = ctypes.CDLL(path)
     P, I, F, V = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float, ctypes.c_void_p
     D, PL = ctypes.POINTER(CAttnDesc), ctypes.POINTER(CKvPool)
     sig = {
@@ -101,7 +118,6 @@ def lib() -> ctypes.CDLL:
     L.pfa_status_string.restype = ctypes.c_char_p
     L.pfa_last_hip_error.argtypes = []
     L.pfa_last_hip_error.restype = ctypes.c_int32
-    _lib = L
     return L
 
 

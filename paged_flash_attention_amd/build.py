@@ -3,7 +3,10 @@
     python -m paged_flash_attention_amd.build [--jobs N]
 
 Each .hip source under csrc/ is compiled to an object in _build/, then linked
-in-tree as paged_flash_attention_amd/libpfa.so.
+in-tree as paged_flash_attention_amd/libpfa.so.  A second library,
+libpfa_audit.so, is the same code built with PFA_PREFILL_AUDIT=1 (every prefill
+ring step waits for all loads and all waves); a GPU test checks that the normal
+build gives the same bits.
 """
 from __future__ import annotations
 
@@ -36,9 +39,12 @@ def sources():
     return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
 
 
-def compile_one(src: str) -> str:
-    obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *FLAGS, "-c", src, "-o", obj]
+AUDIT_LIB = os.path.join(HERE, "libpfa_audit.so")
+
+
+def compile_one(src: str, outdir: str = BUILD, defines=()) -> str:
+    obj = os.path.join(outdir, os.path.basename(src) + ".o")
+    cmd = [HIPCC, *FLAGS, *[f"-D{d}" for d in defines], "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed on {src}:\n{r.stdout}\n{r.stderr}")
@@ -50,11 +56,19 @@ def compile_one(src: str) -> str:
 
 
 def build(jobs: int = 8) -> str:
-    os.makedirs(BUILD, exist_ok=True)
+    audit_dir = os.path.join(BUILD, "audit")
+    os.makedirs(audit_dir, exist_ok=True)
     srcs = sources()
     with cf.ThreadPoolExecutor(max_workers=max(1, jobs)) as ex:
-        objs = list(ex.map(compile_one, srcs))
-    tmp = LIB + ".tmp"
+        objs = ex.map(compile_one, srcs)
+        audit_objs = ex.map(lambda f: compile_one(f, audit_dir, ("PFA_PREFILL_AUDIT=1",)), srcs)
+        objs, audit_objs = list(objs), list(audit_objs)
+    link(audit_objs, AUDIT_LIB)
+    return link(objs, LIB)
+
+
+def link(objs, target: str) -> str:
+    tmp = target + ".tmp"
     cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
@@ -64,8 +78,8 @@ def build(jobs: int = 8) -> str:
     missing = [l.split()[-1] for l in nm.stdout.splitlines() if "__device_stub__" in l]
     if missing:
         raise RuntimeError("undefined kernel launch stubs in libpfa.so:\n" + "\n".join(missing))
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, target)
+    return target
 
 
 if __name__ == "__main__":

@@ -71,9 +71,19 @@
 #define PFA_PREFILL_LAUNCH launch_prefill
 #endif
 
+// Barrier audit: with PFA_PREFILL_AUDIT=1 every ring step waits for all of the
+// wave's loads (vmcnt 0) and then for every wave (s_barrier), before and after it
+// refills a stage, and the prologue waits for every tile it issued.  The hand-
+// placed waits of the normal build (each wave waits only for the tile it is about
+// to make visible) must give the same bits; a GPU test compares the two builds.
+#ifndef PFA_PREFILL_AUDIT
+#define PFA_PREFILL_AUDIT 0
+#endif
+
 namespace pfa {
 namespace {
 
+constexpr bool kAudit = PFA_PREFILL_AUDIT != 0;
 constexpr int kRowsPerWave = 32;
 constexpr int kWaves = PFA_PREFILL_ROWS_WG / kRowsPerWave;
 constexpr int kThreads = kWaves * kWave;
@@ -502,13 +512,18 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a, const 
     // ring in two parts, so that LDS reads can be issued right after the barrier
     auto ring_pre = [&](int kb) __attribute__((always_inline)) {
         // in flight: tiles kb+2 and kb+3 (kb+4 is issued below)
-        wait_vmcnt<NL>();                      // this wave's share of tile kb+2 landed
+        if constexpr (kAudit) wait_vmcnt<0>();
+        else wait_vmcnt<NL>();                 // this wave's share of tile kb+2 landed
         lds_sync();                            // everyone's; tile kb-1's stage is free
     };
     auto ring_post = [&](int kb) __attribute__((always_inline)) {
         issue(clamp_page(pg_raw), kst(kb + 4), vst(kb + 4));   // tile min(kb + 4, kb1)
         pg_raw = raw_page(min(kb + 5, kb1));
         zero_tail(kb + 2, vst(kb + 2));
+        if constexpr (kAudit) {
+            wait_vmcnt<0>();
+            lds_sync();
+        }
     };
     auto ring = [&](int kb) __attribute__((always_inline)) { ring_pre(kb); ring_post(kb); };
     // this wave's tiles
@@ -522,7 +537,8 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a, const 
 #pragma unroll
     for (int i = 0; i < 4; ++i) issue(clamp_page(raw_page(min(kb0 + i, kb1))), kst(kb0 + i), vst(kb0 + i));
     pg_raw = raw_page(min(kb0 + 4, kb1));
-    wait_vmcnt<2 * NL>();                      // tiles kb0, kb0+1 landed (kb0+2, kb0+3 in flight)
+    if constexpr (kAudit) wait_vmcnt<0>();
+    else wait_vmcnt<2 * NL>();                 // tiles kb0, kb0+1 landed (kb0+2, kb0+3 in flight)
     lds_sync();
     zero_tail(kb0, vst(kb0));                  // visible after the next barrier
     zero_tail(kb0 + 1, vst(kb0 + 1));
