@@ -350,7 +350,7 @@ pfa_status prefill_like(const pfa_attn_desc* desc, const pfa_kv_pool* pool, cons
                         float* lse_part, float* out, void* stream, bool split_build) {
     PFA_TRY(check_desc(desc));
     PFA_TRY(check_pool(desc, pool));
-    if (desc->kv_dtype != PFA_KV_BF16) return PFA_ERR_UNSUPPORTED;
+    if (desc->kv_dtype == PFA_KV_TQ3) return PFA_ERR_UNSUPPORTED;
     const int g = desc->num_q_heads / desc->num_kv_heads;
     if (!prefill_group_ok(g)) return PFA_ERR_UNSUPPORTED;
     if (batch < 0 || max_q_len < 0 || bt_stride <= 0 || max_seq_len < max_q_len || max_splits < 1)
@@ -372,6 +372,10 @@ pfa_status prefill_like(const pfa_attn_desc* desc, const pfa_kv_pool* pool, cons
     a.q = static_cast<const uint16_t*>(q);
     a.k_pool = static_cast<const uint16_t*>(pool->k_pool);
     a.v_pool = static_cast<const uint16_t*>(pool->v_pool);
+    const bool int8 = desc->kv_dtype == PFA_KV_INT8;
+    a.k_scale = int8 ? pool->k_scale : nullptr;
+    a.v_scale = int8 ? pool->v_scale : nullptr;
+    a.k_smooth = int8 ? pool->k_smooth : nullptr;
     a.cu_q = cu_q;
     a.block_table = block_table;
     a.seq_lens = seq_lens;

@@ -210,8 +210,11 @@ struct CombineArgs {
 
 struct PrefillArgs {
     const uint16_t* q;
-    const uint16_t* k_pool;
+    const uint16_t* k_pool;     // bf16, or INT8 codes (then k_scale != NULL)
     const uint16_t* v_pool;
+    const float* k_scale;       // INT8: [num_pages][Hkv][P]; NULL for BF16
+    const float* v_scale;
+    const float* k_smooth;      // INT8: [D] per-channel key smoothing (q is scaled by it), or NULL
     const int32_t* cu_q;
     const int32_t* block_table;
     const int32_t* seq_lens;

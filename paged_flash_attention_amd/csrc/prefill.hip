@@ -54,11 +54,21 @@
 //    never meets a zero weight.
 //  * Workgroups map to XCDs so that each XCD's L2 holds the K/V of the heads it
 //    serves.  Within an XCD the longest (latest) query tiles go first.
+//  * INT8 caches (KV8): the tiles come in through registers (compiler-tracked
+//    loads, one tile ahead) and are converted into the same bf16 LDS tiles before
+//    the barrier that publishes them.  K is stored exactly, as the codes c (bf16
+//    holds every |c| <= 127), so the MFMA yields q.c exactly (up to fp32
+//    summation), and each score is then multiplied by its key's scale * sm_scale *
+//    log2 e (from LDS) before the mask, max and exp.  V is stored as bf16(c * scale_v): its rounding enters the output
+//    linearly, at most 2^-9 relative per element.  The ring has 4 stages (the
+//    converted tile reuses the stage freed one barrier earlier).
 //  * Split mode covers a short chunk on a long prefix, such as 130 new tokens on
 //    8192.  Such a chunk has too few query tiles to fill 256 CUs, so the key
 //    range is cut into max_splits ranges of split_keys keys, a multiple of 64.
 //    Each workgroup writes a softmax-normalised partial with its natural
 //    log-sum-exp, and the combine kernel then merges them with the sink.
+#include <type_traits>
+
 #include "pfa_device.h"
 
 // Two builds of this file: the default one (256-row workgroups, 64-key tiles,
@@ -158,7 +168,7 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
     return (uint32_t)(uintptr_t)(LDS3 const void*)p;
 }
 
-template <int D, int G, bool SPLIT>
+template <int D, int G, bool SPLIT, bool KV8>
 __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a, const int32_t* __restrict__ block_table) {
     constexpr int TPW = kRowsPerWave / G;               // tokens per wave
     constexpr int TPB = TPW * kWaves;                   // tokens per workgroup
@@ -170,8 +180,14 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a, const 
     constexpr int NL = 2 * DMA_PER_WAVE;                // vector-memory ops per tile per wave
     static_assert(DMA_PER_WAVE >= 1, "tile split");
 
-    // ring of kStages stages, each a K tile then a V tile (keys x D, swizzled)
-    __shared__ __attribute__((aligned(1024))) uint16_t ring_lds[kStages * 2 * kBN * D];
+    // ring of NST stages, each a K tile then a V tile (keys x D, swizzled); INT8
+    // adds each stage's per-key score multipliers
+    constexpr int NST = KV8 ? 4 : kStages;
+    __shared__ __attribute__((aligned(1024))) uint16_t ring_lds[NST * 2 * kBN * D];
+    __shared__ __attribute__((aligned(16))) float kmul_lds[KV8 ? NST * kBN : 4];
+    // INT8 staging: elements of K (and of V) one thread converts per tile
+    constexpr int EPT = kBN * D / kThreads;
+    static_assert(!KV8 || (EPT == 8 || EPT == 16), "INT8 staging");
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);   // wave-uniform
@@ -238,6 +254,9 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a, const 
     // Scores leave the MFMA as s = q.k; p = 2^(c2 s - mu) with c2 = sm_scale * log2 e
     // and mu the row's reference max (log2 units).
     const float c2 = a.sm_scale * kLog2e;
+    // the multiplier of the scores in the exp: c2, or 1 for INT8, whose scores are
+    // scaled per key before the mask (by the key's scale times c2)
+    const float cexp = KV8 ? 1.0f : c2;
     bf16x8 qf[KK];
     {
         const uint16_t* qp = a.q + ((int64_t)(cq0 + tok_l) * Hq + h_l) * D + 8 * half;
@@ -245,6 +264,18 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a, const 
         for (int kk = 0; kk < KK; ++kk) {
             uint4 v = make_uint4(0, 0, 0, 0);
             if (row_ok) v = *reinterpret_cast<const uint4*>(qp + 16 * kk);
+            if constexpr (KV8) {
+                // keys stored smoothed (k / s, s a power of two): q meets q * s, exact
+                if (a.k_smooth) {
+                    const float* sp = a.k_smooth + 16 * kk + 8 * half;
+                    uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        w[i] = pack_bf16_rne(bf16_lo(w[i]) * smooth_pow2(__ldg(sp + 2 * i)),
+                                             bf16_hi(w[i]) * smooth_pow2(__ldg(sp + 2 * i + 1)));
+                    v = make_uint4(w[0], w[1], w[2], w[3]);
+                }
+            }
             qf[kk] = __builtin_bit_cast(bf16x8, v);
         }
         // The direct loads below are invisible to the compiler's vmcnt tracking.
@@ -288,12 +319,75 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a, const 
     const uint32_t ring0 = lds_addr(ring_lds);
     constexpr uint32_t kTileBytes = kBN * D * 2;
     auto issue = [&](int pg, uint32_t kdst, uint32_t vdst) __attribute__((always_inline)) {
+        if constexpr (KV8) return;
         const int64_t pbase = (int64_t)pg * page_stride;
 #pragma unroll
         for (int i = 0; i < DMA_PER_WAVE; ++i) {
             const uint32_t row0 = (wave * DMA_PER_WAVE + i) * ROWS_PER_DMA;
             dma16(kpool_h + pbase, koff[i], kdst + row0 * D * 2);
             dma16(vpool_h + pbase, voff[i], vdst + row0 * D * 2);
+        }
+    };
+
+    // ---- INT8: tiles through registers ----
+    // Thread tid holds EPT codes of key row tid / (D / EPT) of a tile (8 threads
+    // per row; a wave's 8 rows lie in one page, the page raw_page reads), for K and
+    // for V, plus that row's two scales.
+    typedef typename std::conditional<EPT == 16, uint4, uint2>::type CodeT;
+    const int st_row = tid / (D / EPT), st_chunk = tid % (D / EPT);
+    CodeT st_k{}, st_v{};
+    float st_ks = 0.0f, st_vs = 0.0f;
+    const int8_t* kcodes_h = reinterpret_cast<const int8_t*>(a.k_pool) + (int64_t)kvh * hblk;
+    const int8_t* vcodes_h = reinterpret_cast<const int8_t*>(a.v_pool) + (int64_t)kvh * hblk;
+    auto stage_load = [&](int pg) __attribute__((always_inline)) {
+        if constexpr (KV8) {
+            const int64_t blk = (int64_t)pg * a.num_kv_heads;              // + kvh in the bases
+            const int64_t off = blk * hblk + (st_row % kPage) * D + st_chunk * EPT;
+            st_k = *reinterpret_cast<const CodeT*>(kcodes_h + off);
+            st_v = *reinterpret_cast<const CodeT*>(vcodes_h + off);
+            const int64_t si = (blk + kvh) * kPage + st_row % kPage;
+            st_ks = __ldg(a.k_scale + si);
+            st_vs = __ldg(a.v_scale + si);
+        }
+    };
+    // Convert the staged tile kb (key rows kb*kBN + row) into the bf16 LDS stage
+    // kdst/vdst (same layout and swizzles as the direct loads), and its score
+    // multipliers into kmul_lds[mi .. mi + kBN).  V:
+    // c * scale_v rounded to bf16, 0 past the sequence end (where scales may be
+    // poison).  Multiplier: scale_k * sm_scale * log2 e, 0 past the end (the mask
+    // then sets those scores to -inf).  K: the codes c themselves, exact in bf16.
+    auto stage_convert = [&](int kb, uint32_t kdst, uint32_t vdst, int mi) __attribute__((always_inline)) {
+        if constexpr (KV8) {
+            const int row = st_row;
+            const bool live = kb * kBN + row < n;
+            uint32_t cw[EPT / 4];
+            uint32_t vw_[EPT / 4];
+            __builtin_memcpy(cw, &st_k, sizeof(cw));
+            __builtin_memcpy(vw_, &st_v, sizeof(vw_));
+            uint32_t ko[EPT / 2], vo[EPT / 2];
+            const float vs = live ? st_vs : 0.0f;
+#pragma unroll
+            for (int i = 0; i < EPT / 4; ++i) {
+                float kx[4], vx[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    kx[e] = (float)(int8_t)(cw[i] >> (8 * e));
+                    vx[e] = (float)(int8_t)(vw_[i] >> (8 * e));
+                }
+                ko[2 * i] = pack_hi16(kx[0], kx[1]);
+                ko[2 * i + 1] = pack_hi16(kx[2], kx[3]);
+                vo[2 * i] = live ? pack_bf16_rne(vx[0] * vs, vx[1] * vs) : 0u;
+                vo[2 * i + 1] = live ? pack_bf16_rne(vx[2] * vs, vx[3] * vs) : 0u;
+            }
+#pragma unroll
+            for (int c = 0; c < EPT / 8; ++c) {
+                const int lc = st_chunk * (EPT / 8) + c;             // 8-element chunk in the row
+                const uint32_t kofs_b = (uint32_t)(row * D * 2 + ((lc ^ swz_k<D>(row)) << 4));
+                const uint32_t vofs_b = (uint32_t)(row * D * 2 + ((lc ^ swz_v<D>(row)) << 4));
+                *(LDS3 u32x4*)(uintptr_t)(kdst + kofs_b) = u32x4{ko[4 * c], ko[4 * c + 1], ko[4 * c + 2], ko[4 * c + 3]};
+                *(LDS3 u32x4*)(uintptr_t)(vdst + vofs_b) = u32x4{vo[4 * c], vo[4 * c + 1], vo[4 * c + 2], vo[4 * c + 3]};
+            }
+            if (st_chunk == 0) kmul_lds[mi + row] = live ? st_ks * c2 : 0.0f;
         }
     };
 
@@ -340,6 +434,21 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a, const 
         const int key0 = kb * kBN;
         return (key0 + kBN - 1 <= prefix + w_first) && (W == 0 || (prefix + w_last) - key0 < W);
     };
+    // INT8: multiply each score by its key's multiplier (stage of tile kb).  A lane
+    // holds keys 32h + 8(r/4) + (r%4) + 4*half: four consecutive ones per read.
+    auto scale_scores = [&](int kb, Scores& s) __attribute__((always_inline)) {
+        if constexpr (KV8) {
+            const int mi = ((kb - kb0) % NST) * kBN + 4 * half;
+#pragma unroll
+            for (int h = 0; h < NH; ++h)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const f32x4 m = *(const LDS3 f32x4*)(uintptr_t)lds_addr(&kmul_lds[mi + 32 * h + 8 * q]);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) s[h][4 * q + i] *= m[i];
+                }
+        }
+    };
     auto mask = [&](int kb, Scores& s) __attribute__((always_inline)) {
         // distance of this lane's first key in the tile from its row position
         const int d0 = opaque(pos_l - kb * kBN - 4 * half);
@@ -357,7 +466,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a, const 
     // the fp32 sums).  O and l share the reference, so o/l is unchanged.  mt is
     // the lane's max of the tile's raw scores.
     auto rescale = [&](float mt) __attribute__((always_inline)) {
-        mt = xor32_max(mt) * c2;
+        mt = xor32_max(mt) * cexp;
         if (__any(mt > m_run + 8.0f)) {
             const float m_new = fmaxf(m_run, mt);
             const float mu = (m_new == -INFINITY) ? 0.0f : m_new;
@@ -384,8 +493,8 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a, const 
     // P that the PV MFMA uses (a dot2 with (1, 1))
     auto exp_pair = [&](const Scores& s, Packed& pk, int q, float nmu) __attribute__((always_inline)) {
         const int h = q / 8, r = 2 * (q % 8);
-        const float p0 = fast_exp2(fmaf(s[h][r], c2, nmu));
-        const float p1 = fast_exp2(fmaf(s[h][r + 1], c2, nmu));
+        const float p0 = fast_exp2(fmaf(s[h][r], cexp, nmu));
+        const float p1 = fast_exp2(fmaf(s[h][r + 1], cexp, nmu));
         pk[h][r / 2] = pack_bf16_rne(p0, p1);
         l_run = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(pk[h][r / 2]), as_bf16x2(0x3F803F80u), l_run, false);
     };
@@ -506,20 +615,32 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a, const 
     //     row max of S', then the rescale for tile kb+1.
     // A wave computes only on the tiles kw0..kw1 its rows see; the range's first
     // tile gets its S before ring(kw0 - 1), its last one only P and PV.
-    auto kst = [&](int kb) { return ring0 + (uint32_t)((kb - kb0) % kStages) * (2 * kTileBytes); };
+    auto kst = [&](int kb) { return ring0 + (uint32_t)((kb - kb0) % NST) * (2 * kTileBytes); };
+    auto mst = [&](int kb) { return ((kb - kb0) % NST) * kBN; };
     auto vst = [&](int kb) { return kst(kb) + kTileBytes; };
     int pg_raw;                                // raw page entry of tile min(kb + 4, kb1)
     // ring in two parts, so that LDS reads can be issued right after the barrier
     auto ring_pre = [&](int kb) __attribute__((always_inline)) {
-        // in flight: tiles kb+2 and kb+3 (kb+4 is issued below)
-        if constexpr (kAudit) wait_vmcnt<0>();
-        else wait_vmcnt<NL>();                 // this wave's share of tile kb+2 landed
+        if constexpr (KV8) {
+            // tile kb+2 (staged at ring(kb-1)) into the stage of tile kb-2, which the
+            // barrier of ring(kb-1) freed
+            stage_convert(kb + 2, kst(kb + 2), vst(kb + 2), mst(kb + 2));
+        } else {
+            // in flight: tiles kb+2 and kb+3 (kb+4 is issued below)
+            if constexpr (kAudit) wait_vmcnt<0>();
+            else wait_vmcnt<NL>();             // this wave's share of tile kb+2 landed
+        }
         lds_sync();                            // everyone's; tile kb-1's stage is free
     };
     auto ring_post = [&](int kb) __attribute__((always_inline)) {
-        issue(clamp_page(pg_raw), kst(kb + 4), vst(kb + 4));   // tile min(kb + 4, kb1)
-        pg_raw = raw_page(min(kb + 5, kb1));
-        zero_tail(kb + 2, vst(kb + 2));
+        if constexpr (KV8) {
+            stage_load(clamp_page(pg_raw));    // tile min(kb + 3, kb1)
+            pg_raw = raw_page(min(kb + 4, kb1));
+        } else {
+            issue(clamp_page(pg_raw), kst(kb + 4), vst(kb + 4));   // tile min(kb + 4, kb1)
+            pg_raw = raw_page(min(kb + 5, kb1));
+            zero_tail(kb + 2, vst(kb + 2));
+        }
         if constexpr (kAudit) {
             wait_vmcnt<0>();
             lds_sync();
@@ -534,14 +655,26 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a, const 
     }
     const bool any = kw0 <= kw1;
 
+    if constexpr (KV8) {
+        // tiles kb0 and kb0+1 converted, kb0+2 staged
 #pragma unroll
-    for (int i = 0; i < 4; ++i) issue(clamp_page(raw_page(min(kb0 + i, kb1))), kst(kb0 + i), vst(kb0 + i));
-    pg_raw = raw_page(min(kb0 + 4, kb1));
-    if constexpr (kAudit) wait_vmcnt<0>();
-    else wait_vmcnt<2 * NL>();                 // tiles kb0, kb0+1 landed (kb0+2, kb0+3 in flight)
-    lds_sync();
-    zero_tail(kb0, vst(kb0));                  // visible after the next barrier
-    zero_tail(kb0 + 1, vst(kb0 + 1));
+        for (int i = 0; i < 2; ++i) {
+            stage_load(clamp_page(raw_page(min(kb0 + i, kb1))));
+            stage_convert(kb0 + i, kst(kb0 + i), vst(kb0 + i), mst(kb0 + i));
+        }
+        stage_load(clamp_page(raw_page(min(kb0 + 2, kb1))));
+        pg_raw = raw_page(min(kb0 + 3, kb1));
+        lds_sync();
+    } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) issue(clamp_page(raw_page(min(kb0 + i, kb1))), kst(kb0 + i), vst(kb0 + i));
+        pg_raw = raw_page(min(kb0 + 4, kb1));
+        if constexpr (kAudit) wait_vmcnt<0>();
+        else wait_vmcnt<2 * NL>();             // tiles kb0, kb0+1 landed (kb0+2, kb0+3 in flight)
+        lds_sync();
+        zero_tail(kb0, vst(kb0));              // visible after the next barrier
+        zero_tail(kb0 + 1, vst(kb0 + 1));
+    }
 
     Scores s_a, s_b;                           // scores of the current / next tile
     Packed pk;
@@ -551,11 +684,13 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a, const 
         for (; kb < kw0 - 1; ++kb) ring(kb);
         // tile kw0 became visible at ring(kw0 - 2) or in the prologue
         qk_block(false, 0, kst(kw0), s_a, s_b, pk);
+        scale_scores(kw0, s_a);
         mask_max(kw0, s_a);
         if (kw0 > kb0) ring(kb++);             // ring(kw0 - 1)
         // fused iterations kw0 .. kw1-1, two per round (the score buffers swap)
         auto fused = [&](int t, Scores& sc, Scores& sn) __attribute__((always_inline)) {
             qk_block(true, kPairs1, kst(t + 1), sn, sc, pk);
+            scale_scores(t + 1, sn);
             if (!tile_full(t + 1)) mask(t + 1, sn);
             ring_pre(t);
             pv_head(vst(t), vh);
@@ -612,7 +747,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a, const 
         }
 }
 
-template <int D, int G>
+template <int D, int G, bool KV8>
 hipError_t launch_dg(const PrefillArgs& a, hipStream_t s) {
     constexpr int TPB = kRowsPerWave / G * kWaves;
     const int n_tiles = (a.max_q_len + TPB - 1) / TPB;
@@ -621,21 +756,21 @@ hipError_t launch_dg(const PrefillArgs& a, hipStream_t s) {
     const int64_t grid = (items + kXcds - 1) / kXcds * kXcds;
     if (grid == 0) return hipSuccess;
     if (split)
-        hipLaunchKernelGGL((prefill_kernel<D, G, true>), dim3((unsigned)grid), dim3(kThreads), 0, s, a, a.block_table);
+        hipLaunchKernelGGL((prefill_kernel<D, G, true, KV8>), dim3((unsigned)grid), dim3(kThreads), 0, s, a, a.block_table);
     else
-        hipLaunchKernelGGL((prefill_kernel<D, G, false>), dim3((unsigned)grid), dim3(kThreads), 0, s, a, a.block_table);
+        hipLaunchKernelGGL((prefill_kernel<D, G, false, KV8>), dim3((unsigned)grid), dim3(kThreads), 0, s, a, a.block_table);
     return hipGetLastError();
 }
 
-template <int D>
+template <int D, bool KV8>
 hipError_t launch_d(const PrefillArgs& a, hipStream_t s) {
     switch (a.num_q_heads / a.num_kv_heads) {
-        case 1: return launch_dg<D, 1>(a, s);
-        case 2: return launch_dg<D, 2>(a, s);
-        case 4: return launch_dg<D, 4>(a, s);
-        case 8: return launch_dg<D, 8>(a, s);
-        case 16: return launch_dg<D, 16>(a, s);
-        case 32: return launch_dg<D, 32>(a, s);
+        case 1: return launch_dg<D, 1, KV8>(a, s);
+        case 2: return launch_dg<D, 2, KV8>(a, s);
+        case 4: return launch_dg<D, 4, KV8>(a, s);
+        case 8: return launch_dg<D, 8, KV8>(a, s);
+        case 16: return launch_dg<D, 16, KV8>(a, s);
+        case 32: return launch_dg<D, 32, KV8>(a, s);
         default: return hipErrorInvalidValue;
     }
 }
@@ -644,7 +779,8 @@ hipError_t launch_d(const PrefillArgs& a, hipStream_t s) {
 
 hipError_t PFA_PREFILL_LAUNCH(const PrefillArgs& a, int head_dim, hipStream_t s) {
     if (a.batch == 0 || a.max_q_len == 0) return hipSuccess;
-    return head_dim == 128 ? launch_d<128>(a, s) : launch_d<64>(a, s);
+    if (a.k_scale) return head_dim == 128 ? launch_d<128, true>(a, s) : launch_d<64, true>(a, s);
+    return head_dim == 128 ? launch_d<128, false>(a, s) : launch_d<64, false>(a, s);
 }
 
 }  // namespace pfa

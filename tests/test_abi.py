@@ -206,7 +206,7 @@ def pre(d, p, **kw):
 
 
 def test_prefill_validation():
-    assert pre(desc(kv_dtype=1), pool(k_scale=FAKE.value, v_scale=FAKE.value)) == UNSUP
+    assert pre(desc(kv_dtype=1), pool()) == NULL                             # INT8 pool without scales
     assert pre(desc(num_q_heads=64 * 3, num_kv_heads=3), pool()) == UNSUP   # G = 64
     assert pre(desc(), pool(), cu=None) == NULL
     assert pre(desc(), pool(), out=None) == NULL
@@ -250,7 +250,7 @@ def ver(d, p, **kw):
 
 def test_verify_validation():
     assert ver(desc(), pool(), mq=17) == SHAPE                               # more than 16 tokens
-    assert ver(desc(kv_dtype=1), pool(k_scale=FAKE.value, v_scale=FAKE.value)) == UNSUP
+    assert ver(desc(kv_dtype=1), pool()) == NULL                             # INT8 pool without scales
     assert ver(desc(), pool(), out=None) == NULL
     assert ver(desc(), pool(), S=96, ms=11) == SHAPE                         # not a multiple of 64
     assert ver(desc(), pool(), S=64, ms=15) == WORKSPACE                     # 1024/64 = 16 ranges
@@ -286,7 +286,7 @@ def test_tq3_pool_validation():
     assert kvw(desc(kv_dtype=2), pool()) == NULL                           # 3-bit pool without scales
     assert dec(desc(kv_dtype=2), pool()) == NULL
     assert kvw(desc(kv_dtype=2), pool(k_smooth=FAKE.value, **tq)) == UNSUP  # smoothing is INT8-only
-    assert pre(desc(kv_dtype=2), pool(**tq)) == UNSUP                      # prefill: BF16 only
+    assert pre(desc(kv_dtype=2), pool(**tq)) == UNSUP                      # prefill: BF16 or INT8
     assert ver(desc(kv_dtype=2), pool(**tq)) == UNSUP
     assert ain(desc(kv_dtype=2), pool(**tq)) == UNSUP
     assert decf(desc(kv_dtype=2), pool(**tq)) == UNSUP                     # no fused merge
