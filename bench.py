@@ -83,7 +83,7 @@ def verify_bytes(case) -> int:
     once per (sequence, KV head), the chunk's q and fp32 out, the block-table entries."""
     p = case.p
     vis = visible_keys(case.seq_lens, p.window)
-    kv = int(vis.sum()) * p.num_kv_heads * 2 * p.head_dim * 2
+    kv = int(vis.sum()) * p.num_kv_heads * kv_bytes_per_key_head(p)
     T = int(case.q_lens.sum())
     return kv + T * p.num_q_heads * p.head_dim * (2 + 4) + int((np.asarray(case.seq_lens) + 15).sum() // 16) * 4
 
@@ -522,6 +522,10 @@ def main():
         "prefill_causal_8192": lambda: W.prefill_llama8b(prompt=8192),
         "prefill_causal_1024": lambda: W.prefill_llama8b(prompt=1024),
         "prefill_chunk130_on_8192": lambda: W.prefill_llama8b(prompt=130, prefix=8192),
+        "prefill_int8_causal_8192": lambda: W.prefill_llama8b(prompt=8192, kv_dtype="int8"),
+        "prefill_int8_causal_1024": lambda: W.prefill_llama8b(prompt=1024, kv_dtype="int8"),
+        "prefill_int8_chunk130_on_8192": lambda: W.prefill_llama8b(prompt=130, prefix=8192, kv_dtype="int8"),
+        "verify_int8_16tok_batch1_ctx1024": lambda: W.verify_qwen4b_int8(),
         "mixed_full_prefill_2x2048": lambda: W.mixed_gptoss(layer="full", part="prefill"),
         "mixed_window_prefill_2x2048": lambda: W.mixed_gptoss(layer="window", part="prefill"),
         "attn_input_1x8192": lambda: W.attn_input_qwen4b(),
@@ -617,6 +621,8 @@ def main():
                          ("kv_write_bf16_8192", 40), ("kv_write_int8_8192", 40), ("kv_write_tq3_8192", 40),
                          ("mixed_full_decode_b64", 30), ("mixed_window_decode_b64", 50),
                          ("prefill_causal_8192", 30), ("prefill_causal_1024", 50),
+                         ("prefill_int8_causal_8192", 20), ("prefill_int8_causal_1024", 50),
+                         ("prefill_int8_chunk130_on_8192", 20), ("verify_int8_16tok_batch1_ctx1024", 50),
                          ("prefill_chunk130_on_8192", 20), ("mixed_full_prefill_2x2048", 20),
                          ("mixed_window_prefill_2x2048", 30),
                          ("verify_16tok_batch1_ctx1024", 50), ("verify_16tok_batch1_ctx1024_graph", 200),

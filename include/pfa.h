@@ -43,8 +43,8 @@
  *    the pool.
  *
  * Supported shapes: head_dim 64 or 128; page_size 16; Hq % Hkv == 0.
- *  - Decode: group size G = Hq/Hkv in {1,2,4,8}.
- *  - Prefill and verify: G in {1,2,4,8,16,32}; BF16 K/V.
+ *  - Decode: group size G = Hq/Hkv in {1,2,4,8}; BF16, INT8 or TQ3 K/V.
+ *  - Prefill and verify: G in {1,2,4,8,16,32}; BF16 or INT8 K/V.
  */
 #ifndef PFA_H
 #define PFA_H
@@ -331,6 +331,12 @@ pfa_status pfa_paged_attn_combine(const pfa_attn_desc* desc, const float* o_part
  *   kernel build (128-row workgroups, 32-key tiles) whether or not the key range
  *   is split: each workgroup then sees only a few tiles, and the smaller
  *   workgroups keep more of them resident per CU.
+ *
+ *   INT8 pools (the TileInfer.jl performance page prefills over its INT8 cache
+ *   too) are attended as the cache they stand for, code * scale (* the smoothing
+ *   factor).  Scores use the exact codes and each key's scale in fp32; values
+ *   enter the matrix cores as bf16(code * scale_v), an error of at most 2^-9
+ *   relative per value element.  TQ3 pools return PFA_ERR_UNSUPPORTED.
  */
 pfa_status pfa_paged_attn_prefill(const pfa_attn_desc* desc, const pfa_kv_pool* pool,
                                   const void* q, const int32_t* cu_q,

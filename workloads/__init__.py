@@ -273,12 +273,17 @@ def decode_batch32_ctx512_8192(seed=2, batch=32, lo=512, hi=8192, fixed_len=None
     return make_case(name, seed, p, lens, np.ones(batch, np.int32), split_keys=split_keys)
 
 
-def prefill_llama8b(seed=3, prompt=1024, prefix=0):
+def prefill_llama8b(seed=3, prompt=1024, prefix=0, kv_dtype="bf16"):
     """Llama-3.1-8B attention shape (32 q / 8 KV heads, D 128), causal; a fresh
-    prompt, or ``prompt`` new tokens on a restored ``prefix``-token paged prefix."""
-    p = AttnParams(32, 8, 128)
+    prompt, or ``prompt`` new tokens on a restored ``prefix``-token paged prefix.
+    ``kv_dtype`` "int8": the same over an INT8 cache (raw K/V N(0,1) with 1%
+    outliers at +-8, as the INT8 decode workload)."""
+    p = AttnParams(32, 8, 128, kv_dtype=kv_dtype)
     name = f"prefill_causal_{prompt}" if prefix == 0 else f"prefill_chunk{prompt}_on_{prefix}"
-    return make_case(name, seed, p, [prefix + prompt], [prompt], split_keys=0)
+    if kv_dtype != "bf16":
+        name = name.replace("prefill_", f"prefill_{kv_dtype}_", 1)
+    return make_case(name, seed, p, [prefix + prompt], [prompt], split_keys=0,
+                     outlier_frac=0.0 if kv_dtype == "bf16" else 0.01)
 
 
 def kv_write_prompt(kv_dtype="bf16", seed=12, prompt=8192):
@@ -352,6 +357,14 @@ def verify_qwen4b(seed=6, batch=1, tokens=16, ctx=1024, lo=None, hi=None):
         name = f"verify_{tokens}tok_batch{batch}_ctx{ctx}"
     q_lens = np.full(batch, tokens, np.int32)
     return make_case(name, seed, p, ctxs + q_lens, q_lens, split_keys=0)
+
+
+def verify_qwen4b_int8(seed=6, batch=1, tokens=16, ctx=1024):
+    """The verify step above over an INT8 cache (1% outliers at +-8)."""
+    c = verify_qwen4b(seed, batch, tokens, ctx)
+    p = AttnParams(32, 8, 128, kv_dtype="int8")
+    return make_case(c.name.replace("verify_", "verify_int8_", 1), seed, p, c.seq_lens, c.q_lens,
+                     split_keys=0, outlier_frac=0.01)
 
 
 # ---------------------------------------------------------------------------
