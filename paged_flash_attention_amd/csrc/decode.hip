@@ -25,12 +25,15 @@
 //    load instruction covers a contiguous 512*elem-byte run.  The wave's next page
 //    is prefetched while the current one is consumed; two or three pages in
 //    flight (a ring of register sets) measured no faster.  For INT8 and for G = 8
-//    the page ids are scalar loads issued a page ahead (see kScalarIds).
-//  * q.k: v_dot2_f32_bf16 on (q, k) bf16 pairs.  INT8 codes are offset to the
-//    unsigned byte c+128 (v_cvt_f32_ubyteN, exact in bf16), and 128*sum(q) is
-//    subtracted from the dot.  With key smoothing (keys stored as k/s per
-//    channel, the "INT8 KV cache" section's smoothing by the key norm's weight,
-//    s taken as a power of two), q is first scaled by s, which is exact in bf16.
+//    the page ids are scalar loads issued a page ahead (see kScalarIds), and two
+//    register sets take the pages in turn.
+//  * q.k: v_dot2_f32_bf16 on (q, k) bf16 pairs.  INT8: v_dot2_f32_f16 on fp16
+//    pairs, the codes as 1152 + c (one byte permute per two codes builds the fp16
+//    words 0x64uu = 1024 + u, u = c + 128), and 1152*sum(q) is subtracted from
+//    the dot.  q is scaled per head by a power of two into fp16's range (exact
+//    for every element within 2^28 of the head's largest).  With key smoothing (keys stored as k/s per channel, the "INT8 KV
+//    cache" section's smoothing by the key norm's weight, s taken as a power of
+//    two), q is first scaled by s, which is exact too.
 //    A lane's partial dots for the G heads go through a transposed butterfly over
 //    the LPK lanes, on DPP moves only (group_reduce.h).  Slot j of a lane holds
 //    head (j ^ myhead), so each stage adds a partner's slots to its own lower half
@@ -66,17 +69,31 @@ __device__ __forceinline__ uint32_t dw(const uint4& c, int i) {
 }
 __device__ __forceinline__ uint32_t dw(const uint2& c, int i) { return i == 0 ? c.x : c.y; }
 
-// K chunk -> four bf16 pairs.  BF16: as loaded.  INT8: u = c + 128 per element,
-// exact in bf16; the caller subtracts 128*sum(q).
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ f16x2 as_f16x2(uint32_t w) { return __builtin_bit_cast(f16x2, w); }
+__device__ __forceinline__ float f16_lo(uint32_t w) { return (float)as_f16x2(w).x; }
+__device__ __forceinline__ float f16_hi(uint32_t w) { return (float)as_f16x2(w).y; }
+// Round two floats to fp16 (nearest, ties to even) and pack.
+__device__ __forceinline__ uint32_t pack_f16_rne(float lo, float hi) {
+    f16x2 v = {(_Float16)lo, (_Float16)hi};
+    return __builtin_bit_cast(uint32_t, v);
+}
+
+// K chunk -> four pairs for the q.k dot2.  BF16: the bf16 pairs as loaded.
+// INT8: fp16 pairs 1152 + c, exact.  The byte u = c + 128 (the code with its sign
+// bit flipped) becomes the low byte of the fp16 word 0x64uu = 1024 + u, so one
+// byte permute against the constant 0x64 bytes builds two elements; the caller
+// subtracts 1152*sum(q).
 __device__ __forceinline__ void k_pairs(const uint4& c, uint32_t (&k)[4]) {
     k[0] = c.x; k[1] = c.y; k[2] = c.z; k[3] = c.w;
 }
+constexpr float kK8Offset = 1152.0f;
 __device__ __forceinline__ void k_pairs(const uint2& c, uint32_t (&k)[4]) {
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
         const uint32_t u = dw(c, h) ^ 0x80808080u;
-        k[2 * h] = pack_hi16((float)(u & 0xffu), (float)((u >> 8) & 0xffu));
-        k[2 * h + 1] = pack_hi16((float)((u >> 16) & 0xffu), (float)(u >> 24));
+        k[2 * h] = __builtin_amdgcn_perm(0x64646464u, u, 0x04010400u);        // (u0, u1)
+        k[2 * h + 1] = __builtin_amdgcn_perm(0x64646464u, u, 0x04030402u);    // (u2, u3)
     }
 }
 
@@ -246,19 +263,44 @@ void decode_kernel(DecodeArgs a, const int32_t* __restrict__ block_table) {
                                             bf16_hi(q[j][w]) * smooth_pow2(sv[2 * w + 1]));
         }
     }
-    float qbias = 0.0f;   // INT8: 128 * sum_d q[myhead][d]
+    float c2 = a.sm_scale * kLog2e;      // scores kept in log2 units
+    float qbias = 0.0f;   // INT8: 1152 * sum_d q'[myhead][d]
     if constexpr (INT8) {
+        // q meets the fp16 key pairs in fp16.  Each head is first scaled by the
+        // power of two 2^sh that brings its largest |q| into [2^14, 2^15); a bf16
+        // element then converts exactly unless it is more than 2^28 below that
+        // largest one (a subnormal in fp16), where the rounding is below the fp32
+        // summation error of the dot.  The score is scaled back by 2^-sh.
+        __shared__ uint32_t qmax[G];
+        if (lane < G) qmax[lane] = 0u;
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+        for (int j = 0; j < G; ++j) {
+            uint32_t mx = 0u;   // bit patterns of |bf16| order as the values do
+#pragma unroll
+            for (int w = 0; w < 4; ++w) mx = max(mx, max(q[j][w] & 0x7fffu, (q[j][w] >> 16) & 0x7fffu));
+            atomicMax(&qmax[j ^ myhead], mx);
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
         float part[G];
 #pragma unroll
         for (int j = 0; j < G; ++j) {
+            const int sh = min(141 - (int)(qmax[j ^ myhead] >> 7), 127);   // 14 - exponent of the max
             float t = 0.0f;
 #pragma unroll
-            for (int w = 0; w < 4; ++w) t += bf16_lo(q[j][w]) + bf16_hi(q[j][w]);
+            for (int w = 0; w < 4; ++w) {
+                q[j][w] = pack_f16_rne(ldexpf(bf16_lo(q[j][w]), sh), ldexpf(bf16_hi(q[j][w]), sh));
+                t += f16_lo(q[j][w]) + f16_hi(q[j][w]);
+            }
             part[j] = t;
+            if (j == 0) c2 = ldexpf(c2, -sh);   // slot 0 is this lane's own head
         }
-        qbias = 128.0f * transpose_reduce<LPK, G>(part);
+        qbias = kK8Offset * transpose_reduce<LPK, G>(part);
     }
-    const float c2 = a.sm_scale * kLog2e;      // scores kept in log2 units
 
     const int p0 = lo / kPage, p1 = (hi - 1) / kPage;
     const int32_t* bt = block_table + (int64_t)b * a.bt_stride;
@@ -320,17 +362,19 @@ void decode_kernel(DecodeArgs a, const int32_t* __restrict__ block_table) {
 #pragma unroll
             for (int j = 0; j < G; ++j) {
                 float t = 0.0f;
-                int w0 = 0;
-                if constexpr (INT8 && PAIRED) {
+                if constexpr (INT8) {
                     // the chain's first product in the three-operand form with a zero
                     // addend (the compiler otherwise zeroes a register and accumulates
                     // in place: one more VALU op per head and key)
-                    asm("v_dot2_f32_bf16 %0, %1, %2, 0" : "=v"(t) : "v"(q[j][0]), "v"(kp[0]));
-                    w0 = 1;
-                }
+                    asm("v_dot2_f32_f16 %0, %1, %2, 0" : "=v"(t) : "v"(q[j][0]), "v"(kp[0]));
 #pragma unroll
-                for (int w = w0; w < 4; ++w)
-                    t = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(q[j][w]), as_bf16x2(kp[w]), t, false);
+                    for (int w = 1; w < 4; ++w)
+                        t = __builtin_amdgcn_fdot2(as_f16x2(q[j][w]), as_f16x2(kp[w]), t, false);
+                } else {
+#pragma unroll
+                    for (int w = 0; w < 4; ++w)
+                        t = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(q[j][w]), as_bf16x2(kp[w]), t, false);
+                }
                 acc[j] = t;
             }
             float dot = transpose_reduce<LPK, G>(acc);
@@ -439,19 +483,26 @@ void decode_kernel(DecodeArgs a, const int32_t* __restrict__ block_table) {
         pb ^= 1;
     };
     // page p is consumed from one register set while page p+1 loads into the other
-    PageRegs rn;
     if constexpr (kScalarIds<G, INT8>) {
-        load_page(page_id(p0), rn);
+        // two sets used in turn (a copy from one to the other would cost a move per
+        // register and page)
+        PageRegs ra, rb;
+        load_page(page_id(p0), ra);
         int nid = page_id(p0 + 1);
-        for (int p = p0; p <= p1; ++p) {
-            PageRegs rc = rn;
-            if (p < p1) {
-                load_page(nid, rn);
-                nid = page_id(p + 2);
+        int p = p0;
+        for (; p < p1; p += 2) {
+            load_page(nid, rb);
+            nid = page_id(p + 2);
+            page(p, ra);
+            if (p + 1 < p1) {
+                load_page(nid, ra);
+                nid = page_id(p + 3);
             }
-            page(p, rc);
+            page(p + 1, rb);
         }
+        if (p == p1) page(p, ra);
     } else {
+        PageRegs rn;
         const int32_t* vbt = a.block_table + (int64_t)b * a.bt_stride;
         load_page(__ldg(vbt + p0), rn);
         for (int p = p0; p <= p1; ++p) {

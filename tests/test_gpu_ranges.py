@@ -173,3 +173,27 @@ def test_decode_int8_value_magnitudes(ci):
         for b in range(case.batch):
             sb = float(np.max(np.abs(ref[b])))
             assert np.max(np.abs(got[b] - ref[b])) <= INT8_TOL["max_abs"] * sb, f"sequence {b}"
+
+
+# ---------------------------------------------------------------------------
+# INT8 query magnitudes: the INT8 kernels take q in fp16 after a per-head power-
+# of-two scale; heads far apart in magnitude, a zero head, and elements far below
+# their head's largest (fp16 subnormals after the scale) must not matter
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("G", [8, 4, 1])
+def test_decode_int8_query_magnitudes(G):
+    Hkv = 4 if G == 8 else 2
+    Hq = G * Hkv
+    case = W.make_case(f"qm_g{G}", 490 + G, P(Hq, Hkv, 128, kv="int8", seed=G), [77, 1500, 2048],
+                       [1, 1, 1], outlier_frac=0.01)
+    x = (case.q.astype(np.uint32) << np.uint32(16)).view(np.float32).copy()   # [B, Hq, D]
+    exps = np.array([4, -24, 0, -7, 2, -15, 1, -3] * 4)[:Hq].astype(np.float32)
+    x *= np.exp2(exps)[None, :, None]
+    x[:, 1] = 0.0                                   # a head that is all zero
+    x[:, 0, ::17] *= np.float32(2.0 ** -40)         # elements far below their head's largest
+    case.q = (x.view(np.uint32) >> np.uint32(16)).astype(np.uint16)   # power-of-two scaling: exact in bf16
+    g = GpuCase(case)
+    ref = O.decode(case.q, oracle_pool(case), case.block_table, case.seq_lens, case.p)
+    for S in (0, 256):
+        assert_close(g.decode(split_keys=S), ref, INT8_TOL, f"int8 query magnitudes G={G} S={S}")
