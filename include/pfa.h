@@ -37,10 +37,14 @@
  *  - Errors: host-checkable problems return a status and launch nothing.  That
  *    covers NULL pointers, inconsistent sizes and unsupported shapes.  A failed
  *    launch returns PFA_ERR_HIP, and pfa_last_hip_error() then gives the hipError_t
- *    code (thread-local).  Device-resident contents are the caller's contract: valid
- *    page ids and seq_lens[s] <= bt_stride*P.  The kernels clamp page ids and
- *    lengths so that a broken contract gives wrong numbers, never an access outside
- *    the pool.
+ *    code (thread-local).  Device-resident contents are the caller's contract:
+ *    block-table entries in [0, num_pages), 0 <= seq_lens[s] <= bt_stride*P, each
+ *    sequence's new-token count (from cu_q / cu_new) between 0 and seq_lens[s]
+ *    (and at most max_q_len), and cu arrays that stay inside the q/out tensors.
+ *    The kernels clamp page ids and lengths so that a broken page id or length
+ *    gives wrong numbers, never an access outside the pool or the block table.  A
+ *    debug build of the library (PFA_BOUNDS_CHECK=1, libpfa_debug.so) also reports
+ *    such violations: see pfa_bounds_errors.
  *
  * Supported shapes: head_dim 64 or 128; page_size 16; Hq % Hkv == 0.
  *  - Decode: group size G = Hq/Hkv in {1,2,4,8}; BF16, INT8 or TQ3 K/V.
@@ -396,6 +400,24 @@ int32_t pfa_decode_num_splits(int32_t max_seq_len, int32_t split_keys);
  * arithmetic only.
  */
 size_t pfa_decode_workspace_bytes(const pfa_attn_desc* desc, int32_t batch, int32_t max_splits);
+
+/*
+ * pfa_bounds_errors: the device-side contract violations the kernels met on the
+ * current device since the last call, as PFA_BOUNDS_* bits in *flags; the word is
+ * then cleared.  Only a library built with PFA_BOUNDS_CHECK=1 (libpfa_debug.so)
+ * checks: its kernels test each block-table entry they read against
+ * [0, num_pages) and each length against its limits, and OR a bit into a device
+ * error word.  Both builds clamp the same way, so a violation still yields wrong
+ * numbers and no access outside the pool; the debug build also says so.  This
+ * call synchronises the device (it is a debugging aid, not a hot-path call).  The
+ * normal build returns PFA_ERR_UNSUPPORTED and sets *flags to 0.  PFA_ERR_NULL if
+ * flags is NULL.
+ */
+#define PFA_BOUNDS_PAGE 1u     /* a block-table entry outside [0, num_pages)                   */
+#define PFA_BOUNDS_SEQ_LEN 2u  /* seq_lens[s] < 0 or > bt_stride*P, or beyond the keys the      */
+                               /* call covers (max_splits * split_keys)                        */
+#define PFA_BOUNDS_Q_LEN 4u    /* a new-token count < 0, > seq_lens[s], or > max_q_len          */
+pfa_status pfa_bounds_errors(uint32_t* flags);
 
 /* Static description of a status code; never NULL. */
 const char* pfa_status_string(pfa_status status);

@@ -29,8 +29,11 @@ EXPORTS = ("pfa_kv_write", "pfa_attn_input", "pfa_paged_attn_decode", "pfa_paged
            "pfa_paged_attn_decode_static", "pfa_paged_attn_combine",
            "pfa_paged_attn_prefill", "pfa_paged_attn_verify", "pfa_decode_num_splits",
            "pfa_decode_workspace_bytes",
-           "pfa_prefill_num_splits", "pfa_verify_num_splits", "pfa_tq3_codebook", "pfa_status_string",
-           "pfa_last_hip_error")
+           "pfa_prefill_num_splits", "pfa_verify_num_splits", "pfa_tq3_codebook", "pfa_bounds_errors",
+           "pfa_status_string", "pfa_last_hip_error")
+
+# pfa_bounds_errors bits (debug build)
+BOUNDS_PAGE, BOUNDS_SEQ_LEN, BOUNDS_Q_LEN = 1, 2, 4
 
 
 class PfaError(RuntimeError):
@@ -60,7 +63,8 @@ class CKvPool(ctypes.Structure):
                 ("num_pages", ctypes.c_int32), ("k_smooth", ctypes.c_void_p)]
 
 
-AUDIT_LIB_PATH = os.path.join(_HERE, "libpfa_audit.so")   # prefill barrier-audit build (tests)
+# debug build: prefill barrier audit + device-side bounds checks (tests, debugging)
+DEBUG_LIB_PATH = os.path.join(_HERE, "libpfa_debug.so")
 
 _lib = None
 
@@ -74,8 +78,8 @@ def lib() -> ctypes.CDLL:
 
 
 def use_library(L: Optional[ctypes.CDLL]) -> Optional[ctypes.CDLL]:
-    """Route the entry points below through another loaded build (e.g. the audit
-    build, from load_library(AUDIT_LIB_PATH)); None restores libpfa.so.  Returns
+    """Route the entry points below through another loaded build (e.g. the debug
+    build, from load_library(DEBUG_LIB_PATH)); None restores libpfa.so.  Returns
     the build used before."""
     global _lib
     prev = _lib
@@ -114,6 +118,8 @@ def load_library(path: str) -> ctypes.CDLL:
     L.pfa_verify_num_splits.restype = ctypes.c_int32
     L.pfa_tq3_codebook.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.POINTER(ctypes.c_float)]
     L.pfa_tq3_codebook.restype = ctypes.c_int
+    L.pfa_bounds_errors.argtypes = [ctypes.POINTER(ctypes.c_uint32)]
+    L.pfa_bounds_errors.restype = ctypes.c_int
     L.pfa_status_string.argtypes = [ctypes.c_int]
     L.pfa_status_string.restype = ctypes.c_char_p
     L.pfa_last_hip_error.argtypes = []
@@ -444,7 +450,17 @@ def paged_attn_verify(desc: AttnDesc, pool: KVPool, q, cu_q, block_table, seq_le
     _check("pfa_paged_attn_verify", st)
 
 
-__all__ = ["AttnDesc", "KVPool", "PfaError", "EXPORTS", "lib", "kv_write", "attn_input", "decode_num_splits",
+def bounds_errors() -> int:
+    """The PFA_BOUNDS_* bits the kernels of the loaded build reported on the current
+    device since the last call (then cleared); synchronises the device.  Raises
+    PfaError (PFA_ERR_UNSUPPORTED) on the normal build, which does not check."""
+    flags = ctypes.c_uint32(0)
+    _check("pfa_bounds_errors", lib().pfa_bounds_errors(ctypes.byref(flags)))
+    return int(flags.value)
+
+
+__all__ = ["AttnDesc", "KVPool", "PfaError", "EXPORTS", "lib", "kv_write", "bounds_errors",
+           "DEBUG_LIB_PATH", "load_library", "use_library", "attn_input", "decode_num_splits",
            "decode_workspace_bytes",
            "tq3_codebook", "paged_attn_decode_static", "STATIC_SCRATCH_BYTES",
            "prefill_num_splits", "verify_num_splits", "paged_attn_decode", "paged_attn_decode_fused",

@@ -4,9 +4,12 @@
 
 Each .hip source under csrc/ is compiled to an object in _build/, then linked
 in-tree as paged_flash_attention_amd/libpfa.so.  A second library,
-libpfa_audit.so, is the same code built with PFA_PREFILL_AUDIT=1 (every prefill
-ring step waits for all loads and all waves); a GPU test checks that the normal
-build gives the same bits.
+libpfa_debug.so, is the same code built with
+  PFA_PREFILL_AUDIT=1  every prefill ring step waits for all loads and all waves
+                       (a GPU test checks that the normal build gives the same bits);
+  PFA_BOUNDS_CHECK=1   the kernels report block-table entries and lengths outside
+                       the device-side contract in an error word
+                       (pfa_bounds_errors).
 """
 from __future__ import annotations
 
@@ -39,7 +42,8 @@ def sources():
     return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
 
 
-AUDIT_LIB = os.path.join(HERE, "libpfa_audit.so")
+DEBUG_LIB = os.path.join(HERE, "libpfa_debug.so")
+DEBUG_DEFINES = ("PFA_PREFILL_AUDIT=1", "PFA_BOUNDS_CHECK=1")
 
 
 def compile_one(src: str, outdir: str = BUILD, defines=()) -> str:
@@ -56,14 +60,14 @@ def compile_one(src: str, outdir: str = BUILD, defines=()) -> str:
 
 
 def build(jobs: int = 8) -> str:
-    audit_dir = os.path.join(BUILD, "audit")
-    os.makedirs(audit_dir, exist_ok=True)
+    debug_dir = os.path.join(BUILD, "debug")
+    os.makedirs(debug_dir, exist_ok=True)
     srcs = sources()
     with cf.ThreadPoolExecutor(max_workers=max(1, jobs)) as ex:
         objs = ex.map(compile_one, srcs)
-        audit_objs = ex.map(lambda f: compile_one(f, audit_dir, ("PFA_PREFILL_AUDIT=1",)), srcs)
-        objs, audit_objs = list(objs), list(audit_objs)
-    link(audit_objs, AUDIT_LIB)
+        debug_objs = ex.map(lambda f: compile_one(f, debug_dir, DEBUG_DEFINES), srcs)
+        objs, debug_objs = list(objs), list(debug_objs)
+    link(debug_objs, DEBUG_LIB)
     return link(objs, LIB)
 
 

@@ -109,9 +109,48 @@ pfa_status static_scratch(void** ptr) {
     return PFA_OK;
 }
 
+// The device error word of the bounds-check build (PFA_BOUNDS_CHECK=1), one per
+// GPU; its address comes from hipGetSymbolAddress once per device, like the
+// scratch array's.  The normal build passes no error word to its kernels.
+static __device__ uint32_t bounds_word;
+
+pfa_status bounds_word_ptr(uint32_t** ptr) {
+    *ptr = nullptr;
+    if constexpr (!pfa::kBoundsCheck) return PFA_OK;
+    static std::mutex mu;
+    static void* addr[kMaxDevices] = {};
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_status(e);
+    if (dev < 0 || dev >= kMaxDevices) return PFA_ERR_UNSUPPORTED;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!addr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(bounds_word));
+        if (e != hipSuccess) return hip_status(e);
+        if (!p) return PFA_ERR_HIP;
+        addr[dev] = p;
+    }
+    *ptr = static_cast<uint32_t*>(addr[dev]);
+    return PFA_OK;
+}
+
 }  // namespace
 
 extern "C" {
+
+pfa_status pfa_bounds_errors(uint32_t* flags) {
+    if (!flags) return PFA_ERR_NULL;
+    *flags = 0u;
+    if constexpr (!pfa::kBoundsCheck) return PFA_ERR_UNSUPPORTED;
+    uint32_t* w = nullptr;
+    PFA_TRY(bounds_word_ptr(&w));
+    PFA_TRY(hip_status(hipDeviceSynchronize()));
+    PFA_TRY(hip_status(hipMemcpy(flags, w, sizeof(uint32_t), hipMemcpyDeviceToHost)));
+    const uint32_t zero = 0u;
+    PFA_TRY(hip_status(hipMemcpy(w, &zero, sizeof(uint32_t), hipMemcpyHostToDevice)));
+    return PFA_OK;
+}
 
 pfa_status pfa_kv_write(const pfa_attn_desc* desc, const pfa_kv_pool* pool, const void* k_new,
                         const void* v_new, const int32_t* cu_new, const int32_t* seq_lens,
@@ -144,6 +183,7 @@ pfa_status pfa_kv_write(const pfa_attn_desc* desc, const pfa_kv_pool* pool, cons
     a.num_kv_heads = desc->num_kv_heads;
     a.head_dim = desc->head_dim;
     a.book = tq3_book();
+    PFA_TRY(bounds_word_ptr(&a.err));
     return hip_status(pfa::launch_kv_write(a, desc->kv_dtype, (hipStream_t)stream));
 }
 
@@ -186,6 +226,7 @@ pfa_status pfa_attn_input(const pfa_attn_desc* desc, const pfa_kv_pool* pool,
     a.num_q_heads = desc->num_q_heads;
     a.num_kv_heads = desc->num_kv_heads;
     a.rope_max_pos = prm->rope_max_pos;
+    PFA_TRY(bounds_word_ptr(&a.err));
     return hip_status(pfa::launch_attn_input(a, desc->head_dim, desc->kv_dtype == PFA_KV_INT8,
                                              (hipStream_t)stream));
 }
@@ -263,6 +304,7 @@ pfa_status decode_like(const pfa_attn_desc* desc, const pfa_kv_pool* pool, const
     a.max_splits = max_splits;
     a.window = desc->window;
     a.sm_scale = desc->sm_scale;
+    PFA_TRY(bounds_word_ptr(&a.err));
     if (desc->kv_dtype == PFA_KV_TQ3)
         return hip_status(pfa::launch_decode_tq3(a, desc->head_dim, tq3_book(), (hipStream_t)stream));
     return hip_status(pfa::launch_decode(a, desc->head_dim, desc->kv_dtype == PFA_KV_INT8,
@@ -393,6 +435,7 @@ pfa_status prefill_like(const pfa_attn_desc* desc, const pfa_kv_pool* pool, cons
     a.split_keys = max_splits > 1 ? split_keys : 0;
     a.max_splits = max_splits;
     a.sm_scale = desc->sm_scale;
+    PFA_TRY(bounds_word_ptr(&a.err));
     if (!split_build) return hip_status(pfa::launch_prefill(a, desc->head_dim, (hipStream_t)stream));
     PFA_TRY(hip_status(pfa::launch_prefill_split(a, desc->head_dim, (hipStream_t)stream)));
     if (max_splits == 1) return PFA_OK;

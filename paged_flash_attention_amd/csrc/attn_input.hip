@@ -67,11 +67,14 @@ __global__ __launch_bounds__(256) void attn_input_kernel(AttnInputArgs a) {
     const int s = __builtin_amdgcn_readfirstlane(wave_find_seq(a.cu_new, a.batch, tok));
     const int c0 = __ldg(a.cu_new + s), c1 = __ldg(a.cu_new + s + 1);
     const int pos = __ldg(a.seq_lens + s) - (c1 - c0) + (tok - c0);
+    report(a.err, pos < 0, PFA_BOUNDS_Q_LEN);
+    report(a.err, pos >= 0 && pos / kPage >= a.bt_stride, PFA_BOUNDS_SEQ_LEN);
     bool slot_ok = tok < c1 && pos >= 0 && pos / kPage < a.bt_stride;
     int64_t slot0 = 0;              // (page * Hkv) * P + offset: add kvh * P
     if (slot_ok) {
         const int page = __ldg(a.block_table + (int64_t)s * a.bt_stride + pos / kPage);
         slot_ok = page >= 0 && page < a.num_pages;
+        report(a.err, !slot_ok, PFA_BOUNDS_PAGE);
         slot0 = (int64_t)page * Hkv * kPage + (pos % kPage);
     }
     const int prow = min(max(pos, 0), a.rope_max_pos - 1);

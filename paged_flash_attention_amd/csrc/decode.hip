@@ -186,6 +186,9 @@ void decode_kernel(DecodeArgs a, const int32_t* __restrict__ block_table) {
     const int64_t row0 = (int64_t)b * Hq + head0;                // (b, head0)
 
     int len = __ldg(a.seq_lens + b);
+    report(a.err, len < 0 || len > a.bt_stride * kPage ||
+                      (!FINAL && sp == 0 && (int64_t)a.max_splits * a.split_keys < len),
+           PFA_BOUNDS_SEQ_LEN);
     len = min(max(len, 0), a.bt_stride * kPage);
     int lo = a.window > 0 ? max(0, len - a.window) : 0;         // first visible key
     int hi = len;
@@ -319,6 +322,7 @@ void decode_kernel(DecodeArgs a, const int32_t* __restrict__ block_table) {
     // ahead of the loads that use it
     auto page_id = [&](int p) __attribute__((always_inline)) { return __ldg(bt + min(p, p1)); };
     auto load_page = [&](int raw_id, PageRegs& r) __attribute__((always_inline)) {
+        report(a.err, raw_id < 0 || raw_id >= a.num_pages, PFA_BOUNDS_PAGE);
         const int id = min(max(raw_id, 0), a.num_pages - 1);
         const int64_t blk = (int64_t)id * Hkv + kvh;
         const char* kp = kbase + blk * head_stride * EB + lane_off;

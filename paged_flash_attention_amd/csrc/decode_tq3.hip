@@ -63,6 +63,9 @@ __global__ __launch_bounds__(kWave) void decode_tq3_kernel(DecodeArgs a, Tq3Book
     const int64_t row0 = (int64_t)b * Hq + head0;
 
     int len = __ldg(a.seq_lens + b);
+    report(a.err, len < 0 || len > a.bt_stride * kPage ||
+                      (!FINAL && sp == 0 && (int64_t)a.max_splits * a.split_keys < len),
+           PFA_BOUNDS_SEQ_LEN);
     len = min(max(len, 0), a.bt_stride * kPage);
     int lo = a.window > 0 ? max(0, len - a.window) : 0;
     int hi = len;
@@ -122,7 +125,9 @@ __global__ __launch_bounds__(kWave) void decode_tq3_kernel(DecodeArgs a, Tq3Book
     uint32_t kb[NS][3], vb[NS][3];
     float ks[NS], vs[NS];
     auto page_block = [&](int p) __attribute__((always_inline)) {
-        const int id = min(max(__ldg(bt + p), 0), a.num_pages - 1);
+        const int raw = __ldg(bt + p);
+        report(a.err, raw < 0 || raw >= a.num_pages, PFA_BOUNDS_PAGE);
+        const int id = min(max(raw, 0), a.num_pages - 1);
         return ((int64_t)id * Hkv + kvh) * kPage;          // first vector of the (page, head) block
     };
     auto load_step = [&](int64_t blk, int r) __attribute__((always_inline)) {

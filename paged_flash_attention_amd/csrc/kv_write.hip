@@ -43,10 +43,13 @@ __global__ __launch_bounds__(256) void kv_write_kernel(KvWriteArgs a) {
         const int c0 = __ldg(a.cu_new + s), c1 = __ldg(a.cu_new + s + 1);
         const int pos = __ldg(a.seq_lens + s) - (c1 - c0) + (tok - c0);
         const int pidx = pos / kPage;
+        report(a.err, pos < 0, PFA_BOUNDS_Q_LEN);
+        report(a.err, pos >= 0 && pidx >= a.bt_stride, PFA_BOUNDS_SEQ_LEN);
         ok = tok < c1 && pos >= 0 && pidx < a.bt_stride;
         if (ok) {
             const int page = __ldg(a.block_table + (int64_t)s * a.bt_stride + pidx);
             ok = page >= 0 && page < a.num_pages;
+            report(a.err, !ok, PFA_BOUNDS_PAGE);
             sdst = ((int64_t)page * a.num_kv_heads + head) * kPage + (pos % kPage);
             dst = sdst * D + chunk * 8;
         }
@@ -122,10 +125,13 @@ __global__ __launch_bounds__(256) void kv_write_tq3_kernel(KvWriteArgs a) {
         const int c0 = __ldg(a.cu_new + s), c1 = __ldg(a.cu_new + s + 1);
         const int pos = __ldg(a.seq_lens + s) - (c1 - c0) + (tok - c0);
         const int pidx = pos / kPage;
+        report(a.err, pos < 0, PFA_BOUNDS_Q_LEN);
+        report(a.err, pos >= 0 && pidx >= a.bt_stride, PFA_BOUNDS_SEQ_LEN);
         ok = tok < c1 && pos >= 0 && pidx < a.bt_stride;
         if (ok) {
             const int page = __ldg(a.block_table + (int64_t)s * a.bt_stride + pidx);
             ok = page >= 0 && page < a.num_pages;
+            report(a.err, !ok, PFA_BOUNDS_PAGE);
             sdst = ((int64_t)page * a.num_kv_heads + head) * kPage + (pos % kPage);
         }
     }

@@ -6,6 +6,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "pfa.h"
+
 namespace pfa {
 
 constexpr int kWave = 64;
@@ -145,6 +147,23 @@ struct Tq3Book {
     float t[3];
 };
 
+// Bounds-check build (PFA_BOUNDS_CHECK=1): the kernels also report violations of
+// the device-side contract (page ids, lengths) by OR-ing PFA_BOUNDS_* bits into
+// an error word (Args::err).  The clamps that keep every access in bounds are the
+// same in both builds.
+#ifndef PFA_BOUNDS_CHECK
+#define PFA_BOUNDS_CHECK 0
+#endif
+constexpr bool kBoundsCheck = PFA_BOUNDS_CHECK != 0;
+
+// One lane of the active ones ORs `bit` into *err when any of them is `bad`.
+__device__ __forceinline__ void report(uint32_t* err, bool bad, uint32_t bit) {
+    if constexpr (kBoundsCheck) {
+        const uint64_t m = __ballot(bad);
+        if (m != 0 && __lane_id() == (unsigned)(__ffsll((unsigned long long)m) - 1)) atomicOr(err, bit);
+    }
+}
+
 struct KvWriteArgs {
     const uint16_t* k_new;
     const uint16_t* v_new;
@@ -158,6 +177,8 @@ struct KvWriteArgs {
     const float* k_smooth;      // INT8: [D] per-channel key smoothing, or NULL
     int32_t bt_stride, batch, num_tokens, num_pages, num_kv_heads, head_dim;
     Tq3Book book;               // 3-bit pools only
+
+    uint32_t* err;             // bounds-check build: the error word; else NULL
 };
 
 struct DecodeArgs {
@@ -177,6 +198,7 @@ struct DecodeArgs {
     int32_t bt_stride, batch, num_pages, num_q_heads, num_kv_heads;
     int32_t split_keys, max_splits, window;
     float sm_scale;
+    uint32_t* err;             // bounds-check build: the error word; else NULL
 };
 
 struct AttnInputArgs {
@@ -195,6 +217,8 @@ struct AttnInputArgs {
     const float* k_smooth;      // INT8: [D] per-channel key smoothing, or NULL
     float eps;
     int32_t bt_stride, batch, num_tokens, num_pages, num_q_heads, num_kv_heads, rope_max_pos;
+
+    uint32_t* err;             // bounds-check build: the error word; else NULL
 };
 
 struct CombineArgs {
@@ -225,6 +249,8 @@ struct PrefillArgs {
     int32_t bt_stride, batch, num_pages, num_q_heads, num_kv_heads, max_q_len, window;
     int32_t split_keys, max_splits;   // max_splits == 1: no split
     float sm_scale;
+
+    uint32_t* err;             // bounds-check build: the error word; else NULL
 };
 
 // kv_dtype: 0 bf16, 1 int8, 2 3-bit rotated

@@ -213,8 +213,17 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a, const 
     const int cq0 = __ldg(a.cu_q + b);
     const int q_len = __ldg(a.cu_q + b + 1) - cq0;
     const int tok0 = tile * TPB;
+    const int n_raw = __ldg(a.seq_lens + b);
+    if constexpr (kBoundsCheck) {
+        if (tile == 0 && split == 0) {
+            report(a.err, n_raw < 0 || n_raw > a.bt_stride * kPage ||
+                              (SPLIT && (int64_t)a.max_splits * a.split_keys < n_raw),
+                   PFA_BOUNDS_SEQ_LEN);
+            report(a.err, q_len < 0 || q_len > a.max_q_len || q_len > n_raw, PFA_BOUNDS_Q_LEN);
+        }
+    }
     if (tok0 >= q_len) return;
-    const int n = min(__ldg(a.seq_lens + b), a.bt_stride * kPage);
+    const int n = min(max(n_raw, 0), a.bt_stride * kPage);
     const int prefix = n - q_len;
     const int Hq = a.num_q_heads;
     const int W = a.window;
@@ -297,11 +306,16 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a, const 
                   "a wave's rows lie in one page");
     const int wpage = wave * DMA_PER_WAVE * ROWS_PER_DMA / kPage;    // which page of the tile
     // raw block-table entry of a tile's page for this wave (a scalar load), and
-    // its clamp to the pool; the load is issued one tile before its value is used
+    // its clamp to the pool; the load is issued one tile before its value is used.
+    // The entry's index stays inside the sequence's row even when a broken length
+    // leaves no visible page (npg <= 0, or a tile range below 0).
     auto raw_page = [&](int kb) __attribute__((always_inline)) {
-        return __ldg(bt + min(kb * (kBN / kPage) + wpage, npg - 1));
+        return __ldg(bt + min(max(kb * (kBN / kPage) + wpage, 0), max(npg, 1) - 1));
     };
-    auto clamp_page = [&](int v) __attribute__((always_inline)) { return min(max(v, 0), a.num_pages - 1); };
+    auto clamp_page = [&](int v) __attribute__((always_inline)) {
+        report(a.err, v < 0 || v >= a.num_pages, PFA_BOUNDS_PAGE);
+        return min(max(v, 0), a.num_pages - 1);
+    };
     const int lrow = lane / CPR;                          // row within one direct load
     const int lchunk = lane % CPR;                        // physical chunk this lane fills
     // per-lane byte offsets within a page-head block (the same for every tile)

@@ -33,6 +33,24 @@ def test_library_exports_every_declared_symbol():
         assert hasattr(L, s), s
 
 
+def test_debug_build_exports_the_same_symbols_and_bounds_query():
+    """libpfa_debug.so (barrier audit + device-side bounds checks) exports the same
+    ABI.  pfa_bounds_errors: NULL flags -> PFA_ERR_NULL in both builds; the normal
+    build does not check and returns PFA_ERR_UNSUPPORTED with flags 0, before any
+    HIP call."""
+    D = pfa.load_library(pfa.DEBUG_LIB_PATH)
+    for s in header_symbols():
+        assert hasattr(D, s), s
+    assert D.pfa_bounds_errors(None) == NULL
+    L = pfa.lib()
+    assert L.pfa_bounds_errors(None) == NULL
+    f = ctypes.c_uint32(7)
+    assert L.pfa_bounds_errors(ctypes.byref(f)) == UNSUP
+    assert f.value == 0
+    with pytest.raises(pfa.PfaError, match="UNSUPPORTED"):
+        pfa.bounds_errors()
+
+
 def test_status_strings_and_splits():
     L = pfa.lib()
     for st in range(6):

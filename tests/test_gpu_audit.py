@@ -1,9 +1,10 @@
 """Barrier audit of the prefill kernels.  Their direct HBM -> LDS tile loads are
 issued as inline asm, which the compiler does not track, so the waits before a
 tile is read (each wave waits for its own loads of that tile, then one barrier)
-are placed by hand.  libpfa_audit.so is the same source built with
-PFA_PREFILL_AUDIT=1: every ring step waits for all of the wave's loads and then
-for all waves, before and after each refill.  If a hand-placed wait were too
+are placed by hand.  libpfa_debug.so is the same source built with
+PFA_PREFILL_AUDIT=1 (and the device-side bounds checks, which change no
+arithmetic): every ring step waits for all of the wave's loads and then for all
+waves, before and after each refill.  If a hand-placed wait were too
 short, the normal build would read a stage before its tile landed and its bits
 would differ from the audit build's; here they must be equal, on both kernel
 builds (64-key unsplit, 32-key split) and on verify steps."""
@@ -23,7 +24,7 @@ def audit_lib():
     if not torch.cuda.is_available():
         pytest.skip("no GPU")
     pfa.lib()
-    return pfa.load_library(pfa.AUDIT_LIB_PATH)
+    return pfa.load_library(pfa.DEBUG_LIB_PATH)
 
 
 AUDIT_CASES = [
