@@ -400,6 +400,47 @@ def run_verify_graph(case, torch, pfa, gs, steps, warmup):
     return dict(step_ms=t0.elapsed_time(t1) / steps, split_keys=sk, max_splits=ms, kv_bytes=verify_bytes(case))
 
 
+def run_decode_graph(case, torch, pfa, gs, steps, warmup):
+    """The decode step (kv_write + split decode + combine) captured once in a HIP graph
+    and replayed: the step without host launch gaps, which dominate a one-sequence
+    step.  One pool (its 16 MB stay in the MALL between replays)."""
+    g, _, (kn, vn, cun) = setup_case(case, torch, pfa, gs, copies_for_bytes=0)
+    p = case.p
+    B, Hq, D = case.batch, p.num_q_heads, p.head_dim
+    max_len = int(case.seq_lens.max())
+    S = case.split_keys
+    ms = pfa.decode_num_splits(max_len, S)
+    op = torch.empty((B, Hq, ms, D), device="cuda")
+    lp = torch.empty((B, Hq, ms), device="cuda")
+    out = torch.empty((B, Hq, D), device="cuda")
+
+    def step():
+        pfa.kv_write(g.desc, g.pool, kn, vn, cun, g.seq_lens, g.bt)
+        pfa.paged_attn_decode(g.desc, g.pool, g.q, g.bt, g.seq_lens, max_len, S, ms, o_part=op, lse_part=lp)
+        pfa.paged_attn_combine(g.desc, op, lp, g.seq_lens, S, ms, out)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    for _ in range(warmup):
+        graph.replay()
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(steps):
+        graph.replay()
+    t1.record()
+    torch.cuda.synchronize()
+    return dict(step_ms=t0.elapsed_time(t1) / steps, split_keys=S, max_splits=ms, decode_bytes=decode_bytes(case))
+
+
 # ---------------------------------------------------------------------------
 # CPU baseline: the oracle as it stands
 # ---------------------------------------------------------------------------
@@ -511,6 +552,7 @@ def main():
         "decode_batch32_ctx8192_s1024": lambda: W.decode_batch32_ctx512_8192(fixed_len=8192, split_keys=1024),
         "decode_batch32_ctx512_8192_fused": lambda: W.decode_batch32_ctx512_8192(),
         "decode_1seq_ctx1024": lambda: W.decode_1seq_ctx1024(),
+        "decode_1seq_ctx1024_graph": lambda: W.decode_1seq_ctx1024(),
         "decode_int8_batch8_ctx32768": lambda: W.decode_int8_qwen30b(),
         "decode_int8_batch8_ctx32768_smooth": lambda: W.decode_int8_qwen30b(smooth=True),
         "decode_tq3_batch8_ctx32768": lambda: W.decode_tq3_qwen30b(),
@@ -551,6 +593,10 @@ def main():
             gbs = r["kv_write_bytes"] / (r["kv_write_ms"] * 1e-3) / 1e9
             r.update(metric="kv write GB/s", kernel_gbs=round(gbs, 1), frac_of_hbm_peak=round(gbs / HBM_PEAK_GBS, 4))
             return case, r
+        if name.startswith("decode") and name.endswith("_graph"):
+            r = run_decode_graph(case, torch, pfa, gs, steps, warmup)
+            r.update(metric="decode step us (graph replay)")
+            return case, r
         if name.endswith("_graph"):
             r = run_verify_graph(case, torch, pfa, gs, steps, warmup)
             r.update(metric="verify step us (graph replay)")
@@ -589,8 +635,10 @@ def main():
                     frac=r["frac_of_hbm_peak"], traffic=None)
         case = case.case
     elif args.workload.endswith("_graph"):
-        value = r["kv_bytes"] / (r["step_ms"] * 1e-3) / 1e9
-        unit, metric = "GB/s", "verify step GB/s (HBM, graph replay)"
+        value = r.get("kv_bytes", r.get("decode_bytes", 0)) / (r["step_ms"] * 1e-3) / 1e9
+        unit = "GB/s"
+        metric = "decode step GB/s (graph replay)" if args.workload.startswith("decode") else \
+            "verify step GB/s (HBM, graph replay)"
         roof = dict(bound="hbm", achieved=round(value, 1), peak=HBM_PEAK_GBS, unit="GB/s",
                     frac=round(value / HBM_PEAK_GBS, 4), traffic=None)
     elif args.workload.startswith("verify"):
@@ -614,7 +662,8 @@ def main():
 
     extra = {}
     if not args.no_extra and args.workload == "decode_batch32_ctx512_8192":
-        for name, st in (("decode_1seq_ctx1024", 100), ("decode_batch32_ctx512_8192_fused", 50),
+        for name, st in (("decode_1seq_ctx1024", 100), ("decode_1seq_ctx1024_graph", 200),
+                         ("decode_batch32_ctx512_8192_fused", 50),
                          ("decode_batch32_ctx8192", 30), ("decode_batch32_ctx8192_s1024", 30),
                          ("decode_int8_batch8_ctx32768", 30), ("decode_int8_batch8_ctx32768_smooth", 30),
                          ("decode_tq3_batch8_ctx32768", 30),
@@ -652,6 +701,8 @@ def main():
                     extra[name] = dict(us=rr["decode_us"], gbs=rr["kernel_gbs"],
                                        frac_of_hbm_peak=rr["frac_of_hbm_peak"],
                                        step_us=round(rr["step_ms"] * 1e3, 2))
+                    if rr.get("combine_us") is not None:
+                        extra[name]["combine_us"] = rr["combine_us"]
             except Exception as e:   # report, never hide
                 extra[name] = dict(error=str(e)[:200])
             torch.cuda.empty_cache()
@@ -669,7 +720,7 @@ def main():
         "dtype": {"bf16": "bf16", "int8": "int8", "tq3": "fp32"}[p.kv_dtype], "data": "synthetic",
         "config": {"workload": case.name, "batch": case.batch, "q_heads": p.num_q_heads,
                    "kv_heads": p.num_kv_heads, "head_dim": p.head_dim, "page_size": p.page_size,
-                   "split_keys": case.split_keys if not is_prefill else None,
+                   "split_keys": r.get("split_keys", case.split_keys if not is_prefill else None),
                    "max_seq_len": int(case.seq_lens.max()), "window": p.window,
                    "sinks": p.sinks is not None, "parallelism": "single GPU"},
         "roofline": roof,

@@ -62,7 +62,7 @@ def _prefill_check(case, sample=None, seed=0, verify=False):
 
 
 def test_decode_1seq_ctx1024():
-    _decode_check(W.decode_1seq_ctx1024(), splits=(0, 256))
+    _decode_check(W.decode_1seq_ctx1024(), splits=(0, 64, 256))
 
 
 def test_decode_batch32_ctx512_8192():
