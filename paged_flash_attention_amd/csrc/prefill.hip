@@ -390,8 +390,9 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a, const 
                 }
                 ko[2 * i] = pack_hi16(kx[0], kx[1]);
                 ko[2 * i + 1] = pack_hi16(kx[2], kx[3]);
-                vo[2 * i] = live ? pack_bf16_rne(vx[0] * vs, vx[1] * vs) : 0u;
-                vo[2 * i + 1] = live ? pack_bf16_rne(vx[2] * vs, vx[3] * vs) : 0u;
+                // past the end vs is 0 and the codes are finite: the pair is (+-)0
+                vo[2 * i] = pack_bf16_rne(vx[0] * vs, vx[1] * vs);
+                vo[2 * i + 1] = pack_bf16_rne(vx[2] * vs, vx[3] * vs);
             }
 #pragma unroll
             for (int c = 0; c < EPT / 8; ++c) {
