@@ -214,9 +214,16 @@ def _expect(t: Optional[torch.Tensor], shape, dtype, name: str, optional: bool =
         raise ValueError(f"{name} is required")
     if t.dtype != dtype:
         raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
-    if t.dim() != len(shape) or any(w is not None and int(n) != int(w) for n, w in zip(t.shape, shape)):
+    sh = t.shape
+    ok = len(sh) == len(shape)
+    if ok:
+        for n, w in zip(sh, shape):
+            if w is not None and n != w:
+                ok = False
+                break
+    if not ok:
         want = "(" + ", ".join("*" if w is None else str(int(w)) for w in shape) + ")"
-        raise ValueError(f"{name} must have shape {want}, got {tuple(t.shape)}")
+        raise ValueError(f"{name} must have shape {want}, got {tuple(sh)}")
     return t
 
 
@@ -257,8 +264,15 @@ def _ptr(t: Optional[torch.Tensor]):
     return t.data_ptr()
 
 
+_raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+
+
 def _stream(stream, ref: torch.Tensor):
+    """The stream to enqueue on: `stream` (a torch stream or a raw hipStream_t), or
+    torch's current stream on ref's device."""
     if stream is None:
+        if _raw_stream is not None:
+            return ctypes.c_void_p(_raw_stream(ref.device.index))
         stream = torch.cuda.current_stream(ref.device)
     return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
 
