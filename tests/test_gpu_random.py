@@ -5,7 +5,7 @@ configurations that combine them (operation, head dim, GQA group, KV dtype, wind
 sinks, ragged lengths, split size) to catch interactions those cases miss.  Each
 case is drawn from its own seed, so a failure names a reproducible configuration.
 The draws stay inside the library's documented limits and sizes the oracle finishes
-in about a second.
+in about a second.  Draws 30 and on also put prefill and verify on INT8 caches.
 """
 import numpy as np
 import pytest
@@ -18,8 +18,9 @@ from gpu_support import BF16_TOL, GpuCase, assert_close, oracle_pool, pool_bits_
 
 pytestmark = pytest.mark.gpu
 
-N_CASES = 30
+N_CASES = 60
 OPS = ("decode", "decode", "fused", "prefill", "verify")
+INT8_PREFILL_FROM = 30     # draws from here on also put prefill and verify on an INT8 cache
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -37,6 +38,8 @@ def draw(i):
     if op in ("prefill", "verify"):
         kv = "bf16"
         G = int(rng.choice([1, 2, 4, 8, 16, 32]))
+        if i >= INT8_PREFILL_FROM:
+            kv = str(rng.choice(["bf16", "int8"]))
     else:
         kv = str(rng.choice(["bf16", "int8", "tq3"] if op == "decode" else ["bf16", "int8"]))
         G = int(rng.choice([1, 2, 4, 8]))
@@ -98,4 +101,4 @@ def test_random_config(i):
         max_len = max(lens)
         sp = {"auto": "auto", "none": None, "split": (64, -(-max_len // 64))}[split]
         got = g.prefill(split=sp) if op == "prefill" else g.verify(split=sp)
-        assert_close(got, ref, BF16_TOL, f"{op} split={split}")
+        assert_close(got, ref, tol, f"{op} split={split}")
