@@ -12,8 +12,12 @@
 // no visible key carry lse = -inf and weigh 0.  The leading run of such splits
 // is skipped without reading its o rows.
 //
-// One 64-lane wave per (row, h) runs merge_splits (merge_splits.h).
-// The work is tiny: rows*Hq*splits*(D+1)*4 bytes read.
+// Up to 128 splits, one 64-lane wave per (row, h, 64-element slice of D) runs
+// merge_splits_short, which has all the row's partials in flight at once, at the
+// smallest depth of 8, 16, 32, 64 and 128 that holds the row's split count.
+// Above 128, one wave per (row, h) runs the chunked merge_splits
+// (merge_splits.h).  The two give the same bits.
+// The work is tiny: rows*Hq*splits*(D+1)*4 bytes read, so the time is latency.
 #include "merge_splits.h"
 
 namespace pfa {
@@ -21,11 +25,17 @@ namespace {
 
 constexpr int kMaxLdsSplits = 1024;
 
-template <int D>
+// NS > 0: every row has at most NS <= 128 splits; a wave merges one 64-element
+// slice of D through merge_splits_short at the depth its row needs.  NS = 0: any
+// count, a wave per (row, head) through the chunked merge.
+template <int D, int NS>
 __global__ __launch_bounds__(64) void combine_kernel(CombineArgs a) {
-    __shared__ float w_lds[kMaxLdsSplits];
-    const int h = blockIdx.x % a.num_q_heads;
-    const int r = blockIdx.x / a.num_q_heads;
+    __shared__ float w_lds[NS > 0 ? 1 : kMaxLdsSplits];
+    constexpr int kSlices = NS > 0 ? D / kWave : 1;
+    const int slice = blockIdx.x % kSlices;
+    const int bh_id = blockIdx.x / kSlices;
+    const int h = bh_id % a.num_q_heads;
+    const int r = bh_id / a.num_q_heads;
     int row = r;
     int ns = a.max_splits;
     if (a.cu_rows) {
@@ -38,21 +48,37 @@ __global__ __launch_bounds__(64) void combine_kernel(CombineArgs a) {
         ns = min((len + a.split_keys - 1) / a.split_keys, a.max_splits);
     }
     const int64_t bh = (int64_t)row * a.num_q_heads + h;
-    merge_splits<D, kMaxLdsSplits>(a.lse_part + bh * a.max_splits, a.o_part + bh * a.max_splits * D, ns,
-                                   a.sinks ? a.sinks + h : nullptr, w_lds, a.out + bh * D);
+    const float* lse = a.lse_part + bh * a.max_splits;
+    const float* op = a.o_part + bh * a.max_splits * D;
+    const float* sink = a.sinks ? a.sinks + h : nullptr;
+    if constexpr (NS > 0)
+        merge_splits_short_any<D, NS>(lse, op + slice * kWave, max(ns, 0), sink, a.out + bh * D + slice * kWave);
+    else
+        merge_splits<D, kMaxLdsSplits>(lse, op, ns, sink, w_lds, a.out + bh * D);
+}
+
+template <int D>
+hipError_t launch_d(const CombineArgs& a, unsigned bh, hipStream_t s) {
+    const int n = a.max_splits;
+    const dim3 g(bh * (D / kWave)), b(64);
+    if (n <= 8) hipLaunchKernelGGL((combine_kernel<D, 8>), g, b, 0, s, a);
+    else if (n <= 16) hipLaunchKernelGGL((combine_kernel<D, 16>), g, b, 0, s, a);
+    else if (n <= 32) hipLaunchKernelGGL((combine_kernel<D, 32>), g, b, 0, s, a);
+    else if (n <= 64) hipLaunchKernelGGL((combine_kernel<D, 64>), g, b, 0, s, a);
+    else if (n <= 128) hipLaunchKernelGGL((combine_kernel<D, 128>), g, b, 0, s, a);
+    else hipLaunchKernelGGL((combine_kernel<D, 0>), dim3(bh), b, 0, s, a);
+    return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_combine(const CombineArgs& a, int head_dim, hipStream_t s) {
     const int64_t rows = a.cu_rows ? (int64_t)a.batch * a.rows_per_seq : a.batch;
-    const unsigned grid = (unsigned)(rows * a.num_q_heads);
-    if (grid == 0) return hipSuccess;
-    if (head_dim == 128)
-        hipLaunchKernelGGL((combine_kernel<128>), dim3(grid), dim3(64), 0, s, a);
-    else
-        hipLaunchKernelGGL((combine_kernel<64>), dim3(grid), dim3(64), 0, s, a);
-    return hipGetLastError();
+    const int64_t n = rows * a.num_q_heads;
+    if (n == 0) return hipSuccess;
+    if (n * (head_dim / kWave) > 0x7fffffff) return hipErrorInvalidValue;
+    const unsigned bh = (unsigned)n;
+    return head_dim == 128 ? launch_d<128>(a, bh, s) : launch_d<64>(a, bh, s);
 }
 
 }  // namespace pfa
