@@ -186,13 +186,16 @@ __global__ __launch_bounds__(kWave) void decode_tq3_kernel(DecodeArgs a, Tq3Book
             valid[r] = key >= lo && key < hi;
             s[r] = valid[r] ? dot * (ksr * c2) : -INFINITY;
         }
-        // ---- running max, lazy rescale ----
+        // ---- running max, lazy rescale with headroom: the reference max moves only
+        // when a head's max exceeds it by more than 8, so every weight is <= 2^8
+        // (no overflow in fp32 or bf16) and the rescale, G*8 multiplies, runs on
+        // few pages.  o and l share the reference, so o/l and m + log2(l) hold. ----
         float pm = s[0];
 #pragma unroll
         for (int r = 1; r < NS; ++r) pm = fmaxf(pm, s[r]);
         pm = stride_max<L>(pm);
         const float m_new = fmaxf(m_run, pm);
-        if (__any(m_new > m_run)) {
+        if (__any(m_new > m_run + 8.0f)) {
             const float alpha = fast_exp2(m_run - m_new);   // 0 on the first page
             l_run *= alpha;
 #pragma unroll
