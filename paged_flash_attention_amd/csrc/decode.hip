@@ -50,12 +50,14 @@
 //    weight can overflow or flush) and shares the pair through LDS:
 //      - BF16: the (v_a, v_b) pairs are built by v_perm; l sums the same rounded
 //        weights (a dot2 with (1, 1)), so numerator and denominator agree;
-//      - INT8: the code pairs are u = c + 128 (exact in bf16, from
-//        v_cvt_f32_ubyteN), and 128 * (the sum of the same rounded weights) is
-//        subtracted at the end.
-//  * At the end of a split each wave reduces its partial o across key groups and
-//    writes o/l with lse = ln(sum e^s) (split mode), or the final output with the
-//    sink (unsplit mode).
+//      - INT8: by columns.  The page's V codes go through LDS, and each lane owns
+//        the columns d = lane + 64c of all 16 keys (transposed 8-bit reads), so
+//        its o is 8 heads x D/64 columns instead of 8 heads x 8 elements of its
+//        key group: 205 -> 159 registers, 3 waves per SIMD (83 -> 77 us at batch
+//        8 x 32768).  The codes enter as signed bf16 (exact).
+//  * At the end of a split each wave reduces its partial o across key groups (INT8
+//    at G = 8: nothing to reduce) and writes o/l with lse = ln(sum e^s) (split
+//    mode), or the final output with the sink (unsplit mode).
 #include "group_reduce.h"
 #include "merge_splits.h"
 
@@ -139,6 +141,35 @@ __device__ __forceinline__ void v_pairs(const uint2& a, const uint2& b, uint32_t
     }
 }
 
+// Column p.v (INT8 at G = 8).  A page's V tile is staged in LDS with its rows in
+// key-pair order, and each lane reads the columns it owns (d = lane + 64c) for
+// 8 rows at a time with ds_read_b64_tr_b8: in each 16-lane group, lane j points
+// at row j/2, bytes 8(j%2)..+7 of an 8 x 16-byte block, and lane i receives
+// column i of the block, rows in order (checked on gfx950).  The codes enter the
+// dot2 as signed bf16 (exact), so no offset is carried.
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+#define LDS3 __attribute__((address_space(3)))
+// rows (2u, 2u+1) of a transposed read -> bf16 pair u, from the signed codes
+__device__ __forceinline__ void vcol_pairs(i32x2 x, uint32_t (&v)[4]) {
+    v[0] = pack_hi16((float)(int8_t)x.x, (float)(int8_t)(x.x >> 8));
+    v[1] = pack_hi16((float)(int8_t)(x.x >> 16), (float)(x.x >> 24));
+    v[2] = pack_hi16((float)(int8_t)x.y, (float)(int8_t)(x.y >> 8));
+    v[3] = pack_hi16((float)(int8_t)(x.y >> 16), (float)(x.y >> 24));
+}
+
+// An empty asm that makes x depend on every element of o: loads addressed by x
+// cannot then be hoisted above the code that produced o.
+template <int G, int N>
+__device__ __forceinline__ void order_after(uint32_t& x, float (&o)[G][N]) {
+    static_assert(G * N <= 16, "asm operands");
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+        if constexpr (N == 1) asm volatile("" : "+v"(x) : "v"(o[g][0]));
+        else asm volatile("" : "+v"(x) : "v"(o[g][0]), "v"(o[g][1]));
+    }
+}
+
 // Splits whose merge weights sit in LDS at a time, in the fused merge.
 constexpr int kFusedMergeChunk = 256;
 
@@ -162,6 +193,9 @@ void decode_kernel(DecodeArgs a, const int32_t* __restrict__ block_table) {
     constexpr int NLOAD = kPage / KPL;         // loads per page per tensor
     constexpr int HG = LPK / G;                // lanes holding each head after the reduce
     constexpr bool PAIRED = G >= 8;            // p.v by dot2 on key pairs
+    constexpr bool VCOL = INT8 && PAIRED;      // column p.v through an LDS V tile
+    constexpr int NC = D / kWave;              // VCOL: columns per lane
+    constexpr int OJ = VCOL ? NC : 8;          // o elements per lane and head
     static_assert(G <= LPK, "group size");
     static_assert(!PAIRED || NLOAD % 2 == 0, "key pairs");
     typedef typename Chunk<INT8>::T CT;
@@ -170,6 +204,10 @@ void decode_kernel(DecodeArgs a, const int32_t* __restrict__ block_table) {
     // G = 8 [key pair][key group][head] bf16 pairs
     __shared__ __attribute__((aligned(16))) float p_buf[2][kPage][G];
     __shared__ float w_lds[FINAL ? 1 : kFusedMergeChunk];
+    // VCOL: the page's V rows, row 2m + h holding key h of key pair m (the pair
+    // one lane's weights cover: keys kg + KPL*i and kg + KPL*(i+1), i even,
+    // m = KPL*(i/2) + kg)
+    __shared__ __attribute__((aligned(16))) int8_t v_lds[VCOL ? kPage * D : 16];
 
     const int lane = threadIdx.x;
     const int sub = lane % LPK;
@@ -316,7 +354,8 @@ void decode_kernel(DecodeArgs a, const int32_t* __restrict__ block_table) {
 
     // a page's K/V (and INT8 scales) as this lane loads them
     struct PageRegs {
-        CT k[NLOAD], v[NLOAD];
+        CT k[NLOAD], v[VCOL ? 1 : NLOAD];
+        uint32_t vt[VCOL ? D / 16 : 1];   // VCOL: 16-byte pieces of the V tile, 1024 bytes apart
         float ks[NLOAD], vs[NLOAD];
     };
     // a page's block-table entry (a scalar load; the index is clamped to the
@@ -332,7 +371,15 @@ void decode_kernel(DecodeArgs a, const int32_t* __restrict__ block_table) {
 #pragma unroll
         for (int i = 0; i < NLOAD; ++i) {
             r.k[i] = *reinterpret_cast<const CT*>(kp + i * 512 * EB);
-            r.v[i] = *reinterpret_cast<const CT*>(vp + i * 512 * EB);
+            if constexpr (!VCOL) r.v[i] = *reinterpret_cast<const CT*>(vp + i * 512 * EB);
+        }
+        if constexpr (VCOL) {
+            const char* vt = vbase + blk * head_stride + 16 * lane;
+#pragma unroll
+            for (int c = 0; c < D / 64; ++c) {
+                const uint4 x = *reinterpret_cast<const uint4*>(vt + 1024 * c);
+                r.vt[4 * c] = x.x; r.vt[4 * c + 1] = x.y; r.vt[4 * c + 2] = x.z; r.vt[4 * c + 3] = x.w;
+            }
         }
         if constexpr (INT8) {
 #pragma unroll
@@ -343,19 +390,33 @@ void decode_kernel(DecodeArgs a, const int32_t* __restrict__ block_table) {
         }
     };
 
-    float o[G][8];
+    float o[G][OJ];
 #pragma unroll
     for (int g = 0; g < G; ++g)
 #pragma unroll
-        for (int j = 0; j < 8; ++j) o[g][j] = 0.0f;
+        for (int j = 0; j < OJ; ++j) o[g][j] = 0.0f;
+    // VCOL: this lane's byte offset into the V tile for the transposed reads
+    const int tr_off = ((lane % 16) / 2) * D + 16 * (lane / 16) + 8 * (lane % 2);
     float m_run = -INFINITY;   // running max (log2 units) of this lane's head
     float l_run = 0.0f;        // this lane's share of sum 2^(s - m_run) (its keys, its head)
-    float w_run = 0.0f;        // INT8 paired: this lane's share of the sum of the rounded weights
 
     int pb = 0;
     // one page: scores, lazy rescale, weights, p.v
     auto page = [&](int p, PageRegs& r) __attribute__((always_inline)) {
         const int kpos0 = p * kPage;
+        if constexpr (VCOL) {
+            // the V tile into LDS, rows in key-pair order (the previous page's reads
+            // of it were issued earlier, and a wave's LDS accesses run in order).
+            // The codes of keys outside [lo, hi) are finite and meet weight 0.
+#pragma unroll
+            for (int c = 0; c < D / 64; ++c) {
+                const int byte = 1024 * c + 16 * lane;
+                const int k = byte / D;
+                const int row = 2 * ((k / (2 * KPL)) * KPL + k % KPL) + (k / KPL) % 2;
+                *reinterpret_cast<uint4*>(&v_lds[row * D + byte % D]) =
+                    make_uint4(r.vt[4 * c], r.vt[4 * c + 1], r.vt[4 * c + 2], r.vt[4 * c + 3]);
+            }
+        }
 
         // ---- scores ----
         float s[NLOAD];
@@ -402,12 +463,11 @@ void decode_kernel(DecodeArgs a, const int32_t* __restrict__ block_table) {
         if (__any(m_new > m_run + 8.0f)) {
             const float alpha = fast_exp2(m_run - m_new);   // 0 on the first page
             l_run *= alpha;
-            if constexpr (INT8 && PAIRED) w_run *= alpha;
 #pragma unroll
             for (int g = 0; g < G; ++g) {
                 const float ag = lane_read(alpha, g * HG);
 #pragma unroll
-                for (int j = 0; j < 8; ++j) o[g][j] *= ag;
+                for (int j = 0; j < OJ; ++j) o[g][j] *= ag;
             }
             m_run = m_new;
         }
@@ -432,7 +492,6 @@ void decode_kernel(DecodeArgs a, const int32_t* __restrict__ block_table) {
                 if constexpr (INT8) {
                     l_run += p0 + p1;
                     pr = pack_bf16_rne(valid[i] ? p0 * r.vs[i] : 0.0f, valid[i + 1] ? p1 * r.vs[i + 1] : 0.0f);
-                    w_run = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(pr), as_bf16x2(0x3F803F80u), w_run, false);
                 } else {
                     pr = pack_bf16_rne(p0, p1);
                     l_run = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(pr), as_bf16x2(0x3F803F80u), l_run, false);
@@ -444,49 +503,96 @@ void decode_kernel(DecodeArgs a, const int32_t* __restrict__ block_table) {
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
         // ---- p.v ----
-        CT vcur[NLOAD];
-#pragma unroll
-        for (int i = 0; i < NLOAD; ++i) vcur[i] = r.v[i];
-        if constexpr (!INT8) {
-            // BF16 values past the sequence end may be poison: zero them (weight 0 *
-            // NaN), on the pages that cross [lo, hi) only
-            if (!(kpos0 >= lo && kpos0 + kPage <= hi)) {
-#pragma unroll
-                for (int i = 0; i < NLOAD; ++i)
-                    if (!valid[i]) vcur[i] = CT{};
-            }
-        }
-        if constexpr (!PAIRED) {
-#pragma unroll
-            for (int i = 0; i < NLOAD; ++i) {
-                float pw[G];
-#pragma unroll
-                for (int g = 0; g < G; ++g) pw[g] = p_buf[pb][i * KPL + kg][g];
-                float x[8];
-                v_floats(vcur[i], x);
-#pragma unroll
-                for (int g = 0; g < G; ++g)
-#pragma unroll
-                    for (int j = 0; j < 8; ++j) o[g][j] = fmaf(pw[g], x[j], o[g][j]);
-            }
-        } else {
-            const uint4* pp4 = reinterpret_cast<const uint4*>(&p_buf[pb][0][0]);
-#pragma unroll
-            for (int i = 0; i < NLOAD; i += 2) {
-                uint32_t vv[8];
-                v_pairs(vcur[i], vcur[i + 1], vv);
-                // the G weight pairs of keys (i, i+1) of this key group
-                uint32_t pp[G];
+        if constexpr (VCOL) {
+            // pair m's G weight pairs from LDS (the same words for every lane), read
+            // one pair ahead; the lane's columns from the V tile, 8 rows (4 pairs)
+            // per transposed read.  Each read's address passes through an empty asm
+            // that also takes the last result of the pair before, so the compiler
+            // cannot hoist every pair's reads (64 registers) to the top.
+            const uint32_t pp_base = (uint32_t)(uintptr_t)(const LDS3 void*)&p_buf[pb][0][0];
+            const LDS3 char* vt = (const LDS3 char*)v_lds + tr_off;
+            auto read_pp = [&](uint32_t addr, uint32_t (&pp)[G]) __attribute__((always_inline)) {
 #pragma unroll
                 for (int q4 = 0; q4 < G / 4; ++q4) {
-                    const uint4 w = pp4[((i / 2) * KPL + kg) * (G / 4) + q4];
+                    const u32x4 w = *(const LDS3 u32x4*)(uintptr_t)(addr + 16 * q4);
                     pp[4 * q4] = w.x; pp[4 * q4 + 1] = w.y; pp[4 * q4 + 2] = w.z; pp[4 * q4 + 3] = w.w;
                 }
+            };
+            i32x2 raw[2][NC];
 #pragma unroll
-                for (int g = 0; g < G; ++g)
+            for (int h = 0; h < 2; ++h)
 #pragma unroll
-                    for (int j = 0; j < 8; ++j)
-                        o[g][j] = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(pp[g]), as_bf16x2(vv[j]), o[g][j], false);
+                for (int c = 0; c < NC; ++c)
+                    raw[h][c] = __builtin_amdgcn_ds_read_tr8_b64_v2i32((LDS3 i32x2*)(vt + 8 * h * D + 64 * c));
+            uint32_t ppc[G], ppn[G], pp_b = pp_base;
+            read_pp(pp_b, ppc);
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                uint32_t vv[NC][4];
+#pragma unroll
+                for (int c = 0; c < NC; ++c) vcol_pairs(raw[h][c], vv[c]);
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const int m = 4 * h + u;
+                    if (m + 1 < 8) {
+                        order_after(pp_b, o);
+                        read_pp(pp_b + (m + 1) * G * 4, ppn);
+                    }
+#pragma unroll
+                    for (int g = 0; g < G; ++g)
+#pragma unroll
+                        for (int c = 0; c < NC; ++c)
+                            o[g][c] = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(ppc[g]), as_bf16x2(vv[c][u]), o[g][c],
+                                                                      false);
+#pragma unroll
+                    for (int g = 0; g < G; ++g) ppc[g] = ppn[g];
+                }
+            }
+        } else {
+            CT vcur[NLOAD];
+#pragma unroll
+            for (int i = 0; i < NLOAD; ++i) vcur[i] = r.v[i];
+            if constexpr (!INT8) {
+                // BF16 values past the sequence end may be poison: zero them (weight 0 *
+                // NaN), on the pages that cross [lo, hi) only
+                if (!(kpos0 >= lo && kpos0 + kPage <= hi)) {
+#pragma unroll
+                    for (int i = 0; i < NLOAD; ++i)
+                        if (!valid[i]) vcur[i] = CT{};
+                }
+            }
+            if constexpr (!PAIRED) {
+#pragma unroll
+                for (int i = 0; i < NLOAD; ++i) {
+                    float pw[G];
+#pragma unroll
+                    for (int g = 0; g < G; ++g) pw[g] = p_buf[pb][i * KPL + kg][g];
+                    float x[8];
+                    v_floats(vcur[i], x);
+#pragma unroll
+                    for (int g = 0; g < G; ++g)
+#pragma unroll
+                        for (int j = 0; j < 8; ++j) o[g][j] = fmaf(pw[g], x[j], o[g][j]);
+                }
+            } else {
+                const uint4* pp4 = reinterpret_cast<const uint4*>(&p_buf[pb][0][0]);
+#pragma unroll
+                for (int i = 0; i < NLOAD; i += 2) {
+                    uint32_t vv[8];
+                    v_pairs(vcur[i], vcur[i + 1], vv);
+                    // the G weight pairs of keys (i, i+1) of this key group
+                    uint32_t pp[G];
+#pragma unroll
+                    for (int q4 = 0; q4 < G / 4; ++q4) {
+                        const uint4 w = pp4[((i / 2) * KPL + kg) * (G / 4) + q4];
+                        pp[4 * q4] = w.x; pp[4 * q4 + 1] = w.y; pp[4 * q4 + 2] = w.z; pp[4 * q4 + 3] = w.w;
+                    }
+#pragma unroll
+                    for (int g = 0; g < G; ++g)
+#pragma unroll
+                        for (int j = 0; j < 8; ++j)
+                            o[g][j] = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(pp[g]), as_bf16x2(vv[j]), o[g][j], false);
+                }
             }
         }
         pb ^= 1;
@@ -521,32 +627,30 @@ void decode_kernel(DecodeArgs a, const int32_t* __restrict__ block_table) {
         }
     }
 
-    // ---- reduce across key groups; head g's row is written by the lanes of key
-    // group g % KPL ----
+    // ---- reduce across key groups (VCOL: each lane's columns are complete); head
+    // g's row is written by the lanes of key group g % KPL, or VCOL by all lanes ----
+    if constexpr (!VCOL) {
 #pragma unroll
-    for (int g = 0; g < G; ++g)
+        for (int g = 0; g < G; ++g)
 #pragma unroll
-        for (int j = 0; j < 8; ++j) o[g][j] = stride_sum<LPK>(o[g][j]);
+            for (int j = 0; j < 8; ++j) o[g][j] = stride_sum<LPK>(o[g][j]);
+    }
     const float l_tot = stride_sum<LPK>(l_run);
-    float w_tot = 0.0f;
-    if constexpr (INT8 && PAIRED) w_tot = stride_sum<LPK>(w_run);
 #pragma unroll
     for (int g = 0; g < G; ++g) {
         const float mg = lane_read(m_run, g * HG);
         const float lg = lane_read(l_tot, g * HG);
-        if constexpr (INT8 && PAIRED) {   // the codes entered as c + 128
-            const float off = 128.0f * lane_read(w_tot, g * HG);
-#pragma unroll
-            for (int j = 0; j < 8; ++j) o[g][j] -= off;
-        }
         float den = lg;
         if constexpr (FINAL) {
             if (a.sinks) den += fast_exp2(__ldg(a.sinks + head0 + g) * kLog2e - mg);
         }
         const float f = (FINAL && !(den > 0.0f)) ? 0.0f : 1.0f / den;
-        if (g % KPL == kg) {
-            float* dst = FINAL ? a.out + (row0 + g) * D + sub * 8
-                               : a.o_part + ((row0 + g) * a.max_splits + sp) * D + sub * 8;
+        float* row = FINAL ? a.out + (row0 + g) * D : a.o_part + ((row0 + g) * a.max_splits + sp) * D;
+        if constexpr (VCOL) {
+#pragma unroll
+            for (int c = 0; c < NC; ++c) put(row + 64 * c + lane, o[g][c] * f);
+        } else if (g % KPL == kg) {
+            float* dst = row + sub * 8;
             if (fused) {
 #pragma unroll
                 for (int j = 0; j < 8; ++j) put(dst + j, o[g][j] * f);
