@@ -420,7 +420,11 @@ void decode_kernel(DecodeArgs a, const int32_t* __restrict__ block_table) {
 
         // ---- scores ----
         float s[NLOAD];
-        bool valid[NLOAD];
+        bool valid[NLOAD];   // BF16
+        auto outside = [&](int i) __attribute__((always_inline)) {
+            const int key = kpos0 + i * KPL + kg;
+            return key < lo || key >= hi;
+        };
 #pragma unroll
         for (int i = 0; i < NLOAD; ++i) {
             uint32_t kp[4];
@@ -447,9 +451,27 @@ void decode_kernel(DecodeArgs a, const int32_t* __restrict__ block_table) {
             float dot = transpose_reduce<LPK, G>(acc);
             if constexpr (INT8) dot -= qbias;
             const float sc = INT8 ? c2 * r.ks[i] : c2;
-            const int key = kpos0 + i * KPL + kg;
-            valid[i] = key >= lo && key < hi;
-            s[i] = valid[i] ? dot * sc : -INFINITY;
+            if constexpr (INT8) {
+                s[i] = dot * sc;
+            } else {
+                const int key = kpos0 + i * KPL + kg;
+                valid[i] = key >= lo && key < hi;
+                s[i] = valid[i] ? dot * sc : -INFINITY;
+            }
+        }
+        // INT8 (VALU-bound) masks only the pages that cross [lo, hi), a split's first
+        // and last at most: the scores of keys outside become -inf by a select, never
+        // by arithmetic, since their scales may be poison, and their value scales
+        // become 0 (the weight is then 0, not 0 * NaN).
+        if constexpr (INT8) {
+            if (!(kpos0 >= lo && kpos0 + kPage <= hi)) {
+#pragma unroll
+                for (int i = 0; i < NLOAD; ++i) {
+                    const bool out = outside(i);
+                    s[i] = out ? -INFINITY : s[i];
+                    r.vs[i] = out ? 0.0f : r.vs[i];
+                }
+            }
         }
         // ---- running max, lazy rescale with headroom: the reference max moves only
         // when a head's max exceeds it by more than 8, so every weight is <= 2^8
@@ -471,15 +493,14 @@ void decode_kernel(DecodeArgs a, const int32_t* __restrict__ block_table) {
             }
             m_run = m_new;
         }
-        // ---- weights, shared within the wave (masked keys weigh 0; an INT8 scale
-        // of a masked slot may be poison, so it is selected away) ----
+        // ---- weights, shared within the wave (masked keys weigh 0) ----
         if constexpr (!PAIRED) {
 #pragma unroll
             for (int i = 0; i < NLOAD; ++i) {
                 const float pw = fast_exp2(s[i] - m_run);      // 0 for masked keys
                 l_run += pw;
                 float pv = pw;
-                if constexpr (INT8) pv = valid[i] ? pw * r.vs[i] : 0.0f;
+                if constexpr (INT8) pv = pw * r.vs[i];
                 if (sub % HG == 0) p_buf[pb][i * KPL + kg][myhead] = pv;
             }
         } else {
@@ -491,7 +512,7 @@ void decode_kernel(DecodeArgs a, const int32_t* __restrict__ block_table) {
                 uint32_t pr;
                 if constexpr (INT8) {
                     l_run += p0 + p1;
-                    pr = pack_bf16_rne(valid[i] ? p0 * r.vs[i] : 0.0f, valid[i + 1] ? p1 * r.vs[i + 1] : 0.0f);
+                    pr = pack_bf16_rne(p0 * r.vs[i], p1 * r.vs[i + 1]);
                 } else {
                     pr = pack_bf16_rne(p0, p1);
                     l_run = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(pr), as_bf16x2(0x3F803F80u), l_run, false);
