@@ -161,7 +161,6 @@ __global__ __launch_bounds__(kWave) void decode_tq3_kernel(DecodeArgs a, Tq3Book
         const int64_t nblk = more ? page_block(p + 1) : 0;
         // ---- scores of the page: one per lane and step (this lane's head) ----
         float s[NS];
-        bool valid[NS];
         uint32_t vw[NS];
         float vsc[NS];
 #pragma unroll
@@ -182,9 +181,19 @@ __global__ __launch_bounds__(kWave) void decode_tq3_kernel(DecodeArgs a, Tq3Book
                 acc[j] = d;
             }
             const float dot = transpose_reduce<L, G>(acc);
-            const int key = p * kPage + r * R + kr;
-            valid[r] = key >= lo && key < hi;
-            s[r] = valid[r] ? dot * (ksr * c2) : -INFINITY;
+            s[r] = dot * (ksr * c2);
+        }
+        // masks on the pages that cross [lo, hi) only: the scores of keys outside
+        // become -inf by a select (their scales may be poison) and their value
+        // scales 0, so the weight is 0 rather than 0 * NaN
+        if (!(p * kPage >= lo && p * kPage + kPage <= hi)) {
+#pragma unroll
+            for (int r = 0; r < NS; ++r) {
+                const int key = p * kPage + r * R + kr;
+                const bool out = key < lo || key >= hi;
+                s[r] = out ? -INFINITY : s[r];
+                vsc[r] = out ? 0.0f : vsc[r];
+            }
         }
         // ---- running max, lazy rescale with headroom: the reference max moves only
         // when a head's max exceeds it by more than 8, so every weight is <= 2^8
@@ -211,7 +220,7 @@ __global__ __launch_bounds__(kWave) void decode_tq3_kernel(DecodeArgs a, Tq3Book
         for (int r = 0; r < NS; ++r) {
             const float pw = fast_exp2(s[r] - m_run);      // 0 for masked keys
             l_run += pw;
-            const float pv = valid[r] ? pw * vsc[r] : 0.0f;   // the scale of a masked slot may be NaN
+            const float pv = pw * vsc[r];
             if (sub % HG == 0) p_buf[r][kr][myhead] = pv;
         }
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
