@@ -5,8 +5,10 @@
 Each .hip source under csrc/ is compiled to an object in _build/, then linked
 in-tree as paged_flash_attention_amd/libpfa.so.  A second library,
 libpfa_debug.so, is the same code built with
-  PFA_PREFILL_AUDIT=1  every prefill ring step waits for all loads and all waves
-                       (a GPU test checks that the normal build gives the same bits);
+  PFA_PREFILL_AUDIT=1  every prefill ring step waits for all loads and all waves,
+  PFA_DECODE_AUDIT=1   and every INT8 decode page at G = 8 for all of its wave's
+                       direct loads (GPU tests check that the normal build gives
+                       the same bits);
   PFA_BOUNDS_CHECK=1   the kernels report block-table entries and lengths outside
                        the device-side contract in an error word
                        (pfa_bounds_errors).
@@ -43,7 +45,7 @@ def sources():
 
 
 DEBUG_LIB = os.path.join(HERE, "libpfa_debug.so")
-DEBUG_DEFINES = ("PFA_PREFILL_AUDIT=1", "PFA_BOUNDS_CHECK=1")
+DEBUG_DEFINES = ("PFA_PREFILL_AUDIT=1", "PFA_DECODE_AUDIT=1", "PFA_BOUNDS_CHECK=1")
 
 
 def compile_one(src: str, outdir: str = BUILD, defines=()) -> str:

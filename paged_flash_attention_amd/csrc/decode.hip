@@ -61,8 +61,17 @@
 #include "group_reduce.h"
 #include "merge_splits.h"
 
+// Audit: with PFA_DECODE_AUDIT=1 every INT8 page at G = 8 waits for all of the
+// wave's direct loads (the next page's too) before it reads its ring stage; a GPU
+// test checks that the normal build gives the same bits.
+#ifndef PFA_DECODE_AUDIT
+#define PFA_DECODE_AUDIT 0
+#endif
+
 namespace pfa {
 namespace {
+
+constexpr bool kDecodeAudit = PFA_DECODE_AUDIT != 0;
 
 template <bool INT8> struct Chunk;
 template <> struct Chunk<false> { typedef uint4 T; };   // 8 bf16
@@ -149,6 +158,7 @@ __device__ __forceinline__ void v_pairs(const uint2& a, const uint2& b, uint32_t
 // dot2 as signed bf16 (exact), so no offset is carried.
 typedef int i32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 #define LDS3 __attribute__((address_space(3)))
 // rows (2u, 2u+1) of a transposed read -> bf16 pair u, from the signed codes
 __device__ __forceinline__ void vcol_pairs(i32x2 x, uint32_t (&v)[4]) {
@@ -198,16 +208,23 @@ void decode_kernel(DecodeArgs a, const int32_t* __restrict__ block_table) {
     constexpr int OJ = VCOL ? NC : 8;          // o elements per lane and head
     static_assert(G <= LPK, "group size");
     static_assert(!PAIRED || NLOAD % 2 == 0, "key pairs");
+    static_assert(!VCOL || (2 * kPage * D + 512) * 2 >= kFusedMergeChunk * 4, "merge weights in the ring");
     typedef typename Chunk<INT8>::T CT;
 
     // weights of a page, double-buffered: [key][head] floats (G <= 4), or for
-    // G = 8 [key pair][key group][head] bf16 pairs
-    __shared__ __attribute__((aligned(16))) float p_buf[2][kPage][G];
-    __shared__ float w_lds[FINAL ? 1 : kFusedMergeChunk];
-    // VCOL: the page's V rows, row 2m + h holding key h of key pair m (the pair
-    // one lane's weights cover: keys kg + KPL*i and kg + KPL*(i+1), i even,
-    // m = KPL*(i/2) + kg)
-    __shared__ __attribute__((aligned(16))) int8_t v_lds[VCOL ? kPage * D : 16];
+    // G = 8 [key pair][key group][head] bf16 pairs (VCOL: one buffer, since a
+    // wave's LDS accesses run in order)
+    __shared__ __attribute__((aligned(16))) float p_buf[VCOL ? 1 : 2][kPage][G];
+    // VCOL: a 2-stage ring of pages loaded straight from HBM (global_load_lds):
+    // per stage the K tile, the V tile (16 rows of D codes each), then the K and
+    // the V scales (256 bytes each, four copies of the page's 16).  After the page
+    // loop the fused merge takes the ring for its weights.
+    constexpr int kTile = kPage * D;
+    constexpr int kStage = 2 * kTile + 512;
+    constexpr int NDMA = 2 * (kTile / 1024) + 2;   // direct loads per page
+    __shared__ __attribute__((aligned(16))) int8_t ring[VCOL ? 2 * kStage : 16];
+    __shared__ float w_own[(FINAL || VCOL) ? 1 : kFusedMergeChunk];
+    float* const w_lds = VCOL ? reinterpret_cast<float*>(ring) : w_own;
 
     const int lane = threadIdx.x;
     const int sub = lane % LPK;
@@ -353,11 +370,13 @@ void decode_kernel(DecodeArgs a, const int32_t* __restrict__ block_table) {
     const int lane_off = lane * 8 * EB;
 
     // a page's K/V (and INT8 scales) as this lane loads them
+    // (VCOL: the page's ring stage instead)
     struct PageRegs {
-        CT k[NLOAD], v[VCOL ? 1 : NLOAD];
-        uint32_t vt[VCOL ? D / 16 : 1];   // VCOL: 16-byte pieces of the V tile, 1024 bytes apart
-        float ks[NLOAD], vs[NLOAD];
+        CT k[VCOL ? 1 : NLOAD], v[VCOL ? 1 : NLOAD];
+        float ks[VCOL ? 1 : NLOAD], vs[VCOL ? 1 : NLOAD];
+        uint32_t st;   // VCOL: LDS byte address of the stage
     };
+    const uint32_t ring0 = (uint32_t)(uintptr_t)(const LDS3 void*)ring;
     // a page's block-table entry (a scalar load; the index is clamped to the
     // split's last page so that the read stays inside the row), read one page
     // ahead of the loads that use it
@@ -366,26 +385,32 @@ void decode_kernel(DecodeArgs a, const int32_t* __restrict__ block_table) {
         report(a.err, raw_id < 0 || raw_id >= a.num_pages, PFA_BOUNDS_PAGE);
         const int id = min(max(raw_id, 0), a.num_pages - 1);
         const int64_t blk = (int64_t)id * Hkv + kvh;
-        const char* kp = kbase + blk * head_stride * EB + lane_off;
-        const char* vp = vbase + blk * head_stride * EB + lane_off;
-#pragma unroll
-        for (int i = 0; i < NLOAD; ++i) {
-            r.k[i] = *reinterpret_cast<const CT*>(kp + i * 512 * EB);
-            if constexpr (!VCOL) r.v[i] = *reinterpret_cast<const CT*>(vp + i * 512 * EB);
-        }
         if constexpr (VCOL) {
-            const char* vt = vbase + blk * head_stride + 16 * lane;
+            // straight into the stage: the tiles as they lie in the pool, then the
+            // scales (lane l loads the page's scale l % 16)
+            const char* kt = kbase + blk * head_stride;
+            const char* vt = vbase + blk * head_stride;
 #pragma unroll
-            for (int c = 0; c < D / 64; ++c) {
-                const uint4 x = *reinterpret_cast<const uint4*>(vt + 1024 * c);
-                r.vt[4 * c] = x.x; r.vt[4 * c + 1] = x.y; r.vt[4 * c + 2] = x.z; r.vt[4 * c + 3] = x.w;
+            for (int c = 0; c < kTile / 1024; ++c) {
+                dma16(kt + 1024 * c, 16u * (uint32_t)lane, r.st + 1024 * c);
+                dma16(vt + 1024 * c, 16u * (uint32_t)lane, r.st + kTile + 1024 * c);
             }
-        }
-        if constexpr (INT8) {
+            dma4(a.k_scale + blk * kPage, 4u * (uint32_t)(lane % kPage), r.st + 2 * kTile);
+            dma4(a.v_scale + blk * kPage, 4u * (uint32_t)(lane % kPage), r.st + 2 * kTile + 256);
+        } else {
+            const char* kp = kbase + blk * head_stride * EB + lane_off;
+            const char* vp = vbase + blk * head_stride * EB + lane_off;
 #pragma unroll
             for (int i = 0; i < NLOAD; ++i) {
-                r.ks[i] = __ldg(a.k_scale + blk * kPage + i * KPL + kg);
-                r.vs[i] = __ldg(a.v_scale + blk * kPage + i * KPL + kg);
+                r.k[i] = *reinterpret_cast<const CT*>(kp + i * 512 * EB);
+                r.v[i] = *reinterpret_cast<const CT*>(vp + i * 512 * EB);
+            }
+            if constexpr (INT8) {
+#pragma unroll
+                for (int i = 0; i < NLOAD; ++i) {
+                    r.ks[i] = __ldg(a.k_scale + blk * kPage + i * KPL + kg);
+                    r.vs[i] = __ldg(a.v_scale + blk * kPage + i * KPL + kg);
+                }
             }
         }
     };
@@ -395,8 +420,13 @@ void decode_kernel(DecodeArgs a, const int32_t* __restrict__ block_table) {
     for (int g = 0; g < G; ++g)
 #pragma unroll
         for (int j = 0; j < OJ; ++j) o[g][j] = 0.0f;
-    // VCOL: this lane's byte offset into the V tile for the transposed reads
-    const int tr_off = ((lane % 16) / 2) * D + 16 * (lane / 16) + 8 * (lane % 2);
+    // VCOL: this lane's byte offset into a stage's V tile for the transposed reads.
+    // Lane j of a 16-lane group points at row j/2 of an 8-row block in key-pair
+    // order: pair m = j/4 (+4 per block), member (j/2) % 2, which is pool row
+    // m % KPL + KPL * (2 * (m / KPL) + member); the next block is kTrStep on.
+    const int tr_j = lane % 16, tr_m = tr_j / 4, tr_t = (tr_j / 2) % 2;
+    const int tr_off = (tr_m % KPL + KPL * (2 * (tr_m / KPL) + tr_t)) * D + 16 * (lane / 16) + 8 * (tr_j % 2);
+    constexpr int kTrStep = (KPL == 4 ? 8 : 4) * D;
     float m_run = -INFINITY;   // running max (log2 units) of this lane's head
     float l_run = 0.0f;        // this lane's share of sum 2^(s - m_run) (its keys, its head)
 
@@ -405,22 +435,17 @@ void decode_kernel(DecodeArgs a, const int32_t* __restrict__ block_table) {
     auto page = [&](int p, PageRegs& r) __attribute__((always_inline)) {
         const int kpos0 = p * kPage;
         if constexpr (VCOL) {
-            // the V tile into LDS, rows in key-pair order (the previous page's reads
-            // of it were issued earlier, and a wave's LDS accesses run in order).
-            // The codes of keys outside [lo, hi) are finite and meet weight 0.
-#pragma unroll
-            for (int c = 0; c < D / 64; ++c) {
-                const int byte = 1024 * c + 16 * lane;
-                const int k = byte / D;
-                const int row = 2 * ((k / (2 * KPL)) * KPL + k % KPL) + (k / KPL) % 2;
-                *reinterpret_cast<uint4*>(&v_lds[row * D + byte % D]) =
-                    make_uint4(r.vt[4 * c], r.vt[4 * c + 1], r.vt[4 * c + 2], r.vt[4 * c + 3]);
-            }
+            // this page's stage has landed once at most the next page's direct loads
+            // (issued before this page whenever p < p1) are in flight; the memory
+            // clobber keeps the stage's LDS reads below the wait
+            if (!kDecodeAudit && p < p1) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NDMA) : "memory");
+            else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         }
 
         // ---- scores ----
         float s[NLOAD];
         bool valid[NLOAD];   // BF16
+        float vsl[NLOAD];    // INT8: the value scales (VCOL: from the stage)
         auto outside = [&](int i) __attribute__((always_inline)) {
             const int key = kpos0 + i * KPL + kg;
             return key < lo || key >= hi;
@@ -428,7 +453,12 @@ void decode_kernel(DecodeArgs a, const int32_t* __restrict__ block_table) {
 #pragma unroll
         for (int i = 0; i < NLOAD; ++i) {
             uint32_t kp[4];
-            k_pairs(r.k[i], kp);
+            if constexpr (VCOL) {
+                const u32x2 w = *(const LDS3 u32x2*)(uintptr_t)(r.st + (i * KPL + kg) * D + sub * 8);
+                k_pairs(make_uint2(w.x, w.y), kp);
+            } else {
+                k_pairs(r.k[i], kp);
+            }
             float acc[G];
 #pragma unroll
             for (int j = 0; j < G; ++j) {
@@ -450,7 +480,15 @@ void decode_kernel(DecodeArgs a, const int32_t* __restrict__ block_table) {
             }
             float dot = transpose_reduce<LPK, G>(acc);
             if constexpr (INT8) dot -= qbias;
-            const float sc = INT8 ? c2 * r.ks[i] : c2;
+            float ksv = 0.0f;
+            if constexpr (VCOL) {
+                ksv = *(const LDS3 float*)(uintptr_t)(r.st + 2 * kTile + 4 * (i * KPL + kg));
+                vsl[i] = *(const LDS3 float*)(uintptr_t)(r.st + 2 * kTile + 256 + 4 * (i * KPL + kg));
+            } else if constexpr (INT8) {
+                ksv = r.ks[i];
+                vsl[i] = r.vs[i];
+            }
+            const float sc = INT8 ? c2 * ksv : c2;
             if constexpr (INT8) {
                 s[i] = dot * sc;
             } else {
@@ -469,7 +507,7 @@ void decode_kernel(DecodeArgs a, const int32_t* __restrict__ block_table) {
                 for (int i = 0; i < NLOAD; ++i) {
                     const bool out = outside(i);
                     s[i] = out ? -INFINITY : s[i];
-                    r.vs[i] = out ? 0.0f : r.vs[i];
+                    vsl[i] = out ? 0.0f : vsl[i];
                 }
             }
         }
@@ -500,7 +538,7 @@ void decode_kernel(DecodeArgs a, const int32_t* __restrict__ block_table) {
                 const float pw = fast_exp2(s[i] - m_run);      // 0 for masked keys
                 l_run += pw;
                 float pv = pw;
-                if constexpr (INT8) pv = pw * r.vs[i];
+                if constexpr (INT8) pv = pw * vsl[i];
                 if (sub % HG == 0) p_buf[pb][i * KPL + kg][myhead] = pv;
             }
         } else {
@@ -512,7 +550,7 @@ void decode_kernel(DecodeArgs a, const int32_t* __restrict__ block_table) {
                 uint32_t pr;
                 if constexpr (INT8) {
                     l_run += p0 + p1;
-                    pr = pack_bf16_rne(p0 * r.vs[i], p1 * r.vs[i + 1]);
+                    pr = pack_bf16_rne(p0 * vsl[i], p1 * vsl[i + 1]);
                 } else {
                     pr = pack_bf16_rne(p0, p1);
                     l_run = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(pr), as_bf16x2(0x3F803F80u), l_run, false);
@@ -531,7 +569,7 @@ void decode_kernel(DecodeArgs a, const int32_t* __restrict__ block_table) {
             // that also takes the last result of the pair before, so the compiler
             // cannot hoist every pair's reads (64 registers) to the top.
             const uint32_t pp_base = (uint32_t)(uintptr_t)(const LDS3 void*)&p_buf[pb][0][0];
-            const LDS3 char* vt = (const LDS3 char*)v_lds + tr_off;
+            const LDS3 char* vt = (const LDS3 char*)(uintptr_t)(r.st + kTile + tr_off);
             auto read_pp = [&](uint32_t addr, uint32_t (&pp)[G]) __attribute__((always_inline)) {
 #pragma unroll
                 for (int q4 = 0; q4 < G / 4; ++q4) {
@@ -544,7 +582,7 @@ void decode_kernel(DecodeArgs a, const int32_t* __restrict__ block_table) {
             for (int h = 0; h < 2; ++h)
 #pragma unroll
                 for (int c = 0; c < NC; ++c)
-                    raw[h][c] = __builtin_amdgcn_ds_read_tr8_b64_v2i32((LDS3 i32x2*)(vt + 8 * h * D + 64 * c));
+                    raw[h][c] = __builtin_amdgcn_ds_read_tr8_b64_v2i32((LDS3 i32x2*)(vt + h * kTrStep + 64 * c));
             uint32_t ppc[G], ppn[G], pp_b = pp_base;
             read_pp(pp_b, ppc);
 #pragma unroll
@@ -616,13 +654,15 @@ void decode_kernel(DecodeArgs a, const int32_t* __restrict__ block_table) {
                 }
             }
         }
-        pb ^= 1;
+        if constexpr (!VCOL) pb ^= 1;
     };
     // page p is consumed from one register set while page p+1 loads into the other
     if constexpr (kScalarIds<G, INT8>) {
         // two sets used in turn (a copy from one to the other would cost a move per
         // register and page)
         PageRegs ra, rb;
+        ra.st = ring0;
+        rb.st = ring0 + kStage;
         load_page(page_id(p0), ra);
         int nid = page_id(p0 + 1);
         int p = p0;

@@ -118,30 +118,6 @@ __device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const
 template <int D> __device__ __forceinline__ int swz_k(int r) { return D == 128 ? (r & 15) : ((r >> 1) & 7); }
 template <int D> __device__ __forceinline__ int swz_v(int r) { return D == 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1); }
 
-// Wait until at most N vector-memory operations of this wave are outstanding.
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-    static_assert(N >= 0 && N < 64, "vmcnt");
-    __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
-}
-
-// 16-byte direct load HBM -> LDS: lane l's 16 bytes come from base + voff (bytes)
-// and land at LDS byte address lds + 16*l.  base and lds are wave-uniform.  Issued
-// as asm, so the compiler keeps no LDS-DMA bookkeeping of its own: it would
-// otherwise make every transposed LDS read wait for all direct loads in flight.
-// The caller orders LDS accesses against these loads (vmcnt waits and barriers).
-// (M0 is the LDS base; a write of M0 needs one wait state before the load.)
-__device__ __forceinline__ void dma16(const void* base, uint32_t voff, uint32_t lds) {
-    // (readfirstlane returns int: both halves go through uint32_t, so that the
-    // low word is zero-extended)
-    const uint64_t p = (uint64_t)(uintptr_t)base;
-    const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(p >> 32));
-    const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)p);
-    const uint64_t sb = ((uint64_t)hi << 32) | lo;
-    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
-                 :: "v"(voff), "s"(sb), "s"(__builtin_amdgcn_readfirstlane(lds)) : "memory");
-}
-
 // A wave-uniform pointer, held in scalar registers.
 template <typename T>
 __device__ __forceinline__ T* uniform_ptr(T* p) {

@@ -1,4 +1,4 @@
-"""Barrier audit of the prefill kernels.  Their direct HBM -> LDS tile loads are
+"""Barrier audit of the prefill kernels and of the INT8 decode at G = 8.  Their direct HBM -> LDS tile loads are
 issued as inline asm, which the compiler does not track, so the waits before a
 tile is read (each wave waits for its own loads of that tile, then one barrier)
 are placed by hand.  libpfa_debug.so is the same source built with
@@ -7,7 +7,11 @@ arithmetic): every ring step waits for all of the wave's loads and then for all
 waves, before and after each refill.  If a hand-placed wait were too
 short, the normal build would read a stage before its tile landed and its bits
 would differ from the audit build's; here they must be equal, on both kernel
-builds (64-key unsplit, 32-key split) and on verify steps."""
+builds (64-key unsplit, 32-key split) and on verify steps.
+
+The INT8 decode at G = 8 loads each page's K and V tiles and scales straight into
+a 2-stage LDS ring the same way, one page ahead; the audit build (PFA_DECODE_AUDIT=1)
+waits for all of them before every page."""
 import numpy as np
 import pytest
 import torch
@@ -63,3 +67,37 @@ def test_prefill_bits_equal_the_barrier_audit_build(ci, audit_lib):
         assert np.all(np.isfinite(normal))
         assert np.array_equal(normal.view(np.uint32), audited.view(np.uint32)), \
             f"case {ci} {kind}: {np.sum(normal != audited)} outputs differ from the audit build"
+
+
+DECODE_AUDIT_CASES = [
+    # (params, seq_lens, split_keys): INT8, G = 8
+    (dict(Hq=32, Hkv=4, D=128), [33, 1000, 4100], (0, 256, 64)),
+    (dict(Hq=32, Hkv=4, D=128, window=300, sinks=True), [2049, 16, 700], (0, 256)),
+    (dict(Hq=64, Hkv=8, D=64, sinks=True), [1500, 17], (0, 128)),
+]
+
+
+@pytest.mark.parametrize("ci", range(len(DECODE_AUDIT_CASES)))
+@pytest.mark.parametrize("smooth", [False, True], ids=["plain", "smoothed"])
+def test_int8_decode_bits_equal_the_audit_build(ci, smooth, audit_lib):
+    prm, lens, splits = DECODE_AUDIT_CASES[ci]
+    p = W.AttnParams(prm["Hq"], prm["Hkv"], prm["D"], kv_dtype="int8", window=prm.get("window", 0),
+                     sinks=W.sinks_normal(720 + ci, prm["Hq"]) if prm.get("sinks") else None)
+    kw = dict(key_weight=W.key_norm_weight(730 + ci, prm["D"])) if smooth else {}
+    case = W.make_case(f"daudit{ci}", 720 + ci, p, lens, np.ones(len(lens), np.int32), outlier_frac=0.01, **kw)
+    g = GpuCase(case)
+    def run(S, fused):
+        return g.decode_fused(split_keys=S, calls=1)[0][0] if fused else g.decode(split_keys=S)
+
+    for S in splits:
+        for fused in (False, True):
+            if fused and S == 0:
+                continue
+            normal = run(S, fused)
+            prev = pfa.use_library(audit_lib)
+            try:
+                audited = run(S, fused)
+            finally:
+                pfa.use_library(prev)
+            assert np.array_equal(normal.view(np.uint32), audited.view(np.uint32)), \
+                f"case {ci} S={S} fused={fused}: {np.sum(normal != audited)} outputs differ from the audit build"
