@@ -12,11 +12,11 @@
 // no visible key carry lse = -inf and weigh 0.  The leading run of such splits
 // is skipped without reading its o rows.
 //
-// Up to 128 splits, one 64-lane wave per (row, h, 64-element slice of D) runs
-// merge_splits_short, which has all the row's partials in flight at once, at the
-// smallest depth of 8, 16, 32, 64 and 128 that holds the row's split count.
-// Above 128, one wave per (row, h) runs the chunked merge_splits
-// (merge_splits.h).  The two give the same bits.
+// Up to 128 splits, merge_splits_short has all the row's partials in flight at
+// once, at the smallest depth of 8, 16, 32, 64 and 128 that holds the row's split
+// count; one 64-lane wave takes a 64-element slice of D where (row, h) items are
+// fewer than 8192, else the whole row.  Above 128 splits, one wave per (row, h)
+// runs the chunked merge_splits (merge_splits.h).  All give the same bits.
 // The work is tiny: rows*Hq*splits*(D+1)*4 bytes read, so the time is latency.
 #include "merge_splits.h"
 
@@ -25,13 +25,14 @@ namespace {
 
 constexpr int kMaxLdsSplits = 1024;
 
-// NS > 0: every row has at most NS <= 128 splits; a wave merges one 64-element
-// slice of D through merge_splits_short at the depth its row needs.  NS = 0: any
-// count, a wave per (row, head) through the chunked merge.
-template <int D, int NS>
+// NS > 0: every row has at most NS <= 128 splits, merged by merge_splits_short at
+// the depth the row needs; a wave takes one 64-element slice of D (SLICE) or the
+// whole row.  NS = 0: any count, a wave per (row, head) through the chunked merge.
+template <int D, int NS, bool SLICE>
 __global__ __launch_bounds__(64) void combine_kernel(CombineArgs a) {
     __shared__ float w_lds[NS > 0 ? 1 : kMaxLdsSplits];
-    constexpr int kSlices = NS > 0 ? D / kWave : 1;
+    constexpr int kSlices = (NS > 0 && SLICE) ? D / kWave : 1;
+    constexpr int E = D / (kWave * kSlices);     // elements per lane: D/64 for a whole row
     const int slice = blockIdx.x % kSlices;
     const int bh_id = blockIdx.x / kSlices;
     const int h = bh_id % a.num_q_heads;
@@ -52,22 +53,38 @@ __global__ __launch_bounds__(64) void combine_kernel(CombineArgs a) {
     const float* op = a.o_part + bh * a.max_splits * D;
     const float* sink = a.sinks ? a.sinks + h : nullptr;
     if constexpr (NS > 0)
-        merge_splits_short_any<D, NS>(lse, op + slice * kWave, max(ns, 0), sink, a.out + bh * D + slice * kWave);
+        merge_splits_short_any<D, NS, E>(lse, op + slice * kWave, max(ns, 0), sink, a.out + bh * D + slice * kWave);
     else
         merge_splits<D, kMaxLdsSplits>(lse, op, ns, sink, w_lds, a.out + bh * D);
 }
 
+// Slices pay where (row, head) items are few: the headline decode's 1024 items
+// run as 2048 waves.  Where items are many (a 1024-token prefill chunk: 32768)
+// a second wave per item only repeats the prologue, and the whole row goes to
+// one wave (at D = 128 and up to 64 splits, whose 2 x 64 row registers fit).
+constexpr int64_t kSliceBelow = 8192;
+
+template <int D, bool SLICE>
+hipError_t launch_ds(const CombineArgs& a, unsigned bh, hipStream_t s) {
+    const int n = a.max_splits;
+    const dim3 g(bh * (SLICE ? D / kWave : 1)), b(64);
+    if (n <= 8) hipLaunchKernelGGL((combine_kernel<D, 8, SLICE>), g, b, 0, s, a);
+    else if (n <= 16) hipLaunchKernelGGL((combine_kernel<D, 16, SLICE>), g, b, 0, s, a);
+    else if (n <= 32) hipLaunchKernelGGL((combine_kernel<D, 32, SLICE>), g, b, 0, s, a);
+    else if (n <= 64) hipLaunchKernelGGL((combine_kernel<D, 64, SLICE>), g, b, 0, s, a);
+    else if (n <= 128 && SLICE) hipLaunchKernelGGL((combine_kernel<D, 128, true>), g, b, 0, s, a);
+    else hipLaunchKernelGGL((combine_kernel<D, 0, false>), dim3(bh), b, 0, s, a);
+    return hipGetLastError();
+}
+
 template <int D>
 hipError_t launch_d(const CombineArgs& a, unsigned bh, hipStream_t s) {
-    const int n = a.max_splits;
-    const dim3 g(bh * (D / kWave)), b(64);
-    if (n <= 8) hipLaunchKernelGGL((combine_kernel<D, 8>), g, b, 0, s, a);
-    else if (n <= 16) hipLaunchKernelGGL((combine_kernel<D, 16>), g, b, 0, s, a);
-    else if (n <= 32) hipLaunchKernelGGL((combine_kernel<D, 32>), g, b, 0, s, a);
-    else if (n <= 64) hipLaunchKernelGGL((combine_kernel<D, 64>), g, b, 0, s, a);
-    else if (n <= 128) hipLaunchKernelGGL((combine_kernel<D, 128>), g, b, 0, s, a);
-    else hipLaunchKernelGGL((combine_kernel<D, 0>), dim3(bh), b, 0, s, a);
-    return hipGetLastError();
+    if constexpr (D == 64) {
+        return launch_ds<D, true>(a, bh, s);   // one slice is the whole row
+    } else {
+        const bool slice = (int64_t)bh < kSliceBelow || a.max_splits > 64;
+        return slice ? launch_ds<D, true>(a, bh, s) : launch_ds<D, false>(a, bh, s);
+    }
 }
 
 }  // namespace

@@ -94,34 +94,44 @@ __device__ __forceinline__ void merge_splits(const float* lse, const float* op, 
     for (int e = 0; e < E; ++e) o[e] = acc[e] * inv;
 }
 
-// The same merge for one 64-element slice of D (a lane per element) and a split
-// count known to be at most NS <= 128, with every load issued before the loads'
-// first use: the lse values (NS/64 per lane), then the slice of every o row.
-// The loads go through buffer resources that end at row ns, so rows past the
-// count read 0 with no memory access and no branch.  The arithmetic is
-// merge_splits' in the same order, so the two give the same bits: split i's
-// weight e^(lse_i - M) is broadcast for the fma of row i; lane L sums the
-// weights of splits i_first + L and i_first + L + 64, as the chunked loop does;
-// rows outside [i_first, ns) take no fma (the window-hidden ones were never
-// written).  op and out point at the slice in row 0; rows are D floats apart.
-template <int D, int NS, bool COHERENT = false>
+// The same merge for E * 64 elements of D (a lane per E consecutive elements: one
+// 64-element slice, or E = D/64 for a whole row) and a split count known to be
+// at most NS <= 128, with every load issued before the loads' first use: the lse
+// values (NS/64 per lane), then the lane's elements of every o row.  The loads go
+// through buffer resources that end at row ns, so rows past the count read 0
+// with no memory access and no branch.  The arithmetic is merge_splits' in the
+// same order, so the two give the same bits: split i's weight e^(lse_i - M) is
+// broadcast for the fma of row i; lane L sums the weights of splits i_first + L
+// and i_first + L + 64, as the chunked loop does; rows outside [i_first, ns)
+// take no fma (the window-hidden ones were never written).  op and out point at
+// the lane group's first element in row 0; rows are D floats apart.
+template <int D, int NS, int E = 1, bool COHERENT = false>
 __device__ __forceinline__ void merge_splits_short(const float* lse, const float* op, int ns, const float* sink_p,
                                                    float* out) {
     static_assert(NS >= 1 && NS <= 2 * kWave, "at most two lse per lane");
+    static_assert((E == 1 || E == 2) && NS * E <= 128, "registers");
     constexpr int K = NS > kWave ? 2 : 1;                // lse values per lane
     constexpr int kAux = COHERENT ? 16 : 0;              // sc1: agent-coherent load
     const int lane = (int)__lane_id();
     const __amdgpu_buffer_rsrc_t rl = __builtin_amdgcn_make_buffer_rsrc((void*)lse, 0, ns * 4, 0x00020000);
-    const int o_bytes = ns > 0 ? ((ns - 1) * D + kWave) * 4 : 0;    // through the slice of row ns-1
+    const int o_bytes = ns > 0 ? ((ns - 1) * D + kWave * E) * 4 : 0;    // through row ns-1's elements
     const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc((void*)op, 0, o_bytes, 0x00020000);
     float l[K];
 #pragma unroll
     for (int k = 0; k < K; ++k)
         l[k] = __int_as_float(__builtin_amdgcn_raw_buffer_load_b32(rl, (k * kWave + lane) * 4, 0, kAux));
-    float v[NS];
+    float v[NS][E];
 #pragma unroll
-    for (int u = 0; u < NS; ++u)
-        v[u] = __int_as_float(__builtin_amdgcn_raw_buffer_load_b32(ro, (u * D + lane) * 4, 0, kAux));
+    for (int u = 0; u < NS; ++u) {
+        const int off = (u * D + lane * E) * 4;
+        if constexpr (E == 2) {
+            const auto x = __builtin_amdgcn_raw_buffer_load_b64(ro, off, 0, kAux);
+            v[u][0] = __uint_as_float(x[0]);
+            v[u][1] = __uint_as_float(x[1]);
+        } else {
+            v[u][0] = __int_as_float(__builtin_amdgcn_raw_buffer_load_b32(ro, off, 0, kAux));
+        }
+    }
 
     float m = -INFINITY, first = (float)ns;
 #pragma unroll
@@ -151,32 +161,36 @@ __device__ __forceinline__ void merge_splits_short(const float* lse, const float
     }
     const float wsum = stride_sum<1>(part);
 
-    float acc = 0.0f;
+    float acc[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) acc[e] = 0.0f;
 #pragma unroll
     for (int i = 0; i < NS; ++i) {
         // a select, not a branch: a branch lets the compiler sink row i's load
         // into it, and the rows would then arrive one round trip at a time
         const bool take = i >= i_first && i < ns;
         const float wi = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w[i / kWave]), i % kWave));
-        acc = take ? fmaf(wi, v[i], acc) : acc;
+#pragma unroll
+        for (int e = 0; e < E; ++e) acc[e] = take ? fmaf(wi, v[i][e], acc[e]) : acc[e];
     }
     const float z = wsum + (has_sink ? __expf(sink - ms) : 0.0f);
     const float inv = z > 0.0f ? 1.0f / z : 0.0f;
-    out[lane] = acc * inv;
+#pragma unroll
+    for (int e = 0; e < E; ++e) out[lane * E + e] = acc[e] * inv;
 }
 
 // merge_splits_short at the smallest depth of NS, NS/2, ..., 8 that holds this
 // row's ns (the branch is uniform and comes before any load).
-template <int D, int NS, bool COHERENT = false>
+template <int D, int NS, int E = 1, bool COHERENT = false>
 __device__ __forceinline__ void merge_splits_short_any(const float* lse, const float* op, int ns, const float* sink_p,
                                                        float* out) {
     if constexpr (NS > 8) {
         if (ns <= NS / 2) {
-            merge_splits_short_any<D, NS / 2, COHERENT>(lse, op, ns, sink_p, out);
+            merge_splits_short_any<D, NS / 2, E, COHERENT>(lse, op, ns, sink_p, out);
             return;
         }
     }
-    merge_splits_short<D, NS, COHERENT>(lse, op, ns, sink_p, out);
+    merge_splits_short<D, NS, E, COHERENT>(lse, op, ns, sink_p, out);
 }
 
 }  // namespace pfa

@@ -1,7 +1,9 @@
 """The combine kernel (LSE merge of split partials, TileInfer.jl performance page,
 "Fused kernels, FlashAttention and PagedAttention") at split counts on both sides
 of each launch depth: rows of up to 8, 16, 32, 64 and 128 splits are loaded at
-once, longer ones through the chunked merge.
+once, longer ones through the chunked merge; and with (row, head) items on both
+sides of the launch's slice threshold (a wave per 64-element slice of D, or per
+whole row).
 
 The partials are synthetic and seeded: lse values spread over several units, a
 leading run of -inf splits per sequence (the splits a window hides, whose o rows
@@ -108,3 +110,30 @@ def test_one_shot_and_chunked_merge_give_the_same_bits(ns_max, D):
     short = gpu_combine(o_gpu, lse_gpu, lens, ns_max, D, sinks)
     chunked = gpu_combine(o_w, l_w, lens, wide, D, sinks)
     assert np.array_equal(short.view(np.uint32), chunked.view(np.uint32))
+
+
+@pytest.mark.parametrize("ms", [9, 33, 64])
+def test_whole_row_waves_for_many_rows(ms):
+    """1030 rows x 8 heads = 8240 (row, head) items at D = 128: past the launch's
+    slice threshold, so one wave takes a whole row (2 elements per lane).  Against
+    the oracle, and bit-equal to the chunked merge on the same partials (laid out
+    with 129 splits per row)."""
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    D, B = 128, 1030
+    rng = np.random.default_rng(3000 + ms)
+    lens = rng.integers(1, ms * S + 1, B).astype(np.int32)
+    hidden = list(rng.integers(0, 3, B) * (ms // 4))
+    sinks = (rng.standard_normal(Hq) * 2).astype(np.float32)
+    o, lse, o_gpu, lse_gpu = partials(4000 + ms, B, ms, D, lens, hidden, sinks)
+    ref = O.combine(o.astype(np.float64), lse.astype(np.float64), lens, S, sinks)
+    got = gpu_combine(o_gpu, lse_gpu, lens, ms, D, sinks)
+    assert np.isfinite(got).all()
+    np.testing.assert_allclose(got, ref, rtol=0, atol=ATOL)
+    wide = 129
+    o_w = np.full((B, Hq, wide, D), np.nan, np.float32)
+    l_w = np.full((B, Hq, wide), np.nan, np.float32)
+    o_w[:, :, :ms] = o_gpu
+    l_w[:, :, :ms] = lse_gpu
+    chunked = gpu_combine(o_w, l_w, lens, wide, D, sinks)
+    assert np.array_equal(got.view(np.uint32), chunked.view(np.uint32))
