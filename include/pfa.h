@@ -351,9 +351,11 @@ pfa_status pfa_paged_attn_prefill(const pfa_attn_desc* desc, const pfa_kv_pool* 
 
 /*
  * A prefill split choice for `num_cus` compute units (0 means 256).  It returns
- * max_splits, 1 when the query tiles alone give at least two workgroups per CU,
- * and writes the matching split_keys to *split_keys (0 when unsplit).  This is
- * host-side arithmetic only.
+ * max_splits, 1 when the query tiles alone give at least two workgroups per CU
+ * or when the keys beyond the chunk (max_seq_len - max_q_len) are fewer than
+ * half the chunk (a fresh prompt's causal triangle runs faster unsplit than
+ * split and merged), and writes the matching split_keys to *split_keys (0 when
+ * unsplit).  This is host-side arithmetic only.
  */
 int32_t pfa_prefill_num_splits(const pfa_attn_desc* desc, int32_t batch, int32_t max_q_len,
                                int32_t max_seq_len, int32_t num_cus, int32_t* split_keys);
