@@ -334,7 +334,9 @@ pfa_status pfa_paged_attn_combine(const pfa_attn_desc* desc, const float* o_part
  *   With a sliding window of at most 512 keys, the work runs on the KV-split
  *   kernel build (128-row workgroups, 32-key tiles) whether or not the key range
  *   is split: each workgroup then sees only a few tiles, and the smaller
- *   workgroups keep more of them resident per CU.
+ *   workgroups keep more of them resident per CU.  So does an unsplit chunk whose
+ *   256-row query tiles would number fewer than 256 (fewer workgroups than the
+ *   MI355X has CUs): the 128-row tiles double them.
  *
  *   INT8 pools (the TileInfer.jl performance page prefills over its INT8 cache
  *   too) are attended as the cache they stand for, code * scale (* the smoothing

@@ -73,3 +73,18 @@ def pool_bits_equal(gpu_pool: pfa.KVPool, ref: dict, kv_dtype: str):
             np.array_equal(gpu_pool.v.cpu().numpy(), ref["v"]) and
             np.array_equal(f32(gpu_pool.k_scale), ref["k_scale"].view(np.uint32)) and
             np.array_equal(f32(gpu_pool.v_scale), ref["v_scale"].view(np.uint32)))
+
+
+def main_build_batch(prm: dict, lens: list, qlens: list):
+    """The case's sequences repeated until an unsplit prefill of them has at least
+    256 of the 256-row build's query tiles (batch x KV heads x ceil(max_q_len /
+    (256 / G))): smaller unsplit chunks run on the 128-row build, so this is how a
+    small case reaches the 256-row one.  None for windows of at most 512 keys,
+    which always take the 128-row build."""
+    if 0 < prm.get("window", 0) <= 512:
+        return None
+    G = prm["Hq"] // prm["Hkv"]
+    tiles = prm["Hkv"] * -(-max(qlens) // (256 // G))
+    k = max(1, -(-256 // (len(lens) * tiles)))
+    return lens * k, qlens * k
+

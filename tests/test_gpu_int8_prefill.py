@@ -17,7 +17,7 @@ import torch
 import oracle as O
 import paged_flash_attention_amd as pfa
 import workloads as W
-from gpu_support import INT8_TOL, GpuCase, assert_close, oracle_pool
+from gpu_support import INT8_TOL, GpuCase, assert_close, main_build_batch, oracle_pool
 
 pytestmark = pytest.mark.gpu
 
@@ -73,6 +73,22 @@ def test_int8_prefill_parity(ci):
     for split in (None, (64, -(-n // 64)), (256, -(-n // 256))):
         got = g.prefill(split=split)
         assert_close(got, ref, tol, f"int8 prefill {name} split={split}")
+
+
+I8_MAIN_BUILD = [ci for ci, c in enumerate(INT8_PREFILL_CASES) if main_build_batch(c[1], c[2], c[3]) is not None]
+
+
+@pytest.mark.parametrize("ci", I8_MAIN_BUILD, ids=[INT8_PREFILL_CASES[ci][0] for ci in I8_MAIN_BUILD])
+def test_int8_prefill_parity_on_the_256_row_build(ci):
+    """As above, the sequences repeated until the unsplit chunk takes the 256-row build."""
+    name, prm, lens, qlens, extra = INT8_PREFILL_CASES[ci]
+    lens, qlens = main_build_batch(prm, lens, qlens)
+    case = _case(f"i8p256_{name}", 860 + ci, prm, lens, qlens, extra)
+    g = GpuCase(case)
+    ref = O.paged_attention(case.q, case.cu_q, oracle_pool(case), case.block_table, case.seq_lens, case.p)
+    scale = max(1.0, float(np.max(np.abs(ref)))) if "v_mags" in extra else 1.0
+    tol = dict(INT8_TOL, max_abs=INT8_TOL["max_abs"] * scale)
+    assert_close(g.prefill(split=None), ref, tol, f"int8 prefill {name} on the 256-row build ({len(lens)} sequences)")
 
 
 INT8_VERIFY_CASES = [

@@ -19,7 +19,7 @@ import torch
 import oracle as O
 import paged_flash_attention_amd as pfa
 import workloads as W
-from gpu_support import (BF16_TOL, INT8_TOL, GpuCase, assert_close, bits_of, dev_bf16, dev_i32,
+from gpu_support import (BF16_TOL, INT8_TOL, GpuCase, assert_close, bits_of, dev_bf16, dev_i32, main_build_batch,
                          gpu_attn_input, oracle_attn_input, oracle_pool, pool_bits_equal, tol_of)
 
 pytestmark = pytest.mark.gpu
@@ -380,6 +380,21 @@ def test_prefill_parity(ci):
     for split in (None, (64, -(-max(lens) // 64)), (256, -(-max(lens) // 256))):
         got = g.prefill(split=split)
         assert_close(got, ref, BF16_TOL, f"prefill case {ci} split={split}")
+
+
+MAIN_BUILD_CASES = [ci for ci, c in enumerate(PREFILL_CASES) if main_build_batch(*c) is not None]
+
+
+@pytest.mark.parametrize("ci", MAIN_BUILD_CASES)
+def test_prefill_parity_on_the_256_row_build(ci):
+    """The prefill cases whose build is not fixed by a short window, their sequences
+    repeated until the unsplit chunk takes the 256-row (64-key tile) build."""
+    prm, lens, qlens = PREFILL_CASES[ci]
+    lens, qlens = main_build_batch(prm, lens, qlens)
+    case = W.make_case(f"pre256_{ci}", 260 + ci, P(seed=ci, **prm), lens, qlens, split_keys=0)
+    g = GpuCase(case)
+    ref = O.paged_attention(case.q, case.cu_q, oracle_pool(case), case.block_table, case.seq_lens, case.p)
+    assert_close(g.prefill(split=None), ref, BF16_TOL, f"prefill case {ci} on the 256-row build ({len(lens)} sequences)")
 
 
 def test_prefill_split_choice():
