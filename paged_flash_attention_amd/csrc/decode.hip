@@ -155,18 +155,12 @@ __device__ __forceinline__ void v_pairs(const uint2& a, const uint2& b, uint32_t
 // 8 rows at a time with ds_read_b64_tr_b8: in each 16-lane group, lane j points
 // at row j/2, bytes 8(j%2)..+7 of an 8 x 16-byte block, and lane i receives
 // column i of the block, rows in order (checked on gfx950).  The codes enter the
-// dot2 as signed bf16 (exact), so no offset is carried.
+// dot2 as the keys' do, fp16 pairs 1152 + c (k_pairs), against fp16 weights; the
+// offset leaves at the end as 1152 times the sum of the rounded weights.
 typedef int i32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 #define LDS3 __attribute__((address_space(3)))
-// rows (2u, 2u+1) of a transposed read -> bf16 pair u, from the signed codes
-__device__ __forceinline__ void vcol_pairs(i32x2 x, uint32_t (&v)[4]) {
-    v[0] = pack_hi16((float)(int8_t)x.x, (float)(int8_t)(x.x >> 8));
-    v[1] = pack_hi16((float)(int8_t)(x.x >> 16), (float)(x.x >> 24));
-    v[2] = pack_hi16((float)(int8_t)x.y, (float)(int8_t)(x.y >> 8));
-    v[3] = pack_hi16((float)(int8_t)(x.y >> 16), (float)(x.y >> 24));
-}
 
 // An empty asm that makes x depend on every element of o: loads addressed by x
 // cannot then be hoisted above the code that produced o.
@@ -209,6 +203,10 @@ void decode_kernel(DecodeArgs a, const int32_t* __restrict__ block_table) {
     static_assert(G <= LPK, "group size");
     static_assert(!PAIRED || NLOAD % 2 == 0, "key pairs");
     static_assert(!VCOL || (2 * kPage * D + 512) * 2 >= kFusedMergeChunk * 4, "merge weights in the ring");
+    // VCOL with two lanes per head (D = 128): the two lanes of a head end the
+    // butterfly on different keys, so each lane scores and weighs half the keys
+    constexpr bool JOINT = VCOL && HG == 2;
+    constexpr int NS = JOINT ? NLOAD / 2 : NLOAD;   // scores per lane and page
     typedef typename Chunk<INT8>::T CT;
 
     // weights of a page, double-buffered: [key][head] floats (G <= 4), or for
@@ -374,9 +372,11 @@ void decode_kernel(DecodeArgs a, const int32_t* __restrict__ block_table) {
     struct PageRegs {
         CT k[VCOL ? 1 : NLOAD], v[VCOL ? 1 : NLOAD];
         float ks[VCOL ? 1 : NLOAD], vs[VCOL ? 1 : NLOAD];
-        uint32_t st;   // VCOL: LDS byte address of the stage
+        const LDS3 int8_t* st;   // VCOL: the page's stage
     };
-    const uint32_t ring0 = (uint32_t)(uintptr_t)(const LDS3 void*)ring;
+    // (stage addresses as LDS pointers, so that constant offsets fold into the reads)
+    const LDS3 int8_t* const ring3 = (const LDS3 int8_t*)ring;
+    auto lds_u32 = [](const LDS3 int8_t* x) __attribute__((always_inline)) { return (uint32_t)(uintptr_t)x; };
     // a page's block-table entry (a scalar load; the index is clamped to the
     // split's last page so that the read stays inside the row), read one page
     // ahead of the loads that use it
@@ -392,11 +392,11 @@ void decode_kernel(DecodeArgs a, const int32_t* __restrict__ block_table) {
             const char* vt = vbase + blk * head_stride;
 #pragma unroll
             for (int c = 0; c < kTile / 1024; ++c) {
-                dma16(kt + 1024 * c, 16u * (uint32_t)lane, r.st + 1024 * c);
-                dma16(vt + 1024 * c, 16u * (uint32_t)lane, r.st + kTile + 1024 * c);
+                dma16(kt + 1024 * c, 16u * (uint32_t)lane, lds_u32(r.st + 1024 * c));
+                dma16(vt + 1024 * c, 16u * (uint32_t)lane, lds_u32(r.st + kTile + 1024 * c));
             }
-            dma4(a.k_scale + blk * kPage, 4u * (uint32_t)(lane % kPage), r.st + 2 * kTile);
-            dma4(a.v_scale + blk * kPage, 4u * (uint32_t)(lane % kPage), r.st + 2 * kTile + 256);
+            dma4(a.k_scale + blk * kPage, 4u * (uint32_t)(lane % kPage), lds_u32(r.st + 2 * kTile));
+            dma4(a.v_scale + blk * kPage, 4u * (uint32_t)(lane % kPage), lds_u32(r.st + 2 * kTile + 256));
         } else {
             const char* kp = kbase + blk * head_stride * EB + lane_off;
             const char* vp = vbase + blk * head_stride * EB + lane_off;
@@ -429,6 +429,16 @@ void decode_kernel(DecodeArgs a, const int32_t* __restrict__ block_table) {
     constexpr int kTrStep = (KPL == 4 ? 8 : 4) * D;
     float m_run = -INFINITY;   // running max (log2 units) of this lane's head
     float l_run = 0.0f;        // this lane's share of sum 2^(s - m_run) (its keys, its head)
+    // VCOL: a weight enters the p.v dot2 as fp16 w = p * vs * 2^-vexp (vs the key's
+    // value scale).  vexp is wave-uniform and only rises: whenever a value scale
+    // exceeds vlim = 2^(vexp + 7), vexp moves to 4 above the exponent of the page's
+    // largest scale and o and wsum are rescaled by the power of two, so w <= 2^8 *
+    // 2^7 always fits fp16.  Scales far below the largest lose fp16 precision:
+    // a weight below 2^-14 keeps an absolute error of at most 2^-25, which bounds
+    // the output's error by about 2^-16 times the split's largest value scale.
+    int vexp = -1000;
+    float vlim = 0.0f;
+    float wsum = 0.0f;   // VCOL: sum of this lane's head's rounded weights (its key groups)
 
     int pb = 0;
     // one page: scores, lazy rescale, weights, p.v
@@ -443,18 +453,55 @@ void decode_kernel(DecodeArgs a, const int32_t* __restrict__ block_table) {
         }
 
         // ---- scores ----
-        float s[NLOAD];
+        float s[NS];
         bool valid[NLOAD];   // BF16
-        float vsl[NLOAD];    // INT8: the value scales (VCOL: from the stage)
+        float vsl[NS];       // INT8: the value scales (VCOL: from the stage)
+        // the load group of score i (JOINT: lane t = sub % 2 of a head pair holds
+        // load groups 2i + t)
+        auto group_of = [&](int i) __attribute__((always_inline)) { return JOINT ? 2 * i + (sub & 1) : i; };
         auto outside = [&](int i) __attribute__((always_inline)) {
-            const int key = kpos0 + i * KPL + kg;
+            const int key = kpos0 + group_of(i) * KPL + kg;
             return key < lo || key >= hi;
         };
+        if constexpr (JOINT) {
+            // load groups (2i, 2i+1) in one butterfly over 2G sums: slot 2a + b holds
+            // head (a ^ myhead) on group 2i + (b ^ t), so the lanes end on
+            // (head sub / 2, group 2i + sub % 2)
+            const int own = (sub & 1) * KPL * D, oth = KPL * D - own;
 #pragma unroll
-        for (int i = 0; i < NLOAD; ++i) {
+            for (int i = 0; i < NS; ++i) {
+                const LDS3 int8_t* kr = r.st + (2 * i * KPL + kg) * D + sub * 8;
+                const u32x2 wa = *(const LDS3 u32x2*)(kr + own);
+                const u32x2 wb = *(const LDS3 u32x2*)(kr + oth);
+                uint32_t ka[4], kb[4];
+                k_pairs(make_uint2(wa.x, wa.y), ka);
+                k_pairs(make_uint2(wb.x, wb.y), kb);
+                float acc[2 * G];
+#pragma unroll
+                for (int a2 = 0; a2 < G; ++a2) {
+                    float ta, tb;
+                    asm("v_dot2_f32_f16 %0, %1, %2, 0" : "=v"(ta) : "v"(q[a2][0]), "v"(ka[0]));
+                    asm("v_dot2_f32_f16 %0, %1, %2, 0" : "=v"(tb) : "v"(q[a2][0]), "v"(kb[0]));
+#pragma unroll
+                    for (int w = 1; w < 4; ++w) {
+                        ta = __builtin_amdgcn_fdot2(as_f16x2(q[a2][w]), as_f16x2(ka[w]), ta, false);
+                        tb = __builtin_amdgcn_fdot2(as_f16x2(q[a2][w]), as_f16x2(kb[w]), tb, false);
+                    }
+                    acc[2 * a2] = ta;
+                    acc[2 * a2 + 1] = tb;
+                }
+                const float dot = transpose_reduce<LPK, 2 * G>(acc) - qbias;
+                const int key = group_of(i) * KPL + kg;
+                const float ksv = *(const LDS3 float*)(r.st + 2 * kTile + 4 * key);
+                vsl[i] = *(const LDS3 float*)(r.st + 2 * kTile + 256 + 4 * key);
+                s[i] = dot * (c2 * ksv);
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < (JOINT ? 0 : NLOAD); ++i) {
             uint32_t kp[4];
             if constexpr (VCOL) {
-                const u32x2 w = *(const LDS3 u32x2*)(uintptr_t)(r.st + (i * KPL + kg) * D + sub * 8);
+                const u32x2 w = *(const LDS3 u32x2*)(r.st + (i * KPL + kg) * D + sub * 8);
                 k_pairs(make_uint2(w.x, w.y), kp);
             } else {
                 k_pairs(r.k[i], kp);
@@ -482,8 +529,8 @@ void decode_kernel(DecodeArgs a, const int32_t* __restrict__ block_table) {
             if constexpr (INT8) dot -= qbias;
             float ksv = 0.0f;
             if constexpr (VCOL) {
-                ksv = *(const LDS3 float*)(uintptr_t)(r.st + 2 * kTile + 4 * (i * KPL + kg));
-                vsl[i] = *(const LDS3 float*)(uintptr_t)(r.st + 2 * kTile + 256 + 4 * (i * KPL + kg));
+                ksv = *(const LDS3 float*)(r.st + 2 * kTile + 4 * (i * KPL + kg));
+                vsl[i] = *(const LDS3 float*)(r.st + 2 * kTile + 256 + 4 * (i * KPL + kg));
             } else if constexpr (INT8) {
                 ksv = r.ks[i];
                 vsl[i] = r.vs[i];
@@ -504,11 +551,31 @@ void decode_kernel(DecodeArgs a, const int32_t* __restrict__ block_table) {
         if constexpr (INT8) {
             if (!(kpos0 >= lo && kpos0 + kPage <= hi)) {
 #pragma unroll
-                for (int i = 0; i < NLOAD; ++i) {
+                for (int i = 0; i < NS; ++i) {
                     const bool out = outside(i);
                     s[i] = out ? -INFINITY : s[i];
                     vsl[i] = out ? 0.0f : vsl[i];
                 }
+            }
+        }
+        if constexpr (VCOL) {
+            bool big = false;
+#pragma unroll
+            for (int i = 0; i < NS; ++i) big |= vsl[i] > vlim;
+            if (__any(big)) {   // the first page with a non-zero scale, then rarely
+                float vm = vsl[0];
+#pragma unroll
+                for (int i = 1; i < NS; ++i) vm = fmaxf(vm, vsl[i]);
+                vm = stride_max<1>(vm);                                       // > 0 here
+                const int en = __builtin_amdgcn_readfirstlane(__builtin_amdgcn_frexp_expf(vm)) - 3;
+                const float f = ldexpf(1.0f, vexp - en);                       // 0 the first time
+#pragma unroll
+                for (int g = 0; g < G; ++g)
+#pragma unroll
+                    for (int j = 0; j < OJ; ++j) o[g][j] *= f;
+                wsum *= f;
+                vexp = en;
+                vlim = ldexpf(1.0f, en + 7);
             }
         }
         // ---- running max, lazy rescale with headroom: the reference max moves only
@@ -516,13 +583,23 @@ void decode_kernel(DecodeArgs a, const int32_t* __restrict__ block_table) {
         // (no overflow in fp32 or bf16) and the rescale, G*8 multiplies, runs on
         // few pages.  o and l share the reference, so o/l and m + log2(l) hold. ----
         float pm = s[0];
+        float m_new;
+        if constexpr (JOINT && NS == 2) {
+            // (VALU-bound: the maxima without fmaxf's input quieting moves; the
+            // head pair's lanes first)
+            pm = vmax(s[0], s[1]);
+            pm = xor32_vmax(xor16_vmax(vmax(pm, dpp_xor<1>(pm))));
+            m_new = vmax(m_run, pm);
+        } else {
 #pragma unroll
-        for (int i = 1; i < NLOAD; ++i) pm = fmaxf(pm, s[i]);
-        pm = stride_max<LPK>(pm);
-        const float m_new = fmaxf(m_run, pm);
+            for (int i = 1; i < NLOAD; ++i) pm = fmaxf(pm, s[i]);
+            pm = stride_max<LPK>(pm);
+            m_new = fmaxf(m_run, pm);
+        }
         if (__any(m_new > m_run + 8.0f)) {
             const float alpha = fast_exp2(m_run - m_new);   // 0 on the first page
             l_run *= alpha;
+            if constexpr (VCOL) wsum *= alpha;
 #pragma unroll
             for (int g = 0; g < G; ++g) {
                 const float ag = lane_read(alpha, g * HG);
@@ -544,11 +621,27 @@ void decode_kernel(DecodeArgs a, const int32_t* __restrict__ block_table) {
         } else {
             // the weights of keys (i, i+1) as one bf16 pair, at [i/2][kg][head]
             uint32_t* pp_buf = reinterpret_cast<uint32_t*>(&p_buf[pb][0][0]);
+            if constexpr (JOINT) {
+                // lane t weighs group 2i + t; lane 0 of the pair packs both
 #pragma unroll
-            for (int i = 0; i < NLOAD; i += 2) {
+                for (int i = 0; i < NS; ++i) {
+                    const float pw = fast_exp2(s[i] - m_run);
+                    l_run += pw;
+                    const float pv = pw * ldexpf(vsl[i], -vexp);
+                    const uint32_t pr = pack_f16_rne(pv, dpp_xor<1>(pv));
+                    wsum = __builtin_amdgcn_fdot2(as_f16x2(pr), as_f16x2(0x3C003C00u), wsum, false);
+                    if (sub % HG == 0) pp_buf[(i * KPL + kg) * G + myhead] = pr;
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < (JOINT ? 0 : NLOAD); i += 2) {
                 const float p0 = fast_exp2(s[i] - m_run), p1 = fast_exp2(s[i + 1] - m_run);
                 uint32_t pr;
-                if constexpr (INT8) {
+                if constexpr (VCOL) {
+                    l_run += p0 + p1;
+                    pr = pack_f16_rne(p0 * ldexpf(vsl[i], -vexp), p1 * ldexpf(vsl[i + 1], -vexp));
+                    wsum = __builtin_amdgcn_fdot2(as_f16x2(pr), as_f16x2(0x3C003C00u), wsum, false);
+                } else if constexpr (INT8) {
                     l_run += p0 + p1;
                     pr = pack_bf16_rne(p0 * vsl[i], p1 * vsl[i + 1]);
                 } else {
@@ -569,7 +662,7 @@ void decode_kernel(DecodeArgs a, const int32_t* __restrict__ block_table) {
             // that also takes the last result of the pair before, so the compiler
             // cannot hoist every pair's reads (64 registers) to the top.
             const uint32_t pp_base = (uint32_t)(uintptr_t)(const LDS3 void*)&p_buf[pb][0][0];
-            const LDS3 char* vt = (const LDS3 char*)(uintptr_t)(r.st + kTile + tr_off);
+            const LDS3 int8_t* vt = r.st + kTile + tr_off;
             auto read_pp = [&](uint32_t addr, uint32_t (&pp)[G]) __attribute__((always_inline)) {
 #pragma unroll
                 for (int q4 = 0; q4 < G / 4; ++q4) {
@@ -589,7 +682,7 @@ void decode_kernel(DecodeArgs a, const int32_t* __restrict__ block_table) {
             for (int h = 0; h < 2; ++h) {
                 uint32_t vv[NC][4];
 #pragma unroll
-                for (int c = 0; c < NC; ++c) vcol_pairs(raw[h][c], vv[c]);
+                for (int c = 0; c < NC; ++c) k_pairs(make_uint2((uint32_t)raw[h][c].x, (uint32_t)raw[h][c].y), vv[c]);
 #pragma unroll
                 for (int u = 0; u < 4; ++u) {
                     const int m = 4 * h + u;
@@ -601,8 +694,7 @@ void decode_kernel(DecodeArgs a, const int32_t* __restrict__ block_table) {
                     for (int g = 0; g < G; ++g)
 #pragma unroll
                         for (int c = 0; c < NC; ++c)
-                            o[g][c] = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(ppc[g]), as_bf16x2(vv[c][u]), o[g][c],
-                                                                      false);
+                            o[g][c] = __builtin_amdgcn_fdot2(as_f16x2(ppc[g]), as_f16x2(vv[c][u]), o[g][c], false);
 #pragma unroll
                     for (int g = 0; g < G; ++g) ppc[g] = ppn[g];
                 }
@@ -661,8 +753,8 @@ void decode_kernel(DecodeArgs a, const int32_t* __restrict__ block_table) {
         // two sets used in turn (a copy from one to the other would cost a move per
         // register and page)
         PageRegs ra, rb;
-        ra.st = ring0;
-        rb.st = ring0 + kStage;
+        ra.st = ring3;
+        rb.st = ring3 + kStage;
         load_page(page_id(p0), ra);
         int nid = page_id(p0 + 1);
         int p = p0;
@@ -696,7 +788,9 @@ void decode_kernel(DecodeArgs a, const int32_t* __restrict__ block_table) {
 #pragma unroll
             for (int j = 0; j < 8; ++j) o[g][j] = stride_sum<LPK>(o[g][j]);
     }
-    const float l_tot = stride_sum<LPK>(l_run);
+    // (JOINT: the two lanes of a head summed different keys)
+    const float l_tot = stride_sum<LPK>(JOINT ? l_run + dpp_xor<1>(l_run) : l_run);
+    const float w_tot = VCOL ? stride_sum<LPK>(wsum) : 0.0f;
 #pragma unroll
     for (int g = 0; g < G; ++g) {
         const float mg = lane_read(m_run, g * HG);
@@ -708,8 +802,10 @@ void decode_kernel(DecodeArgs a, const int32_t* __restrict__ block_table) {
         const float f = (FINAL && !(den > 0.0f)) ? 0.0f : 1.0f / den;
         float* row = FINAL ? a.out + (row0 + g) * D : a.o_part + ((row0 + g) * a.max_splits + sp) * D;
         if constexpr (VCOL) {
+            // the offset out (1152 per unit of weight), then the scale 2^vexp back
+            const float wg = lane_read(w_tot, g * HG);
 #pragma unroll
-            for (int c = 0; c < NC; ++c) put(row + 64 * c + lane, o[g][c] * f);
+            for (int c = 0; c < NC; ++c) put(row + 64 * c + lane, ldexpf(fmaf(-kK8Offset, wg, o[g][c]) * f, vexp));
         } else if (g % KPL == kg) {
             float* dst = row + sub * 8;
             if (fused) {

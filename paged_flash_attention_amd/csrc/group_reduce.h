@@ -10,7 +10,9 @@ namespace pfa {
 // Transposed butterfly over the LPK lanes of a key group (LPK = 16 or 8), on the
 // VALU only (DPP moves, no LDS).  On entry, slot j of this lane holds its partial
 // sum for head (j ^ myhead), myhead = (lane % LPK) / (LPK / G).  On return, slot 0
-// holds this lane's head's full sum over the group.
+// holds this lane's head's full sum over the group.  (A "head" is any of G sums
+// the group shares: G = LPK, two keys of 8 heads each, leaves every lane a sum of
+// its own.)
 //
 // Each stage adds the partner's slot j ^ delta to slot j for the lower half of the
 // live slots.  The partner is lane ^ m, with m = 15 (row mirror), 7 (half-row
@@ -43,7 +45,7 @@ __device__ __forceinline__ void mirror_stage(float (&acc)[G]) {
 template <int LPK, int G>
 __device__ __forceinline__ float transpose_reduce(float (&acc)[G]) {
     static_assert(LPK == 16 || LPK == 8, "lanes per key");
-    static_assert(G >= 1 && G <= 8 && G <= LPK, "group size");
+    static_assert(G >= 1 && G <= LPK, "group size");
     constexpr int N1 = G, N2 = N1 > 1 ? N1 / 2 : 1, N3 = N2 > 1 ? N2 / 2 : 1, N4 = N3 > 1 ? N3 / 2 : 1;
     if constexpr (LPK == 16) {
         mirror_stage<LPK, G, 15, N1>(acc);

@@ -89,6 +89,29 @@ __device__ __forceinline__ float xor16_sum(float x) {
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// v_max_f32 / v_max3_f32 as they stand.  fmaxf makes the compiler quiet
+// signalling NaNs in inputs it cannot prove canonical (a move per operand); these
+// are for scores, which are never NaN where they are compared.
+__device__ __forceinline__ float vmax(float a, float b) {
+    float r;
+    asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+    return r;
+}
+__device__ __forceinline__ float vmax3(float a, float b, float c) {
+    float r;
+    asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+    return r;
+}
+// vmax over lanes i and i ^ 16, i ^ 32 (the permlane swaps)
+__device__ __forceinline__ float xor16_vmax(float x) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return vmax(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xor32_vmax(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return vmax(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
 // x + / max with x of lane (lane ^ M).  M = 16 and 32 use the permlane swaps (VALU);
 // the others a DPP or swizzle move.
 template <int M>
