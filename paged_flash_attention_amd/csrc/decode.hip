@@ -300,66 +300,6 @@ void decode_kernel(DecodeArgs a, const int32_t* __restrict__ block_table) {
         hi = min(hi, s0 + a.split_keys);
     }
 
-    // q: slot j holds head (j ^ myhead), dims sub*8 .. sub*8+7, as bf16 pairs
-    uint32_t q[G][4];
-#pragma unroll
-    for (int j = 0; j < G; ++j) {
-        const uint16_t* qp = a.q + (row0 + (j ^ myhead)) * D + sub * 8;
-        const uint4 v = *reinterpret_cast<const uint4*>(qp);
-        q[j][0] = v.x; q[j][1] = v.y; q[j][2] = v.z; q[j][3] = v.w;
-    }
-    if constexpr (INT8) {
-        if (a.k_smooth) {   // keys stored smoothed (k / s): the query meets q * s (s a power of two: exact)
-            const float4* sp = reinterpret_cast<const float4*>(a.k_smooth + sub * 8);
-            const float4 s0 = __ldg(sp), s1 = __ldg(sp + 1);
-            const float sv[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
-#pragma unroll
-            for (int j = 0; j < G; ++j)
-#pragma unroll
-                for (int w = 0; w < 4; ++w)
-                    q[j][w] = pack_bf16_rne(bf16_lo(q[j][w]) * smooth_pow2(sv[2 * w]),
-                                            bf16_hi(q[j][w]) * smooth_pow2(sv[2 * w + 1]));
-        }
-    }
-    float c2 = a.sm_scale * kLog2e;      // scores kept in log2 units
-    float qbias = 0.0f;   // INT8: 1152 * sum_d q'[myhead][d]
-    if constexpr (INT8) {
-        // q meets the fp16 key pairs in fp16.  Each head is first scaled by the
-        // power of two 2^sh that brings its largest |q| into [2^14, 2^15); a bf16
-        // element then converts exactly unless it is more than 2^28 below that
-        // largest one (a subnormal in fp16), where the rounding is below the fp32
-        // summation error of the dot.  The score is scaled back by 2^-sh.
-        __shared__ uint32_t qmax[G];
-        if (lane < G) qmax[lane] = 0u;
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-#pragma unroll
-        for (int j = 0; j < G; ++j) {
-            uint32_t mx = 0u;   // bit patterns of |bf16| order as the values do
-#pragma unroll
-            for (int w = 0; w < 4; ++w) mx = max(mx, max(q[j][w] & 0x7fffu, (q[j][w] >> 16) & 0x7fffu));
-            atomicMax(&qmax[j ^ myhead], mx);
-        }
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        float part[G];
-#pragma unroll
-        for (int j = 0; j < G; ++j) {
-            const int sh = min(141 - (int)(qmax[j ^ myhead] >> 7), 127);   // 14 - exponent of the max
-            float t = 0.0f;
-#pragma unroll
-            for (int w = 0; w < 4; ++w) {
-                q[j][w] = pack_f16_rne(ldexpf(bf16_lo(q[j][w]), sh), ldexpf(bf16_hi(q[j][w]), sh));
-                t += f16_lo(q[j][w]) + f16_hi(q[j][w]);
-            }
-            part[j] = t;
-            if (j == 0) c2 = ldexpf(c2, -sh);   // slot 0 is this lane's own head
-        }
-        qbias = kK8Offset * transpose_reduce<LPK, G>(part);
-    }
-
     const int p0 = lo / kPage, p1 = (hi - 1) / kPage;
     const int32_t* bt = block_table + (int64_t)b * a.bt_stride;
     const int64_t head_stride = (int64_t)kPage * D;              // elements per page-head block
@@ -414,6 +354,152 @@ void decode_kernel(DecodeArgs a, const int32_t* __restrict__ block_table) {
             }
         }
     };
+
+    // kScalarIds: two register sets (VCOL: two ring stages) take the pages in turn.
+    // The first page's loads go out right after q's own loads, so the INT8 query
+    // setup below runs while both are in flight.
+    PageRegs ra, rb;
+    ra.st = ring3;
+    rb.st = ring3 + kStage;
+    auto issue_first = [&]() __attribute__((always_inline)) {
+        if constexpr (kScalarIds<G, INT8>) load_page(page_id(p0), ra);
+    };
+
+    // q: slot j holds head (j ^ myhead), dims sub*8 .. sub*8+7, as bf16 pairs.
+    // INT8: q meets the fp16 key pairs in fp16.  Each head is first scaled by the
+    // power of two 2^sh that brings its largest |q| into [2^14, 2^15); a bf16
+    // element then converts exactly unless it is more than 2^28 below that
+    // largest one (a subnormal in fp16), where the rounding is below the fp32
+    // summation error of the dot.  The score is scaled back by 2^-sh.
+    uint32_t q[G][4];
+    float c2 = a.sm_scale * kLog2e;      // scores kept in log2 units
+    float qbias = 0.0f;   // INT8: 1152 * sum_d q'[myhead][d]
+    if constexpr (VCOL) {
+        // The KPL key groups hold the same q elements.  Each converts G/KPL of
+        // the heads, and the wave shares them through the ring's second
+        // stage, which no page load writes before the page loop: per head and
+        // lane its 4 fp16 pairs and its part of the head's element sum.
+        constexpr int HPK = G / KPL;
+        static_assert(HPK >= 1 && HPK * KPL == G, "heads per key group");
+        static_assert(G * LPK * 16 + LPK * G * 4 <= kStage, "q staging in one stage");
+        __shared__ uint32_t qmax[G];
+        if (lane < G) qmax[lane] = 0u;
+        uint32_t qc[HPK][4];
+#pragma unroll
+        for (int e = 0; e < HPK; ++e) {
+            const uint4 v = *reinterpret_cast<const uint4*>(a.q + (row0 + kg * HPK + e) * D + sub * 8);
+            qc[e][0] = v.x; qc[e][1] = v.y; qc[e][2] = v.z; qc[e][3] = v.w;
+        }
+        issue_first();   // (stage 0; the staging below uses stage 1)
+        if (a.k_smooth) {   // keys stored smoothed (k / s): the query meets q * s (s a power of two: exact)
+            const float4* sp = reinterpret_cast<const float4*>(a.k_smooth + sub * 8);
+            const float4 s0 = __ldg(sp), s1 = __ldg(sp + 1);
+            const float sv[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+#pragma unroll
+            for (int e = 0; e < HPK; ++e)
+#pragma unroll
+                for (int w = 0; w < 4; ++w)
+                    qc[e][w] = pack_bf16_rne(bf16_lo(qc[e][w]) * smooth_pow2(sv[2 * w]),
+                                             bf16_hi(qc[e][w]) * smooth_pow2(sv[2 * w + 1]));
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+        for (int e = 0; e < HPK; ++e) {
+            uint32_t mx = 0u;   // bit patterns of |bf16| order as the values do
+#pragma unroll
+            for (int w = 0; w < 4; ++w) mx = max(mx, max(qc[e][w] & 0x7fffu, (qc[e][w] >> 16) & 0x7fffu));
+            atomicMax(&qmax[kg * HPK + e], mx);
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        LDS3 int8_t* const stage1 = (LDS3 int8_t*)ring + kStage;
+        LDS3 u32x4* const qs = (LDS3 u32x4*)stage1;                       // [G][LPK]
+        LDS3 float* const ts = (LDS3 float*)(stage1 + G * LPK * 16);       // [LPK][G]
+#pragma unroll
+        for (int e = 0; e < HPK; ++e) {
+            const int h = kg * HPK + e;
+            const int sh = min(141 - (int)(qmax[h] >> 7), 127);   // 14 - exponent of the max
+            float t = 0.0f;
+            u32x4 w4;
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                const uint32_t x = pack_f16_rne(ldexpf(bf16_lo(qc[e][w]), sh), ldexpf(bf16_hi(qc[e][w]), sh));
+                t += f16_lo(x) + f16_hi(x);
+                w4[w] = x;
+            }
+            qs[h * LPK + sub] = w4;
+            ts[sub * G + h] = t;
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        float part[G];
+#pragma unroll
+        for (int j = 0; j < G; ++j) {
+            const u32x4 w4 = qs[(j ^ myhead) * LPK + sub];
+            q[j][0] = w4.x; q[j][1] = w4.y; q[j][2] = w4.z; q[j][3] = w4.w;
+            part[j] = ts[sub * G + (j ^ myhead)];
+        }
+        c2 = ldexpf(c2, -min(141 - (int)(qmax[myhead] >> 7), 127));
+        qbias = kK8Offset * transpose_reduce<LPK, G>(part);
+        // the staging reads are complete before the page loads write the stage
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    } else {
+#pragma unroll
+        for (int j = 0; j < G; ++j) {
+            const uint16_t* qp = a.q + (row0 + (j ^ myhead)) * D + sub * 8;
+            const uint4 v = *reinterpret_cast<const uint4*>(qp);
+            q[j][0] = v.x; q[j][1] = v.y; q[j][2] = v.z; q[j][3] = v.w;
+        }
+        issue_first();
+        if constexpr (INT8) {
+            if (a.k_smooth) {   // keys stored smoothed (k / s): the query meets q * s (s a power of two: exact)
+                const float4* sp = reinterpret_cast<const float4*>(a.k_smooth + sub * 8);
+                const float4 s0 = __ldg(sp), s1 = __ldg(sp + 1);
+                const float sv[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+#pragma unroll
+                for (int j = 0; j < G; ++j)
+#pragma unroll
+                    for (int w = 0; w < 4; ++w)
+                        q[j][w] = pack_bf16_rne(bf16_lo(q[j][w]) * smooth_pow2(sv[2 * w]),
+                                                bf16_hi(q[j][w]) * smooth_pow2(sv[2 * w + 1]));
+            }
+        }
+        if constexpr (INT8) {
+            __shared__ uint32_t qmax[G];
+            if (lane < G) qmax[lane] = 0u;
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+            for (int j = 0; j < G; ++j) {
+                uint32_t mx = 0u;   // bit patterns of |bf16| order as the values do
+#pragma unroll
+                for (int w = 0; w < 4; ++w) mx = max(mx, max(q[j][w] & 0x7fffu, (q[j][w] >> 16) & 0x7fffu));
+                atomicMax(&qmax[j ^ myhead], mx);
+            }
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            float part[G];
+#pragma unroll
+            for (int j = 0; j < G; ++j) {
+                const int sh = min(141 - (int)(qmax[j ^ myhead] >> 7), 127);   // 14 - exponent of the max
+                float t = 0.0f;
+#pragma unroll
+                for (int w = 0; w < 4; ++w) {
+                    q[j][w] = pack_f16_rne(ldexpf(bf16_lo(q[j][w]), sh), ldexpf(bf16_hi(q[j][w]), sh));
+                    t += f16_lo(q[j][w]) + f16_hi(q[j][w]);
+                }
+                part[j] = t;
+                if (j == 0) c2 = ldexpf(c2, -sh);   // slot 0 is this lane's own head
+            }
+            qbias = kK8Offset * transpose_reduce<LPK, G>(part);
+        }
+    }
 
     float o[G][OJ];
 #pragma unroll
@@ -752,10 +838,6 @@ void decode_kernel(DecodeArgs a, const int32_t* __restrict__ block_table) {
     if constexpr (kScalarIds<G, INT8>) {
         // two sets used in turn (a copy from one to the other would cost a move per
         // register and page)
-        PageRegs ra, rb;
-        ra.st = ring3;
-        rb.st = ring3 + kStage;
-        load_page(page_id(p0), ra);
         int nid = page_id(p0 + 1);
         int p = p0;
         for (; p < p1; p += 2) {
