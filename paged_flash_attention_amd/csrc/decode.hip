@@ -668,21 +668,7 @@ void decode_kernel(DecodeArgs a, const int32_t* __restrict__ block_table) {
         // when a head's max exceeds it by more than 8, so every weight is <= 2^8
         // (no overflow in fp32 or bf16) and the rescale, G*8 multiplies, runs on
         // few pages.  o and l share the reference, so o/l and m + log2(l) hold. ----
-        float pm = s[0];
-        float m_new;
-        if constexpr (JOINT && NS == 2) {
-            // (VALU-bound: the maxima without fmaxf's input quieting moves; the
-            // head pair's lanes first)
-            pm = vmax(s[0], s[1]);
-            pm = xor32_vmax(xor16_vmax(vmax(pm, dpp_xor<1>(pm))));
-            m_new = vmax(m_run, pm);
-        } else {
-#pragma unroll
-            for (int i = 1; i < NLOAD; ++i) pm = fmaxf(pm, s[i]);
-            pm = stride_max<LPK>(pm);
-            m_new = fmaxf(m_run, pm);
-        }
-        if (__any(m_new > m_run + 8.0f)) {
+        auto rescale = [&](float m_new) __attribute__((always_inline)) {
             const float alpha = fast_exp2(m_run - m_new);   // 0 on the first page
             l_run *= alpha;
             if constexpr (VCOL) wsum *= alpha;
@@ -693,6 +679,24 @@ void decode_kernel(DecodeArgs a, const int32_t* __restrict__ block_table) {
                 for (int j = 0; j < OJ; ++j) o[g][j] *= ag;
             }
             m_run = m_new;
+        };
+        if constexpr (JOINT && NS == 2) {
+            // VALU-bound: a page whose scores all stay within the headroom needs no
+            // max at all, so each lane only compares its own scores with its head's
+            // threshold m_run + 8; the maxima (without fmaxf's input quieting
+            // moves, the head pair's lanes first) are taken when one is above it
+            if (__any(s[0] > m_run + 8.0f || s[1] > m_run + 8.0f)) {
+                float pm = vmax(s[0], s[1]);
+                pm = xor32_vmax(xor16_vmax(vmax(pm, dpp_xor<1>(pm))));
+                rescale(vmax(m_run, pm));
+            }
+        } else {
+            float pm = s[0];
+#pragma unroll
+            for (int i = 1; i < NLOAD; ++i) pm = fmaxf(pm, s[i]);
+            pm = stride_max<LPK>(pm);
+            const float m_new = fmaxf(m_run, pm);
+            if (__any(m_new > m_run + 8.0f)) rescale(m_new);
         }
         // ---- weights, shared within the wave (masked keys weigh 0) ----
         if constexpr (!PAIRED) {
