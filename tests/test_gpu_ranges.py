@@ -1,7 +1,7 @@
 """Parity away from N(0,1) inputs: large logits, keys whose norms grow along the
 sequence (a row's maximum jumps as later keys arrive, so the online softmax moves
 its reference maximum mid-row), sliding windows longer than 512 keys, and INT8
-value vectors from 1e-4 to 1e4 in magnitude.
+value vectors from 1e-30 to 1e30 in magnitude.
 
 Each case runs every kernel build that serves it (decode split and unsplit at
 G = 4 and 8, prefill on the 64-key build and on the 32-key KV-split build, verify)
@@ -150,6 +150,9 @@ V_MAG_CASES = [
     ("1e3", [1e3]),
     ("1e4", [1e4]),
     ("mixed", [1e-4, 1.0, 1e3, 1e4]),
+    # far ends of the bf16 range: the fp16 weights' exponent follows the value scales
+    ("1e-30", [1e-30]),
+    ("1e30", [1e30]),
 ]
 
 
