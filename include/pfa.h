@@ -99,7 +99,8 @@ typedef struct {
     int32_t page_size;         /* P: 16                                               */
     int32_t kv_dtype;          /* pfa_kv_dtype                                        */
     int32_t window;            /* 0 = full attention; W > 0: keys pos-W < j <= pos    */
-    float sm_scale;            /* multiplies q.k (e.g. 1/sqrt(D))                     */
+    float sm_scale;            /* multiplies q.k (e.g. 1/sqrt(D)); decode, prefill and */
+                               /* verify need it positive and finite (PFA_ERR_SHAPE)  */
     const float* sinks;        /* device [Hq] fp32 sink logits, or NULL               */
 } pfa_attn_desc;
 

@@ -32,6 +32,13 @@ pfa_status check_desc(const pfa_attn_desc* d) {
     return PFA_OK;
 }
 
+// The attention kernels take the softmax maximum over scores before the scale
+// (prefill) or fold the scale into per-key factors, which holds for a positive
+// scale only.
+pfa_status check_scale(const pfa_attn_desc* d) {
+    return (d->sm_scale > 0.0f && d->sm_scale <= 3.4e38f) ? PFA_OK : PFA_ERR_SHAPE;   // (false for NaN)
+}
+
 pfa_status check_pool(const pfa_attn_desc* d, const pfa_kv_pool* p) {
     if (!p || !p->k_pool || !p->v_pool) return PFA_ERR_NULL;
     if (d->kv_dtype != PFA_KV_BF16 && (!p->k_scale || !p->v_scale)) return PFA_ERR_NULL;
@@ -261,6 +268,7 @@ pfa_status decode_like(const pfa_attn_desc* desc, const pfa_kv_pool* pool, const
                        float* o_part, float* lse_part, int32_t* counters, float* out, void* stream,
                        bool fused) {
     PFA_TRY(check_desc(desc));
+    PFA_TRY(check_scale(desc));
     PFA_TRY(check_pool(desc, pool));
     const int g = desc->num_q_heads / desc->num_kv_heads;
     if (!decode_group_ok(g)) return PFA_ERR_UNSUPPORTED;
@@ -336,6 +344,7 @@ pfa_status pfa_paged_attn_decode_static(const pfa_attn_desc* desc, const pfa_kv_
                                         const int32_t* seq_lens, int32_t batch, int32_t max_seq_len,
                                         int32_t split_keys, float* out, void* stream) {
     PFA_TRY(check_desc(desc));
+    PFA_TRY(check_scale(desc));
     if (split_keys < 0 || batch < 0 || max_seq_len < 0) return PFA_ERR_SHAPE;
     const int32_t ms = split_keys == 0 ? 1 : pfa_decode_num_splits(max_seq_len, split_keys);
     const size_t o_bytes = (size_t)batch * desc->num_q_heads * ms * desc->head_dim * sizeof(float);
@@ -391,6 +400,7 @@ pfa_status prefill_like(const pfa_attn_desc* desc, const pfa_kv_pool* pool, cons
                         int32_t max_seq_len, int32_t split_keys, int32_t max_splits, float* o_part,
                         float* lse_part, float* out, void* stream, bool split_build) {
     PFA_TRY(check_desc(desc));
+    PFA_TRY(check_scale(desc));
     PFA_TRY(check_pool(desc, pool));
     if (desc->kv_dtype == PFA_KV_TQ3) return PFA_ERR_UNSUPPORTED;
     const int g = desc->num_q_heads / desc->num_kv_heads;

@@ -180,6 +180,24 @@ def test_decode_validation():
     assert dec(desc(), pool(), batch=0, q=None) == OK
 
 
+def test_scale_must_be_positive_and_finite():
+    """The kernels take the softmax maximum before the scale: a scale <= 0, inf or
+    NaN is refused by decode (plain, fused, static), prefill and verify, before any
+    launch."""
+    for bad in (0.0, -0.088, float("inf"), float("nan")):
+        assert dec(desc(sm_scale=bad), pool()) == SHAPE
+        assert decf(desc(sm_scale=bad), pool()) == SHAPE
+        assert pre(desc(sm_scale=bad), pool()) == SHAPE
+        assert ver(desc(sm_scale=bad), pool()) == SHAPE
+        L = pfa.lib()
+        d, p = desc(sm_scale=bad), pool()
+        assert L.pfa_paged_attn_decode_static(ctypes.byref(d), ctypes.byref(p), FAKE, FAKE, 4096, FAKE,
+                                              4, 1024, 256, FAKE, None) == SHAPE
+    # the KV write and the combine do not use it
+    assert kvw(desc(sm_scale=0.0), pool(), T=0, batch=0) == OK
+    assert comb(desc(sm_scale=0.0), batch=0, out=None) == OK
+
+
 def decf(d, p, **kw):
     a = dict(q=FAKE, bt=FAKE, stride=64, sl=FAKE, batch=4, max_len=1024, S=256, ms=4,
              op=FAKE, lp=FAKE, ctr=FAKE, out=FAKE)
