@@ -421,10 +421,11 @@ def run_verify_graph(case, torch, pfa, gs, steps, warmup):
     return dict(step_ms=t0.elapsed_time(t1) / steps, split_keys=sk, max_splits=ms, kv_bytes=verify_bytes(case))
 
 
-def run_decode_graph(case, torch, pfa, gs, steps, warmup):
-    """The decode step (kv_write + split decode + combine) captured once in a HIP graph
-    and replayed: the step without host launch gaps, which dominate a one-sequence
-    step.  One pool (its 16 MB stay in the MALL between replays)."""
+def run_decode_graph(case, torch, pfa, gs, steps, warmup, fused=False):
+    """The decode step (kv_write + split decode + combine, or with fused=True kv_write +
+    the fused decode) captured once in a HIP graph and replayed: the step without host
+    launch gaps, which dominate a one-sequence step.  One pool (its 16 MB stay in the
+    MALL between replays)."""
     g, _, (kn, vn, cun) = setup_case(case, torch, pfa, gs, copies_for_bytes=0)
     p = case.p
     B, Hq, D = case.batch, p.num_q_heads, p.head_dim
@@ -434,9 +435,13 @@ def run_decode_graph(case, torch, pfa, gs, steps, warmup):
     op = torch.empty((B, Hq, ms, D), device="cuda")
     lp = torch.empty((B, Hq, ms), device="cuda")
     out = torch.empty((B, Hq, D), device="cuda")
+    ctr = torch.zeros(B * p.num_kv_heads, dtype=torch.int32, device="cuda")
 
     def step():
         pfa.kv_write(g.desc, g.pool, kn, vn, cun, g.seq_lens, g.bt)
+        if fused:
+            pfa.paged_attn_decode_fused(g.desc, g.pool, g.q, g.bt, g.seq_lens, max_len, S, ms, op, lp, ctr, out)
+            return
         pfa.paged_attn_decode(g.desc, g.pool, g.q, g.bt, g.seq_lens, max_len, S, ms, o_part=op, lse_part=lp)
         pfa.paged_attn_combine(g.desc, op, lp, g.seq_lens, S, ms, out)
 
@@ -574,6 +579,8 @@ def main():
         "decode_batch32_ctx512_8192_fused": lambda: W.decode_batch32_ctx512_8192(),
         "decode_1seq_ctx1024": lambda: W.decode_1seq_ctx1024(),
         "decode_1seq_ctx1024_graph": lambda: W.decode_1seq_ctx1024(),
+        "decode_1seq_ctx1024_fused": lambda: W.decode_1seq_ctx1024(),
+        "decode_1seq_ctx1024_fused_graph": lambda: W.decode_1seq_ctx1024(),
         "decode_int8_batch8_ctx32768": lambda: W.decode_int8_qwen30b(),
         "decode_int8_batch8_ctx32768_smooth": lambda: W.decode_int8_qwen30b(smooth=True),
         "decode_tq3_batch8_ctx32768": lambda: W.decode_tq3_qwen30b(),
@@ -615,7 +622,7 @@ def main():
             r.update(metric="kv write GB/s", kernel_gbs=round(gbs, 1), frac_of_hbm_peak=round(gbs / HBM_PEAK_GBS, 4))
             return case, r
         if name.startswith("decode") and name.endswith("_graph"):
-            r = run_decode_graph(case, torch, pfa, gs, steps, warmup)
+            r = run_decode_graph(case, torch, pfa, gs, steps, warmup, fused="_fused" in name)
             r.update(metric="decode step us (graph replay)")
             return case, r
         if name.endswith("_graph"):
@@ -684,6 +691,7 @@ def main():
     extra = {}
     if not args.no_extra and args.workload == "decode_batch32_ctx512_8192":
         for name, st in (("decode_1seq_ctx1024", 100), ("decode_1seq_ctx1024_graph", 200),
+                         ("decode_1seq_ctx1024_fused", 100), ("decode_1seq_ctx1024_fused_graph", 200),
                          ("decode_batch32_ctx512_8192_fused", 50),
                          ("decode_batch32_ctx8192", 30), ("decode_batch32_ctx8192_s1024", 30),
                          ("decode_int8_batch8_ctx32768", 30), ("decode_int8_batch8_ctx32768_smooth", 30),

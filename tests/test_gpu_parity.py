@@ -493,9 +493,11 @@ def test_decode_equals_last_prefill_row():
 # a decode step under HIP graph capture: every replay equals the eager step
 # ---------------------------------------------------------------------------
 
-@pytest.mark.parametrize("kv", ["bf16", "int8", "tq3"])
-def test_decode_step_replays_in_a_graph(kv):
-    """kv_write + split decode + combine captured once and replayed four times, with
+@pytest.mark.parametrize("kv,fused", [("bf16", False), ("int8", False), ("tq3", False),
+                                      ("bf16", True), ("int8", True)])
+def test_decode_step_replays_in_a_graph(kv, fused):
+    """kv_write + split decode + combine (or the fused decode, whose last split per
+    row merges and clears its counter) captured once and replayed four times, with
     eager work and synchronisations between the replays; each replay is bit-identical
     to the eager step (the calls record no memset nodes)."""
     case = W.make_case(f"graph_{kv}", 310, P(32, 8, 128, kv=kv, window=0), [100, 700, 1500, 33],
@@ -510,9 +512,13 @@ def test_decode_step_replays_in_a_graph(kv):
     op = torch.zeros((B, Hq, ms, D), device="cuda")
     lp = torch.zeros((B, Hq, ms), device="cuda")
     out = torch.zeros((B, Hq, D), device="cuda")
+    ctr = torch.zeros(B * case.p.num_kv_heads, dtype=torch.int32, device="cuda")
 
     def step():
         pfa.kv_write(g.desc, g.pool, kn, vn, cun, g.seq_lens, g.bt)
+        if fused:
+            pfa.paged_attn_decode_fused(g.desc, g.pool, g.q, g.bt, g.seq_lens, max_len, S, ms, op, lp, ctr, out)
+            return
         pfa.paged_attn_decode(g.desc, g.pool, g.q, g.bt, g.seq_lens, max_len, S, ms, o_part=op, lse_part=lp)
         pfa.paged_attn_combine(g.desc, op, lp, g.seq_lens, S, ms, out)
 
@@ -535,5 +541,7 @@ def test_decode_step_replays_in_a_graph(kv):
         graph.replay()
         torch.cuda.synchronize()
         assert torch.equal(out, ref), f"replay {i} differs from the eager step"
+        if fused:
+            assert not ctr.any(), "the fused decode leaves its counters at zero"
     assert_close(ref.cpu().numpy(), O.decode(case.q, oracle_pool(case), case.block_table, case.seq_lens, case.p),
-                 tol_of(case), f"graph step ({kv})")
+                 tol_of(case), f"graph step ({kv}, fused={fused})")
