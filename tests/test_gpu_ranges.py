@@ -156,12 +156,17 @@ V_MAG_CASES = [
 ]
 
 
+V_MAG_SHAPES = [(32, 4, 128), (64, 8, 64)]   # G = 8 at D 128 (head-pair scores) and at D 64
+
+
+@pytest.mark.parametrize("shape", V_MAG_SHAPES, ids=["d128", "d64"])
 @pytest.mark.parametrize("ci", range(len(V_MAG_CASES)), ids=[c[0] for c in V_MAG_CASES])
-def test_decode_int8_value_magnitudes(ci):
-    """32 q / 4 KV heads, D 128, INT8: the output meets 3e-2 relative to its own
-    magnitude (max |ref|), with no overflow or flush of the weights."""
+def test_decode_int8_value_magnitudes(ci, shape):
+    """G = 8, INT8 (32 q / 4 KV heads at D 128, 64 / 8 at D 64): the output meets 3e-2
+    relative to its own magnitude (max |ref|), with no overflow or flush of the weights."""
     name, mags = V_MAG_CASES[ci]
-    case = W.make_case(f"vm_{name}", 480 + ci, P(32, 4, 128, kv="int8", seed=ci), [40, 700, 2100],
+    Hq, Hkv, D = shape
+    case = W.make_case(f"vm_{name}_{D}", 480 + ci + D, P(Hq, Hkv, D, kv="int8", seed=ci), [40, 700, 2100],
                        [1, 1, 1], outlier_frac=0.01, v_mags=mags)
     g = GpuCase(case)
     ref = O.decode(case.q, oracle_pool(case), case.block_table, case.seq_lens, case.p)
@@ -170,7 +175,8 @@ def test_decode_int8_value_magnitudes(ci):
         got = g.decode(split_keys=S)
         assert np.all(np.isfinite(got)), f"value magnitudes {name} S={S}: non-finite output"
         max_abs, rel = errors(got, ref)
-        print(f"value magnitudes {name} S={S}: max_abs/scale={max_abs / scale:.3e} rel_l2={rel:.3e}", flush=True)
+        print(f"value magnitudes {name} D={D} S={S}: max_abs/scale={max_abs / scale:.3e} rel_l2={rel:.3e}",
+              flush=True)
         assert max_abs <= INT8_TOL["max_abs"] * scale
         # per sequence, against its own magnitude (the mixed case spans 8 decades)
         for b in range(case.batch):
