@@ -709,7 +709,8 @@ void decode_kernel(DecodeArgs a, const int32_t* __restrict__ block_table) {
                 if (sub % HG == 0) p_buf[pb][i * KPL + kg][myhead] = pv;
             }
         } else {
-            // the weights of keys (i, i+1) as one bf16 pair, at [i/2][kg][head]
+            // the weights of keys (i, i+1) as one pair (BF16: bf16; INT8: fp16 scaled by
+            // 2^-vexp), at [i/2][kg][head]
             uint32_t* pp_buf = reinterpret_cast<uint32_t*>(&p_buf[pb][0][0]);
             if constexpr (JOINT) {
                 // lane t weighs group 2i + t; lane 0 of the pair packs both
@@ -727,13 +728,10 @@ void decode_kernel(DecodeArgs a, const int32_t* __restrict__ block_table) {
             for (int i = 0; i < (JOINT ? 0 : NLOAD); i += 2) {
                 const float p0 = fast_exp2(s[i] - m_run), p1 = fast_exp2(s[i + 1] - m_run);
                 uint32_t pr;
-                if constexpr (VCOL) {
+                if constexpr (VCOL) {   // (every paired INT8 build)
                     l_run += p0 + p1;
                     pr = pack_f16_rne(p0 * ldexpf(vsl[i], -vexp), p1 * ldexpf(vsl[i + 1], -vexp));
                     wsum = __builtin_amdgcn_fdot2(as_f16x2(pr), as_f16x2(0x3C003C00u), wsum, false);
-                } else if constexpr (INT8) {
-                    l_run += p0 + p1;
-                    pr = pack_bf16_rne(p0 * vsl[i], p1 * vsl[i + 1]);
                 } else {
                     pr = pack_bf16_rne(p0, p1);
                     l_run = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(pr), as_bf16x2(0x3F803F80u), l_run, false);
