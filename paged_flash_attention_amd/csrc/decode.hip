@@ -8,8 +8,9 @@
 // vector.  It also loads 32-key tiles and each half of the head dimension
 // separately, so the INT8 kernel stays spill-free.
 //
-// MI355X design.  The kernel is HBM-bound, and each K/V element is used by exactly
-// one lane group, so K/V go straight from HBM to registers:
+// MI355X design.  The kernel is HBM-bound (INT8 at G = 8: bound by VALU issue), and
+// each K/V element is used by exactly one lane group, so K/V go straight from HBM to
+// registers (INT8 at G = 8: straight into a 2-stage LDS ring, below):
 //  * One wave per (split, KV head, sequence) streams the split's pages, with the
 //    next page always in flight.  The grid is 1-D with the KV head fastest, then
 //    the split, then the sequence: workgroup i runs on XCD i % 8, so each XCD
@@ -31,30 +32,39 @@
 //    pairs, the codes as 1152 + c (one byte permute per two codes builds the fp16
 //    words 0x64uu = 1024 + u, u = c + 128), and 1152*sum(q) is subtracted from
 //    the dot.  q is scaled per head by a power of two into fp16's range (exact
-//    for every element within 2^28 of the head's largest).  With key smoothing (keys stored as k/s per channel, the "INT8 KV
-//    cache" section's smoothing by the key norm's weight, s taken as a power of
-//    two), q is first scaled by s, which is exact too.
+//    for every element within 2^28 of the head's largest); at G = 8 the key
+//    groups of a wave share that conversion through LDS.  With key smoothing
+//    (keys stored as k/s per channel, the "INT8 KV cache" section's smoothing by
+//    the key norm's weight, s taken as a power of two), q is first scaled by s,
+//    which is exact too.
 //    A lane's partial dots for the G heads go through a transposed butterfly over
 //    the LPK lanes, on DPP moves only (group_reduce.h).  Slot j of a lane holds
 //    head (j ^ myhead), so each stage adds a partner's slots to its own lower half
 //    with no selects, and ends with the lane holding its own head's full score.
+//    INT8 at G = 8, D = 128 (two lanes per head) runs it over two keys at once,
+//    so the two lanes of a head end on different keys and each scores half.
 //  * The softmax max is taken per page and the rescale is lazy with headroom: o
 //    and l are rescaled only when some head's max exceeds the reference max by
 //    more than 8 (log2 units), so weights stay <= 2^8.  At G = 8 a rescale on
 //    every growth ran on most of a split's first pages (INT8 at batch 8 x 32768:
-//    92 -> 85 us).  The weights p are shared within the wave through LDS.
+//    92 -> 85 us).  (INT8 at G = 8 compares each score with its head's threshold
+//    and reduces the page max across lanes only when one passes.)  The weights p
+//    are shared within the wave through LDS.
 //  * p.v: for G <= 4, fp32 FMAs on the lane's 8 elements for all G heads.  For
 //    G = 8, the VALU budget forces dot2 on key pairs from two loads.  The lane
-//    that computes a head's weights w (p, or p*scale_v for INT8) for two keys
-//    rounds them to a bf16 pair once (nearest even; bf16 has fp32's range, so no
-//    weight can overflow or flush) and shares the pair through LDS:
-//      - BF16: the (v_a, v_b) pairs are built by v_perm; l sums the same rounded
-//        weights (a dot2 with (1, 1)), so numerator and denominator agree;
-//      - INT8: by columns.  The page's V codes go through LDS, and each lane owns
+//    that computes a head's weights w for two keys rounds them to a pair once
+//    (nearest even) and shares the pair through LDS:
+//      - BF16: w = p as a bf16 pair; the (v_a, v_b) pairs are built by v_perm; l
+//        sums the same rounded weights (a dot2 with (1, 1)), so numerator and
+//        denominator agree;
+//      - INT8: by columns.  The page's V codes sit in LDS, and each lane owns
 //        the columns d = lane + 64c of all 16 keys (transposed 8-bit reads), so
 //        its o is 8 heads x D/64 columns instead of 8 heads x 8 elements of its
-//        key group: 205 -> 159 registers, 3 waves per SIMD (83 -> 77 us at batch
-//        8 x 32768).  The codes enter as signed bf16 (exact).
+//        key group (205 -> 159 registers).  The codes enter as the keys do, fp16
+//        1152 + c, against w = p*scale_v*2^-vexp as an fp16 pair: vexp is a
+//        wave-uniform exponent that follows the largest value scale, so w < 2^15
+//        always fits (see vexp below), and 1152 times the sum of the rounded
+//        weights leaves at the end.
 //  * At the end of a split each wave reduces its partial o across key groups (INT8
 //    at G = 8: nothing to reduce) and writes o/l with lse = ln(sum e^s) (split
 //    mode), or the final output with the sink (unsplit mode).
