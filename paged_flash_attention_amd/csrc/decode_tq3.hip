@@ -85,37 +85,6 @@ __global__ __launch_bounds__(kWave) void decode_tq3_kernel(DecodeArgs a, Tq3Book
         hi = min(hi, s0 + a.split_keys);
     }
 
-    // rotated query H_D q / D: in head order across the L lanes of a key group,
-    // then re-read in slot order (slot j = head j ^ myhead)
-    float qr[G][8];
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-        const uint4 v = *reinterpret_cast<const uint4*>(a.q + (row0 + h) * D + sub * 8);
-        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-        float x[8];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            x[2 * i] = bf16_lo(w[i]);
-            x[2 * i + 1] = bf16_hi(w[i]);
-        }
-        fwht_lanes<L>(x, sub);
-        if (kr == 0) {
-            float4* d = reinterpret_cast<float4*>(&q_lds[h][sub * 8]);
-            d[0] = make_float4(x[0] * kInvD, x[1] * kInvD, x[2] * kInvD, x[3] * kInvD);
-            d[1] = make_float4(x[4] * kInvD, x[5] * kInvD, x[6] * kInvD, x[7] * kInvD);
-        }
-    }
-    if (lane < 8) lv[lane] = tq3_level_of(lane, bk);
-    __syncthreads();
-#pragma unroll
-    for (int j = 0; j < G; ++j) {
-        const float4* s4 = reinterpret_cast<const float4*>(&q_lds[j ^ myhead][sub * 8]);
-        const float4 x0 = s4[0], x1 = s4[1];
-        qr[j][0] = x0.x; qr[j][1] = x0.y; qr[j][2] = x0.z; qr[j][3] = x0.w;
-        qr[j][4] = x1.x; qr[j][5] = x1.y; qr[j][6] = x1.z; qr[j][7] = x1.w;
-    }
-    const float c2 = a.sm_scale * kLog2e;      // scores in log2 units
-
     const int p0 = lo / kPage, p1 = (hi - 1) / kPage;
     const int32_t* bt = block_table + (int64_t)b * a.bt_stride;
     const uint8_t* kpool = static_cast<const uint8_t*>(a.k_pool);
@@ -143,6 +112,47 @@ __global__ __launch_bounds__(kWave) void decode_tq3_kernel(DecodeArgs a, Tq3Book
         vs[r] = __ldg(a.v_scale + vec);
     };
 
+    // rotated query H_D q / D.  The R key rows of the wave would each rotate the
+    // same G heads, so row r rotates heads r, r + R, ... (in head order, across its
+    // L lanes) and the wave shares them through LDS; each lane then reads its slots
+    // (slot j = head j ^ myhead).  The first page's loads go out before, so the
+    // rotation runs while they are in flight.
+    {
+        const int64_t blk = page_block(p0);
+#pragma unroll
+        for (int r = 0; r < NS; ++r) load_step(blk, r);
+    }
+    float qr[G][8];
+    constexpr int HPR = (G + R - 1) / R;      // heads per key row
+#pragma unroll
+    for (int e = 0; e < HPR; ++e) {
+        const int h = e * R + kr;
+        if (h < G) {   // (uniform within a key row, whose L lanes run the rotation together)
+            const uint4 v = *reinterpret_cast<const uint4*>(a.q + (row0 + h) * D + sub * 8);
+            const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+            float x[8];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                x[2 * i] = bf16_lo(w[i]);
+                x[2 * i + 1] = bf16_hi(w[i]);
+            }
+            fwht_lanes<L>(x, sub);
+            float4* d = reinterpret_cast<float4*>(&q_lds[h][sub * 8]);
+            d[0] = make_float4(x[0] * kInvD, x[1] * kInvD, x[2] * kInvD, x[3] * kInvD);
+            d[1] = make_float4(x[4] * kInvD, x[5] * kInvD, x[6] * kInvD, x[7] * kInvD);
+        }
+    }
+    if (lane < 8) lv[lane] = tq3_level_of(lane, bk);
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < G; ++j) {
+        const float4* s4 = reinterpret_cast<const float4*>(&q_lds[j ^ myhead][sub * 8]);
+        const float4 x0 = s4[0], x1 = s4[1];
+        qr[j][0] = x0.x; qr[j][1] = x0.y; qr[j][2] = x0.z; qr[j][3] = x0.w;
+        qr[j][4] = x1.x; qr[j][5] = x1.y; qr[j][6] = x1.z; qr[j][7] = x1.w;
+    }
+    const float c2 = a.sm_scale * kLog2e;      // scores in log2 units
+
     float o[G][8];
 #pragma unroll
     for (int g = 0; g < G; ++g)
@@ -151,11 +161,6 @@ __global__ __launch_bounds__(kWave) void decode_tq3_kernel(DecodeArgs a, Tq3Book
     float m_run = -INFINITY;   // running max (log2 units) of this lane's head
     float l_run = 0.0f;        // this lane's share of sum 2^(s - m_run) (its row's keys, its head)
 
-    {
-        const int64_t blk = page_block(p0);
-#pragma unroll
-        for (int r = 0; r < NS; ++r) load_step(blk, r);
-    }
     for (int p = p0; p <= p1; ++p) {
         const bool more = p < p1;
         const int64_t nblk = more ? page_block(p + 1) : 0;
