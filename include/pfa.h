@@ -231,6 +231,14 @@ pfa_status pfa_attn_input(const pfa_attn_desc* desc, const pfa_kv_pool* pool,
  *   A TQ3 pool is attended as the cache it stands for (pfa_kv_dtype).  The kernel
  *   works in the rotated domain: q . x^ = s * ((H_D q / D) . c), and the split's
  *   sum of p * s * c is rotated back by H_D / D at its end.
+ *
+ *   Arithmetic: scores and sums in fp32.  An INT8 pool meets q in fp16 after a
+ *   per-head power-of-two scale (exact for every element within 2^28 of its head's
+ *   largest).  At G = 8 the weights of two keys are rounded to a pair for a dot2:
+ *   bf16 for BF16 pools; for INT8 pools fp16 p * scale_v * 2^-e, with e a power of
+ *   two that follows the split's largest value scale, so no weight overflows, and a
+ *   weight's rounding error is at most 2^-11 of it, or 2^-25 * 2^e for the keys whose
+ *   value scale is more than about 2^21 below that largest one.
  */
 pfa_status pfa_paged_attn_decode(const pfa_attn_desc* desc, const pfa_kv_pool* pool,
                                  const void* q, const int32_t* block_table, int32_t bt_stride,
