@@ -236,9 +236,10 @@ pfa_status pfa_attn_input(const pfa_attn_desc* desc, const pfa_kv_pool* pool,
  *   per-head power-of-two scale (exact for every element within 2^28 of its head's
  *   largest).  At G = 8 the weights of two keys are rounded to a pair for a dot2:
  *   bf16 for BF16 pools; for INT8 pools fp16 p * scale_v * 2^-e, with e a power of
- *   two that follows the split's largest value scale, so no weight overflows, and a
- *   weight's rounding error is at most 2^-11 of it, or 2^-25 * 2^e for the keys whose
- *   value scale is more than about 2^21 below that largest one.
+ *   two that follows the split's largest value scale, so no weight overflows; a
+ *   weight's rounding error is at most 2^-11 of it, or 2^-25 * 2^e in absolute terms
+ *   where p * scale_v is more than about 2^17 below that largest scale (an fp16
+ *   subnormal).
  */
 pfa_status pfa_paged_attn_decode(const pfa_attn_desc* desc, const pfa_kv_pool* pool,
                                  const void* q, const int32_t* block_table, int32_t bt_stride,
