@@ -10,11 +10,6 @@
 
 #include "pfa_device.h"
 
-namespace pfa {
-// INT8 decode at 8 query heads per KV head, on the matrix cores (decode_mfma.hip).
-hipError_t launch_decode_int8_mfma(const DecodeArgs& a, int head_dim, hipStream_t s);
-}  // namespace pfa
-
 namespace {
 
 thread_local int32_t g_last_hip_error = 0;
@@ -320,8 +315,6 @@ pfa_status decode_like(const pfa_attn_desc* desc, const pfa_kv_pool* pool, const
     PFA_TRY(bounds_word_ptr(&a.err));
     if (desc->kv_dtype == PFA_KV_TQ3)
         return hip_status(pfa::launch_decode_tq3(a, desc->head_dim, tq3_book(), (hipStream_t)stream));
-    if (desc->kv_dtype == PFA_KV_INT8 && desc->num_q_heads == 8 * desc->num_kv_heads)
-        return hip_status(pfa::launch_decode_int8_mfma(a, desc->head_dim, (hipStream_t)stream));
     return hip_status(pfa::launch_decode(a, desc->head_dim, desc->kv_dtype == PFA_KV_INT8,
                                          (hipStream_t)stream));
 }

@@ -280,6 +280,8 @@ struct PrefillArgs {
 hipError_t launch_kv_write(const KvWriteArgs& a, int kv_dtype, hipStream_t s);
 hipError_t launch_attn_input(const AttnInputArgs& a, int head_dim, bool int8, hipStream_t s);
 hipError_t launch_decode(const DecodeArgs& a, int head_dim, bool int8, hipStream_t s);
+// INT8 at 8 query heads per KV head, on the matrix cores (launch_decode calls it)
+hipError_t launch_decode_int8_mfma(const DecodeArgs& a, int head_dim, hipStream_t s);
 hipError_t launch_decode_tq3(const DecodeArgs& a, int head_dim, const Tq3Book& bk, hipStream_t s);
 hipError_t launch_combine(const CombineArgs& a, int head_dim, hipStream_t s);
 hipError_t launch_prefill(const PrefillArgs& a, int head_dim, hipStream_t s);

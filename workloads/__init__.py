@@ -308,12 +308,12 @@ def key_norm_weight(seed: int, head_dim: int, n_large: int = 4, large: float = 8
 
 def decode_int8_qwen30b(seed=4, batch=8, ctx=32768, smooth=False):
     """Qwen3-30B-A3B attention shape (32 q / 4 KV heads, D 128), INT8 KV, batch 8 at
-    32768 positions; raw K/V N(0,1) with 1% outliers at +-8.  ``smooth``: keys
+    32768 positions, 1024-key splits; raw K/V N(0,1) with 1% outliers at +-8.  ``smooth``: keys
     shaped by a synthetic key-norm weight and the pool smoothing keys by it."""
     p = AttnParams(32, 4, 128, kv_dtype="int8")
     name = f"decode_int8_batch{batch}_ctx{ctx}" + ("_smooth" if smooth else "")
     return make_case(name, seed, p, np.full(batch, ctx, np.int32), np.ones(batch, np.int32),
-                     outlier_frac=0.01, split_keys=256,
+                     outlier_frac=0.01, split_keys=1024,
                      key_weight=key_norm_weight(seed + 50, 128) if smooth else None)
 
 
