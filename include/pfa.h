@@ -234,9 +234,11 @@ pfa_status pfa_attn_input(const pfa_attn_desc* desc, const pfa_kv_pool* pool,
  *
  *   Arithmetic: scores and sums in fp32.  An INT8 pool meets q in fp16 after a
  *   per-head power-of-two scale (exact for every element within 2^28 of its head's
- *   largest).  At G = 8 the weights of two keys are rounded to a pair for a dot2:
- *   bf16 for BF16 pools; for INT8 pools fp16 p * scale_v * 2^-e, with e a power of
- *   two that follows the split's largest value scale, so no weight overflows; a
+ *   largest).  At G = 8 the weights are rounded once before the p.v products: to
+ *   bf16 pairs for BF16 pools (dot2 on key pairs); for INT8 pools, whose q.k and p.v
+ *   run as fp16 matrix products with fp32 accumulation, to fp16 p * scale_v * 2^-e,
+ *   with e a power of two that follows the split's largest value scale, so no
+ *   weight overflows; a
  *   weight's rounding error is at most 2^-11 of it, or 2^-25 * 2^e in absolute terms
  *   where p * scale_v is more than about 2^17 below that largest scale (an fp16
  *   subnormal).
